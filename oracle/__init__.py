@@ -1,0 +1,51 @@
+"""CPU oracle for the W4A16 group-quantised linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
+bench's CPU-baseline leg may import or run anything in this package; the
+product path (the C-ABI library and its Python binding) never does, and it
+shares no code, table or helper with it.
+
+What it computes, in plain numpy float64 (slow and obviously correct):
+
+* ``rtn_quantize``   asymmetric round-to-nearest group quantiser,
+                     q = round(w/S) + Z, w ~ (q - Z)*S, 4-bit codes, binary16
+                     scale and 4-bit zero per group of input channels
+                     ("LLM Quantization: A Deep Dive...", The Math of
+                     Quantization; "LLM Quantization: INT8, GPTQ, and AWQ
+                     Explained", What quantization actually does).
+* ``awq_scales`` / ``awq_fold_weights`` / ``awq_fold_activations``
+                     the AWQ per-input-channel scale s = mean|X|^alpha and its
+                     fold W*diag(s), x*diag(1/s) ("AWQ + GPTQ Quantization, in
+                     depth", The two algorithms, compactly).
+* ``act_order``      GPTQ act-order group assignment g_idx from the calibration
+                     activations (same page and section).
+* ``pack_codes`` / ``unpack_codes`` / ``pack_zeros`` / ``unpack_zeros``
+                     eight 4-bit values per 32-bit word.
+* ``dequant`` / ``linear``   W^ = (q - Z)*S and y = x W^T in float64.
+* ``layer_bytes`` / ``bits_per_weight``   storage cost of a packed layer.
+
+Pins (tests/test_oracle_*.py, run without a GPU): the S/2 round-trip bound,
+code/zero ranges, idempotence, exact brute force with ``fractions.Fraction`` on
+small tiles, hand-derived worked groups (tests/golden), the pages' storage
+figures (bits per weight at group 128, the 1.5B-model byte budget), the exact
+invariance of the AWQ fold, unit-vector and all-ones probes of the matmul, and
+known-answer packed words.  Every function here is pinned; none is "parity
+unpinned".
+"""
+
+from .quant import (round_half_even, fp16_ceil, group_index, rtn_quantize,
+                    awq_scales, awq_fold_weights, awq_fold_activations,
+                    act_order_h, act_order)
+from .packing import (pack_codes, unpack_codes, pack_zeros, unpack_zeros,
+                      sorted_k_order, pack_codes_act_order)
+from .layer import dequant, dequant_fp16, linear, rel_err
+from .storage import layer_bytes, bits_per_weight
+
+__all__ = [
+    "round_half_even", "fp16_ceil", "group_index", "rtn_quantize",
+    "awq_scales", "awq_fold_weights", "awq_fold_activations", "act_order_h", "act_order",
+    "pack_codes", "unpack_codes", "pack_zeros", "unpack_zeros",
+    "sorted_k_order", "pack_codes_act_order",
+    "dequant", "dequant_fp16", "linear", "rel_err",
+    "layer_bytes", "bits_per_weight",
+]

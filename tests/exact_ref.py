@@ -1,0 +1,105 @@
+"""Exact brute-force references used to pin the oracle (tests only).
+
+Everything here works in exact rational arithmetic (``fractions.Fraction``) and
+by exhaustive search, on tiles small enough for pure-Python loops.  It imports
+nothing from the oracle: it restates the definitions independently, by search
+instead of by closed-form rounding.
+
+* scale: the smallest binary16 value that is >= range/15, found by scanning the
+  sorted list of all positive finite binary16 values.
+* zero point: the integer z in [0, 15] nearest to -w_lo/S (ties to even z).
+* code: the grid index j in [0, 15] whose grid point (j - Z)*S is nearest to w
+  (ties to even j - Z, the rounding of torch.round).
+"""
+
+from __future__ import annotations
+
+import bisect
+from fractions import Fraction
+
+import numpy as np
+
+_POS_FP16 = None
+
+
+def positive_fp16() -> list:
+    """All positive finite binary16 values as exact Fractions, ascending."""
+    global _POS_FP16
+    if _POS_FP16 is None:
+        bits = np.arange(1, 0x7C00, dtype=np.uint16)
+        _POS_FP16 = [Fraction(float(v)) for v in bits.view(np.float16)]
+    return _POS_FP16
+
+
+def fp16_ceil_exact(v: Fraction) -> Fraction:
+    vals = positive_fp16()
+    i = bisect.bisect_left(vals, v)
+    return vals[i]
+
+
+def _nearest_int_in(lo: int, hi: int, target: Fraction, parity_offset: int = 0) -> int:
+    """Integer j in [lo, hi] nearest to target; ties go to even (j - parity_offset)."""
+    best = None
+    for j in range(lo, hi + 1):
+        d = abs(Fraction(j) - target)
+        key = (d, (j - parity_offset) % 2)
+        if best is None or key < best[0]:
+            best = (key, j)
+    return best[1]
+
+
+def quantize_group_exact(ws):
+    """Exact RTN of one group (list of Fractions) -> (S, Z, [q...])."""
+    lo = min([Fraction(0)] + list(ws))
+    hi = max([Fraction(0)] + list(ws))
+    if lo == hi:
+        return Fraction(1), 0, [0] * len(ws)
+    S = fp16_ceil_exact((hi - lo) / 15)
+    Z = _nearest_int_in(0, 15, -lo / S)
+    qs = []
+    for w in ws:
+        # grid point (j - Z)*S nearest to w  <=>  j nearest to w/S + Z
+        qs.append(_nearest_int_in(0, 15, w / S + Z, parity_offset=Z))
+    return S, Z, qs
+
+
+def quantize_exact(w: np.ndarray, group_size: int, g_idx=None, in_scale=None):
+    """Exact RTN of a small matrix; same return shapes as the oracle (but Fractions
+    for the scales).  in_scale multiplies the float64 columns (its float64
+    products are what gets quantised, as in the oracle's definition)."""
+    N, K = w.shape
+    gid = (np.arange(K) // group_size) if g_idx is None else np.asarray(g_idx)
+    G = K // group_size
+    W = w.astype(np.float64)
+    if in_scale is not None:
+        W = W * np.asarray(in_scale, dtype=np.float64)[None, :]
+    codes = np.zeros((N, K), dtype=np.uint8)
+    S = [[None] * N for _ in range(G)]
+    Z = np.zeros((G, N), dtype=np.uint8)
+    for n in range(N):
+        for gam in range(G):
+            ks = [k for k in range(K) if gid[k] == gam]
+            s, z, qs = quantize_group_exact([Fraction(float(W[n, k])) for k in ks])
+            S[gam][n] = s
+            Z[gam, n] = z
+            for k, q in zip(ks, qs):
+                codes[n, k] = q
+    return codes, S, Z
+
+
+def linear_exact(x: np.ndarray, codes, S, Z, group_size: int, g_idx=None):
+    """y[m][n] = sum_k x[m][k] * (q[n][k] - Z[g(k)][n]) * S[g(k)][n], exact triple loop.
+    S may be Fractions or floats (binary16 values)."""
+    M, K = x.shape
+    N = codes.shape[0]
+    gid = (np.arange(K) // group_size) if g_idx is None else np.asarray(g_idx)
+    y = [[Fraction(0)] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                g = int(gid[k])
+                s = S[g][n] if isinstance(S, list) else Fraction(float(S[g, n]))
+                acc += Fraction(float(x[m, k])) * (int(codes[n, k]) - int(Z[g, n])) * s
+            y[m][n] = acc
+    return y
