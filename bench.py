@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Bench of the W4A16 group-quantised linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--configs c3,c4,...]
+
+A step is one call of w4a16_gemm on the headline layer: the 70B-class MLP
+up-projection at decode batch one (M=1, K=8192, N=28672, group 128, asymmetric
+int4), whose metric is HBM throughput.  The other layer configurations (the
+1-4B decode layers, the batch sweep of the 70B layer, the M=2048 prefill GEMM and
+the act-order layout) are timed the same way and reported alongside, each against
+its own roofline.  Prints one JSON line.
+
+Timing: all inputs are resident in device memory before the timed region; the
+weights rotate over a pool of distinct copies larger than twice the 256 MB
+Infinity Cache, so every step streams its weights from HBM.  HIP events recorded on
+the launch stream bracket every launch (their average is the per-launch kernel
+time) and the whole timed region (whole-job time per step).
+
+Throughput figures use algorithmic bytes (packed codes, binary16 scales, packed
+zero points, the act-order permutation, x and y) and algorithmic flops 2*M*N*K.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak, published
+POOL_BYTES = 640 << 20         # > 2 x 256 MB Infinity Cache
+MAX_COPIES = 64
+METRIC = "W4A16 GEMV HBM GB/s (% of peak) at M=1; prefill GEMM TFLOP/s (% MFMA)"
+HEADLINE = ("c3", 1)
+SECONDARY = [("c1", 1), ("c2up", 1), ("c2down", 1), ("c3", 2), ("c3", 4), ("c3", 8), ("c3", 16),
+             ("c4", 2048), ("c5", 1), ("c5", 512)]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = ["w4a16_gemm_amd/csrc/kernels/nibbles.hpp", "w4a16_gemm_amd/csrc/kernels/gemv.hpp",
+                  "w4a16_gemm_amd/csrc/kernels/gemm.hpp", "w4a16_gemm_amd/csrc/kernels/aux.hpp",
+                  "w4a16_gemm_amd/csrc/device.hip"]
+
+
+def algo_bytes(cfg: wl.LayerConfig, M: int) -> int:
+    N, K, G = cfg.N, cfg.K, cfg.G
+    return N * K // 2 + 2 * G * N + G * N // 2 + (4 * K if cfg.act_order else 0) + 2 * M * K + 2 * M * N
+
+
+def algo_flops(cfg: wl.LayerConfig, M: int) -> int:
+    return 2 * M * cfg.N * cfg.K
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+# --- GPU leg (the library only) ---------------------------------------------------
+
+def prepare_layer(cfg: wl.LayerConfig, M_max: int):
+    """Quantise, pack and upload a layer with the library's own host entry points."""
+    import torch
+    import w4a16_gemm_amd as w4
+    dev = torch.device("cuda:0")
+    g = cfg.group_size
+    g_idx = s = None
+    if cfg.act_order or cfg.awq:
+        X = wl.calibration(cfg)
+        g_idx = w4.w4a16_act_order(X, g) if cfg.act_order else None
+        s = w4.w4a16_awq_scales(X) if cfg.awq else None
+    codes, S, Z = w4.w4a16_quantize(wl.weights(cfg), g, g_idx, s)
+    x = wl.activations(cfg, M_max)
+    if s is not None:
+        x = w4.w4a16_awq_fold_activations(x, s)
+    return {
+        "x": torch.from_numpy(x).to(dev),
+        "qweight": torch.from_numpy(w4.w4a16_pack(codes, g_idx, g)).to(dev),
+        "scales": torch.from_numpy(S).to(dev),
+        "qzeros": torch.from_numpy(w4.w4a16_pack_zeros(Z)).to(dev),
+        "g_idx": None if g_idx is None else torch.from_numpy(g_idx).to(dev),
+    }
+
+
+def time_layer(cfg: wl.LayerConfig, M: int, layer, steps: int, warmup: int):
+    import torch
+    import w4a16_gemm_amd as w4
+    lib = w4.lib()
+    dev = layer["x"].device
+    per_copy = algo_bytes(cfg, M) - 2 * M * cfg.K - 2 * M * cfg.N
+    copies = max(1, min(MAX_COPIES, -(-POOL_BYTES // per_copy)))
+    pool = [(layer["qweight"], layer["scales"], layer["qzeros"])]
+    for _ in range(copies - 1):
+        pool.append((layer["qweight"].clone(), layer["scales"].clone(), layer["qzeros"].clone()))
+    x = layer["x"][:M].contiguous()
+    y = torch.empty((M, cfg.N), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    gptr = None if layer["g_idx"] is None else layer["g_idx"].data_ptr()
+    args = [(x.data_ptr(), q.data_ptr(), s.data_ptr(), z.data_ptr(), gptr, cfg.group_size, M, cfg.N, cfg.K,
+             y.data_ptr(), stream.cuda_stream) for q, s, z in pool]
+
+    def launch(i):
+        rc = lib.w4a16_gemm(*args[i % len(args)])
+        if rc != 0:
+            raise RuntimeError(f"w4a16_gemm failed ({rc}): {lib.w4a16_last_error().decode()}")
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    # per-launch events (kernel time) ...
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        launch(warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_launch_ms = [a.elapsed_time(b) for a, b in ev]
+    # ... and the whole timed region without per-launch events (whole-job time)
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    r0.record(stream)
+    for i in range(steps):
+        launch(i)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    region_ms = r0.elapsed_time(r1)
+    del pool
+    return {
+        "copies": copies,
+        "kernel_us_mean": 1e3 * statistics.fmean(per_launch_ms),
+        "kernel_us_median": 1e3 * statistics.median(per_launch_ms),
+        "region_us_per_step": 1e3 * region_ms / steps,
+        "wall_us_per_step": 1e6 * wall_s / steps,
+    }
+
+
+def summarize(cfg, M, t):
+    us = t["kernel_us_mean"]
+    b = algo_bytes(cfg, M)
+    f = algo_flops(cfg, M)
+    out = {
+        "workload": f"{cfg.name}: {cfg.note}", "M": M, "N": cfg.N, "K": cfg.K, "group": cfg.group_size,
+        "act_order": cfg.act_order, "awq": cfg.awq,
+        "us_per_layer": round(us, 3), "us_median": round(t["kernel_us_median"], 3),
+        "region_us_per_step": round(t["region_us_per_step"], 3),
+        "algo_bytes": b, "algo_flops": f,
+        "GBps": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+        "TFLOPs": round(f / us / 1e6, 2), "mfma_frac": round(f / us / 1e6 / MFMA_F16_PEAK_TFLOPS, 4),
+        "weight_copies": t["copies"],
+    }
+    return out
+
+
+# --- CPU baseline (the oracle, as it stands) ----------------------------------------
+
+def cpu_baseline(cfg: wl.LayerConfig, rows: int, repeats: int = 3):
+    import oracle
+    sel = np.arange(rows)
+    w = wl.weights(cfg, sel)
+    codes, S, Z = oracle.rtn_quantize(w, cfg.group_size)
+    x = wl.activations(cfg, 1)
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        oracle.linear(x, codes, S, Z, cfg.group_size)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    sample_bytes = rows * cfg.K // 2 + 2 * cfg.G * rows + cfg.G * rows // 2 + 2 * cfg.K + 2 * rows
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        blas = 1
+    return {
+        "value": round(sample_bytes / t / 1e9, 4), "unit": "GB/s", "cores": blas, "kind": "oracle",
+        "sample": (f"float64 dequant + matmul (numpy) of the first {rows} of {cfg.N} output rows of the "
+                   f"{cfg.name} layer at M=1, median of {repeats}: {t:.2f} s; algorithmic bytes of the "
+                   f"sample / time. Elementwise dequant is single-threaded; BLAS used {blas} threads"),
+        "seconds_per_layer_extrapolated": round(t * cfg.N / rows, 2),
+    }
+
+
+def traffic_for(hash_now: str, key: str):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if data.get("kernel_hash") != hash_now:
+        return None
+    entry = data.get("entries", {}).get(key)
+    return None if entry is None else entry.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--configs", default="all", help="'all', 'headline' or a comma list like c3:1,c4:2048")
+    ap.add_argument("--cpu-rows", type=int, default=8192, help="oracle sample size (rows)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (see the sharding notes); "
+              "run it with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import w4a16_gemm_amd as w4
+    w4.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+
+    if args.configs == "all":
+        todo = [HEADLINE] + SECONDARY
+    elif args.configs == "headline":
+        todo = [HEADLINE]
+    else:
+        todo = []
+        for item in args.configs.split(","):
+            name, m = item.split(":")
+            todo.append((name, int(m)))
+
+    results = {}
+    layers = {}
+    for name, M in todo:
+        cfg = wl.CONFIGS[name]
+        if name not in layers:
+            layers.clear()
+            torch.cuda.empty_cache()
+            log(f"preparing {name} (N={cfg.N} K={cfg.K} g={cfg.group_size})")
+            layers[name] = prepare_layer(cfg, max(cfg.M_list))
+        steps = args.steps if (name, M) == HEADLINE else max(20, args.steps // 4)
+        log(f"timing {name} M={M}: {args.warmup} warmup + {steps} steps")
+        t = time_layer(cfg, M, layers[name], steps, args.warmup)
+        results[f"{name}:M{M}"] = summarize(cfg, M, t)
+        results[f"{name}:M{M}"]["_t"] = t
+        log(f"  {results[f'{name}:M{M}']['us_per_layer']} us")
+    layers.clear()
+
+    hname = f"{HEADLINE[0]}:M{HEADLINE[1]}"
+    if hname not in results:
+        print(json.dumps({"configs": {k: {kk: vv for kk, vv in v.items() if kk != "_t"} for k, v in results.items()}}))
+        return 0
+    head = results[hname]
+    hcfg = wl.CONFIGS[HEADLINE[0]]
+    t = head.pop("_t")
+    for v in results.values():
+        v.pop("_t", None)
+    khash = kernel_hash()
+
+    line = {
+        "metric": METRIC,
+        "value": round(head["algo_bytes"] / t["region_us_per_step"] / 1e3, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t["region_us_per_step"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded; shapes and distributions of the layer configurations)",
+        "config": {
+            "workload": ("70B-class MLP up-projection decode layer: M=1, K=8192, N=28672, group 128, asymmetric "
+                         "int4 weights (fp16 scale, 4-bit zero), fp16 activations, fp32 accumulation"),
+            "M": 1, "K": hcfg.K, "N": hcfg.N, "group_size": hcfg.group_size,
+            "weight_copies_rotated": head["weight_copies"],
+            "accumulate": "f32",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(head["algo_bytes"] / head["us_per_layer"] / 1e3, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(head["algo_bytes"] / head["us_per_layer"] / 1e3 / HBM_PEAK_GBS, 4),
+            "traffic": traffic_for(khash, hname),
+            "kernel": "gemv_m1_kernel",
+            "kernel_us_mean": head["us_per_layer"],
+            "algo_bytes_per_launch": head["algo_bytes"],
+        },
+        "kernel_hash": khash,
+        "configs": results,
+    }
+    pre = results.get("c4:M2048")
+    if pre:
+        line["prefill"] = {
+            "bound": "mfma", "achieved": pre["TFLOPs"], "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": pre["mfma_frac"], "us_per_layer": pre["us_per_layer"], "kernel": "gemm_mfma_kernel",
+            "traffic": traffic_for(khash, "c4:M2048"),
+        }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (cpu_baseline)")
+        line["cpu_baseline"] = cpu_baseline(hcfg, args.cpu_rows)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,173 @@
+/*
+ * w4a16.h -- C ABI of the W4A16 group-quantised linear layer for gfx950 (MI355X).
+ *
+ * The layer is y = x * W^T with W (out x in) stored as 4-bit codes q, one binary16
+ * scale S and one 4-bit zero point Z per group of input channels, and
+ *     W^[n][k] = (q[n][k] - Z[g(k)][n]) * S[g(k)][n]
+ * ("LLM Quantization: A Deep Dive into GPTQ, AWQ, and Post-Training Quantization",
+ * The Math of Quantization: q = round(x/S) + Z, x ~ (q - Z) * S).  The kernel loads
+ * the packed 4-bit weights, expands them in registers with the group's scale and
+ * zero point and multiplies them with 16-bit activations, accumulating in fp32
+ * ("AWQ + GPTQ Quantization, in depth", What W4A16 buys and why decoding gets
+ * faster).  A group is a run of group_size consecutive input channels of one output
+ * row ("How do GPTQ and AWQ differ when quantizing Llama weights to 4 bits?", The
+ * shared setting; FAQ on group_size 128), or, under GPTQ act order, the set of input
+ * channels k with g_idx[k] equal to the group's number ("AWQ + GPTQ Quantization, in
+ * depth", The two algorithms, compactly).
+ *
+ * Conventions for every entry point
+ *   - binary16 values travel as uint16_t bit patterns; the stream is a hipStream_t
+ *     passed as void* (NULL = the null stream).
+ *   - shapes: M rows of activations, N output features, K input features,
+ *     G = K / group_size groups per row.  Requirements: M, N, K > 0;
+ *     group_size in {32, 64, 128}; K % group_size == 0; N % 8 == 0.
+ *   - the caller owns every buffer.  The library keeps no pointer after a call
+ *     returns.  Host entry points are synchronous.  Device entry points are
+ *     asynchronous and stream-ordered: inputs must stay alive, and outputs are
+ *     valid, only once the stream has passed the call.
+ *   - every entry point returns a status (below); on failure nothing is launched
+ *     and w4a16_last_error() (thread-local) describes the cause.  No exception
+ *     crosses the ABI.  There is no silent fallback to a slower path: an argument
+ *     no kernel supports is an error ("AWQ + GPTQ Quantization, in depth",
+ *     Failure modes: kernel fallback).
+ *
+ * Layouts
+ *   x        binary16 [M][K], row-major                               (device)
+ *   y        binary16 [M][N], row-major, written once per element     (device)
+ *   scales   binary16 [G][N], row-major: scale of (group, output)     (device)
+ *   qzeros   int32 [G][N/8]: zero point of (group, n) in bits 4j..4j+3 of word
+ *            [group][n/8], j = n % 8                                  (device)
+ *   g_idx    int32 [K] or NULL: group of every input channel          (act order)
+ *   qweight  int32 buffer of w4a16_qweight_words(N, K, act_order) words, written by
+ *            w4a16_pack and read by the kernels.  Its internal layout is private to
+ *            this library and may change with W4A16_ABI_VERSION; read it back only
+ *            through w4a16_unpack.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A16_ABI_VERSION 1
+
+enum w4a16_status {
+  W4A16_OK = 0,
+  W4A16_ERR_INVALID_ARG = 1,  /* NULL pointer, non-positive size, K % group_size, N % 8,
+                                 a code or zero point above 15 */
+  W4A16_ERR_UNSUPPORTED = 2,  /* group_size not in {32, 64, 128} */
+  W4A16_ERR_BAD_GIDX = 3,     /* g_idx value outside [0, G), a group without exactly
+                                 group_size members, or a stored order that is not a
+                                 permutation */
+  W4A16_ERR_MISALIGNED = 4,   /* a device buffer not aligned to 16 bytes */
+  W4A16_ERR_HIP = 5           /* HIP launch or runtime error; text in w4a16_last_error */
+};
+
+/* W4A16_ABI_VERSION of the built library. */
+int w4a16_abi_version(void);
+
+/* Text of the last failure on the calling thread ("" if none).  The pointer stays
+ * valid until the thread's next call into the library. */
+const char* w4a16_last_error(void);
+
+/* Number of int32 words of the packed weight buffer: N*K/8, plus K when act_order is
+ * non-zero (the stored input-channel order follows the codes).  0 on bad sizes. */
+size_t w4a16_qweight_words(int N, int K, int act_order);
+
+/* ---------------------------------------------------------------------------------
+ * Offline steps, host memory, synchronous.
+ * ------------------------------------------------------------------------------ */
+
+/* Asymmetric 4-bit round-to-nearest group quantiser ("LLM Quantization: INT8, GPTQ,
+ * and AWQ Explained", What quantization actually does: find the range, pick a scale
+ * that spreads the grid across it, round to the nearest grid point; 16 levels at 4
+ * bits per Round-to-nearest, and where it falls apart).  Per (row n, group):
+ *   w_lo = min(0, min w), w_hi = max(0, max w)
+ *   S = smallest binary16 >= (w_hi - w_lo) / 15   (S = 1, Z = 0, q = 0 if w_hi == w_lo)
+ *   Z = clamp(round(-w_lo / S), 0, 15),  q = clamp(round(w / S) + Z, 0, 15)
+ * with round = half to even and all arithmetic in binary64.
+ *   w         binary16 [N][K] weights (out x in)
+ *   g_idx     int32 [K] group of each input channel, or NULL (group k / group_size)
+ *   in_scale  binary64 [K] per-input-channel factor s, or NULL: the weights quantised
+ *             are then w[n][k] * s[k] formed in binary64 (the AWQ fold, "AWQ + GPTQ
+ *             Quantization, in depth", The two algorithms, compactly)
+ *   codes     out uint8 [N][K];  scales out binary16 [G][N];  zeros out uint8 [G][N]
+ * Errors: INVALID_ARG, UNSUPPORTED, BAD_GIDX (also for in_scale <= 0 or not finite). */
+int w4a16_quantize(const uint16_t* w, int N, int K, int group_size, const int32_t* g_idx,
+                   const double* in_scale, uint8_t* codes, uint16_t* scales, uint8_t* zeros);
+
+/* AWQ per-input-channel scale s[k] = (mean over the T calibration tokens of |X[t][k]|)
+ * ** alpha ("AWQ + GPTQ Quantization, in depth", The two algorithms, compactly).  The
+ * mean is formed exactly and rounded once; alpha == 0.5 uses the correctly rounded
+ * square root.  A channel whose activations are all zero gets s = 1.
+ *   xcal binary16 [T][K] (host);  s out binary64 [K].   Errors: INVALID_ARG. */
+int w4a16_awq_scales(const uint16_t* xcal, int T, int K, double alpha, double* s);
+
+/* Activation side of the AWQ fold: x_out[m][k] = binary16(x[m][k] / s[k]), rounded
+ * once to nearest even ("How do GPTQ and AWQ differ...", AWQ: protect the salient
+ * channels).  Host memory; x_out may alias x.  Errors: INVALID_ARG. */
+int w4a16_awq_fold_activations(const uint16_t* x, int M, int K, const double* s, uint16_t* x_out);
+
+/* GPTQ act-order group assignment ("AWQ + GPTQ Quantization, in depth", The two
+ * algorithms, compactly: H = 2 X X^T; act order visits input channels by descending
+ * diag(H)).  Channels are ordered by descending sum_t X[t][k]^2 (computed exactly),
+ * ties by ascending k; the i-th channel in that order gets group i / group_size.
+ *   xcal binary16 [T][K] (host);  g_idx out int32 [K].
+ * Errors: INVALID_ARG, UNSUPPORTED. */
+int w4a16_act_order(const uint16_t* xcal, int T, int K, int group_size, int32_t* g_idx);
+
+/* Pack 4-bit codes into the library's weight buffer.
+ *   codes   uint8 [N][K], values 0..15, in the original input-channel order
+ *   g_idx   NULL (contiguous groups) or the act-order group of every input channel;
+ *           then each row is stored in group-sorted order (stable sort of k by
+ *           g_idx[k]) and that order follows the codes in the buffer
+ *   qweight out int32 [w4a16_qweight_words(N, K, g_idx != NULL)]
+ * Errors: INVALID_ARG, UNSUPPORTED, BAD_GIDX. */
+int w4a16_pack(const uint8_t* codes, const int32_t* g_idx, int group_size, int N, int K,
+               int32_t* qweight);
+
+/* Inverse of w4a16_pack: codes out uint8 [N][K] in the original input-channel order.
+ * g_idx must be non-NULL exactly when the buffer was packed with one (only its
+ * presence is used; the stored order is read from the buffer and checked).
+ * Errors: INVALID_ARG, UNSUPPORTED, BAD_GIDX. */
+int w4a16_unpack(const int32_t* qweight, const int32_t* g_idx, int group_size, int N, int K,
+                 uint8_t* codes);
+
+/* Zero points: zeros uint8 [G][N] (0..15) <-> qzeros int32 [G][N/8] (layout above).
+ * Errors: INVALID_ARG. */
+int w4a16_pack_zeros(const uint8_t* zeros, int G, int N, int32_t* qzeros);
+int w4a16_unpack_zeros(const int32_t* qzeros, int G, int N, uint8_t* zeros);
+
+/* ---------------------------------------------------------------------------------
+ * The layer, device memory, asynchronous on `stream`.
+ * ------------------------------------------------------------------------------ */
+
+/* y = x * W^T with W^ = (q - Z) * S, fp32 accumulation, y rounded once to binary16.
+ * All pointers are device pointers.  g_idx non-NULL selects the act-order layout
+ * (qweight must have been packed with that g_idx; the kernels read the stored order
+ * from qweight and gather x through it).  M == 1 runs the split-K GEMV; larger M the
+ * MFMA GEMM (which, under act order, first gathers x into stream-ordered scratch
+ * memory taken from and returned to the device's default memory pool).
+ * Environment: W4A16_DEBUG_CHECKS=1 also validates g_idx (synchronous copy);
+ * W4A16_FORCE_PATH=gemv|gemm selects a kernel family (for tests).
+ * Errors: INVALID_ARG, UNSUPPORTED, MISALIGNED, BAD_GIDX (debug only), HIP. */
+int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+               const int32_t* qzeros, const int32_t* g_idx, int group_size, int M, int N,
+               int K, uint16_t* y, void* stream);
+
+/* Debug/parity view of the weights: w_out[n][k] = binary16((q - Z) * S) in the
+ * original input-channel order, computed with the same device arithmetic that builds
+ * the GEMM's weight operand.  Device pointers.  Errors as w4a16_gemm. */
+int w4a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
+                  const int32_t* g_idx, int group_size, int N, int K, uint16_t* w_out,
+                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,206 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol, and its
+host-side (offline) entry points agree bit-exactly with the oracle.  Device entry
+points are only exercised on their argument checks (no kernel is launched here)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import w4a16_gemm_amd as w4
+import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = w4.lib()
+    declared = _declared_functions()
+    assert len(declared) == 13
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(w4.EXPORTS) == declared
+
+
+def test_abi_version():
+    assert w4.w4a16_abi_version() == 1
+
+
+def test_qweight_words():
+    assert w4.w4a16_qweight_words(16, 256, False) == 16 * 32
+    assert w4.w4a16_qweight_words(16, 256, True) == 16 * 32 + 256
+    assert w4.lib().w4a16_qweight_words(0, 256, 0) == 0
+
+
+# --- quantiser ------------------------------------------------------------------
+
+def _assert_same_quant(a, b):
+    assert np.array_equal(a[0], b[0])
+    assert np.array_equal(a[1].view(np.uint16), b[1].view(np.uint16))
+    assert np.array_equal(a[2], b[2])
+
+
+@pytest.mark.parametrize("name", list(wl.CONFIGS))
+def test_quantize_bit_exact_on_config_rows(name):
+    cfg = wl.CONFIGS[name]
+    rows = np.linspace(0, cfg.N - 1, 24).astype(np.int64)
+    w = wl.weights(cfg, rows)
+    g_idx = s = None
+    if cfg.act_order:
+        g_idx, _ = oracle.act_order(wl.calibration(cfg), cfg.group_size)
+    if cfg.awq:
+        s = oracle.awq_scales(wl.calibration(cfg))
+    _assert_same_quant(w4.w4a16_quantize(w, cfg.group_size, g_idx, s),
+                       oracle.rtn_quantize(w, cfg.group_size, g_idx, s))
+
+
+def test_quantize_bit_exact_on_special_groups():
+    import json
+    data = json.load(open(os.path.join(ROOT, "tests", "golden", "rtn_worked_groups.json")))
+    for grp in data["groups"]:
+        w = np.array(grp["w"], dtype=np.float16)
+        w = np.tile(w, (8, 32 // w.size + 1))[:, :32]
+        _assert_same_quant(w4.w4a16_quantize(w, 32), oracle.rtn_quantize(w, 32))
+    rng = np.random.default_rng(0)
+    for scale in (1e-6, 1e-3, 1.0, 300.0):       # subnormal scales up to large ones
+        w = (rng.standard_normal((16, 128)) * scale).astype(np.float16)
+        w[3, :32] = 0
+        w[4, 32:64] = np.abs(w[4, 32:64])
+        for g in (32, 64, 128):
+            _assert_same_quant(w4.w4a16_quantize(w, g), oracle.rtn_quantize(w, g))
+
+
+def test_awq_scales_and_fold_bit_exact():
+    cfg = wl.CONFIGS["c2up"]
+    X = wl.calibration(cfg)
+    s = w4.w4a16_awq_scales(X)
+    assert np.array_equal(s, oracle.awq_scales(X))
+    x = wl.activations(cfg, 1)
+    assert np.array_equal(w4.w4a16_awq_fold_activations(x, s).view(np.uint16),
+                          oracle.awq_fold_activations(x, s).view(np.uint16))
+    Xz = X[:, :64].copy()
+    Xz[:, 5] = 0
+    assert np.array_equal(w4.w4a16_awq_scales(Xz), oracle.awq_scales(Xz))
+    # alpha = 0.5 (the configurations' value) goes through the correctly rounded square
+    # root and is bit-exact; another alpha goes through pow(), which libm and numpy do
+    # not round identically, so it agrees to a few ulp only
+    np.testing.assert_allclose(w4.w4a16_awq_scales(Xz, 0.25), oracle.awq_scales(Xz, 0.25), rtol=4e-16)
+
+
+def test_act_order_bit_exact():
+    cfg = wl.CONFIGS["c5"]
+    X = wl.calibration(cfg)
+    assert np.array_equal(w4.w4a16_act_order(X, cfg.group_size), oracle.act_order(X, cfg.group_size)[0])
+    Xt = np.random.default_rng(1).standard_normal((16, 64)).astype(np.float16)
+    Xt[:, 10] = Xt[:, 3]
+    Xt[:, 40] = -Xt[:, 3]
+    assert np.array_equal(w4.w4a16_act_order(Xt, 32), oracle.act_order(Xt, 32)[0])
+
+
+# --- packing ---------------------------------------------------------------------
+
+def test_private_word_layout_known_answer():
+    codes = np.arange(8, dtype=np.uint8)[None, :].repeat(8, 0)
+    codes = np.concatenate([codes] * 4, axis=1)            # K = 32
+    words = w4.w4a16_pack(codes, None, 32).view(np.uint32)
+    # element e of a word sits in nibble (0, 4, 1, 5, 2, 6, 3, 7)[e]
+    assert int(words[0]) == 0x75316420
+    assert np.all(words == 0x75316420)
+    assert np.array_equal(w4.w4a16_pack(np.full((8, 32), 15, np.uint8), None, 32).view(np.uint32),
+                          np.full(32, 0xFFFFFFFF, np.uint32))
+
+
+@pytest.mark.parametrize("act", [False, True])
+@pytest.mark.parametrize("shape", [(8, 64, 32), (24, 256, 64), (40, 512, 128)])
+def test_pack_unpack_round_trip(shape, act):
+    N, K, g = shape
+    codes = wl.random_codes(N, K, seed=K + N)
+    g_idx = None
+    if act:
+        perm = np.random.default_rng(N).permutation(K)
+        g_idx = np.empty(K, np.int32)
+        g_idx[perm] = np.arange(K) // g
+    packed = w4.w4a16_pack(codes, g_idx, g)
+    assert packed.size == w4.w4a16_qweight_words(N, K, act)
+    assert np.array_equal(w4.w4a16_unpack(packed, g_idx, g, N, K), codes)
+    if act:
+        assert np.array_equal(packed[N * K // 8:], oracle.sorted_k_order(g_idx))
+
+
+def test_identity_gidx_packs_like_contiguous():
+    codes = wl.random_codes(16, 128, seed=3)
+    ident = (np.arange(128) // 32).astype(np.int32)
+    a = w4.w4a16_pack(codes, None, 32)
+    b = w4.w4a16_pack(codes, ident, 32)
+    assert np.array_equal(b[:a.size], a)
+    assert np.array_equal(b[a.size:], np.arange(128))
+
+
+def test_pack_zeros_matches_oracle_format():
+    z = wl.random_codes(12, 64, seed=9)          # [G][N]
+    q = w4.w4a16_pack_zeros(z)
+    assert np.array_equal(q, oracle.pack_zeros(z))
+    assert np.array_equal(w4.w4a16_unpack_zeros(q, 12, 64), z)
+
+
+# --- error codes -------------------------------------------------------------------
+
+def _status(fn, *args):
+    with pytest.raises(w4.W4A16Error) as e:
+        fn(*args)
+    return e.value.status
+
+
+def test_error_codes_host():
+    codes = wl.random_codes(8, 64, seed=1)
+    assert _status(w4.w4a16_pack, codes, None, 48) == w4.ERR_UNSUPPORTED
+    assert _status(w4.w4a16_pack, codes[:, :48], None, 32) == w4.ERR_INVALID_ARG   # K % g
+    assert _status(w4.w4a16_pack, codes[:4], None, 32) == w4.ERR_INVALID_ARG       # N % 8
+    bad = codes.copy()
+    bad[0, 0] = 16
+    assert _status(w4.w4a16_pack, bad, None, 32) == w4.ERR_INVALID_ARG
+    g_idx = (np.arange(64) // 32).astype(np.int32)
+    g2 = g_idx.copy()
+    g2[0] = 2
+    assert _status(w4.w4a16_pack, codes, g2, 32) == w4.ERR_BAD_GIDX               # out of range
+    g3 = g_idx.copy()
+    g3[0] = 1
+    assert _status(w4.w4a16_pack, codes, g3, 32) == w4.ERR_BAD_GIDX               # group sizes 31/33
+    packed = w4.w4a16_pack(codes, g_idx, 32)
+    packed[-1] = packed[-2]
+    assert _status(w4.w4a16_unpack, packed, g_idx, 32, 8, 64) == w4.ERR_BAD_GIDX   # not a permutation
+    w = np.zeros((8, 64), np.float16)
+    w[0, 0] = np.inf
+    assert _status(w4.w4a16_quantize, w, 32) == w4.ERR_INVALID_ARG
+    assert _status(w4.w4a16_quantize, np.zeros((8, 64), np.float16), 32, None, np.zeros(64)) == w4.ERR_INVALID_ARG
+    rc = w4.lib().w4a16_pack(bad.ctypes.data, None, 32, 8, 64, np.empty(64, np.int32).ctypes.data)
+    assert rc == w4.ERR_INVALID_ARG and "above 15" in w4.lib().w4a16_last_error().decode()
+
+
+def test_error_codes_device_argument_checks():
+    """Argument checks run before any HIP call, so they are testable without a GPU."""
+    lib = w4.lib()
+    buf = (ctypes.c_uint8 * 4096)()
+    base = (ctypes.addressof(buf) + 15) & ~15
+    ok = ctypes.c_void_p(base)
+    mis = ctypes.c_void_p(base + 2)
+    assert lib.w4a16_gemm(None, ok, ok, ok, None, 128, 1, 8, 128, ok, None) == w4.ERR_INVALID_ARG
+    assert lib.w4a16_gemm(ok, ok, ok, ok, None, 128, 0, 8, 128, ok, None) == w4.ERR_INVALID_ARG
+    assert lib.w4a16_gemm(ok, ok, ok, ok, None, 96, 1, 8, 192, ok, None) == w4.ERR_UNSUPPORTED
+    assert lib.w4a16_gemm(ok, ok, ok, ok, None, 128, 1, 12, 128, ok, None) == w4.ERR_INVALID_ARG
+    assert lib.w4a16_gemm(ok, ok, ok, ok, None, 128, 1, 8, 192, ok, None) == w4.ERR_INVALID_ARG
+    assert lib.w4a16_gemm(mis, ok, ok, ok, None, 128, 1, 8, 128, ok, None) == w4.ERR_MISALIGNED
+    assert lib.w4a16_dequant(ok, ok, ok, None, 64, 8, 128, mis, None) == w4.ERR_MISALIGNED
+    assert lib.w4a16_dequant(ok, None, ok, None, 64, 8, 128, ok, None) == w4.ERR_INVALID_ARG
+    assert lib.w4a16_gemm(mis, ok, ok, ok, None, 128, 1, 8, 128, ok, None) == w4.ERR_MISALIGNED
+    assert "aligned" in lib.w4a16_last_error().decode()

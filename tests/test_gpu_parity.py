@@ -1,0 +1,189 @@
+"""GPU parity of the HIP path against the oracle (needs an MI355X).
+
+Bars: codes, zero points and the act-order mapping bit-exact; the device weight view
+bit-exact against binary16((q - Z) * S); unit-vector probes bit-exact; outputs within
+max|y - y_ref| / rms(y_ref) <= 1e-2 (float64 reference of the quantised layer).
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import w4a16_gemm_amd as w4
+import workloads as wl
+from gpu_common import device, note, oracle_layer, product_layer, run_gemm, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+# Small layers that span several tiles of every kernel and end on a ragged tail.
+SMALL = [
+    # name, M, N, K, group, act_order
+    ("s1", 1, 264, 1536, 128, False),
+    ("s2", 1, 520, 3072, 64, False),
+    ("s3", 1, 136, 512, 32, False),
+    ("s4", 1, 1032, 8192, 128, False),
+    ("s5", 1, 328, 1024, 32, True),
+    ("s6", 3, 264, 1536, 128, False),
+    ("s7", 17, 520, 1024, 64, False),
+    ("s8", 37, 264, 768, 128, True),
+    ("s9", 130, 520, 1152, 32, False),
+    ("s10", 257, 776, 640, 128, False),
+    ("s11", 200, 264, 2048, 32, True),
+    ("s12", 1, 8, 96, 32, False),
+]
+
+
+def _small_cfg(name, M, N, K, g, act, idx):
+    return wl.custom_config(name, 100 + idx, K=K, N=N, group_size=g, M_list=(M,), act_order=act)
+
+
+@pytest.fixture(autouse=True)
+def _clear_env():
+    os.environ.pop("W4A16_FORCE_PATH", None)
+    yield
+    os.environ.pop("W4A16_FORCE_PATH", None)
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_small_layers_match_oracle(case):
+    import torch
+    name, M, N, K, g, act = SMALL[case]
+    cfg = _small_cfg(name, M, N, K, g, act, case)
+    note(f"small {name} M={M} N={N} K={K} g={g} act={act}")
+    prod = product_layer(cfg, M)
+    ref = oracle_layer(cfg, M, np.arange(N))
+    assert np.array_equal(prod["codes"], ref["codes"])
+    if act:
+        assert np.array_equal(prod["g_idx_np"], ref["g_idx"])
+    paths = ["gemv", "gemm"] if M == 1 else ["gemm"]
+    for path in paths:
+        os.environ["W4A16_FORCE_PATH"] = path
+        note(f"  path={path}")
+        y = run_gemm(prod).cpu().numpy()
+        err = oracle.rel_err(y, ref["y_ref"])
+        assert err <= TOL, (path, err)
+    # the device weight view is bit-exact
+    W16 = w4.w4a16_dequant(prod["qweight"], prod["scales"], prod["qzeros"], prod["g_idx"], g, K).cpu().numpy()
+    assert np.array_equal(W16.view(np.uint16), ref["W16"].view(np.uint16))
+    # the device-resident packed buffer unpacks to the oracle's codes
+    back = w4.w4a16_unpack(prod["qweight"].cpu().numpy(), prod["g_idx_np"], g, N, K)
+    assert np.array_equal(back, ref["codes"])
+
+
+@pytest.mark.parametrize("case", [0, 2, 4, 6, 7, 9])
+def test_unit_vector_probes_bit_exact(case):
+    """x = e_k selects column k of W^: y = binary16(W^[:, k]) exactly (one exact
+    product, exact fp32 sums of zeros, one rounding)."""
+    import torch
+    name, _, N, K, g, act = SMALL[case]
+    cfg = _small_cfg(name, 1, N, K, g, act, case)
+    ks = np.unique(np.concatenate([[0, K - 1, K // 2], np.random.default_rng(case).integers(0, K, 13)]))
+    E = wl.unit_vectors(K, ks)
+    prod = product_layer(cfg, 1)
+    ref = oracle_layer(cfg, 1, np.arange(N))
+    expect = ref["W16"][:, ks].T.copy()                       # [len(ks)][N]
+    xe = torch.from_numpy(E).to(device())
+    note(f"probe {name} gemm M={len(ks)}")
+    os.environ["W4A16_FORCE_PATH"] = "gemm"
+    y = run_gemm(prod, x=xe).cpu().numpy()
+    assert np.array_equal(y.view(np.uint16), expect.view(np.uint16))
+    os.environ["W4A16_FORCE_PATH"] = "gemv"
+    for i in range(len(ks)):
+        note(f"probe {name} gemv k={ks[i]}")
+        yi = run_gemm(prod, x=xe[i:i + 1].contiguous()).cpu().numpy()
+        assert np.array_equal(yi[0].view(np.uint16), expect[i].view(np.uint16)), ks[i]
+
+
+def test_all_ones_gives_row_sums():
+    import torch
+    cfg = _small_cfg("ones", 1, 520, 3072, 64, False, 50)
+    prod = product_layer(cfg, 1)
+    ref = oracle_layer(cfg, 1, np.arange(520), x=np.ones((1, 3072), np.float16))
+    ones = torch.ones((4, 3072), dtype=torch.float16, device=device())
+    for path, x in (("gemv", ones[:1]), ("gemm", ones)):
+        os.environ["W4A16_FORCE_PATH"] = path
+        note(f"all-ones {path}")
+        y = run_gemm(prod, x=x.contiguous()).cpu().numpy()
+        for row in y:
+            assert oracle.rel_err(row[None, :], ref["y_ref"]) <= TOL
+
+
+def test_identity_gidx_equals_contiguous_and_runs_are_deterministic():
+    import torch
+    cfg = _small_cfg("ident", 64, 264, 1024, 32, False, 51)
+    prod = product_layer(cfg, 64)
+    ident = torch.from_numpy((np.arange(1024) // 32).astype(np.int32)).to(device())
+    codes = prod["codes"]
+    qw_id = torch.from_numpy(w4.w4a16_pack(codes, ident.cpu().numpy(), 32)).to(device())
+    for M in (1, 64):
+        x = prod["x"][:M].contiguous()
+        note(f"identity g_idx M={M}")
+        a = w4.w4a16_gemm(x, prod["qweight"], prod["scales"], prod["qzeros"], None, 32)
+        b = w4.w4a16_gemm(x, qw_id, prod["scales"], prod["qzeros"], ident, 32)
+        c = w4.w4a16_gemm(x, prod["qweight"], prod["scales"], prod["qzeros"], None, 32)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+def test_device_errors_are_reported():
+    import torch
+    cfg = _small_cfg("err", 2, 264, 1024, 64, False, 52)
+    prod = product_layer(cfg, 2)
+    os.environ["W4A16_FORCE_PATH"] = "gemv"
+    with pytest.raises(w4.W4A16Error) as e:
+        run_gemm(prod)
+    assert e.value.status == w4.ERR_UNSUPPORTED
+    os.environ.pop("W4A16_FORCE_PATH")
+    raw = torch.empty(1024 * 2 + 8, dtype=torch.float16, device=device())
+    x_mis = raw[1:1 + 2 * 1024].view(2, 1024)
+    lib = w4.lib()
+    st = lib.w4a16_gemm(x_mis.data_ptr(), prod["qweight"].data_ptr(), prod["scales"].data_ptr(),
+                        prod["qzeros"].data_ptr(), None, 64, 2, 264, 1024,
+                        torch.empty(2, 264, dtype=torch.float16, device=device()).data_ptr(), None)
+    assert st == w4.ERR_MISALIGNED
+
+
+# --- the configurations at full size (sampled outputs) -------------------------------
+
+FULL = [("c1", 1), ("c2up", 1), ("c2down", 1), ("c3", 1), ("c3", 2), ("c3", 4), ("c3", 8), ("c3", 16),
+        ("c4", 2048), ("c5", 1), ("c5", 512)]
+
+
+@pytest.fixture(scope="module")
+def full_layers():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            cfg = wl.CONFIGS[name]
+            note(f"building {name} (N={cfg.N} K={cfg.K})")
+            cache.clear()
+            cache[name] = product_layer(cfg, max(cfg.M_list))
+        return cache[name]
+    return get
+
+
+@pytest.mark.parametrize("name,M", FULL)
+def test_configs_match_oracle_on_sampled_outputs(full_layers, name, M):
+    import torch
+    cfg = wl.CONFIGS[name]
+    prod = full_layers(name)
+    rows = np.arange(cfg.N) if cfg.N <= 1024 else sample_rows(cfg.N, 96)
+    ref = oracle_layer(cfg, M, rows)
+    # codes of the sampled rows and the act-order mapping are bit-exact
+    assert np.array_equal(prod["codes"][rows], ref["codes"])
+    if cfg.act_order:
+        assert np.array_equal(prod["g_idx_np"], ref["g_idx"])
+    x = prod["x"][:M].contiguous()
+    note(f"config {name} M={M}")
+    y = run_gemm(prod, x=x).cpu().numpy()[:, rows]
+    err = oracle.rel_err(y, ref["y_ref"])
+    assert err <= TOL, err
+    # and a second run is bit-identical (each output written once, fixed order)
+    y2 = run_gemm(prod, x=x).cpu().numpy()[:, rows]
+    assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))

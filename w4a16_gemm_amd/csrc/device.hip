@@ -1,0 +1,247 @@
+// Device entry points of the W4A16 library: argument checks, kernel selection and
+// launches.  Every launch is asynchronous on the caller's stream; launch errors are
+// reported as W4A16_ERR_HIP with the HIP error text.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "internal.hpp"
+#include "kernels/aux.hpp"
+#include "kernels/gemm.hpp"
+#include "kernels/gemv.hpp"
+
+namespace w4a16 {
+namespace {
+
+constexpr int kGemvWaves = 8;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : 7; }
+
+int env_int(const char* name, int fallback) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return fallback;
+  return std::atoi(v);
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return W4A16_OK;
+  return fail(W4A16_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int check_launch(const char* what) { return hip_status(hipGetLastError(), what); }
+
+// Same validation for every device entry point.
+int check_device_args(const void* const* ptrs, int nptrs, int N, int K, int group_size) {
+  for (int i = 0; i < nptrs; ++i)
+    if (!ptrs[i]) return fail(W4A16_ERR_INVALID_ARG, "NULL device buffer (argument %d)", i);
+  if (int st = check_shape(N, K, group_size)) return st;
+  for (int i = 0; i < nptrs; ++i)
+    if (!aligned16(ptrs[i])) return fail(W4A16_ERR_MISALIGNED, "device buffer %d is not 16-byte aligned", i);
+  return W4A16_OK;
+}
+
+// Optional (W4A16_DEBUG_CHECKS=1) check of a device-resident g_idx against the order
+// stored in the weight buffer.  Synchronous.
+int debug_check_gidx(const int32_t* g_idx, const int32_t* qweight, int N, int K, int group_size,
+                     hipStream_t stream) {
+  if (env_int("W4A16_DEBUG_CHECKS", 0) == 0) return W4A16_OK;
+  if (int st = hip_status(hipStreamSynchronize(stream), "hipStreamSynchronize")) return st;
+  std::vector<int32_t> h(K), tail(K), perm(K);
+  if (int st = hip_status(hipMemcpy(h.data(), g_idx, sizeof(int32_t) * K, hipMemcpyDeviceToHost), "hipMemcpy"))
+    return st;
+  if (int st = hip_status(hipMemcpy(tail.data(), qweight + qweight_words(N, K, false),
+                                    sizeof(int32_t) * K, hipMemcpyDeviceToHost),
+                          "hipMemcpy"))
+    return st;
+  if (int st = check_gidx_and_sort(h.data(), K, group_size, perm.data())) return st;
+  for (int p = 0; p < K; ++p)
+    if (tail[p] != perm[p])
+      return fail(W4A16_ERR_BAD_GIDX, "g_idx does not match the order stored in qweight at %d", p);
+  return W4A16_OK;
+}
+
+// --- GEMV (M = 1) ---------------------------------------------------------------
+
+struct GemvShape {
+  int lpr = 0;  // lanes per row
+  int cpl = 0;  // 16-byte chunks per lane per row
+};
+
+// Lanes per row and chunks per lane for K/32 chunks per row: an exact split with the
+// widest rows first, else the widest split that keeps at most 8 chunks per lane.
+GemvShape pick_gemv_shape(int K) {
+  const int C = K / 32;
+  for (int lpr : {64, 32, 16, 8})
+    if (C % lpr == 0 && C / lpr <= 8) return {lpr, C / lpr};
+  for (int lpr : {64, 32, 16, 8})
+    if (lpr <= C || lpr == 8) {
+      const int cpl = (C + lpr - 1) / lpr;
+      if (cpl <= 8) return {lpr, cpl};
+      return {};
+    }
+  return {};
+}
+
+template <int LPR, bool ACT>
+void launch_gemv_cpl(int cpl, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
+                     const half_t* s, const uint32_t* z, half_t* y, int N, int K, int gshift, int rpb) {
+  dim3 block(kGemvWaves * 64);
+#define W4A16_GEMV_CASE(C)                                                                               \
+  case C:                                                                                                \
+    hipLaunchKernelGGL((gemv_m1_kernel<LPR, C, kGemvWaves, ACT>), grid, block, shmem, st, x, qw, s, z, y, \
+                       N, K, gshift, rpb);                                                               \
+    break;
+  switch (cpl) {
+    W4A16_GEMV_CASE(1)
+    W4A16_GEMV_CASE(2)
+    W4A16_GEMV_CASE(3)
+    W4A16_GEMV_CASE(4)
+    W4A16_GEMV_CASE(5)
+    W4A16_GEMV_CASE(6)
+    W4A16_GEMV_CASE(7)
+    W4A16_GEMV_CASE(8)
+    default:
+      break;
+  }
+#undef W4A16_GEMV_CASE
+}
+
+template <bool ACT>
+void launch_gemv(const GemvShape& sh, dim3 grid, size_t shmem, hipStream_t st, const half_t* x,
+                 const uint32_t* qw, const half_t* s, const uint32_t* z, half_t* y, int N, int K, int gshift,
+                 int rpb) {
+  switch (sh.lpr) {
+    case 64: launch_gemv_cpl<64, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, rpb); break;
+    case 32: launch_gemv_cpl<32, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, rpb); break;
+    case 16: launch_gemv_cpl<16, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, rpb); break;
+    default: launch_gemv_cpl<8, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, rpb); break;
+  }
+}
+
+int run_gemv(const GemvShape& sh, bool act, const half_t* x, const uint32_t* qw, const half_t* s,
+             const uint32_t* z, half_t* y, int N, int K, int gshift, hipStream_t st) {
+  const int rpw = 64 / sh.lpr;
+  const int stride = kGemvWaves * rpw;                  // rows per workgroup pass
+  const int passes = (N + stride - 1) / stride;
+  const int target = env_int("W4A16_TUNE_GEMV_BLOCKS", 512);
+  const int per_block = (passes + target - 1) / target;  // passes per workgroup
+  const int rpb = per_block * stride;
+  const dim3 grid((N + rpb - 1) / rpb);
+  const size_t shmem = static_cast<size_t>(K) * sizeof(half_t);
+  if (act)
+    launch_gemv<true>(sh, grid, shmem, st, x, qw, s, z, y, N, K, gshift, rpb);
+  else
+    launch_gemv<false>(sh, grid, shmem, st, x, qw, s, z, y, N, K, gshift, rpb);
+  return check_launch("gemv launch");
+}
+
+// --- GEMM (M > 1) ---------------------------------------------------------------
+
+template <int BM>
+void launch_gemm_bm(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z,
+                    half_t* y, int M, int N, int K, int gshift) {
+  const dim3 grid((N + 255) / 256, (M + BM - 1) / BM);
+  hipLaunchKernelGGL((gemm_mfma_kernel<BM>), grid, dim3(256), 0, st, x, qw, s, z, y, M, N, K, gshift);
+}
+
+int run_gemm(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z,
+             half_t* y, int M, int N, int K, int gshift) {
+  if (M <= 16)
+    launch_gemm_bm<16>(st, x, qw, s, z, y, M, N, K, gshift);
+  else if (M <= 32)
+    launch_gemm_bm<32>(st, x, qw, s, z, y, M, N, K, gshift);
+  else if (M <= 64)
+    launch_gemm_bm<64>(st, x, qw, s, z, y, M, N, K, gshift);
+  else
+    launch_gemm_bm<128>(st, x, qw, s, z, y, M, N, K, gshift);
+  return check_launch("gemm launch");
+}
+
+enum class Path { kAuto, kGemv, kGemm };
+
+Path forced_path() {
+  const char* v = std::getenv("W4A16_FORCE_PATH");
+  if (!v) return Path::kAuto;
+  if (std::strcmp(v, "gemv") == 0) return Path::kGemv;
+  if (std::strcmp(v, "gemm") == 0) return Path::kGemm;
+  return Path::kAuto;
+}
+
+}  // namespace
+}  // namespace w4a16
+
+using namespace w4a16;
+
+extern "C" {
+
+int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
+               const int32_t* g_idx, int group_size, int M, int N, int K, uint16_t* y, void* stream) {
+  clear_error();
+  if (M <= 0) return fail(W4A16_ERR_INVALID_ARG, "M must be positive (M=%d)", M);
+  const void* ptrs[] = {x, qweight, scales, qzeros, y};
+  if (int st = check_device_args(ptrs, 5, N, K, group_size)) return st;
+  const bool act = g_idx != nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (act)
+    if (int s = debug_check_gidx(g_idx, qweight, N, K, group_size, st)) return s;
+
+  const int gshift = log2_group(group_size);
+  const auto* hx = reinterpret_cast<const half_t*>(x);
+  const auto* hq = reinterpret_cast<const uint32_t*>(qweight);
+  const auto* hs = reinterpret_cast<const half_t*>(scales);
+  const auto* hz = reinterpret_cast<const uint32_t*>(qzeros);
+  auto* hy = reinterpret_cast<half_t*>(y);
+
+  const Path forced = forced_path();
+  const GemvShape sh = pick_gemv_shape(K);
+  const bool gemv_ok = M == 1 && sh.lpr != 0;
+  if (forced == Path::kGemv && !gemv_ok)
+    return fail(W4A16_ERR_UNSUPPORTED, "the GEMV path needs M == 1 and K <= 16384 (M=%d K=%d)", M, K);
+  const bool use_gemv = gemv_ok && forced != Path::kGemm;
+
+  if (use_gemv) return run_gemv(sh, act, hx, hq, hs, hz, hy, N, K, gshift, st);
+
+  if (!act) return run_gemm(st, hx, hq, hs, hz, hy, M, N, K, gshift);
+
+  // act order: gather x into stored order in stream-ordered scratch memory
+  half_t* xs = nullptr;
+  const size_t bytes = static_cast<size_t>(M) * K * sizeof(half_t);
+  if (int s = hip_status(hipMallocAsync(reinterpret_cast<void**>(&xs), bytes, st), "hipMallocAsync")) return s;
+  const int32_t* perm = qweight + qweight_words(N, K, false);
+  const size_t total = static_cast<size_t>(M) * K;
+  hipLaunchKernelGGL(gather_x_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, hx,
+                     perm, xs, M, K);
+  int rc = check_launch("gather launch");
+  if (rc == W4A16_OK) rc = run_gemm(st, xs, hq, hs, hz, hy, M, N, K, gshift);
+  const int rf = hip_status(hipFreeAsync(xs, st), "hipFreeAsync");
+  return rc != W4A16_OK ? rc : rf;
+}
+
+int w4a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros, const int32_t* g_idx,
+                  int group_size, int N, int K, uint16_t* w_out, void* stream) {
+  clear_error();
+  const void* ptrs[] = {qweight, scales, qzeros, w_out};
+  if (int st = check_device_args(ptrs, 4, N, K, group_size)) return st;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool act = g_idx != nullptr;
+  if (act)
+    if (int s = debug_check_gidx(g_idx, qweight, N, K, group_size, st)) return s;
+  const size_t words = static_cast<size_t>(N) * (K / 8);
+  const dim3 grid(static_cast<unsigned>((words + 255) / 256));
+  const auto* hq = reinterpret_cast<const uint32_t*>(qweight);
+  const auto* hs = reinterpret_cast<const half_t*>(scales);
+  const auto* hz = reinterpret_cast<const uint32_t*>(qzeros);
+  auto* hw = reinterpret_cast<half_t*>(w_out);
+  const int gshift = log2_group(group_size);
+  if (act)
+    hipLaunchKernelGGL(dequant_kernel<true>, grid, dim3(256), 0, st, hq, hs, hz, hw, N, K, gshift);
+  else
+    hipLaunchKernelGGL(dequant_kernel<false>, grid, dim3(256), 0, st, hq, hs, hz, hw, N, K, gshift);
+  return check_launch("dequant launch");
+}
+
+}  // extern "C"

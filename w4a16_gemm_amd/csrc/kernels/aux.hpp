@@ -1,0 +1,49 @@
+// Small kernels around the two main ones: the weight view used for parity checks
+// and the activation gather of act order.
+#pragma once
+
+#include "nibbles.hpp"
+
+namespace w4a16 {
+
+// w_out[n][k] = binary16((q - Z) * S) in the original input-channel order, built
+// with the same dequant_word the GEMM uses for its weight operand.  One thread per
+// packed word.
+template <bool ACT>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ qw,
+                                                     const half_t* __restrict__ scales,
+                                                     const uint32_t* __restrict__ qzeros,
+                                                     half_t* __restrict__ w_out, int N, int K,
+                                                     int gshift) {
+  const int W = K >> 3;
+  const size_t idx = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<size_t>(N) * W) return;
+  const int n = static_cast<int>(idx / W);
+  const int wd = static_cast<int>(idx % W);
+  const int p0 = wd * 8;
+  const int gi = p0 >> gshift;
+  const DequantConsts dc = make_consts(load_zero(qzeros, gi, N, n), scales[static_cast<size_t>(gi) * N + n]);
+  const half8_t d = dequant_word(qw[idx], dc);
+  half_t* row = w_out + static_cast<size_t>(n) * K;
+  if constexpr (!ACT) {
+    *reinterpret_cast<half8_t*>(row + p0) = d;
+  } else {
+    const int32_t* perm = reinterpret_cast<const int32_t*>(qw + static_cast<size_t>(N) * W);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) row[perm[p0 + e]] = d[e];
+  }
+}
+
+// Act order, M > 1: xs[m][p] = x[m][perm[p]], so that the GEMM sees every group as
+// a contiguous run of input channels.
+__global__ __launch_bounds__(256) void gather_x_kernel(const half_t* __restrict__ x,
+                                                       const int32_t* __restrict__ perm,
+                                                       half_t* __restrict__ xs, int M, int K) {
+  const size_t idx = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<size_t>(M) * K) return;
+  const size_t m = idx / K;
+  const int p = static_cast<int>(idx % K);
+  xs[idx] = x[m * K + perm[p]];
+}
+
+}  // namespace w4a16

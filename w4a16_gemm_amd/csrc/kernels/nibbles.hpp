@@ -1,0 +1,85 @@
+// Register-level expansion of packed 4-bit codes for gfx950.
+//
+// The packed word layout puts element e of a word in nibble {0,4,1,5,2,6,3,7}[e].
+// With that order, two AND-OR operations per 16-bit half pair turn a word into
+// four 32-bit registers, each holding two binary16 values of consecutive elements:
+//
+//   (w & 0x000F000F) | 0x64006400         -> (1024 + q_e0, 1024 + q_e1)
+//   (w & 0x00F000F0) | 0x64006400         -> (1024 + 16 q_e2, 1024 + 16 q_e3)
+//   ((w >> 8) & 0x000F000F) | 0x64006400  -> (1024 + q_e4, 1024 + q_e5)
+//   ((w >> 8) & 0x00F000F0) | 0x64006400  -> (1024 + 16 q_e6, 1024 + 16 q_e7)
+//
+// 0x6400 is binary16 1024.0, whose ulp is 1, so OR-ing a 4-bit (or 4-bit << 4)
+// integer into the mantissa gives the exact values above.  Every later step that
+// turns them into q - Z is exact as well; the only rounding is the final
+// multiplication by the binary16 scale, which is therefore the same rounding as
+// binary16((q - Z) * S) ("AWQ + GPTQ Quantization, in depth", What W4A16 buys:
+// the kernel expands the packed weights to 16 bits in registers with the group's
+// scale and zero point).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+typedef _Float16 half_t;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kMagic = 0x64006400u;  // (1024.0, 1024.0) in binary16
+
+struct Pairs {
+  uint32_t a0;  // (1024 + q0, 1024 + q1)
+  uint32_t b0;  // (1024 + 16 q2, 1024 + 16 q3)
+  uint32_t a1;  // (1024 + q4, 1024 + q5)
+  uint32_t b1;  // (1024 + 16 q6, 1024 + 16 q7)
+};
+
+__device__ __forceinline__ Pairs expand_word(uint32_t w) {
+  Pairs p;
+  p.a0 = (w & 0x000F000Fu) | kMagic;
+  p.b0 = (w & 0x00F000F0u) | kMagic;
+  const uint32_t v = w >> 8;
+  p.a1 = (v & 0x000F000Fu) | kMagic;
+  p.b1 = (v & 0x00F000F0u) | kMagic;
+  return p;
+}
+
+__device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+
+// Per (group, output) constants for building binary16 weights (q - Z) * S.
+struct DequantConsts {
+  half2_t neg_1024_z;  // -(1024 + Z)
+  half2_t neg_64_z;    // -(64 + Z)
+  half2_t scale;       // S
+};
+
+__device__ __forceinline__ DequantConsts make_consts(uint32_t z, half_t s) {
+  DequantConsts c;
+  const half_t a = static_cast<half_t>(-1024.0f - static_cast<float>(z));
+  const half_t b = static_cast<half_t>(-64.0f - static_cast<float>(z));
+  c.neg_1024_z = half2_t{a, a};
+  c.neg_64_z = half2_t{b, b};
+  c.scale = half2_t{s, s};
+  return c;
+}
+
+// Eight binary16 weights binary16((q_e - Z) * S), e = 0..7, in element order.
+__device__ __forceinline__ half8_t dequant_word(uint32_t w, const DequantConsts& c) {
+  const Pairs p = expand_word(w);
+  const half2_t sixteenth = half2_t{static_cast<half_t>(0.0625f), static_cast<half_t>(0.0625f)};
+  const half2_t d0 = (as_h2(p.a0) + c.neg_1024_z) * c.scale;
+  const half2_t d1 = __builtin_elementwise_fma(as_h2(p.b0), sixteenth, c.neg_64_z) * c.scale;
+  const half2_t d2 = (as_h2(p.a1) + c.neg_1024_z) * c.scale;
+  const half2_t d3 = __builtin_elementwise_fma(as_h2(p.b1), sixteenth, c.neg_64_z) * c.scale;
+  return half8_t{d0.x, d0.y, d1.x, d1.y, d2.x, d2.y, d3.x, d3.y};
+}
+
+// Zero point of (group gi, output n) from the packed zero points [G][N/8].
+__device__ __forceinline__ uint32_t load_zero(const uint32_t* __restrict__ qzeros, int gi, int N, int n) {
+  return (qzeros[static_cast<size_t>(gi) * (N >> 3) + (n >> 3)] >> ((n & 7) * 4)) & 0xFu;
+}
+
+}  // namespace w4a16
