@@ -3,6 +3,7 @@
 // reported as W4A16_ERR_HIP with the HIP error text.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <vector>
@@ -14,8 +15,6 @@
 
 namespace w4a16 {
 namespace {
-
-constexpr int kGemvWaves = 8;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -66,9 +65,13 @@ int debug_check_gidx(const int32_t* g_idx, const int32_t* qweight, int N, int K,
 
 // --- GEMV (M = 1) ---------------------------------------------------------------
 
+constexpr int kGemvWaves = 8;
+constexpr size_t kGemvLdsBudget = 144 * 1024;  // of the 160 KB of a gfx950 CU
+
 struct GemvShape {
   int lpr = 0;  // lanes per row
   int cpl = 0;  // 16-byte chunks per lane per row
+  bool exact = false;
 };
 
 // Lanes per row and chunks per lane for K/32 chunks per row: an exact split with the
@@ -76,66 +79,99 @@ struct GemvShape {
 GemvShape pick_gemv_shape(int K) {
   const int C = K / 32;
   for (int lpr : {64, 32, 16, 8})
-    if (C % lpr == 0 && C / lpr <= 8) return {lpr, C / lpr};
+    if (C % lpr == 0 && C / lpr <= 8) return {lpr, C / lpr, true};
   for (int lpr : {64, 32, 16, 8})
     if (lpr <= C || lpr == 8) {
       const int cpl = (C + lpr - 1) / lpr;
-      if (cpl <= 8) return {lpr, cpl};
+      if (cpl <= 8) return {lpr, cpl, false};
       return {};
     }
   return {};
 }
 
-template <int LPR, bool ACT>
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Register-pipeline depth: about 8 KB of codes in flight per wavefront.
+constexpr int gemv_depth(int cpl) { return cpl >= 4 ? 2 : 8 / cpl; }
+
+template <int LPR, int CPL, bool EXACT, bool ACT>
+void launch_gemv_t(dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
+                   const uint16_t* s, const uint32_t* z, half_t* y, int N, int K, int gshift, int steps) {
+  auto kern = gemv_m1_kernel<LPR, CPL, kGemvWaves, gemv_depth(CPL), EXACT, ACT>;
+  // Dynamic LDS above 64 KB has to be allowed per kernel (once per process).
+  static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       static_cast<int>(kGemvLdsBudget));
+  if (lds_ok != hipSuccess && shmem > 64 * 1024) return;  // reported by the caller's launch check
+  hipLaunchKernelGGL(kern, grid, dim3(kGemvWaves * 64), shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+}
+
+template <int LPR, bool EXACT, bool ACT>
 void launch_gemv_cpl(int cpl, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
-                     const half_t* s, const uint32_t* z, half_t* y, int N, int K, int gshift, int rpb) {
-  dim3 block(kGemvWaves * 64);
-#define W4A16_GEMV_CASE(C)                                                                               \
-  case C:                                                                                                \
-    hipLaunchKernelGGL((gemv_m1_kernel<LPR, C, kGemvWaves, ACT>), grid, block, shmem, st, x, qw, s, z, y, \
-                       N, K, gshift, rpb);                                                               \
-    break;
+                     const uint16_t* s, const uint32_t* z, half_t* y, int N, int K, int gshift, int steps) {
   switch (cpl) {
-    W4A16_GEMV_CASE(1)
-    W4A16_GEMV_CASE(2)
-    W4A16_GEMV_CASE(3)
-    W4A16_GEMV_CASE(4)
-    W4A16_GEMV_CASE(5)
-    W4A16_GEMV_CASE(6)
-    W4A16_GEMV_CASE(7)
-    W4A16_GEMV_CASE(8)
-    default:
-      break;
+    case 1: launch_gemv_t<LPR, 1, EXACT, ACT>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 2: launch_gemv_t<LPR, 2, EXACT, ACT>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 3: launch_gemv_t<LPR, 3, EXACT, ACT>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 4: launch_gemv_t<LPR, 4, EXACT, ACT>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 5: launch_gemv_t<LPR, 5, EXACT, ACT>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 6: launch_gemv_t<LPR, 6, EXACT, ACT>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 7: launch_gemv_t<LPR, 7, EXACT, ACT>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    default: launch_gemv_t<LPR, 8, EXACT, ACT>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
   }
-#undef W4A16_GEMV_CASE
 }
 
-template <bool ACT>
-void launch_gemv(const GemvShape& sh, dim3 grid, size_t shmem, hipStream_t st, const half_t* x,
-                 const uint32_t* qw, const half_t* s, const uint32_t* z, half_t* y, int N, int K, int gshift,
-                 int rpb) {
+template <bool EXACT, bool ACT>
+void launch_gemv_lpr(const GemvShape& sh, dim3 grid, size_t shmem, hipStream_t st, const half_t* x,
+                     const uint32_t* qw, const uint16_t* s, const uint32_t* z, half_t* y, int N, int K,
+                     int gshift, int steps) {
   switch (sh.lpr) {
-    case 64: launch_gemv_cpl<64, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, rpb); break;
-    case 32: launch_gemv_cpl<32, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, rpb); break;
-    case 16: launch_gemv_cpl<16, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, rpb); break;
-    default: launch_gemv_cpl<8, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, rpb); break;
+    case 64: launch_gemv_cpl<64, EXACT, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 32: launch_gemv_cpl<32, EXACT, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 16: launch_gemv_cpl<16, EXACT, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    default: launch_gemv_cpl<8, EXACT, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
   }
 }
 
-int run_gemv(const GemvShape& sh, bool act, const half_t* x, const uint32_t* qw, const half_t* s,
+// LDS of one workgroup: the activations plus a rows x (G+1) slab of float2.
+size_t gemv_lds_bytes(int K, int G, int rows) {
+  return static_cast<size_t>(K) * sizeof(half_t) + static_cast<size_t>(rows) * (G + 1) * 2 * sizeof(float);
+}
+
+int run_gemv(const GemvShape& sh, bool act, const half_t* x, const uint32_t* qw, const uint16_t* s,
              const uint32_t* z, half_t* y, int N, int K, int gshift, hipStream_t st) {
-  const int rpw = 64 / sh.lpr;
-  const int stride = kGemvWaves * rpw;                  // rows per workgroup pass
-  const int passes = (N + stride - 1) / stride;
-  const int target = env_int("W4A16_TUNE_GEMV_BLOCKS", 512);
-  const int per_block = (passes + target - 1) / target;  // passes per workgroup
-  const int rpb = per_block * stride;
-  const dim3 grid((N + rpb - 1) / rpb);
-  const size_t shmem = static_cast<size_t>(K) * sizeof(half_t);
-  if (act)
-    launch_gemv<true>(sh, grid, shmem, st, x, qw, s, z, y, N, K, gshift, rpb);
-  else
-    launch_gemv<false>(sh, grid, shmem, st, x, qw, s, z, y, N, K, gshift, rpb);
+  const int G = K >> gshift;
+  const int unit = kGemvWaves * (64 / sh.lpr);                 // rows per unit
+  const int units = (N + unit - 1) / unit;
+  const int per_cu = env_int("W4A16_TUNE_GEMV_BLOCKS_PER_CU", 1);
+  int blocks = std::min(units, std::max(1, device_cus() * std::max(1, per_cu)));
+  if (blocks >= 8) blocks -= blocks % 8;                         // whole XCD rounds
+  int steps = (units + blocks - 1) / blocks;
+  while (gemv_lds_bytes(K, G, steps * unit) > kGemvLdsBudget && blocks < units) {
+    blocks = std::min(units, blocks * 2);
+    steps = (units + blocks - 1) / blocks;
+  }
+  if (gemv_lds_bytes(K, G, steps * unit) > kGemvLdsBudget)
+    return fail(W4A16_ERR_UNSUPPORTED, "GEMV staging for K=%d, G=%d does not fit in LDS", K, G);
+  const dim3 grid(blocks);
+  const size_t shmem = gemv_lds_bytes(K, G, steps * unit);
+  if (sh.exact) {
+    if (act) launch_gemv_lpr<true, true>(sh, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+    else launch_gemv_lpr<true, false>(sh, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+  } else {
+    if (act) launch_gemv_lpr<false, true>(sh, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+    else launch_gemv_lpr<false, false>(sh, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+  }
   return check_launch("gemv launch");
 }
 
@@ -203,7 +239,8 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
     return fail(W4A16_ERR_UNSUPPORTED, "the GEMV path needs M == 1 and K <= 16384 (M=%d K=%d)", M, K);
   const bool use_gemv = gemv_ok && forced != Path::kGemm;
 
-  if (use_gemv) return run_gemv(sh, act, hx, hq, hs, hz, hy, N, K, gshift, st);
+  if (use_gemv)
+    return run_gemv(sh, act, hx, hq, reinterpret_cast<const uint16_t*>(scales), hz, hy, N, K, gshift, st);
 
   if (!act) return run_gemm(st, hx, hq, hs, hz, hy, M, N, K, gshift);
 

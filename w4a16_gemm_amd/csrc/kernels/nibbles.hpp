@@ -37,13 +37,45 @@ struct Pairs {
   uint32_t b1;  // (1024 + 16 q6, 1024 + 16 q7)
 };
 
+// (a & mask) | c in one v_and_or_b32.  gfx9 VOP3 cannot encode two literal
+// constants, so left to itself the compiler emits v_and_b32 + v_or_b32; the mask is
+// passed in a scalar register and c in a vector register instead.  ALU only.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(mask), "v"(c));
+  return d;
+}
+
 __device__ __forceinline__ Pairs expand_word(uint32_t w) {
   Pairs p;
-  p.a0 = (w & 0x000F000Fu) | kMagic;
-  p.b0 = (w & 0x00F000F0u) | kMagic;
+  p.a0 = and_or(w, 0x000F000Fu, kMagic);
+  p.b0 = and_or(w, 0x00F000F0u, kMagic);
   const uint32_t v = w >> 8;
-  p.a1 = (v & 0x000F000Fu) | kMagic;
-  p.b1 = (v & 0x00F000F0u) | kMagic;
+  p.a1 = and_or(v, 0x000F000Fu, kMagic);
+  p.b1 = and_or(v, 0x00F000F0u, kMagic);
+  return p;
+}
+
+// The same pairs without the 1024 offset: masking alone leaves q (or 16 q) in the
+// mantissa of a binary16 with a zero exponent field, i.e. the exact subnormal
+// q * 2^-24.  v_dot2_f32_f16 keeps binary16 subnormal inputs (the kernels run with
+// fp16/fp64 denormals enabled), and every product with an activation is exact in
+// fp32, so the 2^-24 can be folded into the scale afterwards.  One plain AND per
+// pair, no offset to subtract.
+struct SubPairs {
+  uint32_t a0;  // (q0, q1) * 2^-24
+  uint32_t b0;  // (q2, q3) * 16 * 2^-24
+  uint32_t a1;  // (q4, q5) * 2^-24
+  uint32_t b1;  // (q6, q7) * 16 * 2^-24
+};
+
+__device__ __forceinline__ SubPairs expand_word_subnormal(uint32_t w) {
+  SubPairs p;
+  p.a0 = w & 0x000F000Fu;
+  p.b0 = w & 0x00F000F0u;
+  const uint32_t v = w >> 8;
+  p.a1 = v & 0x000F000Fu;
+  p.b1 = v & 0x00F000F0u;
   return p;
 }
 
