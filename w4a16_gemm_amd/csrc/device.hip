@@ -186,6 +186,16 @@ void launch_gemm_bm(hipStream_t st, const half_t* x, const uint32_t* qw, const h
 
 int run_gemm(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z,
              half_t* y, int M, int N, int K, int gshift) {
+  if (M > 128 && K % kBigBK == 0 && static_cast<long long>(M) * K < (1LL << 31) &&
+      env_int("W4A16_TUNE_GEMM_BIG", 1) != 0) {
+    static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_big_kernel),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                         static_cast<int>(kBigLds));
+    if (int rc = hip_status(lds_ok, "hipFuncSetAttribute")) return rc;
+    const int tiles = ((M + kBigBM - 1) / kBigBM) * ((N + kBigBN - 1) / kBigBN);
+    hipLaunchKernelGGL(gemm_big_kernel, dim3(tiles), dim3(512), kBigLds, st, x, qw, s, z, y, M, N, K, gshift);
+    return check_launch("gemm launch");
+  }
   if (M <= 16)
     launch_gemm_bm<16>(st, x, qw, s, z, y, M, N, K, gshift);
   else if (M <= 32)

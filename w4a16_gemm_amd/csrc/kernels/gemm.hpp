@@ -144,4 +144,240 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     }
 }
 
+// Large-M tile: a workgroup of 8 wavefronts (2 along M x 4 along N, two per SIMD)
+// computes a 256 x 256 tile of y; wavefront (wm, wn) owns rows [128 wm, +128) and
+// columns [64 wn, +64) with 8 x 4 blocks of 16x16 fp32 accumulators.
+//  * K advances in tiles of 64 channels.  Lane (r, q) = (lane % 16, lane / 16) of a
+//    wavefront holds, per 16-column block, the 16 codes of channels [16 q, 16 q + 16)
+//    of its column: word s (8 codes) is its B operand of the tile's MFMA step s, and
+//    its A operand in that step is the 8 activations of the same channels.
+//  * Everything a tile needs goes through a 3-stage LDS ring filled with direct-to-LDS
+//    loads two tiles ahead: the activation tile (256 rows x 64 channels, 32 KB), the
+//    raw packed codes (256 columns x 64 channels, 8 KB) and the scales and packed zero
+//    points of the groups of its two 32-channel halves (1.25 KB).  No registers hold
+//    prefetched data, so two wavefronts per SIMD fit in 256 registers each.
+//  * An activation row is 8 slots of 16 bytes; slot j of row r holds the row's chunk
+//    j ^ (r % 8), which lets the 16 rows of an MFMA operand be read without LDS bank
+//    conflicts on gfx950.
+//  * Each wavefront dequantises its 64 columns in registers (the two wavefronts
+//    sharing columns both do it).
+//  * Tiles are dealt out so that the workgroups of one XCD (dispatch is round-robin
+//    over the 8 XCDs) take consecutive tiles of one 256-row panel of x, which then
+//    stays in that XCD's L2.
+// Requirements: K % 64 == 0, group size >= 32 and M * K < 2^31.
+__device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
+  if (ntiles % 8 != 0) return bid;
+  return (bid % 8) * (ntiles / 8) + bid / 8;
+}
+
+// LDS reads written as inline asm.  The compiler cannot tell which stage of the ring
+// a direct-to-LDS load writes, so before every LDS read it would wait for all
+// outstanding global loads, including the prefetch of later tiles; reads it does not
+// see as LDS accesses are ordered by the explicit waits and barriers of the kernel
+// instead.  Each block waits for its own results before it returns.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));   // low half of a flat LDS address
+}
+
+// af[mb] = 16 bytes at addr + 2048 mb, mb = 0..7.
+__device__ __forceinline__ void lds_read_a8(uint32_t addr, half8_t (&af)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n"
+      "ds_read_b128 %1, %8 offset:2048\n"
+      "ds_read_b128 %2, %8 offset:4096\n"
+      "ds_read_b128 %3, %8 offset:6144\n"
+      "ds_read_b128 %4, %8 offset:8192\n"
+      "ds_read_b128 %5, %8 offset:10240\n"
+      "ds_read_b128 %6, %8 offset:12288\n"
+      "ds_read_b128 %7, %8 offset:14336\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(af[4]), "=&v"(af[5]), "=&v"(af[6]),
+        "=&v"(af[7])
+      : "v"(addr)
+      : "memory");
+}
+
+// The same eight A fragments, plus cw[nb] = 8 bytes at b_addr + 256 nb, the 16-bit
+// sc[nb] at s_addr + 32 nb and the 32-bit zw[nb] at z_addr + 8 nb, nb = 0..3.
+__device__ __forceinline__ void lds_read_tile(uint32_t a_addr, uint32_t b_addr, uint32_t s_addr, uint32_t z_addr,
+                                              half8_t (&af)[8], uint2 (&cw)[4], uint32_t (&sc)[4],
+                                              uint32_t (&zw)[4]) {
+  asm volatile(
+      "ds_read_u16 %12, %22\n"
+      "ds_read_u16 %13, %22 offset:32\n"
+      "ds_read_u16 %14, %22 offset:64\n"
+      "ds_read_u16 %15, %22 offset:96\n"
+      "ds_read_b32 %16, %23\n"
+      "ds_read_b32 %17, %23 offset:8\n"
+      "ds_read_b32 %18, %23 offset:16\n"
+      "ds_read_b32 %19, %23 offset:24\n"
+      "ds_read_b64 %8, %21\n"
+      "ds_read_b64 %9, %21 offset:256\n"
+      "ds_read_b64 %10, %21 offset:512\n"
+      "ds_read_b64 %11, %21 offset:768\n"
+      "ds_read_b128 %0, %20\n"
+      "ds_read_b128 %1, %20 offset:2048\n"
+      "ds_read_b128 %2, %20 offset:4096\n"
+      "ds_read_b128 %3, %20 offset:6144\n"
+      "ds_read_b128 %4, %20 offset:8192\n"
+      "ds_read_b128 %5, %20 offset:10240\n"
+      "ds_read_b128 %6, %20 offset:12288\n"
+      "ds_read_b128 %7, %20 offset:14336\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(af[4]), "=&v"(af[5]), "=&v"(af[6]),
+        "=&v"(af[7]), "=&v"(cw[0]), "=&v"(cw[1]), "=&v"(cw[2]), "=&v"(cw[3]), "=&v"(sc[0]), "=&v"(sc[1]),
+        "=&v"(sc[2]), "=&v"(sc[3]), "=&v"(zw[0]), "=&v"(zw[1]), "=&v"(zw[2]), "=&v"(zw[3])
+      : "v"(a_addr), "v"(b_addr), "v"(s_addr), "v"(z_addr)
+      : "memory");
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(), whose release would
+// wait for every outstanding load, prefetches included.  Callers wait for exactly the
+// loads and LDS reads that must be complete (s_waitcnt) before they call it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr int kBigBM = 256, kBigBN = 256, kBigBK = 64, kBigStages = 3;
+constexpr uint32_t kBigLdsA = kBigBM * kBigBK * 2;      // activations of one stage
+constexpr uint32_t kBigLdsB = kBigBN * kBigBK / 2;      // packed codes of one stage
+constexpr uint32_t kBigLdsS = 2 * kBigBN * 2;           // scales [half][column]
+constexpr uint32_t kBigLdsZ = 2 * (kBigBN / 8) * 4;     // packed zero points [half][column / 8]
+constexpr uint32_t kBigStage = kBigLdsA + kBigLdsB + kBigLdsS + kBigLdsZ;
+constexpr size_t kBigLds = static_cast<size_t>(kBigStages) * kBigStage;
+
+__global__ __launch_bounds__(512) void gemm_big_kernel(
+    const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const half_t* __restrict__ scales,
+    const uint32_t* __restrict__ qzeros, half_t* __restrict__ y, int M, int N, int K, int gshift) {
+  constexpr int BM = kBigBM, BN = kBigBN, BK = kBigBK, NS = kBigStages, MB = 8, NB = 4;
+  constexpr int APT = BM * BK / 8 / 512;  // activation chunks (16 B) per thread per stage
+  static_assert(BN * BK / 32 == 512, "one code chunk per thread per stage");
+  static_assert(kBigStage % 16 == 0, "stage alignment");
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int lr = lane & 15;
+  const int lq = lane >> 4;
+  const int tiles_n = (N + BN - 1) / BN;
+  const int ntiles = tiles_n * ((M + BM - 1) / BM);
+  const int tile = xcd_tile(blockIdx.x, ntiles);
+  const int m0 = (tile / tiles_n) * BM;
+  const int n0 = (tile % tiles_n) * BN;
+  const int W = K >> 3;
+  const int KT = K / BK;
+
+  // Activations: lane l of load i writes chunk c = (APT wave + i) * 64 + l = 8 row + slot,
+  // which receives the row's chunk slot ^ (row % 8).  Rows past M re-read row M - 1.
+  int a_off[APT];
+#pragma unroll
+  for (int i = 0; i < APT; ++i) {
+    const int c = (wave * APT + i) * 64 + lane;
+    const int row = c >> 3, slot = c & 7;
+    a_off[i] = min(m0 + row, M - 1) * K + 8 * (slot ^ (row & 7));
+  }
+  // Codes: chunk c = half * BN + column holds channels [32 half, +32) of the column;
+  // columns past N re-read column N - 1.
+  const int b_off = min(n0 + tid % BN, N - 1) * W + 4 * (tid / BN);
+  // Scales (wavefront 0, 16 B per lane) and zero points (wavefront 1, 4 B per lane) of
+  // half h = lane / 32: 8 columns, resp. one packed word of 8 columns, per lane.
+  const int sz_half = lane >> 5;
+  const int s_col = min(n0 + 8 * (lane & 31), N - 8);
+  const int z_word = min(n0 / 8 + (lane & 31), N / 8 - 1);
+
+  // Tile t goes to stage t % NS; tiles past the end re-load the last one into a stage
+  // that is never read again.  The scale / zero load comes first, so that waiting for
+  // tile t alone never waits for more than that load of tile t + 1.
+  auto load_tile = [&](int t) {
+    const int tc = min(t, KT - 1);
+    unsigned char* stage = smem + (t % NS) * kBigStage;
+    const int gi = (tc * BK + 32 * sz_half) >> gshift;
+    if (wave == 0)
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(scales + static_cast<size_t>(gi) * N + s_col),
+          reinterpret_cast<void*>(stage + kBigLdsA + kBigLdsB), 16, 0, 0);
+    else if (wave == 1)
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const void*>(qzeros + static_cast<size_t>(gi) * (N >> 3) + z_word),
+          reinterpret_cast<void*>(stage + kBigLdsA + kBigLdsB + kBigLdsS), 4, 0, 0);
+    const half_t* xt = x + tc * BK;
+#pragma unroll
+    for (int i = 0; i < APT; ++i)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(xt + a_off[i]),
+                                       reinterpret_cast<void*>(stage + (wave * APT + i) * 64 * 16), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(qw + b_off + tc * (BK / 8)),
+                                     reinterpret_cast<void*>(stage + kBigLdsA + wave * 64 * 16), 16, 0, 0);
+  };
+
+  float4_t acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // This lane's LDS byte addresses in stage 0: A fragment mb of MFMA step s at
+  // a_lane + 16 ((2 q + s) ^ (r % 8)) + 2048 mb; code words of block nb at b_lane +
+  // 256 nb; scale of block nb at s_lane + 32 nb; zero word of block nb at z_lane + 8 nb.
+  const uint32_t base = lds_offset(smem);
+  const uint32_t a_lane = base + (wm * 128 + lr) * 128;
+  const uint32_t b_lane = base + kBigLdsA + ((lq >> 1) * BN + wn * 64 + lr) * 16 + (lq & 1) * 8;
+  const uint32_t s_lane = base + kBigLdsA + kBigLdsB + ((lq >> 1) * BN + wn * 64 + lr) * 2;
+  const uint32_t z_lane = base + kBigLdsA + kBigLdsB + kBigLdsS + ((lq >> 1) * (BN / 8) + wn * 8 + (lr >> 3)) * 4;
+  const int z_shift = 4 * (lr & 7);
+
+  // At most APT + 1 loads of this wavefront are newer than the last load of tile t once
+  // tile t + 1 has been issued after it.
+  load_tile(0);
+  load_tile(1);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(APT + 1) : "memory");   // tile 0
+  block_barrier();
+
+  for (int t = 0; t < KT; ++t) {
+    load_tile(t + NS - 1);
+    const uint32_t so = (t % NS) * kBigStage;
+    half8_t af[MB];
+    uint2 cw[NB];
+    uint32_t sc[NB], zw[NB];
+    lds_read_tile(a_lane + so + 16 * ((2 * lq) ^ (lr & 7)), b_lane + so, s_lane + so, z_lane + so, af, cw, sc, zw);
+    DequantConsts dc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      dc[nb] = make_consts((zw[nb] >> z_shift) & 0xFu, __builtin_bit_cast(half_t, static_cast<uint16_t>(sc[nb])));
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (s == 1) lds_read_a8(a_lane + so + 16 * ((2 * lq + 1) ^ (lr & 7)), af);
+      half8_t bf[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) bf[nb] = dequant_word(s == 0 ? cw[nb].x : cw[nb].y, dc[nb]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(APT + 1) : "memory");   // tile t + 1
+    block_barrier();
+  }
+  // the clamped loads past the last tile must land before the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // D layout of the 16x16 MFMA: lane l holds rows 4*(l/16) + r, column l % 16.
+  const int nw = n0 + wn * 64;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = nw + 16 * nb + lr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * 128 + 16 * mb + 4 * lq + r;
+        if (m < M && n < N) y[static_cast<size_t>(m) * N + n] = static_cast<half_t>(acc[mb][nb][r]);
+      }
+    }
+}
+
 }  // namespace w4a16
