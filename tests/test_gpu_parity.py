@@ -34,6 +34,11 @@ SMALL = [
     ("s10", 257, 776, 640, 128, False),
     ("s11", 200, 264, 2048, 32, True),
     ("s12", 1, 8, 96, 32, False),
+    # skinny batches: every (steps per wavefront, slab entries per thread) shape family
+    ("s13", 5, 392, 8192, 32, True),
+    ("s14", 16, 1048, 4096, 64, False),
+    ("s15", 2, 200, 6144, 128, False),
+    ("s16", 9, 72, 2048, 32, True),
 ]
 
 
@@ -43,9 +48,11 @@ def _small_cfg(name, M, N, K, g, act, idx):
 
 @pytest.fixture(autouse=True)
 def _clear_env():
-    os.environ.pop("W4A16_FORCE_PATH", None)
+    for v in ("W4A16_FORCE_PATH", "W4A16_TUNE_GEMM_SKINNY"):
+        os.environ.pop(v, None)
     yield
-    os.environ.pop("W4A16_FORCE_PATH", None)
+    for v in ("W4A16_FORCE_PATH", "W4A16_TUNE_GEMM_SKINNY"):
+        os.environ.pop(v, None)
 
 
 @pytest.mark.parametrize("case", range(len(SMALL)))
@@ -60,12 +67,16 @@ def test_small_layers_match_oracle(case):
     if act:
         assert np.array_equal(prod["g_idx_np"], ref["g_idx"])
     paths = ["gemv", "gemm"] if M == 1 else ["gemm"]
+    if M <= 16:
+        paths.append("gemm-tiled")      # the tiled MFMA kernel instead of the skinny one
     for path in paths:
-        os.environ["W4A16_FORCE_PATH"] = path
+        os.environ["W4A16_FORCE_PATH"] = path.split("-")[0]
+        os.environ["W4A16_TUNE_GEMM_SKINNY"] = "0" if path == "gemm-tiled" else "1"
         note(f"  path={path}")
         y = run_gemm(prod).cpu().numpy()
         err = oracle.rel_err(y, ref["y_ref"])
         assert err <= TOL, (path, err)
+    os.environ.pop("W4A16_TUNE_GEMM_SKINNY", None)
     # the device weight view is bit-exact
     W16 = w4.w4a16_dequant(prod["qweight"], prod["scales"], prod["qzeros"], prod["g_idx"], g, K).cpu().numpy()
     assert np.array_equal(W16.view(np.uint16), ref["W16"].view(np.uint16))

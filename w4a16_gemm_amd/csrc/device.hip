@@ -12,6 +12,7 @@
 #include "kernels/aux.hpp"
 #include "kernels/gemm.hpp"
 #include "kernels/gemv.hpp"
+#include "kernels/skinny.hpp"
 
 namespace w4a16 {
 namespace {
@@ -184,6 +185,60 @@ void launch_gemm_bm(hipStream_t st, const half_t* x, const uint32_t* qw, const h
   hipLaunchKernelGGL((gemm_mfma_kernel<BM>), grid, dim3(256), 0, st, x, qw, s, z, y, M, N, K, gshift);
 }
 
+// Skinny-batch kernel shape: W wavefronts of T 128-channel steps (K = 128 T W), SE
+// slab entries per thread.  waves == 0: not applicable.
+struct SkinnyShape {
+  int waves = 0, t = 0, se = 0;
+};
+
+constexpr int kSkinnyMaxM = 16;
+
+SkinnyShape pick_skinny_shape(int M, int K, int gshift) {
+  SkinnyShape sh;
+  if (M > kSkinnyMaxM || K % 128 != 0) return sh;
+  const int kc = K / 128;
+  for (int t : {1, 2, 4}) {
+    if (kc % t != 0 || kc / t > 16) continue;
+    const int waves = kc / t;
+    const int entries = 16 * (K >> gshift);
+    const int se = (entries + 64 * waves - 1) / (64 * waves);
+    if (se > 4) return sh;
+    sh.waves = waves;
+    sh.t = t;
+    sh.se = se <= 1 ? 1 : (se <= 2 ? 2 : 4);
+    return sh;
+  }
+  return sh;
+}
+
+template <int T, int SE, bool ACT>
+int launch_skinny_t(const SkinnyShape& sh, hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s,
+                    const uint32_t* z, half_t* y, int M, int N, int K, int gshift) {
+  static const hipError_t lds_ok =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_skinny_kernel<T, SE, ACT>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (int rc = hip_status(lds_ok, "hipFuncSetAttribute")) return rc;
+  const size_t lds = skinny_lds_bytes(sh.waves, K >> gshift);
+  const int nblk = (N + 15) / 16;
+  const int per_cu = std::max(1, 16 / sh.waves);
+  const int grid = std::min(nblk, device_cus() * per_cu);
+  hipLaunchKernelGGL((gemm_skinny_kernel<T, SE, ACT>), dim3(grid), dim3(64 * sh.waves), lds, st, x, qw, s, z, y,
+                     M, N, K, gshift);
+  return check_launch("skinny gemm launch");
+}
+
+template <bool ACT>
+int launch_skinny(const SkinnyShape& sh, hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s,
+                  const uint32_t* z, half_t* y, int M, int N, int K, int gshift) {
+#define W4A16_SKINNY(T_, SE_) \
+  if (sh.t == T_ && sh.se == SE_) return launch_skinny_t<T_, SE_, ACT>(sh, st, x, qw, s, z, y, M, N, K, gshift);
+  W4A16_SKINNY(1, 1) W4A16_SKINNY(1, 2) W4A16_SKINNY(1, 4)
+  W4A16_SKINNY(2, 1) W4A16_SKINNY(2, 2) W4A16_SKINNY(2, 4)
+  W4A16_SKINNY(4, 1) W4A16_SKINNY(4, 2) W4A16_SKINNY(4, 4)
+#undef W4A16_SKINNY
+  return fail(W4A16_ERR_UNSUPPORTED, "no skinny kernel for T=%d SE=%d", sh.t, sh.se);
+}
+
 int run_gemm(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z,
              half_t* y, int M, int N, int K, int gshift) {
   if (M > 128 && K % kBigBK == 0 && static_cast<long long>(M) * K < (1LL << 31) &&
@@ -251,6 +306,11 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
 
   if (use_gemv)
     return run_gemv(sh, act, hx, hq, reinterpret_cast<const uint16_t*>(scales), hz, hy, N, K, gshift, st);
+
+  const SkinnyShape sk = pick_skinny_shape(M, K, gshift);
+  if (sk.waves != 0 && env_int("W4A16_TUNE_GEMM_SKINNY", 1) != 0)
+    return act ? launch_skinny<true>(sk, st, hx, hq, hs, hz, hy, M, N, K, gshift)
+               : launch_skinny<false>(sk, st, hx, hq, hs, hz, hy, M, N, K, gshift);
 
   if (!act) return run_gemm(st, hx, hq, hs, hz, hy, M, N, K, gshift);
 

@@ -1,0 +1,179 @@
+// Skinny batches (M <= 16, decode with a few sequences): y^T = W^ x^T on the matrix
+// cores, with the dequantised weights as the A operand (16 output rows per MFMA) and
+// the activations as the B operand (the M rows padded to 16 columns).
+//
+// Like the GEMV this is HBM-bound ("AWQ + GPTQ Quantization, in depth", What W4A16
+// buys: decoding reads every weight once per token), so the layout is built around
+// streaming the codes once with 16-byte loads:
+//  * A workgroup of W wavefronts splits K: wavefront w owns channels
+//    [128 T w, 128 T (w + 1)) and keeps the activations of that slice in registers
+//    for the whole kernel (T x 4 fragments of 8 binary16 per lane).
+//  * The workgroup walks blocks of 16 output rows.  Per block and slice step t, lane
+//    (r, q) = (lane % 16, lane / 16) loads 16 bytes of row r: the 32 channels
+//    [128 (T w + t) + 32 q, +32), whose four words are its A operands of four MFMAs.
+//    The B operand of lane (m, q) in the j-th of them is x[m] at the channels of word
+//    j of that load, so the k order inside an MFMA is a permutation that pairs every
+//    weight with its own activation.
+//  * The 32 channels of one load lie in one group (group size >= 32), so one scale
+//    and one zero point per lane and step build the binary16 weights (q - Z) * S with
+//    one rounding, as in the large-M GEMM.  The scales and zero points of a row block
+//    are staged once in an LDS slab, double buffered, by all threads of the workgroup.
+//  * The W partial 16 x 16 tiles are summed in LDS in a fixed order and rounded once
+//    to binary16.  Codes of the next row block are in flight while a block is computed.
+// Act order: the activation slice is gathered through the stored channel order
+// when it is loaded into registers, so no scratch copy of x is needed.
+#pragma once
+
+#include "nibbles.hpp"
+
+namespace w4a16 {
+
+// Entry of the scale / zero slab: binary16 S and -(1024 + Z) in .x, -(64 + Z) in .y.
+__device__ __forceinline__ uint2 slab_entry(half_t s, uint32_t z) {
+  const half_t a = static_cast<half_t>(-1024.0f - static_cast<float>(z));
+  const half_t b = static_cast<half_t>(-64.0f - static_cast<float>(z));
+  return uint2{static_cast<uint32_t>(__builtin_bit_cast(uint16_t, s)) |
+                   (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) << 16),
+               static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b))};
+}
+
+__device__ __forceinline__ DequantConsts slab_consts(uint2 e) {
+  const half_t s = __builtin_bit_cast(half_t, static_cast<uint16_t>(e.x & 0xFFFFu));
+  const half_t a = __builtin_bit_cast(half_t, static_cast<uint16_t>(e.x >> 16));
+  const half_t b = __builtin_bit_cast(half_t, static_cast<uint16_t>(e.y & 0xFFFFu));
+  DequantConsts c;
+  c.neg_1024_z = half2_t{a, a};
+  c.neg_64_z = half2_t{b, b};
+  c.scale = half2_t{s, s};
+  return c;
+}
+
+// LDS bytes of the kernel for W wavefronts and G groups per row.
+constexpr size_t skinny_lds_bytes(int waves, int groups) {
+  return 2 * static_cast<size_t>(waves) * 256 * sizeof(float) + 2 * static_cast<size_t>(16) * groups * sizeof(uint2);
+}
+
+// T: 128-channel steps per wavefront (K = 128 T W).  SE: slab entries (16 G per row
+// block) loaded per thread, SE * 64 W >= 16 G.
+template <int T, int SE, bool ACT>
+__global__ __launch_bounds__(1024) void gemm_skinny_kernel(
+    const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const half_t* __restrict__ scales,
+    const uint32_t* __restrict__ qzeros, half_t* __restrict__ y, int M, int N, int K, int gshift) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int nthreads = blockDim.x;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int Wd = K >> 3;
+  const int G = K >> gshift;
+  const int slab_n = 16 * G;
+  const int nblk = (N + 15) >> 4;
+  const int kw = wave * 128 * T;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* red = reinterpret_cast<float*>(smem);                                              // [2][W][16 m][16 n]
+  uint2* slab = reinterpret_cast<uint2*>(smem + 2 * static_cast<size_t>(nwaves) * 256 * sizeof(float));  // [2][G][16]
+
+  // Activation slice: xr[t][j] = x[m][kw + 128 t + 32 q + 8 j, +8) for m = lane % 16;
+  // zero for m >= M.
+  half8_t xr[T][4];
+  {
+    const int m = lr < M ? lr : 0;
+    const half_t* xm = x + static_cast<size_t>(m) * K;
+    const int32_t* perm = reinterpret_cast<const int32_t*>(qw + static_cast<size_t>(N) * Wd);
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int p0 = kw + 128 * t + 32 * lq + 8 * j;
+        half8_t v;
+        if constexpr (ACT) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = xm[perm[p0 + e]];
+        } else {
+          v = *reinterpret_cast<const half8_t*>(xm + p0);
+        }
+        xr[t][j] = lr < M ? v : half8_t{};
+      }
+  }
+
+  // Codes of row block b for this lane (rows past N re-read row N - 1).
+  auto load_codes = [&](int b, uint4 (&cw)[T]) {
+    const int n = min(16 * b + lr, N - 1);
+    const uint4* src = reinterpret_cast<const uint4*>(qw + static_cast<size_t>(n) * Wd + (kw >> 3) + 4 * lq);
+#pragma unroll
+    for (int t = 0; t < T; ++t) cw[t] = src[4 * t];   // 128 channels = 16 words = 4 uint4 per step
+  };
+  // Scale and zero word of slab entries tid + u * nthreads of row block b.
+  half_t sv[SE];
+  uint32_t zv[SE];
+  auto load_sz = [&](int b) {
+#pragma unroll
+    for (int u = 0; u < SE; ++u) {
+      const int e = min(tid + u * nthreads, slab_n - 1);
+      const int gi = e >> 4;
+      const int n = min(16 * b + (e & 15), N - 1);
+      sv[u] = scales[static_cast<size_t>(gi) * N + n];
+      zv[u] = qzeros[static_cast<size_t>(gi) * (N >> 3) + (n >> 3)];
+    }
+  };
+  auto write_slab = [&](int b, int buf) {
+#pragma unroll
+    for (int u = 0; u < SE; ++u) {
+      const int e = tid + u * nthreads;
+      if (e < slab_n) {
+        const int n = min(16 * b + (e & 15), N - 1);
+        slab[buf * slab_n + e] = slab_entry(sv[u], (zv[u] >> ((n & 7) * 4)) & 0xFu);
+      }
+    }
+  };
+
+  // One row block: partial tile from this wavefront's slice; each step's code slot is
+  // refilled with the next row block's codes as soon as it has been used, so a load
+  // has a whole row block of work to land.  The slab of the next block is written and
+  // its successor's scales issued; the partial tiles are summed after the barrier.
+  uint4 cw[T];
+  auto row_block = [&](int b, int i) {
+    const int buf = i & 1;
+    const int n_next = min(16 * (b + static_cast<int>(gridDim.x)) + lr, N - 1);
+    const uint4* src = reinterpret_cast<const uint4*>(qw + static_cast<size_t>(n_next) * Wd + (kw >> 3) + 4 * lq);
+    float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int gi = (kw + 128 * t + 32 * lq) >> gshift;
+      const DequantConsts dc = slab_consts(slab[buf * slab_n + gi * 16 + lr]);
+      const uint32_t w4[4] = {cw[t].x, cw[t].y, cw[t].z, cw[t].w};
+      half8_t wf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wf[j] = dequant_word(w4[j], dc);
+      cw[t] = src[4 * t];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j], xr[t][j], acc, 0, 0, 0);
+    }
+    // D layout: lane (r, q) holds rows n = 4 q + 0..3 of column m = r.
+    *reinterpret_cast<float4_t*>(red + ((buf * nwaves + wave) * 16 + lr) * 16 + 4 * lq) = acc;
+    write_slab(b + static_cast<int>(gridDim.x), buf ^ 1);
+    load_sz(b + 2 * static_cast<int>(gridDim.x));
+    __syncthreads();
+    if (tid < 256) {
+      const int m = tid >> 4, n = 16 * b + (tid & 15);
+      if (m < M && n < N) {
+        const float* p = red + buf * nwaves * 256 + tid;
+        float s = 0.f;
+        for (int w = 0; w < nwaves; ++w) s += p[w * 256];
+        y[static_cast<size_t>(m) * N + n] = static_cast<half_t>(s);
+      }
+    }
+  };
+
+  int b = blockIdx.x;
+  load_codes(b, cw);
+  load_sz(b);
+  write_slab(b, 0);
+  load_sz(b + static_cast<int>(gridDim.x));
+  __syncthreads();
+  for (int i = 0; b < nblk; ++i, b += gridDim.x) row_block(b, i);
+}
+
+}  // namespace w4a16
