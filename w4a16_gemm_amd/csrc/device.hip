@@ -144,28 +144,32 @@ void launch_gemv_lpr(const GemvShape& sh, dim3 grid, size_t shmem, hipStream_t s
   }
 }
 
-// LDS of one workgroup: the activations plus a rows x (G+1) slab of float2.
-size_t gemv_lds_bytes(int K, int G, int rows) {
-  return static_cast<size_t>(K) * sizeof(half_t) + static_cast<size_t>(rows) * (G + 1) * 2 * sizeof(float);
+// LDS of one workgroup: the two-slot scale/zero ring (unit rows x (G+1) float2 each),
+// the row results, and the gathered activations under act order.
+size_t gemv_lds_bytes(int K, int G, int unit, int steps, bool act) {
+  return 2 * static_cast<size_t>(unit) * (G + 1) * 2 * sizeof(float) + static_cast<size_t>(steps) * unit * sizeof(float) +
+         (act ? static_cast<size_t>(K) * sizeof(half_t) : 0);
 }
 
 int run_gemv(const GemvShape& sh, bool act, const half_t* x, const uint32_t* qw, const uint16_t* s,
              const uint32_t* z, half_t* y, int N, int K, int gshift, hipStream_t st) {
   const int G = K >> gshift;
   const int unit = kGemvWaves * (64 / sh.lpr);                 // rows per unit
+  if ((unit / 8) * G > kGemvWaves * 64)
+    return fail(W4A16_ERR_UNSUPPORTED, "GEMV staging: %d items per step exceed one per thread", (unit / 8) * G);
   const int units = (N + unit - 1) / unit;
   const int per_cu = env_int("W4A16_TUNE_GEMV_BLOCKS_PER_CU", 1);
   int blocks = std::min(units, std::max(1, device_cus() * std::max(1, per_cu)));
   if (blocks >= 8) blocks -= blocks % 8;                         // whole XCD rounds
   int steps = (units + blocks - 1) / blocks;
-  while (gemv_lds_bytes(K, G, steps * unit) > kGemvLdsBudget && blocks < units) {
+  while (gemv_lds_bytes(K, G, unit, steps, act) > kGemvLdsBudget && blocks < units) {
     blocks = std::min(units, blocks * 2);
     steps = (units + blocks - 1) / blocks;
   }
-  if (gemv_lds_bytes(K, G, steps * unit) > kGemvLdsBudget)
-    return fail(W4A16_ERR_UNSUPPORTED, "GEMV staging for K=%d, G=%d does not fit in LDS", K, G);
+  if (gemv_lds_bytes(K, G, unit, steps, act) > kGemvLdsBudget)
+    return fail(W4A16_ERR_UNSUPPORTED, "GEMV staging for N=%d, K=%d does not fit in LDS", N, K);
   const dim3 grid(blocks);
-  const size_t shmem = gemv_lds_bytes(K, G, steps * unit);
+  const size_t shmem = gemv_lds_bytes(K, G, unit, steps, act);
   if (sh.exact) {
     if (act) launch_gemv_lpr<true, true>(sh, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
     else launch_gemv_lpr<true, false>(sh, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);

@@ -14,27 +14,33 @@
 //    LPR lanes share a row; lane j owns chunks j, j+LPR, ... (CPL of them), so each
 //    wave-wide 16-byte load is one contiguous run of the row.
 //  * Each wavefront walks its rows with a DEPTH-deep register pipeline: the loads
-//    of row t+DEPTH are issued as soon as row t has been consumed.  The first
-//    DEPTH rows are requested before anything else happens in the workgroup.
-//  * Activations are staged once in LDS (gathered through the stored order under
-//    act order) and then held in registers: a lane owns the same chunks in every
-//    row.  The scales and zero points of all the workgroup's rows are staged once in
-//    LDS as one word per (row, group), transposed so that a lane's reads are
-//    conflict-free.
+//    of row t+DEPTH are issued as soon as row t has been consumed.
+//  * Activations are loaded once into registers (under act order gathered through
+//    the stored order via LDS): a lane owns the same chunks in every row.
+//  * Scales and zero points follow the sweep: the (S * 2^24, -Z * S) pairs of one
+//    step's rows are staged in a two-slot LDS ring, one item (8 rows of one group:
+//    16 bytes of scales, one word of zero points) per thread, requested two steps
+//    ahead and published by the workgroup barrier that closes each step.  Staging a
+//    step at a time keeps those small scattered reads in the same DRAM pages as the
+//    weights being streamed and spreads them over the kernel.
 //  * Codes are expanded by masking alone: a pair of nibbles in the mantissa bits of a
 //    binary16 pair with a zero exponent field is the exact subnormal pair
 //    (q, q') * 2^-24 (nibbles.hpp).  v_dot2_f32_f16 multiplies them with the
 //    activations into two fp32 accumulators per chunk, one for the pairs taken from
 //    the low nibbles of each byte and one, 16 times larger, for the high nibbles.
 //    After the chunk t = acc_a + acc_b / 16 = 2^-24 * sum x q, and the zero point and
-//    scale enter once per chunk through two fp32 values staged per (row, group):
+//    scale enter once per chunk:
 //        row += t * (S * 2^24) + (-Z * S) * sum x.
 //    9 VALU instructions per 8 weights in the inner loop, all but the dot products
 //    plain 32-bit AND/shift.
 //  * The LPR partial sums of a row are reduced inside the wavefront with DPP moves
 //    only (mirrors within rows of 16 lanes, row broadcasts across them); the row
-//    result is rounded once to binary16.
+//    result is rounded once to binary16.  Results wait in LDS and are stored at the
+//    end: a store counts against the same wait counter as the loads, so stores in the
+//    loop would hold back the waits for the weight pipeline.
 #pragma once
+
+#include <type_traits>
 
 #include "nibbles.hpp"
 
@@ -71,14 +77,19 @@ __device__ __forceinline__ int xcd_block(int bid, int nblk) {
 // (one row per wavefront row-slot); unit u is processed by workgroup u % nblk at step
 // u / nblk.  At any moment the whole grid streams one contiguous window of the
 // weights, and within a unit the wavefronts read neighbouring rows.
+// LDS: scale/zero ring 2 * STRIDE * (G + 1) float2, row results steps * STRIDE floats,
+// and under act order the gathered activations, K binary16.  Needs OCT * G <= WAVES * 64
+// (one staging item per thread and step) and an even DEPTH.
 template <int LPR, int CPL, int WAVES, int DEPTH, bool EXACT, bool ACT>
 __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
     const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
     const uint32_t* __restrict__ qzeros, half_t* __restrict__ y, int N, int K, int gshift, int steps) {
   static_assert(64 % LPR == 0, "lanes per row must divide the wavefront");
+  static_assert(DEPTH % 2 == 0, "the ring slot of row t is t % 2, the unrolled slot index");
   constexpr int RPW = 64 / LPR;          // rows per wavefront per step
   constexpr int STRIDE = WAVES * RPW;    // rows per unit
   static_assert(STRIDE % 8 == 0, "a unit must cover whole 8-row groups of zero points");
+  constexpr int OCT = STRIDE / 8;        // 8-row groups per unit
   constexpr int NT = WAVES * 64;
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -90,103 +101,120 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   const int C = K >> 5;                  // 32-channel chunks per row
   const int W = K >> 3;                  // words per row
   const int G = K >> gshift;
-  const int GP = G + 1;                  // padded slab row (words)
+  const int GP = G + 1;                  // padded ring row (float2)
   const int nblk = gridDim.x;
   const int blk = xcd_block(blockIdx.x, nblk);
   const int my_row = wave * RPW + rr;    // row inside a unit
   auto row_of = [&](int t) { return (blk + t * nblk) * STRIDE + my_row; };
 
-  half_t* xs = reinterpret_cast<half_t*>(smem);
-  float2* sz = reinterpret_cast<float2*>(smem + static_cast<size_t>(K) * sizeof(half_t));
+  float2* ring = reinterpret_cast<float2*>(smem);                                   // [2][STRIDE][GP]
+  float* ybuf = reinterpret_cast<float*>(smem + 2 * static_cast<size_t>(STRIDE) * GP * sizeof(float2));
+  half_t* xs = reinterpret_cast<half_t*>(ybuf + static_cast<size_t>(steps) * STRIDE);
 
-  // 1. the first DEPTH rows of this wavefront: request the weights now.  Loads are
-  // unconditional (row clamped into the matrix, chunk clamped into the row) so that
-  // no load sits in a divergent branch and the wait counts stay exact.
+  // This lane's chunks (clamped into the row unless the split is exact) and groups.
+  int chunk[CPL], gcol[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    chunk[i] = EXACT ? j + LPR * i : min(j + LPR * i, C - 1);
+    gcol[i] = (chunk[i] << 5) >> gshift;
+  }
+
+  // Staging item of this thread: group gi of the 8 rows [8 o, 8 o + 8) of the unit.
+  const int items = OCT * G;
+  const int it_c = min(tid, items - 1);
+  const int it_g = it_c % G;
+  const int it_o = it_c / G;
+  uint4 zs_s[2];
+  uint32_t zs_z[2];
+  auto load_item = [&](int t, int set) {   // unconditional: rows and steps clamped
+    const int n8 = min((blk + min(t, steps - 1) * nblk) * STRIDE + 8 * it_o, N - 8);
+    zs_s[set] = *reinterpret_cast<const uint4*>(scales + static_cast<size_t>(it_g) * N + n8);
+    zs_z[set] = qzeros[static_cast<size_t>(it_g) * (N >> 3) + (n8 >> 3)];
+  };
+  auto put_item = [&](int set, int slot) {
+    if (tid < items) {
+      float2* dst = ring + (slot * STRIDE + 8 * it_o) * GP + it_g;
+      const uint32_t s8[4] = {zs_s[set].x, zs_s[set].y, zs_s[set].z, zs_s[set].w};
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float S = static_cast<float>(
+            __builtin_bit_cast(half_t, static_cast<uint16_t>((s8[r >> 1] >> (16 * (r & 1))) & 0xFFFFu)));
+        const float Z = static_cast<float>((zs_z[set] >> (4 * r)) & 0xFu);
+        dst[r * GP] = make_float2(S * 16777216.0f, -Z * S);   // both exact in fp32
+      }
+    }
+  };
+
+  // 1. Requests, smallest first so they do not queue behind the weights: the
+  // activations of this lane's chunks (without act order straight into registers),
+  // the staging items of steps 0 and 1, then the first DEPTH rows of codes.
+  uint4 xv[CPL][4];
+  if constexpr (!ACT) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xv[i][q] = reinterpret_cast<const uint4*>(x)[4 * chunk[i] + q];
+  }
+  load_item(0, 0);
+  load_item(1, 1);
   uint4 wb[DEPTH][CPL];
-  auto load_row = [&](uint4 (&dst)[CPL], int n) {
+  auto load_row = [&](uint4 (&dst)[CPL], int n) {   // unconditional: row clamped into the matrix
     const int nc = min(n, N - 1);
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int c = EXACT ? j + LPR * i : min(j + LPR * i, C - 1);
-      dst[i] = *reinterpret_cast<const uint4*>(qw + static_cast<size_t>(nc) * W + 4 * c);
-    }
+    for (int i = 0; i < CPL; ++i)
+      dst[i] = *reinterpret_cast<const uint4*>(qw + static_cast<size_t>(nc) * W + 4 * chunk[i]);
   };
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) load_row(wb[d], row_of(d));  // clamped if steps < DEPTH
 
-  // 2. activations -> LDS (stored order), and the workgroup's scales and zero points
-  // -> a slab with (S * 2^24, -Z * S) in fp32 per (row slot, group), loaded 8 rows
-  // (16 bytes of scales, one word of zeros) at a time.
-  if constexpr (!ACT) {
-    const uint4* src = reinterpret_cast<const uint4*>(x);
-    uint4* dst = reinterpret_cast<uint4*>(xs);
-    for (int i = tid; i < (K >> 3); i += NT) dst[i] = src[i];
-  } else {
+  // 2. Act order: gather the activations into LDS in stored order.  Step 0's items go
+  // to ring slot 0; the barrier publishes both.
+  if constexpr (ACT) {
     const int32_t* perm = reinterpret_cast<const int32_t*>(qw + static_cast<size_t>(N) * W);
     for (int p = tid; p < K; p += NT) xs[p] = x[perm[p]];
   }
-  {
-    constexpr int OCT = STRIDE / 8;      // 8-row groups per unit
-    const int items = steps * OCT * G;
-    for (int it = tid; it < items; it += NT) {
-      const int gi = it % G;
-      const int so = it / G;             // (step, octet)
-      const int t = so / OCT;
-      const int o = so - t * OCT;
-      const int n8 = (blk + t * nblk) * STRIDE + 8 * o;
-      float2* dst = sz + (t * STRIDE + 8 * o) * GP + gi;
-      if (n8 < N) {
-        const uint4 sv = *reinterpret_cast<const uint4*>(scales + static_cast<size_t>(gi) * N + n8);
-        const uint32_t zw = qzeros[static_cast<size_t>(gi) * (N >> 3) + (n8 >> 3)];
-        const uint32_t s8[4] = {sv.x, sv.y, sv.z, sv.w};
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const float S = static_cast<float>(
-              __builtin_bit_cast(half_t, static_cast<uint16_t>((s8[r >> 1] >> (16 * (r & 1))) & 0xFFFFu)));
-          const float Z = static_cast<float>((zw >> (4 * r)) & 0xFu);
-          dst[r * GP] = make_float2(S * 16777216.0f, -Z * S);   // both exact in fp32
-        }
-      }
-    }
-  }
+  put_item(0, 0);
   __syncthreads();
+  if constexpr (ACT) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xv[i][q] = reinterpret_cast<const uint4*>(xs)[4 * chunk[i] + q];
+  }
 
-  // 3. this lane's activations, as pairs, and the per-chunk sums (dot2 with ones)
+  // 3. this lane's activations as pairs, and the per-chunk sums (dot2 with ones);
+  // chunks past the end of the row (inexact split) contribute nothing.
   half2_t xr[CPL][16];
   float xsum[CPL];
-  int gcol[CPL];
   const half2_t ones = half2_t{static_cast<half_t>(1.0f), static_cast<half_t>(1.0f)};
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
-    const int c = j + LPR * i;
-    gcol[i] = (c << 5) >> gshift;
+    const bool live = EXACT || j + LPR * i < C;
     float sx = 0.f;
-    if (EXACT || c < C) {
-      const uint4* src = reinterpret_cast<const uint4*>(xs + 32 * c);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 v = src[q];
-        xr[i][4 * q + 0] = as_h2(v.x);
-        xr[i][4 * q + 1] = as_h2(v.y);
-        xr[i][4 * q + 2] = as_h2(v.z);
-        xr[i][4 * q + 3] = as_h2(v.w);
-      }
-#pragma unroll
-      for (int q = 0; q < 16; ++q) sx = __builtin_amdgcn_fdot2(xr[i][q], ones, sx, false);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) xr[i][q] = half2_t{0, 0};
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = xv[i][q];
+      xr[i][4 * q + 0] = live ? as_h2(v.x) : half2_t{0, 0};
+      xr[i][4 * q + 1] = live ? as_h2(v.y) : half2_t{0, 0};
+      xr[i][4 * q + 2] = live ? as_h2(v.z) : half2_t{0, 0};
+      xr[i][4 * q + 3] = live ? as_h2(v.w) : half2_t{0, 0};
     }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) sx = __builtin_amdgcn_fdot2(xr[i][q], ones, sx, false);
     xsum[i] = sx;
   }
 
-  // 4. rows.  Row t sits in register slot t % DEPTH; its loads were issued DEPTH
-  // steps earlier.  The steady-state loop refills every slot unconditionally; the
-  // last DEPTH steps run without refills, so no load is issued past the end (a wave
-  // cannot retire before its loads return).
-  auto row_step = [&](int t, uint4 (&w)[CPL]) {
-    const int n = row_of(t);
-    const float2* szr = sz + (t * STRIDE + my_row) * GP;
+  // 4. rows.  Row t sits in register slot t % DEPTH; its codes were requested DEPTH
+  // steps earlier, its staging items two steps earlier into set t % 2, and they were
+  // published into ring slot t % 2 by the barrier closing step t - 1.  Every step
+  // (a) requests the items of step t + 2, (b) computes row t and refills its slot,
+  // (c) stages step t + 1 and closes with the barrier.  The last DEPTH steps run
+  // without code refills, so no load is issued past the end.
+  auto row_step = [&](int t, int slot, uint4 (&w)[CPL]) {
+    const float2* szr = ring + (slot * STRIDE + my_row) * GP;
+    float2 sc[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) sc[i] = szr[gcol[i]];
     // The CPL chunks are interleaved word by word: 2*CPL independent dot2
     // accumulation chains (each still summed in the same order).
     float aa[CPL], ab[CPL];
@@ -210,43 +238,56 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      const int c = j + LPR * i;
-      if (EXACT || c < C) {
-        const float2 sc = szr[gcol[i]];
-        const float tq = fmaf(ab[i], 0.0625f, aa[i]);  // 2^-24 * sum x q
-        acc = fmaf(tq, sc.x, acc);                     // + S * sum x q
-        acc = fmaf(sc.y, xsum[i], acc);                // - Z * S * sum x
-      }
+      const float tq = fmaf(ab[i], 0.0625f, aa[i]);  // 2^-24 * sum x q
+      acc = fmaf(tq, sc[i].x, acc);                  // + S * sum x q
+      acc = fmaf(sc[i].y, xsum[i], acc);             // - Z * S * sum x
     }
     return acc;
   };
-  auto finish = [&](int t, float acc) {
-    const int n = row_of(t);
+  // The row total ends in lane LPR - 1 of the row's lane group.
+  auto keep = [&](int t, float acc) {
     acc = lane_group_sum<LPR>(acc);
-    if (n < N && j == LPR - 1) y[n] = static_cast<half_t>(acc);
+    if (j == LPR - 1) ybuf[t * STRIDE + my_row] = acc;
+  };
+  // one step; P = t % 2 at compile time (t0 is a multiple of the even DEPTH)
+  auto step = [&](int t, int d, bool refill, auto P) {
+    constexpr int p = decltype(P)::value;
+    load_item(t + 2, p);                                  // (a) into the set just published
+    const float acc = row_step(t, p, wb[d]);               // (b)
+    if (refill) load_row(wb[d], row_of(t + DEPTH));
+    __builtin_amdgcn_sched_barrier(0);
+    keep(t, acc);
+    put_item(p ^ 1, p ^ 1);                               // (c) step t + 1
+    __syncthreads();
   };
 
   int t0 = 0;
   for (; t0 + 2 * DEPTH <= steps; t0 += DEPTH) {
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const float acc = row_step(t0 + d, wb[d]);
-      load_row(wb[d], row_of(t0 + d + DEPTH));       // refill this slot
-      finish(t0 + d, acc);
+    for (int d = 0; d < DEPTH; d += 2) {
+      step(t0 + d, d, true, std::integral_constant<int, 0>{});
+      step(t0 + d + 1, d + 1, true, std::integral_constant<int, 1>{});
     }
   }
   // between DEPTH and 2*DEPTH - 1 steps remain (or fewer than DEPTH in total)
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) {
-    if (t0 + d < steps) {
-      const float acc = row_step(t0 + d, wb[d]);
-      if (t0 + d + DEPTH < steps) load_row(wb[d], row_of(t0 + d + DEPTH));
-      finish(t0 + d, acc);
-    }
+  for (int d = 0; d < DEPTH; d += 2) {
+    if (t0 + d < steps) step(t0 + d, d, t0 + d + DEPTH < steps, std::integral_constant<int, 0>{});
+    if (t0 + d + 1 < steps) step(t0 + d + 1, d + 1, t0 + d + 1 + DEPTH < steps, std::integral_constant<int, 1>{});
   }
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (t0 + DEPTH + d < steps) finish(t0 + DEPTH + d, row_step(t0 + DEPTH + d, wb[d]));
+  for (int d = 0; d < DEPTH; d += 2) {
+    if (t0 + DEPTH + d < steps) step(t0 + DEPTH + d, d, false, std::integral_constant<int, 0>{});
+    if (t0 + DEPTH + d + 1 < steps) step(t0 + DEPTH + d + 1, d + 1, false, std::integral_constant<int, 1>{});
+  }
+
+  // 5. the workgroup's rows: STRIDE consecutive outputs per step (the last step's
+  // barrier published every result)
+  for (int idx = tid; idx < steps * STRIDE; idx += NT) {
+    const int t = idx / STRIDE;
+    const int n = (blk + t * nblk) * STRIDE + (idx - t * STRIDE);
+    if (n < N) y[n] = static_cast<half_t>(ybuf[idx]);
+  }
 }
 
 }  // namespace w4a16
