@@ -243,18 +243,48 @@ int launch_skinny(const SkinnyShape& sh, hipStream_t st, const half_t* x, const 
   return fail(W4A16_ERR_UNSUPPORTED, "no skinny kernel for T=%d SE=%d", sh.t, sh.se);
 }
 
+// Large-M GEMM.  Full 256 x 256 tiles, except when they would need more than one but
+// less than two rounds of workgroups over the compute units: then one round of full
+// tiles covers the first columns and one round of narrower tiles (64 NB2 wide) the
+// rest, so that neither round leaves compute units idle.
+template <int NB2>
+int launch_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z, half_t* y,
+               int M, int N, int K, int gshift, int split, int n_split, int grid) {
+  static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_big_kernel<NB2>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       static_cast<int>(kBigLds));
+  if (int rc = hip_status(lds_ok, "hipFuncSetAttribute")) return rc;
+  hipLaunchKernelGGL(gemm_big_kernel<NB2>, dim3(grid), dim3(512), kBigLds, st, x, qw, s, z, y, M, N, K, gshift, split,
+                     n_split);
+  return check_launch("gemm launch");
+}
+
+int run_gemm_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z, half_t* y,
+                 int M, int N, int K, int gshift) {
+  const int tiles_m = (M + kBigBM - 1) / kBigBM;
+  const int cus = device_cus();
+  const int full = tiles_m * ((N + 255) / 256);
+  if (full > cus && full < 2 * cus && cus % tiles_m == 0 && env_int("W4A16_TUNE_GEMM_SPLIT", 1) != 0) {
+    const int per_panel = cus / tiles_m;
+    const int n_split = 256 * per_panel;
+    const int rest = N - n_split;
+    const int nb2 = (((rest + per_panel - 1) / per_panel) + 63) / 64;   // 64-column blocks per narrow tile
+    if (rest > 0 && nb2 >= 1 && nb2 <= 3) {
+      const int split = tiles_m * per_panel;
+      const int grid = split + tiles_m * ((rest + 64 * nb2 - 1) / (64 * nb2));
+      if (nb2 == 1) return launch_big<1>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
+      if (nb2 == 2) return launch_big<2>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
+      return launch_big<3>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
+    }
+  }
+  return launch_big<4>(st, x, qw, s, z, y, M, N, K, gshift, 0, 0, full);
+}
+
 int run_gemm(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z,
              half_t* y, int M, int N, int K, int gshift) {
   if (M > 128 && K % kBigBK == 0 && static_cast<long long>(M) * K < (1LL << 31) &&
-      env_int("W4A16_TUNE_GEMM_BIG", 1) != 0) {
-    static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_big_kernel),
-                                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                         static_cast<int>(kBigLds));
-    if (int rc = hip_status(lds_ok, "hipFuncSetAttribute")) return rc;
-    const int tiles = ((M + kBigBM - 1) / kBigBM) * ((N + kBigBN - 1) / kBigBN);
-    hipLaunchKernelGGL(gemm_big_kernel, dim3(tiles), dim3(512), kBigLds, st, x, qw, s, z, y, M, N, K, gshift);
-    return check_launch("gemm launch");
-  }
+      env_int("W4A16_TUNE_GEMM_BIG", 1) != 0)
+    return run_gemm_big(st, x, qw, s, z, y, M, N, K, gshift);
   if (M <= 16)
     launch_gemm_bm<16>(st, x, qw, s, z, y, M, N, K, gshift);
   else if (M <= 32)

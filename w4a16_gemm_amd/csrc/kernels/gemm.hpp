@@ -197,11 +197,93 @@ __device__ __forceinline__ void lds_read_a8(uint32_t addr, half8_t (&af)[8]) {
       : "memory");
 }
 
-// The same eight A fragments, plus cw[nb] = 8 bytes at b_addr + 256 nb, the 16-bit
-// sc[nb] at s_addr + 32 nb and the 32-bit zw[nb] at z_addr + 8 nb, nb = 0..3.
+// The eight A fragments of lds_read_a8, plus for nb < NB: cw[nb] = 8 bytes at
+// b_addr + 256 nb, the 16-bit sc[nb] at s_addr + 32 nb and the 32-bit zw[nb] at
+// z_addr + 8 nb.  One asm statement per NB, waiting for all of its results.
+template <int NB>
 __device__ __forceinline__ void lds_read_tile(uint32_t a_addr, uint32_t b_addr, uint32_t s_addr, uint32_t z_addr,
-                                              half8_t (&af)[8], uint2 (&cw)[4], uint32_t (&sc)[4],
-                                              uint32_t (&zw)[4]) {
+                                              half8_t (&af)[8], uint2 (&cw)[NB], uint32_t (&sc)[NB],
+                                              uint32_t (&zw)[NB]);
+template <>
+__device__ __forceinline__ void lds_read_tile<1>(uint32_t a_addr, uint32_t b_addr, uint32_t s_addr, uint32_t z_addr,
+                                                 half8_t (&af)[8], uint2 (&cw)[1], uint32_t (&sc)[1],
+                                                 uint32_t (&zw)[1]) {
+  asm volatile(
+      "ds_read_u16 %9, %13\n"
+      "ds_read_b32 %10, %14\n"
+      "ds_read_b64 %8, %12\n"
+      "ds_read_b128 %0, %11\n"
+      "ds_read_b128 %1, %11 offset:2048\n"
+      "ds_read_b128 %2, %11 offset:4096\n"
+      "ds_read_b128 %3, %11 offset:6144\n"
+      "ds_read_b128 %4, %11 offset:8192\n"
+      "ds_read_b128 %5, %11 offset:10240\n"
+      "ds_read_b128 %6, %11 offset:12288\n"
+      "ds_read_b128 %7, %11 offset:14336\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(af[4]), "=&v"(af[5]), "=&v"(af[6]),
+        "=&v"(af[7]), "=&v"(cw[0]), "=&v"(sc[0]), "=&v"(zw[0])
+      : "v"(a_addr), "v"(b_addr), "v"(s_addr), "v"(z_addr)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void lds_read_tile<2>(uint32_t a_addr, uint32_t b_addr, uint32_t s_addr, uint32_t z_addr,
+                                                 half8_t (&af)[8], uint2 (&cw)[2], uint32_t (&sc)[2],
+                                                 uint32_t (&zw)[2]) {
+  asm volatile(
+      "ds_read_u16 %10, %16\n"
+      "ds_read_u16 %11, %16 offset:32\n"
+      "ds_read_b32 %12, %17\n"
+      "ds_read_b32 %13, %17 offset:8\n"
+      "ds_read_b64 %8, %15\n"
+      "ds_read_b64 %9, %15 offset:256\n"
+      "ds_read_b128 %0, %14\n"
+      "ds_read_b128 %1, %14 offset:2048\n"
+      "ds_read_b128 %2, %14 offset:4096\n"
+      "ds_read_b128 %3, %14 offset:6144\n"
+      "ds_read_b128 %4, %14 offset:8192\n"
+      "ds_read_b128 %5, %14 offset:10240\n"
+      "ds_read_b128 %6, %14 offset:12288\n"
+      "ds_read_b128 %7, %14 offset:14336\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(af[4]), "=&v"(af[5]), "=&v"(af[6]), "=&v"(af[7]), "=&v"(cw[0]), "=&v"(cw[1]), "=&v"(sc[0]), "=&v"(sc[1]), "=&v"(zw[0]), "=&v"(zw[1])
+      : "v"(a_addr), "v"(b_addr), "v"(s_addr), "v"(z_addr)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void lds_read_tile<3>(uint32_t a_addr, uint32_t b_addr, uint32_t s_addr, uint32_t z_addr,
+                                                 half8_t (&af)[8], uint2 (&cw)[3], uint32_t (&sc)[3],
+                                                 uint32_t (&zw)[3]) {
+  asm volatile(
+      "ds_read_u16 %11, %19\n"
+      "ds_read_u16 %12, %19 offset:32\n"
+      "ds_read_u16 %13, %19 offset:64\n"
+      "ds_read_b32 %14, %20\n"
+      "ds_read_b32 %15, %20 offset:8\n"
+      "ds_read_b32 %16, %20 offset:16\n"
+      "ds_read_b64 %8, %18\n"
+      "ds_read_b64 %9, %18 offset:256\n"
+      "ds_read_b64 %10, %18 offset:512\n"
+      "ds_read_b128 %0, %17\n"
+      "ds_read_b128 %1, %17 offset:2048\n"
+      "ds_read_b128 %2, %17 offset:4096\n"
+      "ds_read_b128 %3, %17 offset:6144\n"
+      "ds_read_b128 %4, %17 offset:8192\n"
+      "ds_read_b128 %5, %17 offset:10240\n"
+      "ds_read_b128 %6, %17 offset:12288\n"
+      "ds_read_b128 %7, %17 offset:14336\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(af[4]), "=&v"(af[5]), "=&v"(af[6]), "=&v"(af[7]), "=&v"(cw[0]), "=&v"(cw[1]), "=&v"(cw[2]), "=&v"(sc[0]), "=&v"(sc[1]), "=&v"(sc[2]), "=&v"(zw[0]), "=&v"(zw[1]), "=&v"(zw[2])
+      : "v"(a_addr), "v"(b_addr), "v"(s_addr), "v"(z_addr)
+      : "memory");
+}
+
+template <>
+__device__ __forceinline__ void lds_read_tile<4>(uint32_t a_addr, uint32_t b_addr, uint32_t s_addr, uint32_t z_addr,
+                                                 half8_t (&af)[8], uint2 (&cw)[4], uint32_t (&sc)[4],
+                                                 uint32_t (&zw)[4]) {
   asm volatile(
       "ds_read_u16 %12, %22\n"
       "ds_read_u16 %13, %22 offset:32\n"
@@ -224,9 +306,7 @@ __device__ __forceinline__ void lds_read_tile(uint32_t a_addr, uint32_t b_addr, 
       "ds_read_b128 %6, %20 offset:12288\n"
       "ds_read_b128 %7, %20 offset:14336\n"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(af[4]), "=&v"(af[5]), "=&v"(af[6]),
-        "=&v"(af[7]), "=&v"(cw[0]), "=&v"(cw[1]), "=&v"(cw[2]), "=&v"(cw[3]), "=&v"(sc[0]), "=&v"(sc[1]),
-        "=&v"(sc[2]), "=&v"(sc[3]), "=&v"(zw[0]), "=&v"(zw[1]), "=&v"(zw[2]), "=&v"(zw[3])
+      : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(af[4]), "=&v"(af[5]), "=&v"(af[6]), "=&v"(af[7]), "=&v"(cw[0]), "=&v"(cw[1]), "=&v"(cw[2]), "=&v"(cw[3]), "=&v"(sc[0]), "=&v"(sc[1]), "=&v"(sc[2]), "=&v"(sc[3]), "=&v"(zw[0]), "=&v"(zw[1]), "=&v"(zw[2]), "=&v"(zw[3])
       : "v"(a_addr), "v"(b_addr), "v"(s_addr), "v"(z_addr)
       : "memory");
 }
@@ -248,12 +328,18 @@ constexpr uint32_t kBigLdsZ = 2 * (kBigBN / 8) * 4;     // packed zero points [h
 constexpr uint32_t kBigStage = kBigLdsA + kBigLdsB + kBigLdsS + kBigLdsZ;
 constexpr size_t kBigLds = static_cast<size_t>(kBigStages) * kBigStage;
 
-__global__ __launch_bounds__(512) void gemm_big_kernel(
-    const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const half_t* __restrict__ scales,
-    const uint32_t* __restrict__ qzeros, half_t* __restrict__ y, int M, int N, int K, int gshift) {
-  constexpr int BM = kBigBM, BN = kBigBN, BK = kBigBK, NS = kBigStages, MB = 8, NB = 4;
+template <int NB>
+__device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uint32_t* __restrict__ qw,
+                                         const half_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
+                                         half_t* __restrict__ y, int M, int N, int K, int gshift, int m0, int n0,
+                                         int n_end) {
+  // NB 16-column blocks per wavefront: the tile is 256 x BN with BN = 64 NB.  The LDS
+  // layout is the one of the widest tile (BN = 256) whatever BN is.  N is the row
+  // pitch of scales, zero points and y; columns at or past n_end are not computed.
+  constexpr int BM = kBigBM, BN = 64 * NB, BL = kBigBN, BK = kBigBK, NS = kBigStages, MB = 8;
+  static_assert(NB >= 1 && NB <= 4, "tile width");
   constexpr int APT = BM * BK / 8 / 512;  // activation chunks (16 B) per thread per stage
-  static_assert(BN * BK / 32 == 512, "one code chunk per thread per stage");
+  static_assert(BL * BK / 32 == 512, "one code chunk per thread per stage (of the widest tile)");
   static_assert(kBigStage % 16 == 0, "stage alignment");
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -263,11 +349,6 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(
   const int wm = wave >> 2, wn = wave & 3;
   const int lr = lane & 15;
   const int lq = lane >> 4;
-  const int tiles_n = (N + BN - 1) / BN;
-  const int ntiles = tiles_n * ((M + BM - 1) / BM);
-  const int tile = xcd_tile(blockIdx.x, ntiles);
-  const int m0 = (tile / tiles_n) * BM;
-  const int n0 = (tile % tiles_n) * BN;
   const int W = K >> 3;
   const int KT = K / BK;
 
@@ -280,14 +361,14 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(
     const int row = c >> 3, slot = c & 7;
     a_off[i] = min(m0 + row, M - 1) * K + 8 * (slot ^ (row & 7));
   }
-  // Codes: chunk c = half * BN + column holds channels [32 half, +32) of the column;
-  // columns past N re-read column N - 1.
-  const int b_off = min(n0 + tid % BN, N - 1) * W + 4 * (tid / BN);
+  // Codes: chunk c = half * BL + column holds channels [32 half, +32) of the column;
+  // columns past the tile (BN < BL) or past N re-read a column of the tile.
+  const int b_off = min(n0 + min(tid % BL, BN - 1), n_end - 1) * W + 4 * (tid / BL);
   // Scales (wavefront 0, 16 B per lane) and zero points (wavefront 1, 4 B per lane) of
   // half h = lane / 32: 8 columns, resp. one packed word of 8 columns, per lane.
   const int sz_half = lane >> 5;
-  const int s_col = min(n0 + 8 * (lane & 31), N - 8);
-  const int z_word = min(n0 / 8 + (lane & 31), N / 8 - 1);
+  const int s_col = min(n0 + 8 * (lane & 31), n_end - 8);
+  const int z_word = min(n0 / 8 + (lane & 31), n_end / 8 - 1);
 
   // Tile t goes to stage t % NS; tiles past the end re-load the last one into a stage
   // that is never read again.  The scale / zero load comes first, so that waiting for
@@ -324,9 +405,10 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(
   // 256 nb; scale of block nb at s_lane + 32 nb; zero word of block nb at z_lane + 8 nb.
   const uint32_t base = lds_offset(smem);
   const uint32_t a_lane = base + (wm * 128 + lr) * 128;
-  const uint32_t b_lane = base + kBigLdsA + ((lq >> 1) * BN + wn * 64 + lr) * 16 + (lq & 1) * 8;
-  const uint32_t s_lane = base + kBigLdsA + kBigLdsB + ((lq >> 1) * BN + wn * 64 + lr) * 2;
-  const uint32_t z_lane = base + kBigLdsA + kBigLdsB + kBigLdsS + ((lq >> 1) * (BN / 8) + wn * 8 + (lr >> 3)) * 4;
+  const uint32_t b_lane = base + kBigLdsA + ((lq >> 1) * BL + wn * 16 * NB + lr) * 16 + (lq & 1) * 8;
+  const uint32_t s_lane = base + kBigLdsA + kBigLdsB + ((lq >> 1) * BL + wn * 16 * NB + lr) * 2;
+  const uint32_t z_lane =
+      base + kBigLdsA + kBigLdsB + kBigLdsS + ((lq >> 1) * (BL / 8) + wn * 2 * NB + (lr >> 3)) * 4;
   const int z_shift = 4 * (lr & 7);
 
   // At most APT + 1 loads of this wavefront are newer than the last load of tile t once
@@ -342,7 +424,8 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(
     half8_t af[MB];
     uint2 cw[NB];
     uint32_t sc[NB], zw[NB];
-    lds_read_tile(a_lane + so + 16 * ((2 * lq) ^ (lr & 7)), b_lane + so, s_lane + so, z_lane + so, af, cw, sc, zw);
+    lds_read_tile<NB>(a_lane + so + 16 * ((2 * lq) ^ (lr & 7)), b_lane + so, s_lane + so, z_lane + so, af, cw, sc,
+                      zw);
     DequantConsts dc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -366,7 +449,7 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // D layout of the 16x16 MFMA: lane l holds rows 4*(l/16) + r, column l % 16.
-  const int nw = n0 + wn * 64;
+  const int nw = n0 + wn * 16 * NB;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -375,9 +458,34 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + wm * 128 + 16 * mb + 4 * lq + r;
-        if (m < M && n < N) y[static_cast<size_t>(m) * N + n] = static_cast<half_t>(acc[mb][nb][r]);
+        if (m < M && n < n_end) y[static_cast<size_t>(m) * N + n] = static_cast<half_t>(acc[mb][nb][r]);
       }
     }
+}
+
+// One launch covers up to two column ranges: workgroups [0, split) take 256 x 256
+// tiles of columns [0, n_split), the rest 256 x 64 NB2 tiles of columns [n_split, N).
+// With one wave of full tiles and one of narrower tiles, both rounds fill the device
+// when the full-width tiles alone would leave most of a second round idle.
+template <int NB2>
+__global__ __launch_bounds__(512) void gemm_big_kernel(const half_t* __restrict__ x, const uint32_t* __restrict__ qw,
+                                                       const half_t* __restrict__ scales,
+                                                       const uint32_t* __restrict__ qzeros, half_t* __restrict__ y,
+                                                       int M, int N, int K, int gshift, int split, int n_split) {
+  const int tiles_m = (M + kBigBM - 1) / kBigBM;
+  const int bid = blockIdx.x;
+  if (bid < split) {
+    const int tiles_n = (n_split + 255) / 256;
+    const int tile = xcd_tile(bid, tiles_m * tiles_n);
+    big_tile<4>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * kBigBM, (tile % tiles_n) * 256,
+                min(N, n_split));
+  } else {
+    constexpr int BN2 = 64 * NB2;
+    const int tiles_n = (N - n_split + BN2 - 1) / BN2;
+    const int tile = xcd_tile(bid - split, tiles_m * tiles_n);
+    big_tile<NB2>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * kBigBM,
+                  n_split + (tile % tiles_n) * BN2, N);
+  }
 }
 
 }  // namespace w4a16
