@@ -146,14 +146,21 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   };
 
   // 1. Requests, smallest first so they do not queue behind the weights: the
-  // activations of this lane's chunks (without act order straight into registers),
-  // the staging items of steps 0 and 1, then the first DEPTH rows of codes.
+  // activations of this lane's chunks (without act order straight into registers;
+  // under act order the stored channel order, 16 bytes per load, all at once), the
+  // staging items of steps 0 and 1, then the first DEPTH rows of codes.
   uint4 xv[CPL][4];
+  constexpr int PPT = (LPR * CPL + 63) / 64;   // 4-entry chunks of the order per thread: covers K
+  int4 pv[PPT];
   if constexpr (!ACT) {
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) xv[i][q] = reinterpret_cast<const uint4*>(x)[4 * chunk[i] + q];
+  } else {
+    const int4* perm4 = reinterpret_cast<const int4*>(qw + static_cast<size_t>(N) * W);
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) pv[u] = perm4[min(tid + u * NT, (K >> 2) - 1)];
   }
   load_item(0, 0);
   load_item(1, 1);
@@ -167,11 +174,26 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) load_row(wb[d], row_of(d));  // clamped if steps < DEPTH
 
-  // 2. Act order: gather the activations into LDS in stored order.  Step 0's items go
-  // to ring slot 0; the barrier publishes both.
+  // 2. Act order: gather the activations into LDS in stored order (all gathers of a
+  // thread in flight together).  Step 0's items go to ring slot 0; the barrier
+  // publishes both.
   if constexpr (ACT) {
-    const int32_t* perm = reinterpret_cast<const int32_t*>(qw + static_cast<size_t>(N) * W);
-    for (int p = tid; p < K; p += NT) xs[p] = x[perm[p]];
+    half_t g[PPT][4];
+#pragma unroll
+    for (int u = 0; u < PPT; ++u) {
+      g[u][0] = x[pv[u].x];
+      g[u][1] = x[pv[u].y];
+      g[u][2] = x[pv[u].z];
+      g[u][3] = x[pv[u].w];
+    }
+#pragma unroll
+    for (int u = 0; u < PPT; ++u)
+      if (tid + u * NT < (K >> 2))
+        *reinterpret_cast<uint2*>(xs + 4 * (tid + u * NT)) =
+            uint2{static_cast<uint32_t>(__builtin_bit_cast(uint16_t, g[u][0])) |
+                      (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, g[u][1])) << 16),
+                  static_cast<uint32_t>(__builtin_bit_cast(uint16_t, g[u][2])) |
+                      (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, g[u][3])) << 16)};
   }
   put_item(0, 0);
   __syncthreads();
