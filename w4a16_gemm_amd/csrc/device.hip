@@ -215,27 +215,29 @@ SkinnyShape pick_skinny_shape(int M, int K, int gshift) {
   return sh;
 }
 
-template <int T, int SE, bool ACT>
+template <int T, int SE, bool ACT, bool SUB>
 int launch_skinny_t(const SkinnyShape& sh, hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s,
                     const uint32_t* z, half_t* y, int M, int N, int K, int gshift) {
   static const hipError_t lds_ok =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_skinny_kernel<T, SE, ACT>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_skinny_kernel<T, SE, ACT, SUB>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (int rc = hip_status(lds_ok, "hipFuncSetAttribute")) return rc;
   const size_t lds = skinny_lds_bytes(sh.waves, K >> gshift);
   const int nblk = (N + 15) / 16;
   const int per_cu = std::max(1, 16 / sh.waves);
   const int grid = std::min(nblk, device_cus() * per_cu);
-  hipLaunchKernelGGL((gemm_skinny_kernel<T, SE, ACT>), dim3(grid), dim3(64 * sh.waves), lds, st, x, qw, s, z, y,
-                     M, N, K, gshift);
+  hipLaunchKernelGGL((gemm_skinny_kernel<T, SE, ACT, SUB>), dim3(grid), dim3(64 * sh.waves), lds, st, x, qw, s, z,
+                     y, M, N, K, gshift);
   return check_launch("skinny gemm launch");
 }
 
 template <bool ACT>
 int launch_skinny(const SkinnyShape& sh, hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s,
                   const uint32_t* z, half_t* y, int M, int N, int K, int gshift) {
-#define W4A16_SKINNY(T_, SE_) \
-  if (sh.t == T_ && sh.se == SE_) return launch_skinny_t<T_, SE_, ACT>(sh, st, x, qw, s, z, y, M, N, K, gshift);
+#define W4A16_SKINNY(T_, SE_)                                                                        \
+  if (sh.t == T_ && sh.se == SE_)                                                                  \
+    return gshift == 7 ? launch_skinny_t<T_, SE_, ACT, true>(sh, st, x, qw, s, z, y, M, N, K, gshift) \
+                       : launch_skinny_t<T_, SE_, ACT, false>(sh, st, x, qw, s, z, y, M, N, K, gshift);
   W4A16_SKINNY(1, 1) W4A16_SKINNY(1, 2) W4A16_SKINNY(1, 4)
   W4A16_SKINNY(2, 1) W4A16_SKINNY(2, 2) W4A16_SKINNY(2, 4)
   W4A16_SKINNY(4, 1) W4A16_SKINNY(4, 2) W4A16_SKINNY(4, 4)

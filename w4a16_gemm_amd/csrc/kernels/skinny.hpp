@@ -55,7 +55,13 @@ constexpr size_t skinny_lds_bytes(int waves, int groups) {
 
 // T: 128-channel steps per wavefront (K = 128 T W).  SE: slab entries (16 G per row
 // block) loaded per thread, SE * 64 W >= 16 G.
-template <int T, int SE, bool ACT>
+// SUB (group size 128, one group per step): the weight operand is the raw codes as
+// binary16 subnormals q * 2^-24 (one AND per pair, as in the decode GEMV), the
+// activations in the pair slots that carry 16 q are pre-scaled by 1/16 (exact), each
+// step's four MFMAs accumulate one group's sum of q x into a fresh tile, and the
+// group's scale and zero point enter once per step:
+//     acc += (S * 2^24) * sum q x + (-Z * S) * sum x.
+template <int T, int SE, bool ACT, bool SUB>
 __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
     const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const half_t* __restrict__ scales,
     const uint32_t* __restrict__ qzeros, half_t* __restrict__ y, int M, int N, int K, int gshift) {
@@ -76,8 +82,10 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
   uint2* slab = reinterpret_cast<uint2*>(smem + 2 * static_cast<size_t>(nwaves) * 256 * sizeof(float));  // [2][G][16]
 
   // Activation slice: xr[t][j] = x[m][kw + 128 t + 32 q + 8 j, +8) for m = lane % 16;
-  // zero for m >= M.
+  // zero for m >= M.  SUB: xs[t] = sum of x[m] over step t's 128 channels, and the
+  // elements 2, 3, 6, 7 of every fragment scaled by 1/16.
   half8_t xr[T][4];
+  float xs[T];
   {
     const int m = lr < M ? lr : 0;
     const half_t* xm = x + static_cast<size_t>(m) * K;
@@ -96,6 +104,30 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
         }
         xr[t][j] = lr < M ? v : half8_t{};
       }
+    if constexpr (SUB) {
+      const half2_t ones = half2_t{static_cast<half_t>(1.0f), static_cast<half_t>(1.0f)};
+      const half_t sixteenth = static_cast<half_t>(0.0625f);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        float sx = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2)
+            sx = __builtin_amdgcn_fdot2(half2_t{xr[t][j][e], xr[t][j][e + 1]}, ones, sx, false);
+        // the group spans the four lane quarters q (lanes r, r + 16, r + 32, r + 48)
+        sx += __shfl_xor(sx, 16);
+        sx += __shfl_xor(sx, 32);
+        xs[t] = sx;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          xr[t][j][2] *= sixteenth;
+          xr[t][j][3] *= sixteenth;
+          xr[t][j][6] *= sixteenth;
+          xr[t][j][7] *= sixteenth;
+        }
+      }
+    }
   }
 
   // Codes of row block b for this lane (rows past N re-read row N - 1).
@@ -124,7 +156,13 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
       const int e = tid + u * nthreads;
       if (e < slab_n) {
         const int n = min(16 * b + (e & 15), N - 1);
-        slab[buf * slab_n + e] = slab_entry(sv[u], (zv[u] >> ((n & 7) * 4)) & 0xFu);
+        const uint32_t z = (zv[u] >> ((n & 7) * 4)) & 0xFu;
+        if constexpr (SUB) {
+          const float S = static_cast<float>(sv[u]);
+          slab[buf * slab_n + e] = __builtin_bit_cast(uint2, make_float2(S * 16777216.0f, -static_cast<float>(z) * S));
+        } else {
+          slab[buf * slab_n + e] = slab_entry(sv[u], z);
+        }
       }
     }
   };
@@ -141,15 +179,37 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
     float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      const int gi = (kw + 128 * t + 32 * lq) >> gshift;
-      const DequantConsts dc = slab_consts(slab[buf * slab_n + gi * 16 + lr]);
       const uint32_t w4[4] = {cw[t].x, cw[t].y, cw[t].z, cw[t].w};
-      half8_t wf[4];
+      if constexpr (SUB) {
+        half8_t wf[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wf[j] = dequant_word(w4[j], dc);
-      cw[t] = src[4 * t];
+        for (int j = 0; j < 4; ++j) {
+          const SubPairs sp = expand_word_subnormal(w4[j]);
+          wf[j] = __builtin_bit_cast(half8_t, uint4{sp.a0, sp.b0, sp.a1, sp.b1});
+        }
+        cw[t] = src[4 * t];
+        float4_t part = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j], xr[t][j], acc, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j], xr[t][j], part, 0, 0, 0);
+        // rows n = 4 q + r of the tile hold this lane's four results; their group's
+        // (S * 2^24, -Z * S) are four consecutive slab entries
+        const int gi = (kw + 128 * t) >> 7;
+        const float4* e4 = reinterpret_cast<const float4*>(slab + buf * slab_n + gi * 16 + 4 * lq);
+        const float4 e01 = e4[0], e23 = e4[1];
+        acc[0] = fmaf(e01.y, xs[t], fmaf(e01.x, part[0], acc[0]));
+        acc[1] = fmaf(e01.w, xs[t], fmaf(e01.z, part[1], acc[1]));
+        acc[2] = fmaf(e23.y, xs[t], fmaf(e23.x, part[2], acc[2]));
+        acc[3] = fmaf(e23.w, xs[t], fmaf(e23.z, part[3], acc[3]));
+      } else {
+        const int gi = (kw + 128 * t + 32 * lq) >> gshift;
+        const DequantConsts dc = slab_consts(slab[buf * slab_n + gi * 16 + lr]);
+        half8_t wf[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wf[j] = dequant_word(w4[j], dc);
+        cw[t] = src[4 * t];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j], xr[t][j], acc, 0, 0, 0);
+      }
     }
     // D layout: lane (r, q) holds rows n = 4 q + 0..3 of column m = r.
     *reinterpret_cast<float4_t*>(red + ((buf * nwaves + wave) * 16 + lr) * 16 + 4 * lq) = acc;
