@@ -245,10 +245,11 @@ int launch_skinny(const SkinnyShape& sh, hipStream_t st, const half_t* x, const 
   return fail(W4A16_ERR_UNSUPPORTED, "no skinny kernel for T=%d SE=%d", sh.t, sh.se);
 }
 
-// Large-M GEMM.  Full 256 x 256 tiles, except when they would need more than one but
-// less than two rounds of workgroups over the compute units: then one round of full
-// tiles covers the first columns and one round of narrower tiles (64 NB2 wide) the
-// rest, so that neither round leaves compute units idle.
+// Large-M GEMM.  Full 256 x 256 tiles, except (a) when they would need more than one
+// but less than two rounds of workgroups over the compute units: then one round of
+// full tiles covers the first columns and one round of narrower tiles (64 NB2 wide)
+// the rest, so that neither round leaves compute units idle; (b) when they would not
+// fill one round: then narrower tiles for all columns.
 template <int NB2>
 int launch_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z, half_t* y,
                int M, int N, int K, int gshift, int split, int n_split, int grid) {
@@ -277,6 +278,16 @@ int run_gemm_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half
       if (nb2 == 1) return launch_big<1>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
       if (nb2 == 2) return launch_big<2>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
       return launch_big<3>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
+    }
+  }
+  // One round or less: the narrowest tiles that still fit in one round keep the most
+  // compute units busy (a 256 x 128 tile takes about half as long as a 256 x 256 one).
+  if (full < cus && env_int("W4A16_TUNE_GEMM_SPLIT", 1) != 0) {
+    for (int nb : {2, 3}) {
+      const int tiles = tiles_m * ((N + 64 * nb - 1) / (64 * nb));
+      if (tiles <= cus)
+        return nb == 2 ? launch_big<2>(st, x, qw, s, z, y, M, N, K, gshift, 0, 0, tiles)
+                       : launch_big<3>(st, x, qw, s, z, y, M, N, K, gshift, 0, 0, tiles);
     }
   }
   return launch_big<4>(st, x, qw, s, z, y, M, N, K, gshift, 0, 0, full);
