@@ -39,6 +39,11 @@ SMALL = [
     ("s14", 16, 1048, 4096, 64, False),
     ("s15", 2, 200, 6144, 128, False),
     ("s16", 9, 72, 2048, 32, True),
+    # largest K the decode kernel takes; smallest N; K not a multiple of 64 at M > 128;
+    # a single K tile and a single group at M > 128 with act order
+    ("s17", 1, 16, 16384, 128, False),
+    ("s18", 129, 8, 96, 32, False),
+    ("s19", 300, 40, 64, 64, True),
 ]
 
 
@@ -83,6 +88,23 @@ def test_small_layers_match_oracle(case):
     # the device-resident packed buffer unpacks to the oracle's codes
     back = w4.w4a16_unpack(prod["qweight"].cpu().numpy(), prod["g_idx_np"], g, N, K)
     assert np.array_equal(back, ref["codes"])
+
+
+@pytest.mark.parametrize("case,count", [(9, 300), (8, 140), (2, 40)])
+def test_unit_vector_probes_bit_exact_many_rows(case, count):
+    """The same probe with enough rows for the large-M kernels (M > 128: 256-row tiles;
+    M = 40: the tiled kernel)."""
+    import torch
+    name, _, N, K, g, act = SMALL[case]
+    cfg = _small_cfg(name, 1, N, K, g, act, case)
+    ks = np.arange(min(K, count))
+    E = wl.unit_vectors(K, ks)
+    prod = product_layer(cfg, 1)
+    ref = oracle_layer(cfg, 1, np.arange(N))
+    expect = ref["W16"][:, ks].T.copy()
+    note(f"probe {name} M={len(ks)}")
+    y = run_gemm(prod, x=torch.from_numpy(E).to(device())).cpu().numpy()
+    assert np.array_equal(y.view(np.uint16), expect.view(np.uint16))
 
 
 @pytest.mark.parametrize("case", [0, 2, 4, 6, 7, 9])
