@@ -105,10 +105,10 @@ int device_cus() {
 // Register-pipeline depth: about 8 KB of codes in flight per wavefront.
 constexpr int gemv_depth(int cpl) { return cpl >= 4 ? 2 : 8 / cpl; }
 
-template <int LPR, int CPL, bool EXACT, bool ACT>
-void launch_gemv_t(dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
+template <int LPR, int CPL, bool EXACT, bool ACT, int EPT>
+void launch_gemv_e(dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
                    const uint16_t* s, const uint32_t* z, half_t* y, int N, int K, int gshift, int steps) {
-  auto kern = gemv_m1_kernel<LPR, CPL, kGemvWaves, gemv_depth(CPL), EXACT, ACT>;
+  auto kern = gemv_m1_kernel<LPR, CPL, kGemvWaves, gemv_depth(CPL), EXACT, ACT, EPT>;
   // Dynamic LDS above 64 KB has to be allowed per kernel (once per process).
   static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -117,30 +117,41 @@ void launch_gemv_t(dim3 grid, size_t shmem, hipStream_t st, const half_t* x, con
   hipLaunchKernelGGL(kern, grid, dim3(kGemvWaves * 64), shmem, st, x, qw, s, z, y, N, K, gshift, steps);
 }
 
+// Staging rows per thread: one row (EPT = 1) is compiled only for exact splits
+// without act order, the decode shapes of large layers; everything else stages
+// whole 8-row items.
+template <int LPR, int CPL, bool EXACT, bool ACT>
+void launch_gemv_t(int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
+                   const uint16_t* s, const uint32_t* z, half_t* y, int N, int K, int gshift, int steps) {
+  if constexpr (EXACT && !ACT)
+    if (ept == 1) return launch_gemv_e<LPR, CPL, EXACT, ACT, 1>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+  launch_gemv_e<LPR, CPL, EXACT, ACT, 8>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+}
+
 template <int LPR, bool EXACT, bool ACT>
-void launch_gemv_cpl(int cpl, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
+void launch_gemv_cpl(int cpl, int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
                      const uint16_t* s, const uint32_t* z, half_t* y, int N, int K, int gshift, int steps) {
   switch (cpl) {
-    case 1: launch_gemv_t<LPR, 1, EXACT, ACT>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 2: launch_gemv_t<LPR, 2, EXACT, ACT>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 3: launch_gemv_t<LPR, 3, EXACT, ACT>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 4: launch_gemv_t<LPR, 4, EXACT, ACT>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 5: launch_gemv_t<LPR, 5, EXACT, ACT>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 6: launch_gemv_t<LPR, 6, EXACT, ACT>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 7: launch_gemv_t<LPR, 7, EXACT, ACT>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    default: launch_gemv_t<LPR, 8, EXACT, ACT>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 1: launch_gemv_t<LPR, 1, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 2: launch_gemv_t<LPR, 2, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 3: launch_gemv_t<LPR, 3, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 4: launch_gemv_t<LPR, 4, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 5: launch_gemv_t<LPR, 5, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 6: launch_gemv_t<LPR, 6, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 7: launch_gemv_t<LPR, 7, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    default: launch_gemv_t<LPR, 8, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
   }
 }
 
 template <bool EXACT, bool ACT>
-void launch_gemv_lpr(const GemvShape& sh, dim3 grid, size_t shmem, hipStream_t st, const half_t* x,
+void launch_gemv_lpr(const GemvShape& sh, int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x,
                      const uint32_t* qw, const uint16_t* s, const uint32_t* z, half_t* y, int N, int K,
                      int gshift, int steps) {
   switch (sh.lpr) {
-    case 64: launch_gemv_cpl<64, EXACT, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 32: launch_gemv_cpl<32, EXACT, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 16: launch_gemv_cpl<16, EXACT, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    default: launch_gemv_cpl<8, EXACT, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 64: launch_gemv_cpl<64, EXACT, ACT>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 32: launch_gemv_cpl<32, EXACT, ACT>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 16: launch_gemv_cpl<16, EXACT, ACT>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    default: launch_gemv_cpl<8, EXACT, ACT>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
   }
 }
 
@@ -157,6 +168,7 @@ int run_gemv(const GemvShape& sh, bool act, const half_t* x, const uint32_t* qw,
   const int unit = kGemvWaves * (64 / sh.lpr);                 // rows per unit
   if ((unit / 8) * G > kGemvWaves * 64)
     return fail(W4A16_ERR_UNSUPPORTED, "GEMV staging: %d items per step exceed one per thread", (unit / 8) * G);
+  const int ept = unit * G <= kGemvWaves * 64 ? 1 : 8;        // staging rows per thread
   const int units = (N + unit - 1) / unit;
   const int per_cu = env_int("W4A16_TUNE_GEMV_BLOCKS_PER_CU", 1);
   int blocks = std::min(units, std::max(1, device_cus() * std::max(1, per_cu)));
@@ -171,11 +183,11 @@ int run_gemv(const GemvShape& sh, bool act, const half_t* x, const uint32_t* qw,
   const dim3 grid(blocks);
   const size_t shmem = gemv_lds_bytes(K, G, unit, steps, act);
   if (sh.exact) {
-    if (act) launch_gemv_lpr<true, true>(sh, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
-    else launch_gemv_lpr<true, false>(sh, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+    if (act) launch_gemv_lpr<true, true>(sh, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+    else launch_gemv_lpr<true, false>(sh, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
   } else {
-    if (act) launch_gemv_lpr<false, true>(sh, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
-    else launch_gemv_lpr<false, false>(sh, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+    if (act) launch_gemv_lpr<false, true>(sh, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+    else launch_gemv_lpr<false, false>(sh, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
   }
   return check_launch("gemv launch");
 }

@@ -18,11 +18,14 @@
 //  * Activations are loaded once into registers (under act order gathered through
 //    the stored order via LDS): a lane owns the same chunks in every row.
 //  * Scales and zero points follow the sweep: the (S * 2^24, -Z * S) pairs of one
-//    step's rows are staged in a two-slot LDS ring, one item (8 rows of one group:
-//    16 bytes of scales, one word of zero points) per thread, requested two steps
-//    ahead and published by the workgroup barrier that closes each step.  Staging a
-//    step at a time keeps those small scattered reads in the same DRAM pages as the
-//    weights being streamed and spreads them over the kernel.
+//    step's rows are staged in a two-slot LDS ring, requested two steps ahead and
+//    published by the workgroup barrier that closes each step.  A thread stages EPT
+//    rows of one group: EPT = 1 (one row, 2 bytes of scale; eight neighbouring threads
+//    read one 16-byte run) when there are no more entries than threads, so that the
+//    conversion is spread over all wavefronts instead of holding up the barrier, else
+//    EPT = 8 (16 bytes of scales, one word of zero points).  Staging a step at a time
+//    keeps those small scattered reads in the same DRAM pages as the weights being
+//    streamed and spreads them over the kernel.
 //  * Codes are expanded by masking alone: a pair of nibbles in the mantissa bits of a
 //    binary16 pair with a zero exponent field is the exact subnormal pair
 //    (q, q') * 2^-24 (nibbles.hpp).  v_dot2_f32_f16 multiplies them with the
@@ -78,9 +81,9 @@ __device__ __forceinline__ int xcd_block(int bid, int nblk) {
 // u / nblk.  At any moment the whole grid streams one contiguous window of the
 // weights, and within a unit the wavefronts read neighbouring rows.
 // LDS: scale/zero ring 2 * STRIDE * (G + 1) float2, row results steps * STRIDE floats,
-// and under act order the gathered activations, K binary16.  Needs OCT * G <= WAVES * 64
-// (one staging item per thread and step) and an even DEPTH.
-template <int LPR, int CPL, int WAVES, int DEPTH, bool EXACT, bool ACT>
+// and under act order the gathered activations, K binary16.  Needs 8 OCT G / EPT <=
+// WAVES * 64 (at most one staging task per thread and step) and an even DEPTH.
+template <int LPR, int CPL, int WAVES, int DEPTH, bool EXACT, bool ACT, int EPT>
 __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
     const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
     const uint32_t* __restrict__ qzeros, half_t* __restrict__ y, int N, int K, int gshift, int steps) {
@@ -119,27 +122,41 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
     gcol[i] = (chunk[i] << 5) >> gshift;
   }
 
-  // Staging item of this thread: group gi of the 8 rows [8 o, 8 o + 8) of the unit.
-  const int items = OCT * G;
-  const int it_c = min(tid, items - 1);
+  // Staging task of this thread: rows [8 o + r0, 8 o + r0 + EPT) of the unit, group g
+  // (item (o, g) = 8 rows of one group, split over 8 / EPT threads with r0 fastest).
+  static_assert(EPT == 1 || EPT == 8, "staging rows per thread");
+  constexpr int TPI = 8 / EPT;
+  const int tasks = OCT * G * TPI;
+  const int ts_c = min(tid, tasks - 1);
+  const int it_c = ts_c / TPI;
   const int it_g = it_c % G;
   const int it_o = it_c / G;
-  uint4 zs_s[2];
+  const int st_r0 = (ts_c % TPI) * EPT;
+  using ScaleBits = std::conditional_t<EPT == 8, uint4, uint16_t>;
+  ScaleBits zs_s[2];
   uint32_t zs_z[2];
   auto load_item = [&](int t, int set) {   // unconditional: rows and steps clamped
     const int n8 = min((blk + min(t, steps - 1) * nblk) * STRIDE + 8 * it_o, N - 8);
-    zs_s[set] = *reinterpret_cast<const uint4*>(scales + static_cast<size_t>(it_g) * N + n8);
+    if constexpr (EPT == 8)
+      zs_s[set] = *reinterpret_cast<const uint4*>(scales + static_cast<size_t>(it_g) * N + n8);
+    else
+      zs_s[set] = scales[static_cast<size_t>(it_g) * N + n8 + st_r0];
     zs_z[set] = qzeros[static_cast<size_t>(it_g) * (N >> 3) + (n8 >> 3)];
   };
   auto put_item = [&](int set, int slot) {
-    if (tid < items) {
-      float2* dst = ring + (slot * STRIDE + 8 * it_o) * GP + it_g;
-      const uint32_t s8[4] = {zs_s[set].x, zs_s[set].y, zs_s[set].z, zs_s[set].w};
+    if (tid < tasks) {
+      float2* dst = ring + (slot * STRIDE + 8 * it_o + st_r0) * GP + it_g;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const float S = static_cast<float>(
-            __builtin_bit_cast(half_t, static_cast<uint16_t>((s8[r >> 1] >> (16 * (r & 1))) & 0xFFFFu)));
-        const float Z = static_cast<float>((zs_z[set] >> (4 * r)) & 0xFu);
+      for (int r = 0; r < EPT; ++r) {
+        uint32_t bits;
+        if constexpr (EPT == 8) {
+          const uint32_t s8[4] = {zs_s[set].x, zs_s[set].y, zs_s[set].z, zs_s[set].w};
+          bits = (s8[r >> 1] >> (16 * (r & 1))) & 0xFFFFu;
+        } else {
+          bits = zs_s[set];
+        }
+        const float S = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(bits)));
+        const float Z = static_cast<float>((zs_z[set] >> (4 * (st_r0 + r))) & 0xFu);
         dst[r * GP] = make_float2(S * 16777216.0f, -Z * S);   // both exact in fp32
       }
     }
