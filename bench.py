@@ -220,6 +220,30 @@ def copy_probe(mib: int) -> None:
     torch.cuda.empty_cache()
 
 
+def dense_reference_us(cfg: wl.LayerConfig, M: int, iters: int = 30) -> float:
+    """Kernel time of the same layer with dense binary16 weights through the vendor
+    library (torch.matmul, hipBLASLt), x @ W^T with W [N][K] as stored: context for
+    the W4A16 numbers (decode reads 4x the bytes; prefill is the same contraction
+    without dequantisation).  Random operands; nothing of the W4A16 path is used."""
+    import torch
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    w = torch.randn(cfg.N, cfg.K, generator=g, device="cuda:0", dtype=torch.float16)
+    x = torch.randn(M, cfg.K, generator=g, device="cuda:0", dtype=torch.float16)
+    for _ in range(5):
+        torch.matmul(x, w.t())
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        torch.matmul(x, w.t())
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1000.0 / iters
+    del w, x
+    torch.cuda.empty_cache()
+    return round(us, 3)
+
+
 def traffic_for(hash_now: str, key: str):
     try:
         with open(TRAFFIC_FILE) as f:
@@ -240,6 +264,8 @@ def main() -> int:
     ap.add_argument("--configs", default="all", help="'all', 'headline' or a comma list like c3:1,c4:2048")
     ap.add_argument("--cpu-rows", type=int, default=8192, help="oracle sample size (rows)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense-ref", action="store_true",
+                    help="skip timing the dense binary16 library GEMM of the same shapes")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain streaming kernel over this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -339,6 +365,15 @@ def main() -> int:
             "frac": pre["mfma_frac"], "us_per_layer": pre["us_per_layer"], "kernel": "gemm_big_kernel",
             "traffic": traffic_for(khash, "c4:M2048"),
         }
+    if not args.no_dense_ref:
+        log("timing the dense binary16 library GEMM of the decode and prefill shapes")
+        ref = {"library": "torch.matmul (hipBLASLt), binary16 weights [N][K], x @ W^T",
+               "c3:M1_us": dense_reference_us(hcfg, 1, iters=100)}
+        ref["c3:M1_w4a16_speedup"] = round(ref["c3:M1_us"] / head["region_us_per_step"], 2)
+        if pre:
+            ref["c4:M2048_us"] = dense_reference_us(wl.CONFIGS["c4"], 2048, iters=20)
+            ref["c4:M2048_w4a16_speedup"] = round(ref["c4:M2048_us"] / pre["us_per_layer"], 3)
+        line["dense_fp16_reference"] = ref
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (cpu_baseline)")
         line["cpu_baseline"] = cpu_baseline(hcfg, args.cpu_rows)
