@@ -69,12 +69,6 @@ __device__ __forceinline__ float lane_group_sum(float v) {
   return v;
 }
 
-// Workgroup -> position in the sweep, so that the workgroups of one XCD (dispatch
-// is round-robin over the 8 XCDs) own neighbouring row units.
-__device__ __forceinline__ int xcd_block(int bid, int nblk) {
-  if (nblk % 8 != 0) return bid;
-  return (bid % 8) * (nblk / 8) + bid / 8;
-}
 
 // Row schedule.  Rows are grouped into units of STRIDE = WAVES * RPW consecutive rows
 // (one row per wavefront row-slot); unit u is processed by workgroup u % nblk at step

@@ -109,6 +109,14 @@ __device__ __forceinline__ half8_t dequant_word(uint32_t w, const DequantConsts&
   return half8_t{d0.x, d0.y, d1.x, d1.y, d2.x, d2.y, d3.x, d3.y};
 }
 
+// Workgroup -> position in a sweep over row units, so that the workgroups of one XCD
+// (dispatch is round-robin over the 8 XCDs) own neighbouring units: the streams of
+// one XCD's L2 then cover one contiguous stretch of the weights.
+__device__ __forceinline__ int xcd_block(int bid, int nblk) {
+  if (nblk % 8 != 0) return bid;
+  return (bid % 8) * (nblk / 8) + bid / 8;
+}
+
 // Zero point of (group gi, output n) from the packed zero points [G][N/8].
 __device__ __forceinline__ uint32_t load_zero(const uint32_t* __restrict__ qzeros, int gi, int N, int n) {
   return (qzeros[static_cast<size_t>(gi) * (N >> 3) + (n >> 3)] >> ((n & 7) * 4)) & 0xFu;

@@ -8,7 +8,9 @@
 //  * A workgroup of W wavefronts splits K: wavefront w owns channels
 //    [128 T w, 128 T (w + 1)) and keeps the activations of that slice in registers
 //    for the whole kernel (T x 4 fragments of 8 binary16 per lane).
-//  * The workgroup walks blocks of 16 output rows.  Per block and slice step t, lane
+//  * The workgroup walks blocks of 16 output rows (every grid-th block, the workgroups
+//    of one XCD taking neighbouring ones; dealing consecutive blocks to different XCDs
+//    measured 15% slower on the 70B-class layer).  Per block and slice step t, lane
 //    (r, q) = (lane % 16, lane / 16) loads 16 bytes of row r: the 32 channels
 //    [128 (T w + t) + 32 q, +32), whose four words are its A operands of four MFMAs.
 //    The B operand of lane (m, q) in the j-th of them is x[m] at the channels of word
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
     }
   };
 
-  int b = blockIdx.x;
+  int b = xcd_block(blockIdx.x, gridDim.x);   // row blocks b, b + grid, ... (neighbours on one XCD)
   load_codes(b, cw);
   load_sz(b);
   write_slab(b, 0);
