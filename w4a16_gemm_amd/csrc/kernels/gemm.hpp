@@ -157,17 +157,24 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
 //    points of the groups of its two 32-channel halves (1.25 KB).  No registers hold
 //    prefetched data, so two wavefronts per SIMD fit in 256 registers each.
 //  * An activation row is 8 slots of 16 bytes; slot j of row r holds the row's chunk
-//    j ^ (r % 8), which lets the 16 rows of an MFMA operand be read without LDS bank
-//    conflicts on gfx950.
+//    j ^ (r % 8), which spreads the 16 rows of an MFMA operand over the LDS banks (the
+//    reads still meet two-way bank conflicts; a conflict-free arrangement measured no
+//    faster).
 //  * Each wavefront dequantises its 64 columns in registers (the two wavefronts
 //    sharing columns both do it).
-//  * Tiles are dealt out so that the workgroups of one XCD (dispatch is round-robin
-//    over the 8 XCDs) take consecutive tiles of one 256-row panel of x, which then
-//    stays in that XCD's L2.
+//  * Tiles are dealt out per XCD (dispatch is round-robin over the 8 XCDs): when the
+//    tile grid allows, XCD x takes a block of half the row panels by a quarter of the
+//    column tiles (2 x 4 blocks over the grid), so that the x panels and code columns
+//    one K step of its workgroups touches are as few as possible and stay in that
+//    XCD's L2; otherwise consecutive tiles in row-panel order.
 // Requirements: K % 64 == 0, group size >= 32 and M * K < 2^31.
-__device__ __forceinline__ int xcd_tile(int bid, int ntiles) {
+__device__ __forceinline__ int xcd_tile(int bid, int tiles_m, int tiles_n) {
+  const int ntiles = tiles_m * tiles_n;
   if (ntiles % 8 != 0) return bid;
-  return (bid % 8) * (ntiles / 8) + bid / 8;
+  const int x = bid % 8, j = bid / 8;
+  if (tiles_m % 2 != 0 || tiles_n % 4 != 0) return x * (ntiles / 8) + j;
+  const int pa = tiles_m / 2, pb = tiles_n / 4;   // row panels and column tiles per XCD
+  return (pa * (x % 2) + j / pb) * tiles_n + pb * (x / 2) + j % pb;
 }
 
 // LDS reads written as inline asm.  The compiler cannot tell which stage of the ring
@@ -476,13 +483,13 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(const half_t* __restrict_
   const int bid = blockIdx.x;
   if (bid < split) {
     const int tiles_n = (n_split + 255) / 256;
-    const int tile = xcd_tile(bid, tiles_m * tiles_n);
+    const int tile = xcd_tile(bid, tiles_m, tiles_n);
     big_tile<4>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * kBigBM, (tile % tiles_n) * 256,
                 min(N, n_split));
   } else {
     constexpr int BN2 = 64 * NB2;
     const int tiles_n = (N - n_split + BN2 - 1) / BN2;
-    const int tile = xcd_tile(bid - split, tiles_m * tiles_n);
+    const int tile = xcd_tile(bid - split, tiles_m, tiles_n);
     big_tile<NB2>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * kBigBM,
                   n_split + (tile % tiles_n) * BN2, N);
   }
