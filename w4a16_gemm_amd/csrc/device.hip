@@ -207,7 +207,9 @@ struct SkinnyShape {
   int waves = 0, t = 0, se = 0;
 };
 
-constexpr int kSkinnyMaxM = 16;
+constexpr int kSkinnyMaxM = 16;       // rows of one skinny launch (one MFMA column tile)
+constexpr int kSkinnyChunkMaxM = 64;  // larger M: tiled GEMM kernels
+constexpr int kBigMinM = 65;          // the 256-row-tile kernel from here on (when K allows)
 
 SkinnyShape pick_skinny_shape(int M, int K, int gshift) {
   SkinnyShape sh;
@@ -307,7 +309,7 @@ int run_gemm_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half
 
 int run_gemm(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z,
              half_t* y, int M, int N, int K, int gshift) {
-  if (M > 128 && K % kBigBK == 0 && static_cast<long long>(M) * K < (1LL << 31) &&
+  if (M > kBigMinM - 1 && K % kBigBK == 0 && static_cast<long long>(M) * K < (1LL << 31) &&
       env_int("W4A16_TUNE_GEMM_BIG", 1) != 0)
     return run_gemm_big(st, x, qw, s, z, y, M, N, K, gshift);
   if (M <= 16)
@@ -366,10 +368,23 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
   if (use_gemv)
     return run_gemv(sh, act, hx, hq, reinterpret_cast<const uint16_t*>(scales), hz, hy, N, K, gshift, st);
 
-  const SkinnyShape sk = pick_skinny_shape(M, K, gshift);
-  if (sk.waves != 0 && env_int("W4A16_TUNE_GEMM_SKINNY", 1) != 0)
-    return act ? launch_skinny<true>(sk, st, hx, hq, hs, hz, hy, M, N, K, gshift)
-               : launch_skinny<false>(sk, st, hx, hq, hs, hz, hy, M, N, K, gshift);
+  // Up to kSkinnyChunkMaxM rows: the skinny kernel once per 16 rows of x and y.  Every
+  // launch streams the whole weight matrix, but the launches after the first find most
+  // of it in the last-level cache, and the tiled kernel below is latency-bound at
+  // these sizes (one 256-column tile per workgroup, a fraction of the CUs busy).
+  const SkinnyShape sk = pick_skinny_shape(std::min(M, kSkinnyMaxM), K, gshift);
+  if (sk.waves != 0 && M <= env_int("W4A16_TUNE_SKINNY_CHUNK_MAX_M", kSkinnyChunkMaxM) &&
+      env_int("W4A16_TUNE_GEMM_SKINNY", 1) != 0) {
+    for (int m0 = 0; m0 < M; m0 += kSkinnyMaxM) {
+      const int mc = std::min(kSkinnyMaxM, M - m0);
+      const half_t* xc = hx + static_cast<size_t>(m0) * K;
+      half_t* yc = hy + static_cast<size_t>(m0) * N;
+      const int rc = act ? launch_skinny<true>(sk, st, xc, hq, hs, hz, yc, mc, N, K, gshift)
+                         : launch_skinny<false>(sk, st, xc, hq, hs, hz, yc, mc, N, K, gshift);
+      if (rc != W4A16_OK) return rc;
+    }
+    return W4A16_OK;
+  }
 
   if (!act) return run_gemm(st, hx, hq, hs, hz, hy, M, N, K, gshift);
 
