@@ -44,9 +44,11 @@ SMALL = [
     ("s17", 1, 16, 16384, 128, False),
     ("s18", 129, 8, 96, 32, False),
     ("s19", 300, 40, 64, 64, True),
-    # batches between the skinny and the prefill kernels: the skinny kernel once per 16
-    # rows (ragged last chunk; act order), and the 256-row-tile kernel from M = 65 on
+    # batches between the skinny and the prefill shapes: the skinny kernel twice (ragged
+    # second launch) at M <= 32, the large-tile kernel with 64-row tiles (M = 33, 64 with
+    # act order) and 128-row tiles (M = 100)
     ("s20", 33, 264, 2048, 128, False),
+    ("s23", 27, 392, 2048, 128, False),
     ("s21", 64, 136, 1024, 32, True),
     ("s22", 100, 264, 512, 128, False),
 ]
@@ -97,8 +99,8 @@ def test_small_layers_match_oracle(case):
 
 @pytest.mark.parametrize("case,count", [(9, 300), (8, 140), (2, 40)])
 def test_unit_vector_probes_bit_exact_many_rows(case, count):
-    """The same probe with enough rows for the other kernels (M > 64: 256-row tiles;
-    M = 40: the skinny kernel in three launches of at most 16 rows)."""
+    """The same probe with enough rows for the other kernels (M > 128: 256-row tiles;
+    M = 40: 64-row tiles)."""
     import torch
     name, _, N, K, g, act = SMALL[case]
     cfg = _small_cfg(name, 1, N, K, g, act, case)

@@ -208,8 +208,8 @@ struct SkinnyShape {
 };
 
 constexpr int kSkinnyMaxM = 16;       // rows of one skinny launch (one MFMA column tile)
-constexpr int kSkinnyChunkMaxM = 64;  // larger M: tiled GEMM kernels
-constexpr int kBigMinM = 65;          // the 256-row-tile kernel from here on (when K allows)
+constexpr int kSkinnyChunkMaxM = 32;  // larger M: tiled GEMM kernels
+constexpr int kBigMinM = 33;          // the large-tile kernel from here on (when K allows)
 
 SkinnyShape pick_skinny_shape(int M, int K, int gshift) {
   SkinnyShape sh;
@@ -259,26 +259,29 @@ int launch_skinny(const SkinnyShape& sh, hipStream_t st, const half_t* x, const 
   return fail(W4A16_ERR_UNSUPPORTED, "no skinny kernel for T=%d SE=%d", sh.t, sh.se);
 }
 
-// Large-M GEMM.  Full 256 x 256 tiles, except (a) when they would need more than one
-// but less than two rounds of workgroups over the compute units: then one round of
-// full tiles covers the first columns and one round of narrower tiles (64 NB2 wide)
-// the rest, so that neither round leaves compute units idle; (b) when they would not
-// fill one round: then narrower tiles for all columns.
-template <int NB2>
+// Large-M GEMM.  BM x 256 tiles (BM = 256 rows; 128 or 64 when the whole batch fits in
+// fewer rows, so that small batches do not pay for padding rows), except (a) when they
+// would need more than one but less than two rounds of workgroups over the compute
+// units: then one round of full-width tiles covers the first columns and one round of
+// narrower tiles (64 NB2 wide) the rest, so that neither round leaves compute units
+// idle; (b) when they would not fill one round: then narrower tiles for all columns.
+template <int NB2, int MB>
 int launch_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z, half_t* y,
                int M, int N, int K, int gshift, int split, int n_split, int grid) {
-  static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_big_kernel<NB2>),
+  static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_big_kernel<NB2, MB>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        static_cast<int>(kBigLds));
   if (int rc = hip_status(lds_ok, "hipFuncSetAttribute")) return rc;
-  hipLaunchKernelGGL(gemm_big_kernel<NB2>, dim3(grid), dim3(512), kBigLds, st, x, qw, s, z, y, M, N, K, gshift, split,
-                     n_split);
+  hipLaunchKernelGGL((gemm_big_kernel<NB2, MB>), dim3(grid), dim3(512), kBigLds, st, x, qw, s, z, y, M, N, K, gshift,
+                     split, n_split);
   return check_launch("gemm launch");
 }
 
-int run_gemm_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z, half_t* y,
-                 int M, int N, int K, int gshift) {
-  const int tiles_m = (M + kBigBM - 1) / kBigBM;
+template <int MB>
+int run_gemm_big_t(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z,
+                   half_t* y, int M, int N, int K, int gshift) {
+  constexpr int BM = 32 * MB;
+  const int tiles_m = (M + BM - 1) / BM;
   const int cus = device_cus();
   const int full = tiles_m * ((N + 255) / 256);
   if (full > cus && full < 2 * cus && cus % tiles_m == 0 && env_int("W4A16_TUNE_GEMM_SPLIT", 1) != 0) {
@@ -289,27 +292,35 @@ int run_gemm_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half
     if (rest > 0 && nb2 >= 1 && nb2 <= 3) {
       const int split = tiles_m * per_panel;
       const int grid = split + tiles_m * ((rest + 64 * nb2 - 1) / (64 * nb2));
-      if (nb2 == 1) return launch_big<1>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
-      if (nb2 == 2) return launch_big<2>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
-      return launch_big<3>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
+      if (nb2 == 1) return launch_big<1, MB>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
+      if (nb2 == 2) return launch_big<2, MB>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
+      return launch_big<3, MB>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
     }
   }
   // One round or less: the narrowest tiles that still fit in one round keep the most
-  // compute units busy (a 256 x 128 tile takes about half as long as a 256 x 256 one).
+  // compute units busy (a BM x 128 tile takes about half as long as a BM x 256 one).
   if (full < cus && env_int("W4A16_TUNE_GEMM_SPLIT", 1) != 0) {
     for (int nb : {2, 3}) {
       const int tiles = tiles_m * ((N + 64 * nb - 1) / (64 * nb));
       if (tiles <= cus)
-        return nb == 2 ? launch_big<2>(st, x, qw, s, z, y, M, N, K, gshift, 0, 0, tiles)
-                       : launch_big<3>(st, x, qw, s, z, y, M, N, K, gshift, 0, 0, tiles);
+        return nb == 2 ? launch_big<2, MB>(st, x, qw, s, z, y, M, N, K, gshift, 0, 0, tiles)
+                       : launch_big<3, MB>(st, x, qw, s, z, y, M, N, K, gshift, 0, 0, tiles);
     }
   }
-  return launch_big<4>(st, x, qw, s, z, y, M, N, K, gshift, 0, 0, full);
+  return launch_big<3, MB>(st, x, qw, s, z, y, M, N, K, gshift, full, N, full);
+}
+
+int run_gemm_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z, half_t* y,
+                 int M, int N, int K, int gshift) {
+  if (M <= 64) return run_gemm_big_t<2>(st, x, qw, s, z, y, M, N, K, gshift);
+  if (M <= 128) return run_gemm_big_t<4>(st, x, qw, s, z, y, M, N, K, gshift);
+  return run_gemm_big_t<8>(st, x, qw, s, z, y, M, N, K, gshift);
 }
 
 int run_gemm(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z,
              half_t* y, int M, int N, int K, int gshift) {
-  if (M > kBigMinM - 1 && K % kBigBK == 0 && static_cast<long long>(M) * K < (1LL << 31) &&
+  if (M >= env_int("W4A16_TUNE_GEMM_BIG_MIN_M", kBigMinM) && K % kBigBK == 0 &&
+      static_cast<long long>(M) * K < (1LL << 31) &&
       env_int("W4A16_TUNE_GEMM_BIG", 1) != 0)
     return run_gemm_big(st, x, qw, s, z, y, M, N, K, gshift);
   if (M <= 16)
@@ -369,9 +380,8 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
     return run_gemv(sh, act, hx, hq, reinterpret_cast<const uint16_t*>(scales), hz, hy, N, K, gshift, st);
 
   // Up to kSkinnyChunkMaxM rows: the skinny kernel once per 16 rows of x and y.  Every
-  // launch streams the whole weight matrix, but the launches after the first find most
-  // of it in the last-level cache, and the tiled kernel below is latency-bound at
-  // these sizes (one 256-column tile per workgroup, a fraction of the CUs busy).
+  // launch streams the whole weight matrix again, so from three launches on the
+  // large-tile kernel with 64-row tiles is faster.
   const SkinnyShape sk = pick_skinny_shape(std::min(M, kSkinnyMaxM), K, gshift);
   if (sk.waves != 0 && M <= env_int("W4A16_TUNE_SKINNY_CHUNK_MAX_M", kSkinnyChunkMaxM) &&
       env_int("W4A16_TUNE_GEMM_SKINNY", 1) != 0) {

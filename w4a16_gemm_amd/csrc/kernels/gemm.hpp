@@ -335,16 +335,21 @@ constexpr uint32_t kBigLdsZ = 2 * (kBigBN / 8) * 4;     // packed zero points [h
 constexpr uint32_t kBigStage = kBigLdsA + kBigLdsB + kBigLdsS + kBigLdsZ;
 constexpr size_t kBigLds = static_cast<size_t>(kBigStages) * kBigStage;
 
-template <int NB>
+template <int NB, int MB>
 __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uint32_t* __restrict__ qw,
                                          const half_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
                                          half_t* __restrict__ y, int M, int N, int K, int gshift, int m0, int n0,
                                          int n_end) {
-  // NB 16-column blocks per wavefront: the tile is 256 x BN with BN = 64 NB.  The LDS
-  // layout is the one of the widest tile (BN = 256) whatever BN is.  N is the row
-  // pitch of scales, zero points and y; columns at or past n_end are not computed.
-  constexpr int BM = kBigBM, BN = 64 * NB, BL = kBigBN, BK = kBigBK, NS = kBigStages, MB = 8;
+  // NB 16-column blocks and MB 16-row blocks per wavefront: the tile is BM x BN with
+  // BM = 32 MB and BN = 64 NB.  The LDS layout is the one of the largest tile (256 x 256)
+  // whatever the tile is.  N is the row pitch of scales, zero points and y; columns at
+  // or past n_end are not computed.  MB = 8 reads LDS through the inline-asm blocks
+  // above; the smaller tiles (few-row batches) use plain loads, which the compiler
+  // orders against the barriers and (seeing no alias with the direct-to-LDS writes)
+  // does not hold behind the prefetches.
+  constexpr int BM = 32 * MB, BN = 64 * NB, BL = kBigBN, BK = kBigBK, NS = kBigStages;
   static_assert(NB >= 1 && NB <= 4, "tile width");
+  static_assert(MB == 2 || MB == 4 || MB == 8, "tile height");
   constexpr int APT = BM * BK / 8 / 512;  // activation chunks (16 B) per thread per stage
   static_assert(BL * BK / 32 == 512, "one code chunk per thread per stage (of the widest tile)");
   static_assert(kBigStage % 16 == 0, "stage alignment");
@@ -411,7 +416,7 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
   // a_lane + 16 ((2 q + s) ^ (r % 8)) + 2048 mb; code words of block nb at b_lane +
   // 256 nb; scale of block nb at s_lane + 32 nb; zero word of block nb at z_lane + 8 nb.
   const uint32_t base = lds_offset(smem);
-  const uint32_t a_lane = base + (wm * 128 + lr) * 128;
+  const uint32_t a_lane = base + (wm * 16 * MB + lr) * 128;
   const uint32_t b_lane = base + kBigLdsA + ((lq >> 1) * BL + wn * 16 * NB + lr) * 16 + (lq & 1) * 8;
   const uint32_t s_lane = base + kBigLdsA + kBigLdsB + ((lq >> 1) * BL + wn * 16 * NB + lr) * 2;
   const uint32_t z_lane =
@@ -431,15 +436,37 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
     half8_t af[MB];
     uint2 cw[NB];
     uint32_t sc[NB], zw[NB];
-    lds_read_tile<NB>(a_lane + so + 16 * ((2 * lq) ^ (lr & 7)), b_lane + so, s_lane + so, z_lane + so, af, cw, sc,
-                      zw);
+    const unsigned char* st = smem + so;   // plain-load view of the same stage (MB < 8)
+    if constexpr (MB == 8) {
+      lds_read_tile<NB>(a_lane + so + 16 * ((2 * lq) ^ (lr & 7)), b_lane + so, s_lane + so, z_lane + so, af, cw, sc,
+                        zw);
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        cw[nb] = *reinterpret_cast<const uint2*>(st + (b_lane - base) + 256 * nb);
+        sc[nb] = *reinterpret_cast<const uint16_t*>(st + (s_lane - base) + 32 * nb);
+        zw[nb] = *reinterpret_cast<const uint32_t*>(st + (z_lane - base) + 8 * nb);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        af[mb] = *reinterpret_cast<const half8_t*>(st + (a_lane - base) + 16 * ((2 * lq) ^ (lr & 7)) + 2048 * mb);
+    }
     DequantConsts dc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
       dc[nb] = make_consts((zw[nb] >> z_shift) & 0xFu, __builtin_bit_cast(half_t, static_cast<uint16_t>(sc[nb])));
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      if (s == 1) lds_read_a8(a_lane + so + 16 * ((2 * lq + 1) ^ (lr & 7)), af);
+      if (s == 1) {
+        if constexpr (MB == 8) {
+          lds_read_a8(a_lane + so + 16 * ((2 * lq + 1) ^ (lr & 7)), af);
+        } else {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            af[mb] = *reinterpret_cast<const half8_t*>(st + (a_lane - base) + 16 * ((2 * lq + 1) ^ (lr & 7)) +
+                                                       2048 * mb);
+        }
+      }
       half8_t bf[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) bf[nb] = dequant_word(s == 0 ? cw[nb].x : cw[nb].y, dc[nb]);
@@ -464,33 +491,35 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
       const int n = nw + 16 * nb + lr;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * 128 + 16 * mb + 4 * lq + r;
+        const int m = m0 + wm * 16 * MB + 16 * mb + 4 * lq + r;
         if (m < M && n < n_end) y[static_cast<size_t>(m) * N + n] = static_cast<half_t>(acc[mb][nb][r]);
       }
     }
 }
 
-// One launch covers up to two column ranges: workgroups [0, split) take 256 x 256
-// tiles of columns [0, n_split), the rest 256 x 64 NB2 tiles of columns [n_split, N).
+// One launch covers up to two column ranges: workgroups [0, split) take BM x 256
+// tiles of columns [0, n_split), the rest BM x 64 NB2 tiles of columns [n_split, N),
+// BM = 32 MB rows (256 for prefill; 128 / 64 for batches of up to 128 / 64 rows).
 // With one wave of full tiles and one of narrower tiles, both rounds fill the device
 // when the full-width tiles alone would leave most of a second round idle.
-template <int NB2>
+template <int NB2, int MB>
 __global__ __launch_bounds__(512) void gemm_big_kernel(const half_t* __restrict__ x, const uint32_t* __restrict__ qw,
                                                        const half_t* __restrict__ scales,
                                                        const uint32_t* __restrict__ qzeros, half_t* __restrict__ y,
                                                        int M, int N, int K, int gshift, int split, int n_split) {
-  const int tiles_m = (M + kBigBM - 1) / kBigBM;
+  constexpr int BM = 32 * MB;
+  const int tiles_m = (M + BM - 1) / BM;
   const int bid = blockIdx.x;
   if (bid < split) {
     const int tiles_n = (n_split + 255) / 256;
     const int tile = xcd_tile(bid, tiles_m, tiles_n);
-    big_tile<4>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * kBigBM, (tile % tiles_n) * 256,
+    big_tile<4, MB>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM, (tile % tiles_n) * 256,
                 min(N, n_split));
   } else {
     constexpr int BN2 = 64 * NB2;
     const int tiles_n = (N - n_split + BN2 - 1) / BN2;
     const int tile = xcd_tile(bid - split, tiles_m, tiles_n);
-    big_tile<NB2>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * kBigBM,
+    big_tile<NB2, MB>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM,
                   n_split + (tile % tiles_n) * BN2, N);
   }
 }
