@@ -310,10 +310,38 @@ int run_gemm_big_t(hipStream_t st, const half_t* x, const uint32_t* qw, const ha
   return launch_big<3, MB>(st, x, qw, s, z, y, M, N, K, gshift, full, N, full);
 }
 
+// Output elements one compute unit works through with BM = 32 MB row tiles, following
+// the tile choice of run_gemm_big_t (the busiest unit).
+long long big_work_per_cu(int MB, int M, int N, int cus) {
+  const long long BM = 32LL * MB;
+  const int tiles_m = static_cast<int>((M + BM - 1) / BM);
+  const int full = tiles_m * ((N + 255) / 256);
+  if (full > cus && full < 2 * cus && cus % tiles_m == 0) {
+    const int per_panel = cus / tiles_m;
+    const int rest = N - 256 * per_panel;
+    const int nb2 = (((rest + per_panel - 1) / per_panel) + 63) / 64;
+    if (rest > 0 && nb2 >= 1 && nb2 <= 3) return BM * 256 + BM * 64 * nb2;
+  }
+  if (full < cus)
+    for (int nb : {2, 3})
+      if (tiles_m * ((N + 64 * nb - 1) / (64 * nb)) <= cus) return BM * 64 * nb;
+  return static_cast<long long>((full + cus - 1) / cus) * BM * 256;
+}
+
 int run_gemm_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z, half_t* y,
                  int M, int N, int K, int gshift) {
-  if (M <= 64) return run_gemm_big_t<2>(st, x, qw, s, z, y, M, N, K, gshift);
-  if (M <= 128) return run_gemm_big_t<4>(st, x, qw, s, z, y, M, N, K, gshift);
+  // Above 128 rows: 128-row tiles when their smaller tiles fill the device enough better
+  // to make up for doing ~1.28x the work per output (twice the dequantisation per MFMA;
+  // measured: the 2048-row layer 351 vs 241 us at 0.88x the work per unit).
+  int mb_auto = M <= 64 ? 2 : M <= 128 ? 4 : 8;
+  if (mb_auto == 8 && env_int("W4A16_TUNE_GEMM_SPLIT", 1) != 0) {
+    const int cus = device_cus();
+    if (static_cast<double>(big_work_per_cu(4, M, N, cus)) * 1.28 < static_cast<double>(big_work_per_cu(8, M, N, cus)))
+      mb_auto = 4;
+  }
+  const int mb = env_int("W4A16_TUNE_GEMM_BIG_MB", mb_auto);
+  if (mb == 2) return run_gemm_big_t<2>(st, x, qw, s, z, y, M, N, K, gshift);
+  if (mb == 4) return run_gemm_big_t<4>(st, x, qw, s, z, y, M, N, K, gshift);
   return run_gemm_big_t<8>(st, x, qw, s, z, y, M, N, K, gshift);
 }
 
