@@ -149,11 +149,15 @@ int w4a16_unpack_zeros(const int32_t* qzeros, int G, int N, uint8_t* zeros);
 /* y = x * W^T with W^ = (q - Z) * S, fp32 accumulation, y rounded once to binary16.
  * All pointers are device pointers.  g_idx non-NULL selects the act-order layout
  * (qweight must have been packed with that g_idx; the kernels read the stored order
- * from qweight and gather x through it).  M == 1 runs the split-K GEMV; larger M the
- * MFMA GEMM (which, under act order, first gathers x into stream-ordered scratch
- * memory taken from and returned to the device's default memory pool).
+ * from qweight and gather x through it).  M == 1 runs the split-K GEMV; 2 <= M <= 32
+ * the skinny-batch MFMA kernel (one launch per 16 rows); larger M the tiled MFMA GEMM
+ * (64-, 128- or 256-row tiles), which under act order first gathers x into
+ * stream-ordered scratch memory taken from and returned to the device's default memory
+ * pool.  Shapes a kernel cannot take (K not a multiple of 128 for the skinny kernel, of
+ * 64 for the large tiles) fall to a smaller tiled MFMA kernel, never to the host.
  * Environment: W4A16_DEBUG_CHECKS=1 also validates g_idx (synchronous copy);
- * W4A16_FORCE_PATH=gemv|gemm selects a kernel family (for tests).
+ * W4A16_FORCE_PATH=gemv|gemm selects a kernel family (for tests); W4A16_TUNE_* switches
+ * change kernel choices and tile shapes (measurements only).
  * Errors: INVALID_ARG, UNSUPPORTED, MISALIGNED, BAD_GIDX (debug only), HIP. */
 int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                const int32_t* qzeros, const int32_t* g_idx, int group_size, int M, int N,
