@@ -180,7 +180,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
     const int nc = min(n, N - 1);
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
-      dst[i] = *reinterpret_cast<const uint4*>(qw + static_cast<size_t>(nc) * W + 4 * chunk[i]);
+      dst[i] = load_stream16(qw + static_cast<size_t>(nc) * W + 4 * chunk[i]);
   };
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) load_row(wb[d], row_of(d));  // clamped if steps < DEPTH

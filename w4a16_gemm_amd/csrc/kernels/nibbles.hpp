@@ -27,6 +27,16 @@ typedef _Float16 half_t;
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16 bytes of packed codes read once per launch (the decode GEMV streams every weight
+// exactly once): a non-temporal load, so the stream does not displace the scales, zero
+// points and activations from the caches.  Measured (same-process A/B): the 70B-class
+// decode layer 23.6 -> 23.0 us, the act-order layer 11.2 -> 10.7 us.  The skinny-batch
+// kernel reads the same way more slowly (+2..4% at M = 2..8) and keeps plain loads.
+__device__ __forceinline__ uint4 load_stream16(const uint32_t* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
 
 constexpr uint32_t kMagic = 0x64006400u;  // (1024.0, 1024.0) in binary16
 
