@@ -399,9 +399,11 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
 
   const Path forced = forced_path();
   const GemvShape sh = pick_gemv_shape(K);
-  const bool gemv_ok = M == 1 && sh.lpr != 0;
+  // the GEMV addresses the codes with 32-bit byte offsets: layers of up to 2 GB of codes
+  const bool gemv_ok = M == 1 && sh.lpr != 0 && static_cast<long long>(N) * K / 2 < (1LL << 31);
   if (forced == Path::kGemv && !gemv_ok)
-    return fail(W4A16_ERR_UNSUPPORTED, "the GEMV path needs M == 1 and K <= 16384 (M=%d K=%d)", M, K);
+    return fail(W4A16_ERR_UNSUPPORTED, "the GEMV path needs M == 1, K <= 16384 and N*K/2 < 2^31 (M=%d N=%d K=%d)",
+                M, N, K);
   const bool use_gemv = gemv_ok && forced != Path::kGemm;
 
   if (use_gemv)

@@ -176,11 +176,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   load_item(0, 0);
   load_item(1, 1);
   uint4 wb[DEPTH][CPL];
+  // the codes part of qweight, N K / 2 < 2^31 bytes (checked by the host)
+  const __amdgpu_buffer_rsrc_t codes = stream_rsrc(qw, static_cast<uint32_t>(N) * static_cast<uint32_t>(W) * 4u);
   auto load_row = [&](uint4 (&dst)[CPL], int n) {   // unconditional: row clamped into the matrix
     const int nc = min(n, N - 1);
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
-      dst[i] = load_stream16(qw + static_cast<size_t>(nc) * W + 4 * chunk[i]);
+      dst[i] = load_stream16(codes, (static_cast<uint32_t>(nc) * static_cast<uint32_t>(W) + 4u * chunk[i]) * 4u);
   };
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) load_row(wb[d], row_of(d));  // clamped if steps < DEPTH
