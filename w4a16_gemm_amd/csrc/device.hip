@@ -412,8 +412,10 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
   // Up to kSkinnyChunkMaxM rows: the skinny kernel once per 16 rows of x and y.  Every
   // launch streams the whole weight matrix again, so from three launches on the
   // large-tile kernel with 64-row tiles is faster.
+  // (The skinny kernel, like the GEMV, addresses the codes with 32-bit byte offsets.)
   const SkinnyShape sk = pick_skinny_shape(std::min(M, kSkinnyMaxM), K, gshift);
-  if (sk.waves != 0 && M <= env_int("W4A16_TUNE_SKINNY_CHUNK_MAX_M", kSkinnyChunkMaxM) &&
+  if (sk.waves != 0 && static_cast<long long>(N) * K / 2 < (1LL << 31) &&
+      M <= env_int("W4A16_TUNE_SKINNY_CHUNK_MAX_M", kSkinnyChunkMaxM) &&
       env_int("W4A16_TUNE_GEMM_SKINNY", 1) != 0) {
     for (int m0 = 0; m0 < M; m0 += kSkinnyMaxM) {
       const int mc = std::min(kSkinnyMaxM, M - m0);

@@ -49,6 +49,11 @@ __device__ __forceinline__ uint4 load_stream16(__amdgpu_buffer_rsrc_t r, uint32_
                                                                          kCpolNonTemporal));
 }
 
+// The same 16-byte buffer load with the default cache policy.
+__device__ __forceinline__ uint4 load_buffer16(__amdgpu_buffer_rsrc_t r, uint32_t byte_offset) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(byte_offset), 0, 0));
+}
+
 constexpr uint32_t kMagic = 0x64006400u;  // (1024.0, 1024.0) in binary16
 
 struct Pairs {

@@ -132,12 +132,18 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
     }
   }
 
-  // Codes of row block b for this lane (rows past N re-read row N - 1).
-  auto load_codes = [&](int b, uint4 (&cw)[T]) {
+  // Codes of row block b for this lane (rows past N re-read row N - 1), read through a
+  // buffer resource over the codes (N K / 2 < 2^31 bytes, checked by the host): 32-bit
+  // byte offsets instead of 64-bit addresses.
+  const __amdgpu_buffer_rsrc_t codes = stream_rsrc(qw, static_cast<uint32_t>(N) * static_cast<uint32_t>(Wd) * 4u);
+  auto code_offset = [&](int b) {   // bytes; step t adds 64 t (128 channels = 16 words)
     const int n = min(16 * b + lr, N - 1);
-    const uint4* src = reinterpret_cast<const uint4*>(qw + static_cast<size_t>(n) * Wd + (kw >> 3) + 4 * lq);
+    return (static_cast<uint32_t>(n) * static_cast<uint32_t>(Wd) + static_cast<uint32_t>((kw >> 3) + 4 * lq)) * 4u;
+  };
+  auto load_codes = [&](int b, uint4 (&cw)[T]) {
+    const uint32_t off = code_offset(b);
 #pragma unroll
-    for (int t = 0; t < T; ++t) cw[t] = src[4 * t];   // 128 channels = 16 words = 4 uint4 per step
+    for (int t = 0; t < T; ++t) cw[t] = load_buffer16(codes, off + 64u * t);
   };
   // Scale and zero word of slab entries tid + u * nthreads of row block b.
   half_t sv[SE];
@@ -176,8 +182,7 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
   uint4 cw[T];
   auto row_block = [&](int b, int i) {
     const int buf = i & 1;
-    const int n_next = min(16 * (b + static_cast<int>(gridDim.x)) + lr, N - 1);
-    const uint4* src = reinterpret_cast<const uint4*>(qw + static_cast<size_t>(n_next) * Wd + (kw >> 3) + 4 * lq);
+    const uint32_t off_next = code_offset(b + static_cast<int>(gridDim.x));
     float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -189,7 +194,7 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
           const SubPairs sp = expand_word_subnormal(w4[j]);
           wf[j] = __builtin_bit_cast(half8_t, uint4{sp.a0, sp.b0, sp.a1, sp.b1});
         }
-        cw[t] = src[4 * t];
+        cw[t] = load_buffer16(codes, off_next + 64u * t);
         float4_t part = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j], xr[t][j], part, 0, 0, 0);
@@ -208,7 +213,7 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
         half8_t wf[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) wf[j] = dequant_word(w4[j], dc);
-        cw[t] = src[4 * t];
+        cw[t] = load_buffer16(codes, off_next + 64u * t);
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j], xr[t][j], acc, 0, 0, 0);
       }
