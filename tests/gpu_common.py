@@ -89,6 +89,18 @@ def run_gemm(layer, x=None, y=None):
     return out
 
 
+# The library's weight words keep element e of a word in nibble NIBBLE_OF[e] (its
+# private word layout); the oracle's unpacking reads nibble j as element j.
+NIBBLE_OF = np.array([0, 4, 1, 5, 2, 6, 3, 7])
+
+
+def codes_of_library_words(words) -> np.ndarray:
+    """Codes u8 [rows][K] held by library weight words int32 [rows][K/8] (contiguous
+    groups), decoded with the oracle's unpacking and the layout's nibble order."""
+    nat = oracle.unpack_codes(words)
+    return np.ascontiguousarray(nat.reshape(nat.shape[0], -1, 8)[:, :, NIBBLE_OF].reshape(nat.shape))
+
+
 def sample_rows(N: int, count: int, seed: int = 0) -> np.ndarray:
     rng = np.random.default_rng([31, N, seed])
     rows = set(rng.choice(N, size=min(count, N), replace=False).tolist())

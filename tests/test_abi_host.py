@@ -120,6 +120,15 @@ def test_private_word_layout_known_answer():
                           np.full(32, 0xFFFFFFFF, np.uint32))
 
 
+def test_library_word_decoder_used_by_the_gpu_tests():
+    """The GPU tests decode random library words with the documented nibble order;
+    that decoder inverts w4a16_pack."""
+    from gpu_common import codes_of_library_words
+    codes = wl.random_codes(16, 256, 3)
+    words = w4.w4a16_pack(codes, None, 128).reshape(16, 32)
+    assert np.array_equal(codes_of_library_words(words), codes)
+
+
 @pytest.mark.parametrize("act", [False, True])
 @pytest.mark.parametrize("shape", [(8, 64, 32), (24, 256, 64), (40, 512, 128)])
 def test_pack_unpack_round_trip(shape, act):

@@ -154,3 +154,22 @@ def unit_vectors(K: int, ks) -> np.ndarray:
 def random_codes(N: int, K: int, seed: int) -> np.ndarray:
     """Uniform 4-bit codes u8 [N][K] for packing tests."""
     return np.random.default_rng([1, seed]).integers(0, 16, size=(N, K), dtype=np.uint8)
+
+
+def random_words(rows: int, cols: int, seed: int) -> np.ndarray:
+    """Uniform 32-bit words int32 [rows][cols]: eight independent uniform 4-bit values
+    per word whatever the nibble order, i.e. a packed matrix of uniform codes (or
+    zero points) drawn without packing anything.  Used for layers too large to
+    quantise on the host."""
+    w = np.random.default_rng([2, seed]).integers(0, 1 << 32, size=(rows, cols), dtype=np.uint32)
+    return w.view(np.int32)
+
+
+def random_scales(G: int, N: int, seed: int, lo: float = 0.002, hi: float = 0.01) -> np.ndarray:
+    """binary16 scales [G][N], uniform in [lo, hi)."""
+    return np.random.default_rng([3, seed]).uniform(lo, hi, size=(G, N)).astype(np.float16)
+
+
+def random_activations(M: int, K: int, seed: int) -> np.ndarray:
+    """binary16 activations [M][K] ~ N(0, 1)."""
+    return np.random.default_rng([4, seed]).standard_normal((M, K)).astype(np.float16)
