@@ -149,8 +149,9 @@ int w4a16_unpack_zeros(const int32_t* qzeros, int G, int N, uint8_t* zeros);
 /* y = x * W^T with W^ = (q - Z) * S, fp32 accumulation, y rounded once to binary16.
  * All pointers are device pointers.  g_idx non-NULL selects the act-order layout
  * (qweight must have been packed with that g_idx; the kernels read the stored order
- * from qweight and gather x through it).  M == 1 runs the split-K GEMV (K <= 16384 and
- * under 2 GB of codes, else the MFMA kernels); 2 <= M <= 32 (under 2 GB of codes)
+ * from qweight and gather x through it).  M == 1 runs the split-K GEMV (K <= 65536, at
+ * most 512 groups per row and under 2 GB of codes, else the MFMA kernels; rows longer
+ * than 8192 channels are split over several wavefronts); 2 <= M <= 32 (under 2 GB of codes)
  * the skinny-batch MFMA kernel (one launch per 16 rows); larger M the tiled MFMA GEMM
  * (64-, 128- or 256-row tiles), which under act order first gathers x into
  * stream-ordered scratch memory taken from and returned to the device's default memory

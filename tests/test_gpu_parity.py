@@ -51,6 +51,14 @@ SMALL = [
     ("s23", 27, 392, 2048, 128, False),
     ("s21", 64, 136, 1024, 32, True),
     ("s22", 100, 264, 512, 128, False),
+    # long rows (K > 8192): the decode GEMV splits a row over 2 / 4 / 8 wavefronts;
+    # exact slices, act order, ragged slices (K = 28672: 224 of 256 lane chunks), an odd
+    # chunk count (uneven slices) and the longest row (K = 65536, 512 groups)
+    ("s24", 1, 264, 16384, 128, False),
+    ("s25", 1, 136, 12288, 64, True),
+    ("s26", 1, 72, 28672, 128, False),
+    ("s27", 1, 40, 10272, 32, False),
+    ("s28", 1, 16, 65536, 128, False),
 ]
 
 
@@ -114,7 +122,7 @@ def test_unit_vector_probes_bit_exact_many_rows(case, count):
     assert np.array_equal(y.view(np.uint16), expect.view(np.uint16))
 
 
-@pytest.mark.parametrize("case", [0, 2, 4, 6, 7, 9])
+@pytest.mark.parametrize("case", [0, 2, 4, 6, 7, 9, 23, 24, 25, 26])
 def test_unit_vector_probes_bit_exact(case):
     """x = e_k selects column k of W^: y = binary16(W^[:, k]) exactly (one exact
     product, exact fp32 sums of zeros, one rounding)."""

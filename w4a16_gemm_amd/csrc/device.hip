@@ -71,22 +71,27 @@ constexpr size_t kGemvLdsBudget = 144 * 1024;  // of the 160 KB of a gfx950 CU
 
 struct GemvShape {
   int lpr = 0;  // lanes per row
-  int cpl = 0;  // 16-byte chunks per lane per row
+  int cpl = 0;  // 16-byte chunks per lane per row (slice)
   bool exact = false;
+  int wpr = 1;  // wavefronts per row: slices of a long row
 };
 
-// Lanes per row and chunks per lane for K/32 chunks per row: an exact split with the
-// widest rows first, else the widest split that keeps at most 8 chunks per lane.
+// Lanes per row, chunks per lane and slices for K/32 chunks per row.  Up to 256
+// chunks (K <= 8192): an exact split with the widest rows first, else the widest
+// split, at most 4 chunks per lane (more spill the activations out of registers).
+// Longer rows: one wavefront per slice, 2, 4 or 8 slices of at most 256 chunks.
 GemvShape pick_gemv_shape(int K) {
   const int C = K / 32;
-  for (int lpr : {64, 32, 16, 8})
-    if (C % lpr == 0 && C / lpr <= 8) return {lpr, C / lpr, true};
-  for (int lpr : {64, 32, 16, 8})
-    if (lpr <= C || lpr == 8) {
-      const int cpl = (C + lpr - 1) / lpr;
-      if (cpl <= 8) return {lpr, cpl, false};
-      return {};
-    }
+  if (C <= 256) {
+    for (int lpr : {64, 32, 16, 8})
+      if (C % lpr == 0 && C / lpr <= 4) return {lpr, C / lpr, true, 1};
+    for (int lpr : {64, 32, 16, 8})
+      if (lpr <= C || lpr == 8) return {lpr, (C + lpr - 1) / lpr, false, 1};
+  }
+  for (int wpr : {2, 4, 8}) {
+    const int cs = (C + wpr - 1) / wpr;
+    if (cs <= 256) return {64, (cs + 63) / 64, C % wpr == 0 && cs % 64 == 0, wpr};
+  }
   return {};
 }
 
@@ -103,12 +108,12 @@ int device_cus() {
 }
 
 // Register-pipeline depth: about 8 KB of codes in flight per wavefront.
-constexpr int gemv_depth(int cpl) { return cpl >= 4 ? 2 : 8 / cpl; }
+constexpr int gemv_depth(int cpl) { return cpl >= 3 ? 2 : 8 / cpl; }
 
-template <int LPR, int CPL, bool EXACT, bool ACT, int EPT>
+template <int LPR, int CPL, bool EXACT, bool ACT, int EPT, int WPR>
 void launch_gemv_e(dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
                    const uint16_t* s, const uint32_t* z, half_t* y, int N, int K, int gshift, int steps) {
-  auto kern = gemv_m1_kernel<LPR, CPL, kGemvWaves, gemv_depth(CPL), EXACT, ACT, EPT>;
+  auto kern = gemv_m1_kernel<LPR, CPL, kGemvWaves, gemv_depth(CPL), EXACT, ACT, EPT, WPR>;
   // Dynamic LDS above 64 KB has to be allowed per kernel (once per process).
   static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -124,8 +129,8 @@ template <int LPR, int CPL, bool EXACT, bool ACT>
 void launch_gemv_t(int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
                    const uint16_t* s, const uint32_t* z, half_t* y, int N, int K, int gshift, int steps) {
   if constexpr (EXACT && !ACT)
-    if (ept == 1) return launch_gemv_e<LPR, CPL, EXACT, ACT, 1>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
-  launch_gemv_e<LPR, CPL, EXACT, ACT, 8>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+    if (ept == 1) return launch_gemv_e<LPR, CPL, EXACT, ACT, 1, 1>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+  launch_gemv_e<LPR, CPL, EXACT, ACT, 8, 1>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
 }
 
 template <int LPR, bool EXACT, bool ACT>
@@ -135,18 +140,31 @@ void launch_gemv_cpl(int cpl, int ept, dim3 grid, size_t shmem, hipStream_t st, 
     case 1: launch_gemv_t<LPR, 1, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
     case 2: launch_gemv_t<LPR, 2, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
     case 3: launch_gemv_t<LPR, 3, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 4: launch_gemv_t<LPR, 4, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 5: launch_gemv_t<LPR, 5, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 6: launch_gemv_t<LPR, 6, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 7: launch_gemv_t<LPR, 7, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    default: launch_gemv_t<LPR, 8, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    default: launch_gemv_t<LPR, 4, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
   }
+}
+
+// Split rows (K > 8192): 64 lanes per row slice, 3 or 4 chunks per lane, whole 8-row
+// staging items (a row has more than 64 groups).
+template <int WPR, bool EXACT, bool ACT>
+void launch_gemv_split(int cpl, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
+                       const uint16_t* s, const uint32_t* z, half_t* y, int N, int K, int gshift, int steps) {
+  if (cpl == 3) launch_gemv_e<64, 3, EXACT, ACT, 8, WPR>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+  else launch_gemv_e<64, 4, EXACT, ACT, 8, WPR>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
 }
 
 template <bool EXACT, bool ACT>
 void launch_gemv_lpr(const GemvShape& sh, int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x,
                      const uint32_t* qw, const uint16_t* s, const uint32_t* z, half_t* y, int N, int K,
                      int gshift, int steps) {
+  if (sh.wpr > 1) {
+    switch (sh.wpr) {
+      case 2: launch_gemv_split<2, EXACT, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+      case 4: launch_gemv_split<4, EXACT, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+      default: launch_gemv_split<8, EXACT, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    }
+    return;
+  }
   switch (sh.lpr) {
     case 64: launch_gemv_cpl<64, EXACT, ACT>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
     case 32: launch_gemv_cpl<32, EXACT, ACT>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
@@ -156,38 +174,53 @@ void launch_gemv_lpr(const GemvShape& sh, int ept, dim3 grid, size_t shmem, hipS
 }
 
 // LDS of one workgroup: the two-slot scale/zero ring (unit rows x (G+1) float2 each),
-// the row results, and the gathered activations under act order.
-size_t gemv_lds_bytes(int K, int G, int unit, int steps, bool act) {
-  return 2 * static_cast<size_t>(unit) * (G + 1) * 2 * sizeof(float) + static_cast<size_t>(steps) * unit * sizeof(float) +
-         (act ? static_cast<size_t>(K) * sizeof(half_t) : 0);
+// the row (slice) results, and the gathered activations under act order.
+size_t gemv_lds_bytes(int K, int G, int unit, int steps, int wpr, bool act) {
+  return 2 * static_cast<size_t>(unit) * (G + 1) * 2 * sizeof(float) +
+         static_cast<size_t>(steps) * unit * wpr * sizeof(float) + (act ? static_cast<size_t>(K) * sizeof(half_t) : 0);
 }
 
-int run_gemv(const GemvShape& sh, bool act, const half_t* x, const uint32_t* qw, const uint16_t* s,
-             const uint32_t* z, half_t* y, int N, int K, int gshift, hipStream_t st) {
+// Launch plan of the GEMV for one layer; ok == false: the GEMV does not take it (the
+// caller routes the layer to the MFMA kernels).
+struct GemvPlan {
+  bool ok = false;
+  GemvShape sh;
+  int blocks = 0, steps = 0, ept = 8;
+  size_t shmem = 0;
+};
+
+GemvPlan plan_gemv(int N, int K, int gshift, bool act) {
+  GemvPlan p;
+  p.sh = pick_gemv_shape(K);
+  if (p.sh.lpr == 0) return p;
+  if (static_cast<long long>(N) * K / 2 >= (1LL << 31)) return p;   // 32-bit byte offsets into the codes
   const int G = K >> gshift;
-  const int unit = kGemvWaves * (64 / sh.lpr);                 // rows per unit
-  if ((unit / 8) * G > kGemvWaves * 64)
-    return fail(W4A16_ERR_UNSUPPORTED, "GEMV staging: %d items per step exceed one per thread", (unit / 8) * G);
-  const int ept = unit * G <= kGemvWaves * 64 ? 1 : 8;        // staging rows per thread
+  const int unit = kGemvWaves * (64 / p.sh.lpr);                    // rows per unit
+  if ((unit / 8) * G > kGemvWaves * 64) return p;                   // one staging item per thread and step
+  p.ept = unit * G <= kGemvWaves * 64 ? 1 : 8;                      // staging rows per thread
   const int units = (N + unit - 1) / unit;
   const int per_cu = env_int("W4A16_TUNE_GEMV_BLOCKS_PER_CU", 1);
-  int blocks = std::min(units, std::max(1, device_cus() * std::max(1, per_cu)));
-  if (blocks >= 8) blocks -= blocks % 8;                         // whole XCD rounds
-  int steps = (units + blocks - 1) / blocks;
-  while (gemv_lds_bytes(K, G, unit, steps, act) > kGemvLdsBudget && blocks < units) {
-    blocks = std::min(units, blocks * 2);
-    steps = (units + blocks - 1) / blocks;
+  p.blocks = std::min(units, std::max(1, device_cus() * std::max(1, per_cu)));
+  if (p.blocks >= 8) p.blocks -= p.blocks % 8;                      // whole XCD rounds
+  p.steps = (units + p.blocks - 1) / p.blocks;
+  while (gemv_lds_bytes(K, G, unit, p.steps, p.sh.wpr, act) > kGemvLdsBudget && p.blocks < units) {
+    p.blocks = std::min(units, p.blocks * 2);
+    p.steps = (units + p.blocks - 1) / p.blocks;
   }
-  if (gemv_lds_bytes(K, G, unit, steps, act) > kGemvLdsBudget)
-    return fail(W4A16_ERR_UNSUPPORTED, "GEMV staging for N=%d, K=%d does not fit in LDS", N, K);
-  const dim3 grid(blocks);
-  const size_t shmem = gemv_lds_bytes(K, G, unit, steps, act);
-  if (sh.exact) {
-    if (act) launch_gemv_lpr<true, true>(sh, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
-    else launch_gemv_lpr<true, false>(sh, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+  p.shmem = gemv_lds_bytes(K, G, unit, p.steps, p.sh.wpr, act);
+  p.ok = p.shmem <= kGemvLdsBudget;
+  return p;
+}
+
+int run_gemv(const GemvPlan& p, bool act, const half_t* x, const uint32_t* qw, const uint16_t* s,
+             const uint32_t* z, half_t* y, int N, int K, int gshift, hipStream_t st) {
+  const dim3 grid(p.blocks);
+  if (p.sh.exact) {
+    if (act) launch_gemv_lpr<true, true>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
+    else launch_gemv_lpr<true, false>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
   } else {
-    if (act) launch_gemv_lpr<false, true>(sh, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
-    else launch_gemv_lpr<false, false>(sh, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+    if (act) launch_gemv_lpr<false, true>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
+    else launch_gemv_lpr<false, false>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
   }
   return check_launch("gemv launch");
 }
@@ -398,16 +431,14 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
   auto* hy = reinterpret_cast<half_t*>(y);
 
   const Path forced = forced_path();
-  const GemvShape sh = pick_gemv_shape(K);
-  // the GEMV addresses the codes with 32-bit byte offsets: layers of up to 2 GB of codes
-  const bool gemv_ok = M == 1 && sh.lpr != 0 && static_cast<long long>(N) * K / 2 < (1LL << 31);
-  if (forced == Path::kGemv && !gemv_ok)
-    return fail(W4A16_ERR_UNSUPPORTED, "the GEMV path needs M == 1, K <= 16384 and N*K/2 < 2^31 (M=%d N=%d K=%d)",
-                M, N, K);
-  const bool use_gemv = gemv_ok && forced != Path::kGemm;
-
-  if (use_gemv)
-    return run_gemv(sh, act, hx, hq, reinterpret_cast<const uint16_t*>(scales), hz, hy, N, K, gshift, st);
+  const GemvPlan gp = M == 1 ? plan_gemv(N, K, gshift, act) : GemvPlan{};
+  if (forced == Path::kGemv && !gp.ok)
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "the GEMV path needs M == 1, K <= 65536, N*K/2 < 2^31 and at most 512 groups per row "
+                "(M=%d N=%d K=%d group_size=%d)",
+                M, N, K, group_size);
+  if (gp.ok && forced != Path::kGemm)
+    return run_gemv(gp, act, hx, hq, reinterpret_cast<const uint16_t*>(scales), hz, hy, N, K, gshift, st);
 
   // Up to kSkinnyChunkMaxM rows: the skinny kernel once per 16 rows of x and y.  Every
   // launch streams the whole weight matrix again, so from three launches on the

@@ -13,6 +13,11 @@
 //  * A row's K input channels are split into 32-channel chunks (16 bytes of codes).
 //    LPR lanes share a row; lane j owns chunks j, j+LPR, ... (CPL of them), so each
 //    wave-wide 16-byte load is one contiguous run of the row.
+//  * Long rows (more than 256 chunks, K > 8192) are split into WPR contiguous slices,
+//    one per wavefront, so that no lane holds more than four chunks of activations
+//    (more would spill registers).  A slice is a shorter contiguous row in memory;
+//    the WPR wavefronts of a row each take WPR rows per step, one slice of each, and
+//    the WPR partial sums of a row are added in slice order before the rounding.
 //  * Each wavefront walks its rows with a DEPTH-deep register pipeline: the loads
 //    of row t+DEPTH are issued as soon as row t has been consumed.
 //  * Activations are loaded once into registers (under act order gathered through
@@ -74,15 +79,17 @@ __device__ __forceinline__ float lane_group_sum(float v) {
 // (one row per wavefront row-slot); unit u is processed by workgroup u % nblk at step
 // u / nblk.  At any moment the whole grid streams one contiguous window of the
 // weights, and within a unit the wavefronts read neighbouring rows.
-// LDS: scale/zero ring 2 * STRIDE * (G + 1) float2, row results steps * STRIDE floats,
+// LDS: scale/zero ring 2 * STRIDE * (G + 1) float2, row results steps * STRIDE * WPR floats,
 // and under act order the gathered activations, K binary16.  Needs 8 OCT G / EPT <=
 // WAVES * 64 (at most one staging task per thread and step) and an even DEPTH.
-template <int LPR, int CPL, int WAVES, int DEPTH, bool EXACT, bool ACT, int EPT>
+template <int LPR, int CPL, int WAVES, int DEPTH, bool EXACT, bool ACT, int EPT, int WPR>
 __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
     const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
     const uint32_t* __restrict__ qzeros, half_t* __restrict__ y, int N, int K, int gshift, int steps) {
   static_assert(64 % LPR == 0, "lanes per row must divide the wavefront");
   static_assert(DEPTH % 2 == 0, "the ring slot of row t is t % 2, the unrolled slot index");
+  static_assert(WPR == 1 || (LPR == 64 && WAVES % WPR == 0 && WPR % DEPTH == 0),
+                "split rows: one row per wavefront, whole register slots per step");
   constexpr int RPW = 64 / LPR;          // rows per wavefront per step
   constexpr int STRIDE = WAVES * RPW;    // rows per unit
   static_assert(STRIDE % 8 == 0, "a unit must cover whole 8-row groups of zero points");
@@ -96,23 +103,32 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   const int rr = lane / LPR;
   const int j = lane % LPR;
   const int C = K >> 5;                  // 32-channel chunks per row
+  const int CS = (C + WPR - 1) / WPR;    // chunks per slice
+  const int h = WPR == 1 ? 0 : wave % WPR;   // this wavefront's slice
   const int W = K >> 3;                  // words per row
   const int G = K >> gshift;
   const int GP = G + 1;                  // padded ring row (float2)
   const int nblk = gridDim.x;
   const int blk = xcd_block(blockIdx.x, nblk);
-  const int my_row = wave * RPW + rr;    // row inside a unit
-  auto row_of = [&](int t) { return (blk + t * nblk) * STRIDE + my_row; };
+  // Row inside a unit at sub-step s (split rows: WPR sub-steps per step, WAVES / WPR
+  // rows each), and the matrix row of the wavefront's seq-th row (seq = t WPR + s).
+  auto unit_row = [&](int s) { return WPR == 1 ? wave * RPW + rr : wave / WPR + (WAVES / WPR) * s; };
+  const int my_row = unit_row(0);
+  auto row_of = [&](int seq) { return (blk + (seq / WPR) * nblk) * STRIDE + unit_row(seq % WPR); };
 
   float2* ring = reinterpret_cast<float2*>(smem);                                   // [2][STRIDE][GP]
   float* ybuf = reinterpret_cast<float*>(smem + 2 * static_cast<size_t>(STRIDE) * GP * sizeof(float2));
-  half_t* xs = reinterpret_cast<half_t*>(ybuf + static_cast<size_t>(steps) * STRIDE);
+  half_t* xs = reinterpret_cast<half_t*>(ybuf + static_cast<size_t>(steps) * STRIDE * WPR);
 
-  // This lane's chunks (clamped into the row unless the split is exact) and groups.
+  // This lane's chunks (clamped into its slice and the row unless the split is exact)
+  // and their groups; `live` chunks lie inside both.
   int chunk[CPL], gcol[CPL];
+  bool live[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
-    chunk[i] = EXACT ? j + LPR * i : min(j + LPR * i, C - 1);
+    const int local = j + LPR * i;
+    chunk[i] = EXACT ? h * CS + local : min(h * CS + min(local, CS - 1), C - 1);
+    live[i] = EXACT || (local < CS && h * CS + local < C);
     gcol[i] = (chunk[i] << 5) >> gshift;
   }
 
@@ -161,17 +177,20 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   // under act order the stored channel order, 16 bytes per load, all at once), the
   // staging items of steps 0 and 1, then the first DEPTH rows of codes.
   uint4 xv[CPL][4];
-  constexpr int PPT = (LPR * CPL + 63) / 64;   // 4-entry chunks of the order per thread: covers K
-  int4 pv[PPT];
+  // Under act order the stored order is read in 4-entry pieces, PPT per thread to
+  // cover the whole row, PB of them in flight per round.
+  constexpr int PPT = (WPR * LPR * CPL + 63) / 64;
+  constexpr int PB = PPT < 4 ? PPT : 4;
+  const int4* perm4 = reinterpret_cast<const int4*>(qw + static_cast<size_t>(N) * W);
+  int4 pv[PB];
   if constexpr (!ACT) {
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) xv[i][q] = reinterpret_cast<const uint4*>(x)[4 * chunk[i] + q];
   } else {
-    const int4* perm4 = reinterpret_cast<const int4*>(qw + static_cast<size_t>(N) * W);
 #pragma unroll
-    for (int u = 0; u < PPT; ++u) pv[u] = perm4[min(tid + u * NT, (K >> 2) - 1)];
+    for (int u = 0; u < PB; ++u) pv[u] = perm4[min(tid + u * NT, (K >> 2) - 1)];
   }
   load_item(0, 0);
   load_item(1, 1);
@@ -185,28 +204,35 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
       dst[i] = load_stream16(codes, (static_cast<uint32_t>(nc) * static_cast<uint32_t>(W) + 4u * chunk[i]) * 4u);
   };
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) load_row(wb[d], row_of(d));  // clamped if steps < DEPTH
+  for (int d = 0; d < DEPTH; ++d) load_row(wb[d], row_of(d));  // clamped if there are fewer rows
 
   // 2. Act order: gather the activations into LDS in stored order (all gathers of a
   // thread in flight together).  Step 0's items go to ring slot 0; the barrier
   // publishes both.
   if constexpr (ACT) {
-    half_t g[PPT][4];
 #pragma unroll
-    for (int u = 0; u < PPT; ++u) {
-      g[u][0] = x[pv[u].x];
-      g[u][1] = x[pv[u].y];
-      g[u][2] = x[pv[u].z];
-      g[u][3] = x[pv[u].w];
+    for (int r0 = 0; r0 < PPT; r0 += PB) {
+      if (r0 > 0) {
+#pragma unroll
+        for (int u = 0; u < PB; ++u) pv[u] = perm4[min(tid + (r0 + u) * NT, (K >> 2) - 1)];
+      }
+      half_t g[PB][4];
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        g[u][0] = x[pv[u].x];
+        g[u][1] = x[pv[u].y];
+        g[u][2] = x[pv[u].z];
+        g[u][3] = x[pv[u].w];
+      }
+#pragma unroll
+      for (int u = 0; u < PB; ++u)
+        if (r0 + u < PPT && tid + (r0 + u) * NT < (K >> 2))
+          *reinterpret_cast<uint2*>(xs + 4 * (tid + (r0 + u) * NT)) =
+              uint2{static_cast<uint32_t>(__builtin_bit_cast(uint16_t, g[u][0])) |
+                        (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, g[u][1])) << 16),
+                    static_cast<uint32_t>(__builtin_bit_cast(uint16_t, g[u][2])) |
+                        (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, g[u][3])) << 16)};
     }
-#pragma unroll
-    for (int u = 0; u < PPT; ++u)
-      if (tid + u * NT < (K >> 2))
-        *reinterpret_cast<uint2*>(xs + 4 * (tid + u * NT)) =
-            uint2{static_cast<uint32_t>(__builtin_bit_cast(uint16_t, g[u][0])) |
-                      (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, g[u][1])) << 16),
-                  static_cast<uint32_t>(__builtin_bit_cast(uint16_t, g[u][2])) |
-                      (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, g[u][3])) << 16)};
   }
   put_item(0, 0);
   __syncthreads();
@@ -224,15 +250,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   const half2_t ones = half2_t{static_cast<half_t>(1.0f), static_cast<half_t>(1.0f)};
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
-    const bool live = EXACT || j + LPR * i < C;
     float sx = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const uint4 v = xv[i][q];
-      xr[i][4 * q + 0] = live ? as_h2(v.x) : half2_t{0, 0};
-      xr[i][4 * q + 1] = live ? as_h2(v.y) : half2_t{0, 0};
-      xr[i][4 * q + 2] = live ? as_h2(v.z) : half2_t{0, 0};
-      xr[i][4 * q + 3] = live ? as_h2(v.w) : half2_t{0, 0};
+      xr[i][4 * q + 0] = live[i] ? as_h2(v.x) : half2_t{0, 0};
+      xr[i][4 * q + 1] = live[i] ? as_h2(v.y) : half2_t{0, 0};
+      xr[i][4 * q + 2] = live[i] ? as_h2(v.z) : half2_t{0, 0};
+      xr[i][4 * q + 3] = live[i] ? as_h2(v.w) : half2_t{0, 0};
     }
 #pragma unroll
     for (int q = 0; q < 16; ++q) sx = __builtin_amdgcn_fdot2(xr[i][q], ones, sx, false);
@@ -245,8 +270,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   // (a) requests the items of step t + 2, (b) computes row t and refills its slot,
   // (c) stages step t + 1 and closes with the barrier.  The last DEPTH steps run
   // without code refills, so no load is issued past the end.
-  auto row_step = [&](int t, int slot, uint4 (&w)[CPL]) {
-    const float2* szr = ring + (slot * STRIDE + my_row) * GP;
+  auto row_step = [&](int slot, int row, uint4 (&w)[CPL]) {
+    const float2* szr = ring + (slot * STRIDE + row) * GP;
     float2 sc[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) sc[i] = szr[gcol[i]];
@@ -279,22 +304,57 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
     }
     return acc;
   };
-  // The row total ends in lane LPR - 1 of the row's lane group.
-  auto keep = [&](int t, float acc) {
+  // The row (slice) total ends in lane LPR - 1 of the row's lane group.
+  auto keep = [&](int t, int row, float acc) {
     acc = lane_group_sum<LPR>(acc);
-    if (j == LPR - 1) ybuf[t * STRIDE + my_row] = acc;
+    if (j == LPR - 1) ybuf[(t * STRIDE + row) * WPR + h] = acc;
   };
   // one step; P = t % 2 at compile time (t0 is a multiple of the even DEPTH)
   auto step = [&](int t, int d, bool refill, auto P) {
     constexpr int p = decltype(P)::value;
     load_item(t + 2, p);                                  // (a) into the set just published
-    const float acc = row_step(t, p, wb[d]);               // (b)
+    const float acc = row_step(p, my_row, wb[d]);         // (b)
     if (refill) load_row(wb[d], row_of(t + DEPTH));
     __builtin_amdgcn_sched_barrier(0);
-    keep(t, acc);
+    keep(t, my_row, acc);
     put_item(p ^ 1, p ^ 1);                               // (c) step t + 1
     __syncthreads();
   };
+  // Split rows: a step is WPR rows of this wavefront (seq = t WPR + s, register slot
+  // s % DEPTH), each refilled with row seq + DEPTH; LAST = the final step, whose
+  // refills past the end are dropped at compile time.
+  auto split_step = [&](int t, auto P, auto LAST) {
+    constexpr int p = decltype(P)::value;
+    constexpr bool last = decltype(LAST)::value;
+    load_item(t + 2, p);
+#pragma unroll
+    for (int s = 0; s < WPR; ++s) {
+      const int row = unit_row(s);
+      const float acc = row_step(p, row, wb[s % DEPTH]);
+      if (!last || s + DEPTH < WPR) load_row(wb[s % DEPTH], row_of(t * WPR + s + DEPTH));
+      __builtin_amdgcn_sched_barrier(0);
+      keep(t, row, acc);
+    }
+    put_item(p ^ 1, p ^ 1);
+    __syncthreads();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using More = std::false_type;
+  using Last = std::true_type;
+  if constexpr (WPR > 1) {
+    int t = 0;
+    for (; t + 2 < steps; t += 2) {
+      split_step(t, I0{}, More{});
+      split_step(t + 1, I1{}, More{});
+    }
+    if (t + 1 < steps) {
+      split_step(t, I0{}, More{});
+      split_step(t + 1, I1{}, Last{});
+    } else {
+      split_step(t, I0{}, Last{});
+    }
+  } else {
 
   int t0 = 0;
   for (; t0 + 2 * DEPTH <= steps; t0 += DEPTH) {
@@ -315,13 +375,17 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
     if (t0 + DEPTH + d < steps) step(t0 + DEPTH + d, d, false, std::integral_constant<int, 0>{});
     if (t0 + DEPTH + d + 1 < steps) step(t0 + DEPTH + d + 1, d + 1, false, std::integral_constant<int, 1>{});
   }
+  }
 
   // 5. the workgroup's rows: STRIDE consecutive outputs per step (the last step's
-  // barrier published every result)
+  // barrier published every result); split rows add their slices in order
   for (int idx = tid; idx < steps * STRIDE; idx += NT) {
     const int t = idx / STRIDE;
     const int n = (blk + t * nblk) * STRIDE + (idx - t * STRIDE);
-    if (n < N) y[n] = static_cast<half_t>(ybuf[idx]);
+    float v = ybuf[idx * WPR];
+#pragma unroll
+    for (int s = 1; s < WPR; ++s) v += ybuf[idx * WPR + s];
+    if (n < N) y[n] = static_cast<half_t>(v);
   }
 }
 
