@@ -152,7 +152,9 @@ int w4a16_unpack_zeros(const int32_t* qzeros, int G, int N, uint8_t* zeros);
  * from qweight and gather x through it).  M == 1 runs the split-K GEMV (K <= 65536, at
  * most 512 groups per row and under 2 GB of codes, else the MFMA kernels; rows longer
  * than 8192 channels are split over several wavefronts); 2 <= M <= 32 (under 2 GB of codes)
- * the skinny-batch MFMA kernel (one launch per 16 rows); larger M the tiled MFMA GEMM
+ * the skinny-batch MFMA kernel (one launch per 16 rows; K > 8192 split over workgroups,
+ * fp32 partials in stream-ordered scratch memory from the device's default pool, summed
+ * by a second kernel); larger M the tiled MFMA GEMM
  * (64-, 128- or 256-row tiles), which under act order first gathers x into
  * stream-ordered scratch memory taken from and returned to the device's default memory
  * pool.  Shapes a kernel cannot take (K not a multiple of 128 for the skinny kernel, of

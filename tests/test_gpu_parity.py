@@ -59,6 +59,12 @@ SMALL = [
     ("s26", 1, 72, 28672, 128, False),
     ("s27", 1, 40, 10272, 32, False),
     ("s28", 1, 16, 65536, 128, False),
+    # long rows at skinny batches: K split over 2 / 4 / 8 workgroup slices, fp32 partials
+    # summed in a second kernel; act order, two launches of 16 + 4 rows, group size 32
+    ("s29", 4, 264, 16384, 128, False),
+    ("s30", 9, 136, 12288, 64, True),
+    ("s31", 20, 72, 28672, 128, False),
+    ("s32", 2, 40, 65536, 32, False),
 ]
 
 

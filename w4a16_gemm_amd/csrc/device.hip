@@ -238,53 +238,67 @@ void launch_gemm_bm(hipStream_t st, const half_t* x, const uint32_t* qw, const h
 // slab entries per thread.  waves == 0: not applicable.
 struct SkinnyShape {
   int waves = 0, t = 0, se = 0;
+  int ks = 1;   // K slices over the workgroups (fp32 partials summed by a second kernel)
 };
 
 constexpr int kSkinnyMaxM = 16;       // rows of one skinny launch (one MFMA column tile)
 constexpr int kSkinnyChunkMaxM = 32;  // larger M: tiled GEMM kernels
 constexpr int kBigMinM = 33;          // the large-tile kernel from here on (when K allows)
 
+// The whole row in one workgroup when it fits (K <= 8192), else the fewest K slices
+// that fit; per slice the most wavefronts (fewest slab entries per thread).
 SkinnyShape pick_skinny_shape(int M, int K, int gshift) {
   SkinnyShape sh;
-  if (M > kSkinnyMaxM || K % 128 != 0) return sh;
-  const int kc = K / 128;
-  for (int t : {1, 2, 4}) {
-    if (kc % t != 0 || kc / t > 16) continue;
-    const int waves = kc / t;
-    const int entries = 16 * (K >> gshift);
-    const int se = (entries + 64 * waves - 1) / (64 * waves);
-    if (se > 4) return sh;
-    sh.waves = waves;
-    sh.t = t;
-    sh.se = se <= 1 ? 1 : (se <= 2 ? 2 : 4);
-    return sh;
+  if (M > kSkinnyMaxM) return sh;
+  for (int ks : {1, 2, 4, 8}) {
+    if (K % (128 * ks) != 0) continue;
+    const int Ks = K / ks;
+    const int kc = Ks / 128;
+    for (int t : {1, 2, 4}) {
+      if (kc % t != 0 || kc / t > 16) continue;
+      const int waves = kc / t;
+      const int entries = 16 * (Ks >> gshift);
+      const int se = (entries + 64 * waves - 1) / (64 * waves);
+      if (se > 4) break;
+      sh.waves = waves;
+      sh.t = t;
+      sh.se = se <= 1 ? 1 : (se <= 2 ? 2 : 4);
+      sh.ks = ks;
+      return sh;
+    }
   }
   return sh;
 }
 
+// ks > 1: partial sums to part [ks][M][N] fp32, then sum_slices_kernel into y.
 template <int T, int SE, bool ACT, bool SUB>
 int launch_skinny_t(const SkinnyShape& sh, hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s,
-                    const uint32_t* z, half_t* y, int M, int N, int K, int gshift) {
+                    const uint32_t* z, half_t* y, float* part, int M, int N, int K, int gshift) {
   static const hipError_t lds_ok =
       hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_skinny_kernel<T, SE, ACT, SUB>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (int rc = hip_status(lds_ok, "hipFuncSetAttribute")) return rc;
-  const size_t lds = skinny_lds_bytes(sh.waves, K >> gshift);
+  const size_t lds = skinny_lds_bytes(sh.waves, (K / sh.ks) >> gshift);
   const int nblk = (N + 15) / 16;
   const int per_cu = std::max(1, 16 / sh.waves);
-  const int grid = std::min(nblk, device_cus() * per_cu);
-  hipLaunchKernelGGL((gemm_skinny_kernel<T, SE, ACT, SUB>), dim3(grid), dim3(64 * sh.waves), lds, st, x, qw, s, z,
-                     y, M, N, K, gshift);
-  return check_launch("skinny gemm launch");
+  const int per_slice = std::min(nblk, std::max(1, device_cus() * per_cu / sh.ks));
+  hipLaunchKernelGGL((gemm_skinny_kernel<T, SE, ACT, SUB>), dim3(per_slice * sh.ks), dim3(64 * sh.waves), lds, st, x,
+                     qw, s, z, y, part, M, N, K, gshift, sh.ks);
+  if (int rc = check_launch("skinny gemm launch")) return rc;
+  if (sh.ks == 1) return W4A16_OK;
+  const size_t count = static_cast<size_t>(M) * N;
+  hipLaunchKernelGGL(sum_slices_kernel, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0, st, part, y,
+                     sh.ks, count);
+  return check_launch("slice sum launch");
 }
 
 template <bool ACT>
 int launch_skinny(const SkinnyShape& sh, hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s,
-                  const uint32_t* z, half_t* y, int M, int N, int K, int gshift) {
-#define W4A16_SKINNY(T_, SE_)                                                                        \
-  if (sh.t == T_ && sh.se == SE_)                                                                  \
-    return gshift == 7 ? launch_skinny_t<T_, SE_, ACT, true>(sh, st, x, qw, s, z, y, M, N, K, gshift) \
-                       : launch_skinny_t<T_, SE_, ACT, false>(sh, st, x, qw, s, z, y, M, N, K, gshift);
+                  const uint32_t* z, half_t* y, float* part, int M, int N, int K, int gshift) {
+#define W4A16_SKINNY(T_, SE_)                                                                              \
+  if (sh.t == T_ && sh.se == SE_)                                                                        \
+    return gshift == 7 ? launch_skinny_t<T_, SE_, ACT, true>(sh, st, x, qw, s, z, y, part, M, N, K, gshift) \
+                       : launch_skinny_t<T_, SE_, ACT, false>(sh, st, x, qw, s, z, y, part, M, N, K, gshift);
   W4A16_SKINNY(1, 1) W4A16_SKINNY(1, 2) W4A16_SKINNY(1, 4)
   W4A16_SKINNY(2, 1) W4A16_SKINNY(2, 2) W4A16_SKINNY(2, 4)
   W4A16_SKINNY(4, 1) W4A16_SKINNY(4, 2) W4A16_SKINNY(4, 4)
@@ -448,15 +462,26 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
   if (sk.waves != 0 && static_cast<long long>(N) * K / 2 < (1LL << 31) &&
       M <= env_int("W4A16_TUNE_SKINNY_CHUNK_MAX_M", kSkinnyChunkMaxM) &&
       env_int("W4A16_TUNE_GEMM_SKINNY", 1) != 0) {
-    for (int m0 = 0; m0 < M; m0 += kSkinnyMaxM) {
+    // K slices: fp32 partial tiles in stream-ordered scratch memory, reused by the
+    // launches of every 16 rows
+    float* part = nullptr;
+    if (sk.ks > 1) {
+      const size_t bytes = static_cast<size_t>(sk.ks) * std::min(M, kSkinnyMaxM) * N * sizeof(float);
+      if (int s = hip_status(hipMallocAsync(reinterpret_cast<void**>(&part), bytes, st), "hipMallocAsync")) return s;
+    }
+    int rc = W4A16_OK;
+    for (int m0 = 0; m0 < M && rc == W4A16_OK; m0 += kSkinnyMaxM) {
       const int mc = std::min(kSkinnyMaxM, M - m0);
       const half_t* xc = hx + static_cast<size_t>(m0) * K;
       half_t* yc = hy + static_cast<size_t>(m0) * N;
-      const int rc = act ? launch_skinny<true>(sk, st, xc, hq, hs, hz, yc, mc, N, K, gshift)
-                         : launch_skinny<false>(sk, st, xc, hq, hs, hz, yc, mc, N, K, gshift);
-      if (rc != W4A16_OK) return rc;
+      rc = act ? launch_skinny<true>(sk, st, xc, hq, hs, hz, yc, part, mc, N, K, gshift)
+               : launch_skinny<false>(sk, st, xc, hq, hs, hz, yc, part, mc, N, K, gshift);
     }
-    return W4A16_OK;
+    if (part) {
+      const int rf = hip_status(hipFreeAsync(part, st), "hipFreeAsync");
+      if (rc == W4A16_OK) rc = rf;
+    }
+    return rc;
   }
 
   if (!act) return run_gemm(st, hx, hq, hs, hz, hy, M, N, K, gshift);

@@ -46,4 +46,15 @@ __global__ __launch_bounds__(256) void gather_x_kernel(const half_t* __restrict_
   xs[idx] = x[m * K + perm[p]];
 }
 
+// Split-K skinny batches: y[i] = binary16(sum over the ks slices of part[s][i]), the
+// slices added in order, one rounding.
+__global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict__ part, half_t* __restrict__ y,
+                                                         int ks, size_t count) {
+  const size_t idx = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= count) return;
+  float v = part[idx];
+  for (int s = 1; s < ks; ++s) v += part[s * count + idx];
+  y[idx] = static_cast<half_t>(v);
+}
+
 }  // namespace w4a16

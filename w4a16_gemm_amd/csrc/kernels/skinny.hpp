@@ -22,6 +22,10 @@
 //    are staged once in an LDS slab, double buffered, by all threads of the workgroup.
 //  * The W partial 16 x 16 tiles are summed in LDS in a fixed order and rounded once
 //    to binary16.  Codes of the next row block are in flight while a block is computed.
+//  * Rows longer than 16 wavefronts x 4 steps x 128 channels (K > 8192) are split into
+//    ks slices over the workgroups: the workgroups of slice s hold the activations of
+//    channels [s K / ks, (s + 1) K / ks) and write fp32 partial tiles, which a second
+//    kernel adds in slice order and rounds once.
 // Act order: the activation slice is gathered through the stored channel order
 // when it is loaded into registers, so no scratch copy of x is needed.
 #pragma once
@@ -63,10 +67,13 @@ constexpr size_t skinny_lds_bytes(int waves, int groups) {
 // step's four MFMAs accumulate one group's sum of q x into a fresh tile, and the
 // group's scale and zero point enter once per step:
 //     acc += (S * 2^24) * sum q x + (-Z * S) * sum x.
+// ks > 1: gridDim.x = ks * (workgroups per slice); partial sums go to part [ks][M][N]
+// (fp32) instead of y.
 template <int T, int SE, bool ACT, bool SUB>
 __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
     const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const half_t* __restrict__ scales,
-    const uint32_t* __restrict__ qzeros, half_t* __restrict__ y, int M, int N, int K, int gshift) {
+    const uint32_t* __restrict__ qzeros, half_t* __restrict__ y, float* __restrict__ part, int M, int N, int K,
+    int gshift, int ks) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -74,10 +81,14 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
   const int nthreads = blockDim.x;
   const int lr = lane & 15, lq = lane >> 4;
   const int Wd = K >> 3;
-  const int G = K >> gshift;
+  const int gs = gridDim.x / ks;                  // workgroups per slice
+  const int slice = blockIdx.x / gs;
+  const int Ks = K / ks;                          // channels per slice
+  const int G = Ks >> gshift;                     // groups per slice (slab rows)
+  const int g0 = slice * G;                       // first group of the slice
   const int slab_n = 16 * G;
   const int nblk = (N + 15) >> 4;
-  const int kw = wave * 128 * T;
+  const int kw = slice * Ks + wave * 128 * T;
 
   extern __shared__ __align__(16) unsigned char smem[];
   float* red = reinterpret_cast<float*>(smem);                                              // [2][W][16 m][16 n]
@@ -152,7 +163,7 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
 #pragma unroll
     for (int u = 0; u < SE; ++u) {
       const int e = min(tid + u * nthreads, slab_n - 1);
-      const int gi = e >> 4;
+      const int gi = g0 + (e >> 4);
       const int n = min(16 * b + (e & 15), N - 1);
       sv[u] = scales[static_cast<size_t>(gi) * N + n];
       zv[u] = qzeros[static_cast<size_t>(gi) * (N >> 3) + (n >> 3)];
@@ -182,7 +193,7 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
   uint4 cw[T];
   auto row_block = [&](int b, int i) {
     const int buf = i & 1;
-    const uint32_t off_next = code_offset(b + static_cast<int>(gridDim.x));
+    const uint32_t off_next = code_offset(b + gs);
     float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -200,7 +211,7 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
         for (int j = 0; j < 4; ++j) part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j], xr[t][j], part, 0, 0, 0);
         // rows n = 4 q + r of the tile hold this lane's four results; their group's
         // (S * 2^24, -Z * S) are four consecutive slab entries
-        const int gi = (kw + 128 * t) >> 7;
+        const int gi = ((kw + 128 * t) >> 7) - g0;
         const float4* e4 = reinterpret_cast<const float4*>(slab + buf * slab_n + gi * 16 + 4 * lq);
         const float4 e01 = e4[0], e23 = e4[1];
         acc[0] = fmaf(e01.y, xs[t], fmaf(e01.x, part[0], acc[0]));
@@ -208,7 +219,7 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
         acc[2] = fmaf(e23.y, xs[t], fmaf(e23.x, part[2], acc[2]));
         acc[3] = fmaf(e23.w, xs[t], fmaf(e23.z, part[3], acc[3]));
       } else {
-        const int gi = (kw + 128 * t + 32 * lq) >> gshift;
+        const int gi = ((kw + 128 * t + 32 * lq) >> gshift) - g0;
         const DequantConsts dc = slab_consts(slab[buf * slab_n + gi * 16 + lr]);
         half8_t wf[4];
 #pragma unroll
@@ -220,8 +231,8 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
     }
     // D layout: lane (r, q) holds rows n = 4 q + 0..3 of column m = r.
     *reinterpret_cast<float4_t*>(red + ((buf * nwaves + wave) * 16 + lr) * 16 + 4 * lq) = acc;
-    write_slab(b + static_cast<int>(gridDim.x), buf ^ 1);
-    load_sz(b + 2 * static_cast<int>(gridDim.x));
+    write_slab(b + gs, buf ^ 1);
+    load_sz(b + 2 * gs);
     __syncthreads();
     if (tid < 256) {
       const int m = tid >> 4, n = 16 * b + (tid & 15);
@@ -229,18 +240,20 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
         const float* p = red + buf * nwaves * 256 + tid;
         float s = 0.f;
         for (int w = 0; w < nwaves; ++w) s += p[w * 256];
-        y[static_cast<size_t>(m) * N + n] = static_cast<half_t>(s);
+        if (ks == 1) y[static_cast<size_t>(m) * N + n] = static_cast<half_t>(s);
+        else part[(static_cast<size_t>(slice) * M + m) * N + n] = s;
       }
     }
   };
 
-  int b = xcd_block(blockIdx.x, gridDim.x);   // row blocks b, b + grid, ... (neighbours on one XCD)
+  // row blocks b, b + gs, ... of this slice (neighbours on one XCD)
+  int b = xcd_block(blockIdx.x - slice * gs, gs);
   load_codes(b, cw);
   load_sz(b);
   write_slab(b, 0);
-  load_sz(b + static_cast<int>(gridDim.x));
+  load_sz(b + gs);
   __syncthreads();
-  for (int i = 0; b < nblk; ++i, b += gridDim.x) row_block(b, i);
+  for (int i = 0; b < nblk; ++i, b += gs) row_block(b, i);
 }
 
 }  // namespace w4a16
