@@ -48,8 +48,8 @@ SECONDARY = [("c1", 1), ("c2up", 1), ("c2down", 1), ("c3", 2), ("c3", 4), ("c3",
              ("c4", 2048), ("c5", 1), ("c5", 512)]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = ["w4a16_gemm_amd/csrc/kernels/nibbles.hpp", "w4a16_gemm_amd/csrc/kernels/gemv.hpp",
-                  "w4a16_gemm_amd/csrc/kernels/gemm.hpp", "w4a16_gemm_amd/csrc/kernels/aux.hpp",
-                  "w4a16_gemm_amd/csrc/device.hip"]
+                  "w4a16_gemm_amd/csrc/kernels/gemm.hpp", "w4a16_gemm_amd/csrc/kernels/skinny.hpp",
+                  "w4a16_gemm_amd/csrc/kernels/aux.hpp", "w4a16_gemm_amd/csrc/device.hip"]
 
 
 def algo_bytes(cfg: wl.LayerConfig, M: int) -> int:
