@@ -244,6 +244,108 @@ def dense_reference_us(cfg: wl.LayerConfig, M: int, iters: int = 30) -> float:
     return round(us, 3)
 
 
+def decode_step_bench(step: wl.DecodeStep, steps: int = 100, warmup: int = 10):
+    """One decode token at batch one of a whole model's quantised linear layers:
+    step.layers x the step's linears, each layer with its own weights (distinct device
+    copies, more than twice the Infinity Cache in all), launched back to back.  Timed
+    eagerly (one library call per layer) and as one HIP graph replay per step; each
+    linear shape also alone.  The unquantised head is timed through the vendor library
+    as context.  Values of the weights do not change the work: they are uniform random
+    packed words and scales (the parity of these shapes is a test)."""
+    import torch
+    import w4a16_gemm_amd as w4
+    lib = w4.lib()
+    dev = torch.device("cuda:0")
+    g = step.group_size
+    shapes = []
+    for i, (name, K, N) in enumerate(step.linears):
+        G = K // g
+        qw = torch.from_numpy(wl.random_words(N, K // 8, seed=900 + i)).to(dev)
+        sc = torch.from_numpy(wl.random_scales(G, N, seed=900 + i)).to(dev)
+        qz = torch.from_numpy(wl.random_words(G, N // 8, seed=950 + i)).to(dev)
+        copies = [(qw, sc, qz)] + [(qw.clone(), sc.clone(), qz.clone()) for _ in range(step.layers - 1)]
+        x = torch.from_numpy(wl.random_activations(1, K, seed=i)).to(dev)
+        y = torch.empty((1, N), dtype=torch.float16, device=dev)
+        nbytes = N * K // 2 + 2 * G * N + G * N // 2 + 2 * K + 2 * N
+        shapes.append({"name": name, "K": K, "N": N, "copies": copies, "x": x, "y": y, "bytes": nbytes})
+
+    def call(sh, layer, stream):
+        q, sc, z = sh["copies"][layer]
+        rc = lib.w4a16_gemm(sh["x"].data_ptr(), q.data_ptr(), sc.data_ptr(), z.data_ptr(), None, g, 1,
+                            sh["N"], sh["K"], sh["y"].data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"w4a16_gemm failed ({rc}): {lib.w4a16_last_error().decode()}")
+
+    def one_step():
+        st = torch.cuda.current_stream(dev).cuda_stream
+        for layer in range(step.layers):
+            for sh in shapes:
+                call(sh, layer, st)
+
+    def region(fn, n):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return 1e3 * a.elapsed_time(b) / n
+
+    eager_us = region(one_step, steps)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        one_step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        one_step()
+    graph_us = region(graph.replay, steps)
+    per_linear = {}
+    for sh in shapes:
+        st = torch.cuda.current_stream(dev).cuda_stream
+        counter = [0]
+
+        def one():
+            call(sh, counter[0] % step.layers, st)
+            counter[0] += 1
+        us = region(one, 4 * step.layers)
+        per_linear[sh["name"]] = {"K": sh["K"], "N": sh["N"], "us": round(us, 3),
+                                  "GBps": round(sh["bytes"] / us / 1e3, 1)}
+    step_bytes = step.layers * sum(sh["bytes"] for sh in shapes)
+    del graph, shapes
+    torch.cuda.empty_cache()
+    # the unquantised head (bfloat16, as the recipe keeps it), vendor library
+    hk, hn = step.head
+    gen = torch.Generator(device=dev).manual_seed(0)
+    wh = torch.randn(hn, hk, generator=gen, device=dev, dtype=torch.bfloat16)
+    xh = torch.randn(1, hk, generator=gen, device=dev, dtype=torch.bfloat16)
+    head_us = region(lambda: torch.matmul(xh, wh.t()), 50)
+    del wh, xh
+    torch.cuda.empty_cache()
+    return {
+        "workload": step.note, "layers": step.layers,
+        "linears": [f"{n} {k}->{m}" for n, k, m in step.linears], "group_size": g,
+        "launches_per_step": step.layers * len(step.linears),
+        "algo_bytes_per_step": step_bytes,
+        "eager_us_per_step": round(eager_us, 2),
+        "graph_us_per_step": round(graph_us, 2),
+        "tokens_per_s_graph": round(1e6 / graph_us, 1),
+        "GBps_graph": round(step_bytes / graph_us / 1e3, 1),
+        "hbm_frac_graph": round(step_bytes / graph_us / 1e3 / HBM_PEAK_GBS, 4),
+        "roofline_us_per_step": round(step_bytes / HBM_PEAK_GBS / 1e3, 2),
+        "per_linear_alone": per_linear,
+        "head_bf16_library_us": round(head_us, 2),
+        "tokens_per_s_graph_with_head": round(1e6 / (graph_us + head_us), 1),
+        "head_note": (f"unquantised {hk}->{hn} head in bfloat16 through torch.matmul (vendor library), "
+                      "timed alone as context; not part of the W4A16 path"),
+    }
+
+
 def traffic_for(hash_now: str, key: str):
     try:
         with open(TRAFFIC_FILE) as f:
@@ -266,6 +368,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-ref", action="store_true",
                     help="skip timing the dense binary16 library GEMM of the same shapes")
+    ap.add_argument("--no-decode-step", action="store_true",
+                    help="skip the whole-decode-step workload of the 1.5B example")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain streaming kernel over this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -374,6 +478,9 @@ def main() -> int:
             ref["c4:M2048_us"] = dense_reference_us(wl.CONFIGS["c4"], 2048, iters=20)
             ref["c4:M2048_w4a16_speedup"] = round(ref["c4:M2048_us"] / pre["us_per_layer"], 3)
         line["dense_fp16_reference"] = ref
+    if not args.no_decode_step and args.configs in ("all", "headline"):
+        log("timing the decode step of the 1.5B example (eager and graph replay)")
+        line["decode_step"] = decode_step_bench(wl.DECODE_1P5B)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (cpu_baseline)")
         line["cpu_baseline"] = cpu_baseline(hcfg, args.cpu_rows)

@@ -173,3 +173,37 @@ def random_scales(G: int, N: int, seed: int, lo: float = 0.002, hi: float = 0.01
 def random_activations(M: int, K: int, seed: int) -> np.ndarray:
     """binary16 activations [M][K] ~ N(0, 1)."""
     return np.random.default_rng([4, seed]).standard_normal((M, K)).astype(np.float16)
+
+
+# --- a whole decode step of a small model -----------------------------------------
+
+@dataclass(frozen=True)
+class DecodeStep:
+    """The quantised linear layers one decode token at batch one runs through, in
+    call order, and the unquantised output head."""
+    name: str
+    layers: int
+    linears: tuple              # (name, K, N) per transformer layer, in call order
+    head: tuple                 # (K, N) of the output head, kept in 16-bit floats
+    group_size: int
+    note: str
+
+
+# "AWQ + GPTQ Quantization, in depth", Worked example: where the bytes go in a 1.5B
+# model: 28 layers, hidden size 1536, MLP width 8960, 12 query and 2 key-value heads of
+# dimension 128 (so q, k, v project 1536 -> 1536 + 256 + 256 = 2048 and o 1536 ->
+# 1536), vocabulary 151,936 with the head tied to the embedding and kept unquantised;
+# linear layers at group size 128.  Gate and up read the same input and run as one
+# 1536 -> 2 x 8960 layer.
+DECODE_1P5B = DecodeStep(
+    "1p5b", 28,
+    (("qkv", 1536, 2048), ("o", 1536, 1536), ("gate_up", 1536, 17920), ("down", 8960, 1536)),
+    (1536, 151936), 128,
+    "1.5B-class model, one decode token at batch one: 28 x (qkv, o, gate+up, down) W4A16 layers")
+
+
+def decode_step_configs(step: DecodeStep = DECODE_1P5B) -> list:
+    """One layer configuration per linear shape of the step (seeded like the others),
+    for parity checks of those shapes."""
+    return [custom_config(f"{step.name}_{name}", 300 + i, K=K, N=N, group_size=step.group_size)
+            for i, (name, K, N) in enumerate(step.linears)]
