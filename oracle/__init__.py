@@ -13,6 +13,11 @@ What it computes, in plain numpy float64 (slow and obviously correct):
                      ("LLM Quantization: A Deep Dive...", The Math of
                      Quantization; "LLM Quantization: INT8, GPTQ, and AWQ
                      Explained", What quantization actually does).
+* ``rtn_quantize_sym`` / ``sym_zeros``
+                     symmetric round-to-nearest group quantiser (absmax on the
+                     4-bit grid -7..7, stored code q + 8, implicit zero point 8;
+                     "INT8, GPTQ, and AWQ Explained", What quantization actually
+                     does; "AWQ + GPTQ Quantization, in depth", Running it).
 * ``awq_scales`` / ``awq_fold_weights`` / ``awq_fold_activations``
                      the AWQ per-input-channel scale s = mean|X|^alpha and its
                      fold W*diag(s), x*diag(1/s) ("AWQ + GPTQ Quantization, in
@@ -34,6 +39,7 @@ unpinned".
 """
 
 from .quant import (round_half_even, fp16_ceil, group_index, rtn_quantize,
+                    rtn_quantize_sym, sym_zeros,
                     awq_scales, awq_fold_weights, awq_fold_activations,
                     act_order_h, act_order)
 from .packing import (pack_codes, unpack_codes, pack_zeros, unpack_zeros,

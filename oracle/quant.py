@@ -104,6 +104,57 @@ def rtn_quantize(w, group_size: int, g_idx=None, in_scale=None):
     return codes, scales, zeros
 
 
+SYM_LEVELS = 7              # 2**(4-1) - 1: the symmetric grid is -7 .. 7
+SYM_ZERO = 8                # stored code of 0 (the implicit zero point)
+
+
+def rtn_quantize_sym(w, group_size: int, g_idx=None, in_scale=None):
+    """Symmetric 4-bit round-to-nearest group quantiser: the absmax scheme of "LLM
+    Quantization: INT8, GPTQ, and AWQ Explained", What quantization actually does
+    (one scale from the block's largest magnitude, round, clamp to the symmetric
+    range), on the 4-bit grid -7 .. 7; the GPTQ recipe of "AWQ + GPTQ Quantization, in
+    depth", Running it, uses the symmetric W4A16 scheme where the AWQ one is asymmetric.
+
+    Returns codes uint8 [N][K] (the signed value plus 8, so the implicit zero point
+    is 8) and scales binary16 [G][N].  Per (row n, group gamma):
+        a = max |w|
+        S = smallest binary16 >= a / 7                  (S = 1 if a = 0)
+        q = clamp(round(w / S), -7, 7),  code = q + 8
+    and w ~ (code - 8) * S.  Same group membership, AWQ factor and float64
+    arithmetic as rtn_quantize.
+    """
+    w = np.asarray(w)
+    assert w.dtype == np.float16 and w.ndim == 2
+    N, K = w.shape
+    assert K % group_size == 0
+    G = K // group_size
+    gid = group_index(K, group_size, g_idx)
+    W = w.astype(np.float64)
+    if in_scale is not None:
+        W = W * np.asarray(in_scale, dtype=np.float64)[None, :]
+
+    codes = np.empty((N, K), dtype=np.uint8)
+    scales = np.empty((G, N), dtype=np.float16)
+    for gamma in range(G):
+        cols = np.nonzero(gid == gamma)[0]
+        assert cols.size == group_size, "every group must have group_size members"
+        Wg = W[:, cols]
+        a = np.abs(Wg).max(axis=1)
+        flat = a == 0.0
+        S16 = fp16_ceil(np.where(flat, 1.0, a / SYM_LEVELS))
+        S16[flat] = np.float16(1.0)
+        S = S16.astype(np.float64)
+        q = np.clip(round_half_even(Wg / S[:, None]), -SYM_LEVELS, SYM_LEVELS)
+        codes[:, cols] = (q + SYM_ZERO).astype(np.uint8)
+        scales[gamma] = S16
+    return codes, scales
+
+
+def sym_zeros(G: int, N: int) -> np.ndarray:
+    """The implicit zero points of a symmetric layer, uint8 [G][N], all 8."""
+    return np.full((G, N), SYM_ZERO, dtype=np.uint8)
+
+
 # --- AWQ ------------------------------------------------------------------------
 
 def awq_scales(xcal, alpha: float = 0.5) -> np.ndarray:

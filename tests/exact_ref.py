@@ -103,3 +103,36 @@ def linear_exact(x: np.ndarray, codes, S, Z, group_size: int, g_idx=None):
                 acc += Fraction(float(x[m, k])) * (int(codes[n, k]) - int(Z[g, n])) * s
             y[m][n] = acc
     return y
+
+
+def quantize_group_exact_sym(ws):
+    """Exact symmetric RTN of one group (list of Fractions) -> (S, [code...]): S is
+    the smallest binary16 with 7 S >= max |w| (found by scan), each code the grid
+    index j in [1, 15] whose point (j - 8) S is nearest to w, ties to even j - 8."""
+    a = max([abs(w) for w in ws] + [Fraction(0)])
+    if a == 0:
+        return Fraction(1), [8] * len(ws)
+    S = fp16_ceil_exact(a / 7)
+    return S, [_nearest_int_in(1, 15, w / S + 8, parity_offset=8) for w in ws]
+
+
+def quantize_exact_sym(w: np.ndarray, group_size: int, g_idx=None, in_scale=None):
+    """Exact symmetric RTN of a small matrix: (codes uint8 [N][K], scales [G][N] as
+    Fractions)."""
+    N, K = w.shape
+    gid = (np.arange(K) // group_size) if g_idx is None else np.asarray(g_idx)
+    G = K // group_size
+    W = w.astype(np.float64)
+    if in_scale is not None:
+        W = W * np.asarray(in_scale, dtype=np.float64)[None, :]
+    codes = np.zeros((N, K), dtype=np.uint8)
+    S = [[None] * N for _ in range(G)]
+    for n in range(N):
+        for gam in range(G):
+            members = np.nonzero(gid == gam)[0]
+            s, qs = quantize_group_exact_sym([Fraction(float(W[n, k])) for k in members])
+            S[gam][n] = s
+            for k, q in zip(members, qs):
+                codes[n, k] = q
+    return codes, S
+

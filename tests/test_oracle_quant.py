@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import workloads as wl
-from exact_ref import fp16_ceil_exact, quantize_exact
+from exact_ref import fp16_ceil_exact, quantize_exact, quantize_exact_sym
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -144,6 +144,71 @@ def test_rtn_invariants_on_configs(name):
         neg = Wg.min(1) < 0
         qmin = codes[np.arange(len(rows)), members[np.argmin(Wg, axis=1)]]
         assert np.all(qmin[neg] == 0)
+
+
+# --- symmetric quantiser --------------------------------------------------------------
+
+def test_sym_worked_groups():
+    data = json.load(open(os.path.join(GOLDEN, "rtn_sym_worked_groups.json")))
+    for grp in data["groups"]:
+        if "w_bits" in grp:
+            w = np.array([int(b, 16) for b in grp["w_bits"]], dtype=np.uint16).view(np.float16)[None, :]
+        else:
+            w = np.array(grp["w"], dtype=np.float16)[None, :]
+        codes, S = oracle.rtn_quantize_sym(w, w.shape[1])
+        assert codes[0].tolist() == grp["codes"], grp["name"]
+        assert float(S[0, 0]) == grp["scale"], grp["name"]
+        assert hex(int(S.view(np.uint16)[0, 0])) == grp["scale_bits"], grp["name"]
+
+
+@pytest.mark.parametrize("g", [2, 4, 8])
+@pytest.mark.parametrize("use_gidx", [False, True])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_sym_rtn_matches_exact_search(g, use_gidx, seed):
+    g_idx = _gidx_random(8, g, seed) if use_gidx else None
+    w = _plant_special_groups(_tile(seed, 8, 8), g, g_idx)
+    c, S = oracle.rtn_quantize_sym(w, g, g_idx)
+    ce, Se = quantize_exact_sym(w, g, g_idx)
+    assert np.array_equal(c, ce)
+    assert all(Fraction(float(S[a, n])) == Se[a][n] for a in range(S.shape[0]) for n in range(S.shape[1]))
+
+
+def test_sym_rtn_with_awq_scale_matches_exact_search():
+    w = _tile(4, 8, 8, scale=0.05)
+    s = np.random.default_rng([9, 4]).uniform(0.3, 3.0, 8)
+    c, S = oracle.rtn_quantize_sym(w, 4, None, s)
+    ce, Se = quantize_exact_sym(w, 4, None, s)
+    assert np.array_equal(c, ce)
+    assert all(Fraction(float(S[a, n])) == Se[a][n] for a in range(2) for n in range(8))
+
+
+@pytest.mark.parametrize("name", ["c1", "c3", "c5"])
+def test_sym_rtn_invariants_on_configs(name):
+    cfg = wl.CONFIGS[name]
+    rows = np.linspace(0, cfg.N - 1, 24).astype(np.int64)
+    w = wl.weights(cfg, rows)
+    g = cfg.group_size
+    g_idx = oracle.act_order(wl.calibration(cfg), g)[0] if cfg.act_order else None
+    codes, S = oracle.rtn_quantize_sym(w, g, g_idx)
+    Z = oracle.sym_zeros(cfg.G, len(rows))
+    W = w.astype(np.float64)
+    gid = oracle.group_index(cfg.K, g, g_idx)
+    Sk = S.astype(np.float64)[gid, :].T
+    What = oracle.dequant(codes, S, Z, g, g_idx)
+    assert np.all(np.abs(W - What) <= Sk / 2)            # within half a step
+    assert codes.min() >= 1 and codes.max() <= 15        # the grid is -7 .. 7
+    for gam in range(cfg.G):
+        members = np.nonzero(gid == gam)[0]
+        a = np.abs(W[:, members]).max(1)
+        prev = np.nextafter(S[gam], np.float16(0)).astype(np.float64)
+        assert np.all(S[gam].astype(np.float64) * 7 >= a) and np.all(prev * 7 < a)
+        # the largest magnitude lands on an end of the grid
+        top = codes[np.arange(len(rows)), members[np.argmax(np.abs(W[:, members]), axis=1)]]
+        assert np.all((top == 1) | (top == 15))
+    # sign symmetry: -w has the same scales and the mirrored codes (round half even is odd)
+    c_neg, S_neg = oracle.rtn_quantize_sym(-w, g, g_idx)
+    assert np.array_equal(S_neg.view(np.uint16), S.view(np.uint16))
+    assert np.array_equal(c_neg.astype(int), 16 - codes.astype(int))
 
 
 # --- AWQ scale and fold -------------------------------------------------------------
