@@ -35,7 +35,8 @@
  *   x        binary16 [M][K], row-major                               (device)
  *   y        binary16 [M][N], row-major, written once per element     (device)
  *   scales   binary16 [G][N], row-major: scale of (group, output)     (device)
- *   qzeros   int32 [G][N/8]: zero point of (group, n) in bits 4j..4j+3 of word
+ *   qzeros   int32 [G][N/8] or NULL (symmetric: every zero point 8): zero point of
+ *            (group, n) in bits 4j..4j+3 of word
  *            [group][n/8], j = n % 8                                  (device)
  *   g_idx    int32 [K] or NULL: group of every input channel          (act order)
  *   qweight  int32 buffer of w4a16_qweight_words(N, K, act_order) words, written by
@@ -100,6 +101,21 @@ size_t w4a16_qweight_words(int N, int K, int act_order);
 int w4a16_quantize(const uint16_t* w, int N, int K, int group_size, const int32_t* g_idx,
                    const double* in_scale, uint8_t* codes, uint16_t* scales, uint8_t* zeros);
 
+/* Symmetric 4-bit round-to-nearest group quantiser: the absmax scheme ("LLM
+ * Quantization: INT8, GPTQ, and AWQ Explained", What quantization actually does: one
+ * scale from the block's largest magnitude, round, clamp to the symmetric range) on the
+ * grid -7 .. 7, as the symmetric W4A16 scheme of the GPTQ recipe ("AWQ + GPTQ
+ * Quantization, in depth", Running it).  Per (row n, group):
+ *   a = max |w|,  S = smallest binary16 >= a / 7   (S = 1 if a == 0)
+ *   q = clamp(round(w / S), -7, 7),  codes = q + 8
+ * so the zero point is 8 for every group and none is stored: pass qzeros = NULL to
+ * w4a16_gemm / w4a16_dequant.  round = half to even, arithmetic in binary64; g_idx and
+ * in_scale as for w4a16_quantize.
+ *   codes out uint8 [N][K] (1 .. 15);  scales out binary16 [G][N]
+ * Errors: INVALID_ARG, UNSUPPORTED, BAD_GIDX. */
+int w4a16_quantize_sym(const uint16_t* w, int N, int K, int group_size, const int32_t* g_idx,
+                       const double* in_scale, uint8_t* codes, uint16_t* scales);
+
 /* AWQ per-input-channel scale s[k] = (mean over the T calibration tokens of |X[t][k]|)
  * ** alpha ("AWQ + GPTQ Quantization, in depth", The two algorithms, compactly).  The
  * mean is formed exactly and rounded once; alpha == 0.5 uses the correctly rounded
@@ -147,7 +163,9 @@ int w4a16_unpack_zeros(const int32_t* qzeros, int G, int N, uint8_t* zeros);
  * ------------------------------------------------------------------------------ */
 
 /* y = x * W^T with W^ = (q - Z) * S, fp32 accumulation, y rounded once to binary16.
- * All pointers are device pointers.  g_idx non-NULL selects the act-order layout
+ * All pointers are device pointers.  qzeros NULL selects symmetric weights (every
+ * zero point 8, codes from w4a16_quantize_sym; no zero points stored or read).
+ * g_idx non-NULL selects the act-order layout
  * (qweight must have been packed with that g_idx; the kernels read the stored order
  * from qweight and gather x through it).  M == 1 runs the split-K GEMV (K <= 65536, at
  * most 512 groups per row and under 2 GB of codes, else the MFMA kernels; rows longer
@@ -169,7 +187,8 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
 
 /* Debug/parity view of the weights: w_out[n][k] = binary16((q - Z) * S) in the
  * original input-channel order, computed with the same device arithmetic that builds
- * the GEMM's weight operand.  Device pointers.  Errors as w4a16_gemm. */
+ * the GEMM's weight operand.  Device pointers; qzeros NULL = symmetric (Z = 8).
+ * Errors as w4a16_gemm. */
 int w4a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
                   const int32_t* g_idx, int group_size, int N, int K, uint16_t* w_out,
                   void* stream);

@@ -44,7 +44,11 @@ def product_layer(cfg: wl.LayerConfig, M: int, x=None):
         if cfg.awq:
             s = w4.w4a16_awq_scales(X)
     w = wl.weights(cfg)
-    codes, S, Z = w4.w4a16_quantize(w, g, g_idx, s)
+    if cfg.sym:
+        codes, S = w4.w4a16_quantize_sym(w, g, g_idx, s)
+        Z = None
+    else:
+        codes, S, Z = w4.w4a16_quantize(w, g, g_idx, s)
     if x is None:
         x = wl.activations(cfg, M)
         if s is not None:
@@ -54,7 +58,7 @@ def product_layer(cfg: wl.LayerConfig, M: int, x=None):
         "x": torch.from_numpy(np.ascontiguousarray(x)).to(dev),
         "qweight": torch.from_numpy(w4.w4a16_pack(codes, g_idx, g)).to(dev),
         "scales": torch.from_numpy(S).to(dev),
-        "qzeros": torch.from_numpy(w4.w4a16_pack_zeros(Z)).to(dev),
+        "qzeros": None if Z is None else torch.from_numpy(w4.w4a16_pack_zeros(Z)).to(dev),
         "g_idx": None if g_idx is None else torch.from_numpy(g_idx).to(dev),
     }
     return layer
@@ -71,7 +75,11 @@ def oracle_layer(cfg: wl.LayerConfig, M: int, rows, x=None):
         if cfg.awq:
             s = oracle.awq_scales(X)
     w = wl.weights(cfg, rows)
-    codes, S, Z = oracle.rtn_quantize(w, g, g_idx, s)
+    if cfg.sym:
+        codes, S = oracle.rtn_quantize_sym(w, g, g_idx, s)
+        Z = oracle.sym_zeros(S.shape[0], S.shape[1])
+    else:
+        codes, S, Z = oracle.rtn_quantize(w, g, g_idx, s)
     if x is None:
         x = wl.activations(cfg, M)
         if s is not None:

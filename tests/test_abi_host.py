@@ -26,7 +26,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = w4.lib()
     declared = _declared_functions()
-    assert len(declared) == 13
+    assert len(declared) == 14
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(w4.EXPORTS) == declared
@@ -78,6 +78,44 @@ def test_quantize_bit_exact_on_special_groups():
         w[4, 32:64] = np.abs(w[4, 32:64])
         for g in (32, 64, 128):
             _assert_same_quant(w4.w4a16_quantize(w, g), oracle.rtn_quantize(w, g))
+
+
+@pytest.mark.parametrize("name", ["c1", "c2up", "c3", "c5"])
+def test_quantize_sym_bit_exact_on_config_rows(name):
+    cfg = wl.CONFIGS[name]
+    rows = np.linspace(0, cfg.N - 1, 24).astype(np.int64)
+    w = wl.weights(cfg, rows)
+    g_idx = s = None
+    if cfg.act_order:
+        g_idx, _ = oracle.act_order(wl.calibration(cfg), cfg.group_size)
+    if cfg.awq:
+        s = oracle.awq_scales(wl.calibration(cfg))
+    c, S = w4.w4a16_quantize_sym(w, cfg.group_size, g_idx, s)
+    co, So = oracle.rtn_quantize_sym(w, cfg.group_size, g_idx, s)
+    assert np.array_equal(c, co) and np.array_equal(S.view(np.uint16), So.view(np.uint16))
+
+
+def test_quantize_sym_bit_exact_on_special_groups():
+    import json
+    data = json.load(open(os.path.join(ROOT, "tests", "golden", "rtn_sym_worked_groups.json")))
+    rng = np.random.default_rng(1)
+    for grp in data["groups"]:
+        if "w_bits" in grp:
+            w = np.array([int(b, 16) for b in grp["w_bits"]], dtype=np.uint16).view(np.float16)
+        else:
+            w = np.array(grp["w"], dtype=np.float16)
+        w = np.tile(w, (8, 32 // w.size + 1))[:, :32]
+        c, S = w4.w4a16_quantize_sym(w, 32)
+        co, So = oracle.rtn_quantize_sym(w, 32)
+        assert np.array_equal(c, co) and np.array_equal(S.view(np.uint16), So.view(np.uint16))
+    for scale in (1e-6, 1e-3, 1.0, 300.0):
+        w = (rng.standard_normal((16, 128)) * scale).astype(np.float16)
+        w[3, :32] = 0
+        w[4, 32:64] = -np.abs(w[4, 32:64])
+        for g in (32, 64, 128):
+            c, S = w4.w4a16_quantize_sym(w, g)
+            co, So = oracle.rtn_quantize_sym(w, g)
+            assert np.array_equal(c, co) and np.array_equal(S.view(np.uint16), So.view(np.uint16))
 
 
 def test_awq_scales_and_fold_bit_exact():

@@ -202,6 +202,49 @@ def test_device_errors_are_reported():
     assert st == w4.ERR_MISALIGNED
 
 
+# --- symmetric weights (qzeros = NULL, every zero point 8) -----------------------------
+
+SYM = [
+    # name, M, N, K, group, act_order: every kernel family and its variants
+    ("y1", 1, 264, 1536, 128, False),     # GEMV, one row per wavefront group
+    ("y2", 1, 136, 16384, 64, True),      # GEMV, rows split over two wavefronts, act order
+    ("y3", 4, 392, 2048, 128, False),     # skinny, subnormal path (group 128)
+    ("y4", 9, 136, 1024, 32, True),       # skinny, dequantised path, act order
+    ("y5", 5, 264, 12288, 128, False),    # skinny, K split over two workgroup slices
+    ("y6", 40, 264, 1024, 64, False),     # large-tile kernel, 64-row tiles
+    ("y7", 300, 520, 640, 128, True),     # large-tile kernel, 256-row tiles, act order
+    ("y8", 3, 72, 96, 32, False),         # tiled fallback kernel (K not a multiple of 128)
+]
+
+
+@pytest.mark.parametrize("case", range(len(SYM)))
+def test_symmetric_layers_match_oracle(case):
+    import torch
+    name, M, N, K, g, act = SYM[case]
+    cfg = wl.custom_config(name, 400 + case, K=K, N=N, group_size=g, M_list=(M,), act_order=act, sym=True)
+    note(f"symmetric {name} M={M} N={N} K={K} g={g} act={act}")
+    prod = product_layer(cfg, M)
+    assert prod["qzeros"] is None
+    ref = oracle_layer(cfg, M, np.arange(N))
+    assert np.array_equal(prod["codes"], ref["codes"])
+    paths = ["gemv", "gemm"] if M == 1 else ["gemm"]
+    for path in paths:
+        os.environ["W4A16_FORCE_PATH"] = path
+        note(f"  path={path}")
+        y = run_gemm(prod).cpu().numpy()
+        assert oracle.rel_err(y, ref["y_ref"]) <= TOL, path
+    os.environ.pop("W4A16_FORCE_PATH", None)
+    W16 = w4.w4a16_dequant(prod["qweight"], prod["scales"], None, prod["g_idx"], g, K).cpu().numpy()
+    assert np.array_equal(W16.view(np.uint16), ref["W16"].view(np.uint16))
+    # unit-vector probes select binary16((code - 8) * S) exactly
+    ks = np.unique(np.concatenate([[0, K - 1], np.random.default_rng(case).integers(0, K, 6)]))
+    E = torch.from_numpy(wl.unit_vectors(K, ks)).to(device())
+    os.environ["W4A16_FORCE_PATH"] = "gemm"
+    ye = run_gemm(prod, x=E).cpu().numpy()
+    os.environ.pop("W4A16_FORCE_PATH")
+    assert np.array_equal(ye.view(np.uint16), ref["W16"][:, ks].T.copy().view(np.uint16))
+
+
 # --- the configurations at full size (sampled outputs) -------------------------------
 
 FULL = [("c1", 1), ("c2up", 1), ("c2down", 1), ("c3", 1), ("c3", 2), ("c3", 4), ("c3", 8), ("c3", 16),

@@ -27,6 +27,8 @@ _SIGNATURES = {
     "w4a16_qweight_words": (ctypes.c_size_t, [_c_int, _c_int, _c_int]),
     "w4a16_quantize": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
                                 _c_void_p, _c_void_p, _c_void_p]),
+    "w4a16_quantize_sym": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
+                                    _c_void_p, _c_void_p]),
     "w4a16_awq_scales": (_c_int, [_c_void_p, _c_int, _c_int, ctypes.c_double, _c_void_p]),
     "w4a16_awq_fold_activations": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p, _c_void_p]),
     "w4a16_act_order": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p]),
@@ -107,6 +109,20 @@ def w4a16_quantize(w, group_size: int, g_idx=None, in_scale=None):
     _check(lib().w4a16_quantize(_ptr(w), N, K, group_size, _ptr(gi), _ptr(sc), _ptr(codes),
                                 _ptr(scales), _ptr(zeros)))
     return codes, scales, zeros
+
+
+def w4a16_quantize_sym(w, group_size: int, g_idx=None, in_scale=None):
+    """Symmetric: binary16 w [N][K] -> (codes uint8 [N][K] in 1..15, scales binary16
+    [G][N]); the zero point is 8 everywhere (pass qzeros=None to the device calls)."""
+    w = _np(w, np.float16, 2)
+    N, K = w.shape
+    G = K // group_size if group_size else 0
+    gi = None if g_idx is None else _np(g_idx, np.int32, 1)
+    sc = None if in_scale is None else _np(in_scale, np.float64, 1)
+    codes = np.empty((N, K), np.uint8)
+    scales = np.empty((max(G, 1), N), np.float16)
+    _check(lib().w4a16_quantize_sym(_ptr(w), N, K, group_size, _ptr(gi), _ptr(sc), _ptr(codes), _ptr(scales)))
+    return codes, scales
 
 
 def w4a16_awq_scales(xcal, alpha: float = 0.5) -> np.ndarray:
@@ -193,7 +209,8 @@ def w4a16_gemm(x, qweight, scales, qzeros, g_idx, group_size: int, y=None, strea
     _dev(x, torch.float16, "x")
     _dev(qweight, torch.int32, "qweight")
     _dev(scales, torch.float16, "scales")
-    _dev(qzeros, torch.int32, "qzeros")
+    if qzeros is not None:                      # None: symmetric weights
+        _dev(qzeros, torch.int32, "qzeros")
     if g_idx is not None:
         _dev(g_idx, torch.int32, "g_idx")
     M, K = x.shape
@@ -205,7 +222,8 @@ def w4a16_gemm(x, qweight, scales, qzeros, g_idx, group_size: int, y=None, strea
     _dev(y, torch.float16, "y")
     if tuple(y.shape) != (M, N):
         raise ValueError(f"y shape {tuple(y.shape)} != {(M, N)}")
-    _check(lib().w4a16_gemm(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(),
+    _check(lib().w4a16_gemm(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(),
+                            None if qzeros is None else qzeros.data_ptr(),
                             None if g_idx is None else g_idx.data_ptr(), group_size, M, N, K,
                             y.data_ptr(), _stream_handle(stream, x.device)))
     return y
@@ -216,14 +234,15 @@ def w4a16_dequant(qweight, scales, qzeros, g_idx, group_size: int, K: int, out=N
     import torch
     _dev(qweight, torch.int32, "qweight")
     _dev(scales, torch.float16, "scales")
-    _dev(qzeros, torch.int32, "qzeros")
+    if qzeros is not None:                      # None: symmetric weights
+        _dev(qzeros, torch.int32, "qzeros")
     if g_idx is not None:
         _dev(g_idx, torch.int32, "g_idx")
     G, N = scales.shape
     if out is None:
         out = torch.empty((N, K), dtype=torch.float16, device=qweight.device)
     _dev(out, torch.float16, "out")
-    _check(lib().w4a16_dequant(qweight.data_ptr(), scales.data_ptr(), qzeros.data_ptr(),
+    _check(lib().w4a16_dequant(qweight.data_ptr(), scales.data_ptr(), None if qzeros is None else qzeros.data_ptr(),
                                None if g_idx is None else g_idx.data_ptr(), group_size, N, K,
                                out.data_ptr(), _stream_handle(stream, qweight.device)))
     return out

@@ -34,6 +34,14 @@ int hip_status(hipError_t e, const char* what) {
 
 int check_launch(const char* what) { return hip_status(hipGetLastError(), what); }
 
+// Zero points as the kernels take them: NULL qzeros = symmetric (Z = 8 everywhere); the
+// kernels' zero-point loads then read the scales ([G][N] binary16, G N / 2 bytes of
+// words needed) and ignore what they read.
+Zeros layer_zeros(const int32_t* qzeros, const uint16_t* scales) {
+  if (qzeros) return Zeros{reinterpret_cast<const uint32_t*>(qzeros), 0};
+  return Zeros{reinterpret_cast<const uint32_t*>(scales), 1};
+}
+
 // Same validation for every device entry point.
 int check_device_args(const void* const* ptrs, int nptrs, int N, int K, int group_size) {
   for (int i = 0; i < nptrs; ++i)
@@ -112,7 +120,7 @@ constexpr int gemv_depth(int cpl) { return cpl >= 3 ? 2 : 8 / cpl; }
 
 template <int LPR, int CPL, bool EXACT, bool ACT, int EPT, int WPR>
 void launch_gemv_e(dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
-                   const uint16_t* s, const uint32_t* z, half_t* y, int N, int K, int gshift, int steps) {
+                   const uint16_t* s, Zeros z, half_t* y, int N, int K, int gshift, int steps) {
   auto kern = gemv_m1_kernel<LPR, CPL, kGemvWaves, gemv_depth(CPL), EXACT, ACT, EPT, WPR>;
   // Dynamic LDS above 64 KB has to be allowed per kernel (once per process).
   static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -127,7 +135,7 @@ void launch_gemv_e(dim3 grid, size_t shmem, hipStream_t st, const half_t* x, con
 // whole 8-row items.
 template <int LPR, int CPL, bool EXACT, bool ACT>
 void launch_gemv_t(int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
-                   const uint16_t* s, const uint32_t* z, half_t* y, int N, int K, int gshift, int steps) {
+                   const uint16_t* s, Zeros z, half_t* y, int N, int K, int gshift, int steps) {
   if constexpr (EXACT && !ACT)
     if (ept == 1) return launch_gemv_e<LPR, CPL, EXACT, ACT, 1, 1>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
   launch_gemv_e<LPR, CPL, EXACT, ACT, 8, 1>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
@@ -135,7 +143,7 @@ void launch_gemv_t(int ept, dim3 grid, size_t shmem, hipStream_t st, const half_
 
 template <int LPR, bool EXACT, bool ACT>
 void launch_gemv_cpl(int cpl, int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
-                     const uint16_t* s, const uint32_t* z, half_t* y, int N, int K, int gshift, int steps) {
+                     const uint16_t* s, Zeros z, half_t* y, int N, int K, int gshift, int steps) {
   switch (cpl) {
     case 1: launch_gemv_t<LPR, 1, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
     case 2: launch_gemv_t<LPR, 2, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
@@ -148,14 +156,14 @@ void launch_gemv_cpl(int cpl, int ept, dim3 grid, size_t shmem, hipStream_t st, 
 // staging items (a row has more than 64 groups).
 template <int WPR, bool EXACT, bool ACT>
 void launch_gemv_split(int cpl, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
-                       const uint16_t* s, const uint32_t* z, half_t* y, int N, int K, int gshift, int steps) {
+                       const uint16_t* s, Zeros z, half_t* y, int N, int K, int gshift, int steps) {
   if (cpl == 3) launch_gemv_e<64, 3, EXACT, ACT, 8, WPR>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
   else launch_gemv_e<64, 4, EXACT, ACT, 8, WPR>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
 }
 
 template <bool EXACT, bool ACT>
 void launch_gemv_lpr(const GemvShape& sh, int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x,
-                     const uint32_t* qw, const uint16_t* s, const uint32_t* z, half_t* y, int N, int K,
+                     const uint32_t* qw, const uint16_t* s, Zeros z, half_t* y, int N, int K,
                      int gshift, int steps) {
   if (sh.wpr > 1) {
     switch (sh.wpr) {
@@ -193,6 +201,11 @@ GemvPlan plan_gemv(int N, int K, int gshift, bool act) {
   GemvPlan p;
   p.sh = pick_gemv_shape(K);
   if (p.sh.lpr == 0) return p;
+  // measurements only: lanes per row forced (rows of at most 256 chunks)
+  const int lpr = env_int("W4A16_TUNE_GEMV_LPR", 0);
+  const int C = K / 32;
+  if (p.sh.wpr == 1 && (lpr == 8 || lpr == 16 || lpr == 32 || lpr == 64) && (C + lpr - 1) / lpr <= 4)
+    p.sh = {lpr, (C + lpr - 1) / lpr, C % lpr == 0, 1};
   if (static_cast<long long>(N) * K / 2 >= (1LL << 31)) return p;   // 32-bit byte offsets into the codes
   const int G = K >> gshift;
   const int unit = kGemvWaves * (64 / p.sh.lpr);                    // rows per unit
@@ -213,7 +226,7 @@ GemvPlan plan_gemv(int N, int K, int gshift, bool act) {
 }
 
 int run_gemv(const GemvPlan& p, bool act, const half_t* x, const uint32_t* qw, const uint16_t* s,
-             const uint32_t* z, half_t* y, int N, int K, int gshift, hipStream_t st) {
+             Zeros z, half_t* y, int N, int K, int gshift, hipStream_t st) {
   const dim3 grid(p.blocks);
   if (p.sh.exact) {
     if (act) launch_gemv_lpr<true, true>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
@@ -228,7 +241,7 @@ int run_gemv(const GemvPlan& p, bool act, const half_t* x, const uint32_t* qw, c
 // --- GEMM (M > 1) ---------------------------------------------------------------
 
 template <int BM>
-void launch_gemm_bm(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z,
+void launch_gemm_bm(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, Zeros z,
                     half_t* y, int M, int N, int K, int gshift) {
   const dim3 grid((N + 255) / 256, (M + BM - 1) / BM);
   hipLaunchKernelGGL((gemm_mfma_kernel<BM>), grid, dim3(256), 0, st, x, qw, s, z, y, M, N, K, gshift);
@@ -273,7 +286,7 @@ SkinnyShape pick_skinny_shape(int M, int K, int gshift) {
 // ks > 1: partial sums to part [ks][M][N] fp32, then sum_slices_kernel into y.
 template <int T, int SE, bool ACT, bool SUB>
 int launch_skinny_t(const SkinnyShape& sh, hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s,
-                    const uint32_t* z, half_t* y, float* part, int M, int N, int K, int gshift) {
+                    Zeros z, half_t* y, float* part, int M, int N, int K, int gshift) {
   static const hipError_t lds_ok =
       hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_skinny_kernel<T, SE, ACT, SUB>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
@@ -294,7 +307,7 @@ int launch_skinny_t(const SkinnyShape& sh, hipStream_t st, const half_t* x, cons
 
 template <bool ACT>
 int launch_skinny(const SkinnyShape& sh, hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s,
-                  const uint32_t* z, half_t* y, float* part, int M, int N, int K, int gshift) {
+                  Zeros z, half_t* y, float* part, int M, int N, int K, int gshift) {
 #define W4A16_SKINNY(T_, SE_)                                                                              \
   if (sh.t == T_ && sh.se == SE_)                                                                        \
     return gshift == 7 ? launch_skinny_t<T_, SE_, ACT, true>(sh, st, x, qw, s, z, y, part, M, N, K, gshift) \
@@ -313,7 +326,7 @@ int launch_skinny(const SkinnyShape& sh, hipStream_t st, const half_t* x, const 
 // narrower tiles (64 NB2 wide) the rest, so that neither round leaves compute units
 // idle; (b) when they would not fill one round: then narrower tiles for all columns.
 template <int NB2, int MB>
-int launch_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z, half_t* y,
+int launch_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, Zeros z, half_t* y,
                int M, int N, int K, int gshift, int split, int n_split, int grid) {
   static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_big_kernel<NB2, MB>),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -325,7 +338,7 @@ int launch_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t
 }
 
 template <int MB>
-int run_gemm_big_t(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z,
+int run_gemm_big_t(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, Zeros z,
                    half_t* y, int M, int N, int K, int gshift) {
   constexpr int BM = 32 * MB;
   const int tiles_m = (M + BM - 1) / BM;
@@ -375,7 +388,7 @@ long long big_work_per_cu(int MB, int M, int N, int cus) {
   return static_cast<long long>((full + cus - 1) / cus) * BM * 256;
 }
 
-int run_gemm_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z, half_t* y,
+int run_gemm_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, Zeros z, half_t* y,
                  int M, int N, int K, int gshift) {
   // Above 128 rows: 128-row tiles when their smaller tiles fill the device enough better
   // to make up for doing ~1.28x the work per output (twice the dequantisation per MFMA;
@@ -392,7 +405,7 @@ int run_gemm_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half
   return run_gemm_big_t<8>(st, x, qw, s, z, y, M, N, K, gshift);
 }
 
-int run_gemm(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, const uint32_t* z,
+int run_gemm(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, Zeros z,
              half_t* y, int M, int N, int K, int gshift) {
   if (M >= env_int("W4A16_TUNE_GEMM_BIG_MIN_M", kBigMinM) && K % kBigBK == 0 &&
       static_cast<long long>(M) * K < (1LL << 31) &&
@@ -430,8 +443,8 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
                const int32_t* g_idx, int group_size, int M, int N, int K, uint16_t* y, void* stream) {
   clear_error();
   if (M <= 0) return fail(W4A16_ERR_INVALID_ARG, "M must be positive (M=%d)", M);
-  const void* ptrs[] = {x, qweight, scales, qzeros, y};
-  if (int st = check_device_args(ptrs, 5, N, K, group_size)) return st;
+  const void* ptrs[] = {x, qweight, scales, y, qzeros};   // qzeros may be NULL: symmetric
+  if (int st = check_device_args(ptrs, qzeros ? 5 : 4, N, K, group_size)) return st;
   const bool act = g_idx != nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (act)
@@ -441,7 +454,7 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
   const auto* hx = reinterpret_cast<const half_t*>(x);
   const auto* hq = reinterpret_cast<const uint32_t*>(qweight);
   const auto* hs = reinterpret_cast<const half_t*>(scales);
-  const auto* hz = reinterpret_cast<const uint32_t*>(qzeros);
+  const Zeros hz = layer_zeros(qzeros, scales);
   auto* hy = reinterpret_cast<half_t*>(y);
 
   const Path forced = forced_path();
@@ -503,8 +516,8 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
 int w4a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros, const int32_t* g_idx,
                   int group_size, int N, int K, uint16_t* w_out, void* stream) {
   clear_error();
-  const void* ptrs[] = {qweight, scales, qzeros, w_out};
-  if (int st = check_device_args(ptrs, 4, N, K, group_size)) return st;
+  const void* ptrs[] = {qweight, scales, w_out, qzeros};   // qzeros may be NULL: symmetric
+  if (int st = check_device_args(ptrs, qzeros ? 4 : 3, N, K, group_size)) return st;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool act = g_idx != nullptr;
   if (act)
@@ -513,7 +526,7 @@ int w4a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t*
   const dim3 grid(static_cast<unsigned>((words + 255) / 256));
   const auto* hq = reinterpret_cast<const uint32_t*>(qweight);
   const auto* hs = reinterpret_cast<const half_t*>(scales);
-  const auto* hz = reinterpret_cast<const uint32_t*>(qzeros);
+  const Zeros hz = layer_zeros(qzeros, scales);
   auto* hw = reinterpret_cast<half_t*>(w_out);
   const int gshift = log2_group(group_size);
   if (act)

@@ -17,6 +17,8 @@ namespace {
 thread_local std::string t_last_error;
 
 constexpr int kLevels = 15;  // 16 grid points, "4 bits ... 16 levels"
+constexpr int kSymLevels = 7;    // symmetric grid -7 .. 7
+constexpr uint8_t kSymZero = 8;  // stored code of 0: the implicit zero point
 
 // Exact binary16 -> binary64.
 double half_to_double(uint16_t h) {
@@ -267,6 +269,52 @@ int w4a16_quantize(const uint16_t* w, int N, int K, int group_size, const int32_
       for (int i = 0; i < group_size; ++i) {
         const double q = std::nearbyint(row[members[i]] / S) + Z;
         qrow[members[i]] = static_cast<uint8_t>(std::min(std::max(q, 0.0), static_cast<double>(kLevels)));
+      }
+    }
+  }
+  return W4A16_OK;
+}
+
+int w4a16_quantize_sym(const uint16_t* w, int N, int K, int group_size, const int32_t* g_idx,
+                       const double* in_scale, uint8_t* codes, uint16_t* scales) {
+  clear_error();
+  if (!w || !codes || !scales) return fail(W4A16_ERR_INVALID_ARG, "NULL buffer");
+  if (int st = check_shape(N, K, group_size)) return st;
+  std::vector<int32_t> order;
+  if (int st = group_members(g_idx, K, group_size, order)) return st;
+  if (in_scale)
+    for (int k = 0; k < K; ++k)
+      if (!(in_scale[k] > 0.0) || !std::isfinite(in_scale[k]))
+        return fail(W4A16_ERR_INVALID_ARG, "in_scale[%d] is not a positive finite number", k);
+  const size_t nk = static_cast<size_t>(N) * K;
+  for (size_t i = 0; i < nk; ++i)
+    if (!half_is_finite(w[i])) return fail(W4A16_ERR_INVALID_ARG, "weight %zu is not finite", i);
+
+  const int G = K / group_size;
+  std::vector<double> row(K);
+  for (int n = 0; n < N; ++n) {
+    for (int k = 0; k < K; ++k) {
+      const double v = half_to_double(w[static_cast<size_t>(n) * K + k]);
+      row[k] = in_scale ? v * in_scale[k] : v;
+    }
+    for (int g = 0; g < G; ++g) {
+      const int32_t* members = order.data() + static_cast<size_t>(g) * group_size;
+      double a = 0.0;
+      for (int i = 0; i < group_size; ++i) a = std::max(a, std::fabs(row[members[i]]));
+      uint8_t* qrow = codes + static_cast<size_t>(n) * K;
+      const size_t gi = static_cast<size_t>(g) * N + n;
+      if (a == 0.0) {  // all-zero group: S = 1, every code 8
+        scales[gi] = 0x3C00;
+        for (int i = 0; i < group_size; ++i) qrow[members[i]] = kSymZero;
+        continue;
+      }
+      const uint16_t sbits = half_ceil(a / kSymLevels);
+      const double S = half_to_double(sbits);
+      scales[gi] = sbits;
+      for (int i = 0; i < group_size; ++i) {
+        const double q = std::min(std::max(std::nearbyint(row[members[i]] / S), -static_cast<double>(kSymLevels)),
+                                  static_cast<double>(kSymLevels));
+        qrow[members[i]] = static_cast<uint8_t>(q + kSymZero);
       }
     }
   }

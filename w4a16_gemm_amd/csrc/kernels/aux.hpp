@@ -12,7 +12,7 @@ namespace w4a16 {
 template <bool ACT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict__ qw,
                                                      const half_t* __restrict__ scales,
-                                                     const uint32_t* __restrict__ qzeros,
+                                                     Zeros qzeros,
                                                      half_t* __restrict__ w_out, int N, int K,
                                                      int gshift) {
   const int W = K >> 3;

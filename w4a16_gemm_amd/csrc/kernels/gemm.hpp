@@ -27,7 +27,7 @@ namespace w4a16 {
 template <int BM>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const half_t* __restrict__ scales,
-    const uint32_t* __restrict__ qzeros, half_t* __restrict__ y, int M, int N, int K, int gshift) {
+    Zeros qzeros, half_t* __restrict__ y, int M, int N, int K, int gshift) {
   static_assert(BM % 16 == 0 && BM >= 16, "BM must be a multiple of 16");
   constexpr int MB = BM / 16;                     // 16-row blocks per wavefront
   constexpr int ACH = BM * 16;                    // 16-byte activation chunks per K tile
@@ -337,7 +337,7 @@ constexpr size_t kBigLds = static_cast<size_t>(kBigStages) * kBigStage;
 
 template <int NB, int MB>
 __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uint32_t* __restrict__ qw,
-                                         const half_t* __restrict__ scales, const uint32_t* __restrict__ qzeros,
+                                         const half_t* __restrict__ scales, Zeros qzeros,
                                          half_t* __restrict__ y, int M, int N, int K, int gshift, int m0, int n0,
                                          int n_end) {
   // NB 16-column blocks and MB 16-row blocks per wavefront: the tile is BM x BN with
@@ -395,7 +395,7 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
           reinterpret_cast<void*>(stage + kBigLdsA + kBigLdsB), 16, 0, 0);
     else if (wave == 1)
       __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(qzeros + static_cast<size_t>(gi) * (N >> 3) + z_word),
+          reinterpret_cast<const void*>(qzeros.words + static_cast<size_t>(gi) * (N >> 3) + z_word),
           reinterpret_cast<void*>(stage + kBigLdsA + kBigLdsB + kBigLdsS), 4, 0, 0);
     const half_t* xt = x + tc * BK;
 #pragma unroll
@@ -454,7 +454,8 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
     DequantConsts dc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      dc[nb] = make_consts((zw[nb] >> z_shift) & 0xFu, __builtin_bit_cast(half_t, static_cast<uint16_t>(sc[nb])));
+      dc[nb] = make_consts((qzeros.word(zw[nb]) >> z_shift) & 0xFu,
+                           __builtin_bit_cast(half_t, static_cast<uint16_t>(sc[nb])));
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (s == 1) {
@@ -505,7 +506,7 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
 template <int NB2, int MB>
 __global__ __launch_bounds__(512) void gemm_big_kernel(const half_t* __restrict__ x, const uint32_t* __restrict__ qw,
                                                        const half_t* __restrict__ scales,
-                                                       const uint32_t* __restrict__ qzeros, half_t* __restrict__ y,
+                                                       Zeros qzeros, half_t* __restrict__ y,
                                                        int M, int N, int K, int gshift, int split, int n_split) {
   constexpr int BM = 32 * MB;
   const int tiles_m = (M + BM - 1) / BM;

@@ -85,7 +85,7 @@ __device__ __forceinline__ float lane_group_sum(float v) {
 template <int LPR, int CPL, int WAVES, int DEPTH, bool EXACT, bool ACT, int EPT, int WPR>
 __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
     const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
-    const uint32_t* __restrict__ qzeros, half_t* __restrict__ y, int N, int K, int gshift, int steps) {
+    Zeros qzeros, half_t* __restrict__ y, int N, int K, int gshift, int steps) {
   static_assert(64 % LPR == 0, "lanes per row must divide the wavefront");
   static_assert(DEPTH % 2 == 0, "the ring slot of row t is t % 2, the unrolled slot index");
   static_assert(WPR == 1 || (LPR == 64 && WAVES % WPR == 0 && WPR % DEPTH == 0),
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
       zs_s[set] = *reinterpret_cast<const uint4*>(scales + static_cast<size_t>(it_g) * N + n8);
     else
       zs_s[set] = scales[static_cast<size_t>(it_g) * N + n8 + st_r0];
-    zs_z[set] = qzeros[static_cast<size_t>(it_g) * (N >> 3) + (n8 >> 3)];
+    zs_z[set] = qzeros.words[static_cast<size_t>(it_g) * (N >> 3) + (n8 >> 3)];
   };
   auto put_item = [&](int set, int slot) {
     if (tid < tasks) {
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
           bits = zs_s[set];
         }
         const float S = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(bits)));
-        const float Z = static_cast<float>((zs_z[set] >> (4 * (st_r0 + r))) & 0xFu);
+        const float Z = static_cast<float>((qzeros.word(zs_z[set]) >> (4 * (st_r0 + r))) & 0xFu);
         dst[r * GP] = make_float2(S * 16777216.0f, -Z * S);   // both exact in fp32
       }
     }

@@ -143,9 +143,24 @@ __device__ __forceinline__ int xcd_block(int bid, int nblk) {
   return (bid % 8) * (nblk / 8) + bid / 8;
 }
 
-// Zero point of (group gi, output n) from the packed zero points [G][N/8].
-__device__ __forceinline__ uint32_t load_zero(const uint32_t* __restrict__ qzeros, int gi, int N, int n) {
-  return (qzeros[static_cast<size_t>(gi) * (N >> 3) + (n >> 3)] >> ((n & 7) * 4)) & 0xFu;
+// Zero points of a layer.  Asymmetric: packed words [G][N/8], Z of (group g, output n)
+// in bits 4 (n % 8) .. +3 of word [g][n / 8].  Symmetric (sym != 0): every Z is 8
+// (the signed code q - 8 in [-7, 7] times S, "LLM Quantization: INT8, GPTQ, and AWQ
+// Explained", What quantization actually does: absmax), nothing is stored, and `words`
+// points at any readable buffer of at least G N / 2 bytes so that the kernels' loads
+// keep their shape; the loaded words are replaced by kSymZeroWord.
+constexpr uint32_t kSymZeroWord = 0x88888888u;
+
+struct Zeros {
+  const uint32_t* words;
+  int sym;
+  __device__ __forceinline__ uint32_t word(uint32_t loaded) const { return sym ? kSymZeroWord : loaded; }
+};
+
+// Zero point of (group gi, output n).
+__device__ __forceinline__ uint32_t load_zero(Zeros z, int gi, int N, int n) {
+  if (z.sym) return 8u;
+  return (z.words[static_cast<size_t>(gi) * (N >> 3) + (n >> 3)] >> ((n & 7) * 4)) & 0xFu;
 }
 
 }  // namespace w4a16

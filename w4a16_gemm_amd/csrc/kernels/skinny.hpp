@@ -72,7 +72,7 @@ constexpr size_t skinny_lds_bytes(int waves, int groups) {
 template <int T, int SE, bool ACT, bool SUB>
 __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
     const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const half_t* __restrict__ scales,
-    const uint32_t* __restrict__ qzeros, half_t* __restrict__ y, float* __restrict__ part, int M, int N, int K,
+    Zeros qzeros, half_t* __restrict__ y, float* __restrict__ part, int M, int N, int K,
     int gshift, int ks) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
       const int gi = g0 + (e >> 4);
       const int n = min(16 * b + (e & 15), N - 1);
       sv[u] = scales[static_cast<size_t>(gi) * N + n];
-      zv[u] = qzeros[static_cast<size_t>(gi) * (N >> 3) + (n >> 3)];
+      zv[u] = qzeros.words[static_cast<size_t>(gi) * (N >> 3) + (n >> 3)];
     }
   };
   auto write_slab = [&](int b, int buf) {
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
       const int e = tid + u * nthreads;
       if (e < slab_n) {
         const int n = min(16 * b + (e & 15), N - 1);
-        const uint32_t z = (zv[u] >> ((n & 7) * 4)) & 0xFu;
+        const uint32_t z = (qzeros.word(zv[u]) >> ((n & 7) * 4)) & 0xFu;
         if constexpr (SUB) {
           const float S = static_cast<float>(sv[u]);
           slab[buf * slab_n + e] = __builtin_bit_cast(uint2, make_float2(S * 16777216.0f, -static_cast<float>(z) * S));

@@ -51,6 +51,7 @@ class LayerConfig:
     awq: bool = False           # calibration-derived per-input-channel scale folded in
     act_order: bool = False     # calibration-derived input-channel ordering (g_idx)
     note: str = ""
+    sym: bool = False           # symmetric quantisation (no zero points)
 
     @property
     def n_outliers(self) -> int:
@@ -85,12 +86,13 @@ CONFIGS = {
 
 def custom_config(name: str, cfg_id: int, K: int, N: int, group_size: int, *,
                   w_std: float = 0.02, outlier_frac: float = 0.005,
-                  outlier_mult: float = 20.0, M_list=(1,), awq=False, act_order=False) -> LayerConfig:
+                  outlier_mult: float = 20.0, M_list=(1,), awq=False, act_order=False,
+                  sym=False) -> LayerConfig:
     """A layer of arbitrary shape with the same distributions (used for small
     parity cases that span several tiles and a ragged tail)."""
     return LayerConfig(name, cfg_id, K=K, N=N, group_size=group_size, w_std=w_std,
                        outlier_frac=outlier_frac, outlier_mult=outlier_mult,
-                       M_list=tuple(M_list), awq=awq, act_order=act_order)
+                       M_list=tuple(M_list), awq=awq, act_order=act_order, sym=sym)
 
 
 def _rng(cfg: LayerConfig, stream: int, *sub: int) -> np.random.Generator:
