@@ -248,7 +248,7 @@ def test_symmetric_layers_match_oracle(case):
 # --- the configurations at full size (sampled outputs) -------------------------------
 
 FULL = [("c1", 1), ("c2up", 1), ("c2down", 1), ("c3", 1), ("c3", 2), ("c3", 4), ("c3", 8), ("c3", 16),
-        ("c4", 2048), ("c5", 1), ("c5", 512)]
+        ("c3s", 1), ("c3s", 16), ("c4", 2048), ("c5", 1), ("c5", 512)]
 
 
 @pytest.fixture(scope="module")
@@ -257,7 +257,7 @@ def full_layers():
 
     def get(name):
         if name not in cache:
-            cfg = wl.CONFIGS[name]
+            cfg = wl.config(name)
             note(f"building {name} (N={cfg.N} K={cfg.K})")
             cache.clear()
             cache[name] = product_layer(cfg, max(cfg.M_list))
@@ -268,7 +268,7 @@ def full_layers():
 @pytest.mark.parametrize("name,M", FULL)
 def test_configs_match_oracle_on_sampled_outputs(full_layers, name, M):
     import torch
-    cfg = wl.CONFIGS[name]
+    cfg = wl.config(name)
     prod = full_layers(name)
     rows = np.arange(cfg.N) if cfg.N <= 1024 else sample_rows(cfg.N, 96)
     ref = oracle_layer(cfg, M, rows)

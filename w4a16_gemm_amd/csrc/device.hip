@@ -35,8 +35,7 @@ int hip_status(hipError_t e, const char* what) {
 int check_launch(const char* what) { return hip_status(hipGetLastError(), what); }
 
 // Zero points as the kernels take them: NULL qzeros = symmetric (Z = 8 everywhere); the
-// kernels' zero-point loads then read the scales ([G][N] binary16, G N / 2 bytes of
-// words needed) and ignore what they read.
+// kernels' zero-point loads then all read the first word of the scales and ignore it.
 Zeros layer_zeros(const int32_t* qzeros, const uint16_t* scales) {
   if (qzeros) return Zeros{reinterpret_cast<const uint32_t*>(qzeros), 0};
   return Zeros{reinterpret_cast<const uint32_t*>(scales), 1};

@@ -395,7 +395,7 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
           reinterpret_cast<void*>(stage + kBigLdsA + kBigLdsB), 16, 0, 0);
     else if (wave == 1)
       __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(qzeros.words + static_cast<size_t>(gi) * (N >> 3) + z_word),
+          reinterpret_cast<const void*>(qzeros.at(static_cast<size_t>(gi) * (N >> 3) + z_word)),
           reinterpret_cast<void*>(stage + kBigLdsA + kBigLdsB + kBigLdsS), 4, 0, 0);
     const half_t* xt = x + tc * BK;
 #pragma unroll

@@ -151,7 +151,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
       zs_s[set] = *reinterpret_cast<const uint4*>(scales + static_cast<size_t>(it_g) * N + n8);
     else
       zs_s[set] = scales[static_cast<size_t>(it_g) * N + n8 + st_r0];
-    zs_z[set] = qzeros.words[static_cast<size_t>(it_g) * (N >> 3) + (n8 >> 3)];
+    zs_z[set] = *qzeros.at(static_cast<size_t>(it_g) * (N >> 3) + (n8 >> 3));
   };
   auto put_item = [&](int set, int slot) {
     if (tid < tasks) {

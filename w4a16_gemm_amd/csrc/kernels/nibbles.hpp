@@ -146,14 +146,16 @@ __device__ __forceinline__ int xcd_block(int bid, int nblk) {
 // Zero points of a layer.  Asymmetric: packed words [G][N/8], Z of (group g, output n)
 // in bits 4 (n % 8) .. +3 of word [g][n / 8].  Symmetric (sym != 0): every Z is 8
 // (the signed code q - 8 in [-7, 7] times S, "LLM Quantization: INT8, GPTQ, and AWQ
-// Explained", What quantization actually does: absmax), nothing is stored, and `words`
-// points at any readable buffer of at least G N / 2 bytes so that the kernels' loads
-// keep their shape; the loaded words are replaced by kSymZeroWord.
+// Explained", What quantization actually does: absmax) and nothing is stored; `words`
+// then points at any readable word, every zero-point load of the kernels reads that one
+// word (so the loads keep their place in the wait counts but stay in the cache), and
+// the loaded words are replaced by kSymZeroWord.
 constexpr uint32_t kSymZeroWord = 0x88888888u;
 
 struct Zeros {
   const uint32_t* words;
   int sym;
+  __device__ __forceinline__ const uint32_t* at(size_t idx) const { return words + (sym ? 0 : idx); }
   __device__ __forceinline__ uint32_t word(uint32_t loaded) const { return sym ? kSymZeroWord : loaded; }
 };
 

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
       const int gi = g0 + (e >> 4);
       const int n = min(16 * b + (e & 15), N - 1);
       sv[u] = scales[static_cast<size_t>(gi) * N + n];
-      zv[u] = qzeros.words[static_cast<size_t>(gi) * (N >> 3) + (n >> 3)];
+      zv[u] = *qzeros.at(static_cast<size_t>(gi) * (N >> 3) + (n >> 3));
     }
   };
   auto write_slab = [&](int b, int buf) {

@@ -29,7 +29,7 @@ can be drawn without drawing the whole matrix), 1 = activations,
 
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 
@@ -82,6 +82,20 @@ CONFIGS = {
                       outlier_frac=0.005, outlier_mult=20.0, M_list=(1, 512), act_order=True,
                       note="act-order layout, group 32"),
 }
+
+
+# Variants of the configurations above (same weights and activations): the 70B-class
+# decode layer quantised symmetrically, the scheme of the GPTQ recipe ("AWQ + GPTQ
+# Quantization, in depth", Running it), without stored zero points.
+VARIANTS = {
+    "c3s": replace(CONFIGS["c3"], name="c3s", sym=True,
+                   note="70B-class MLP up-projection, symmetric int4 (no zero points), decode"),
+}
+
+
+def config(name: str) -> LayerConfig:
+    """A configuration or a variant by name."""
+    return CONFIGS[name] if name in CONFIGS else VARIANTS[name]
 
 
 def custom_config(name: str, cfg_id: int, K: int, N: int, group_size: int, *,
