@@ -20,7 +20,10 @@
  *     passed as void* (NULL = the null stream).
  *   - shapes: M rows of activations, N output features, K input features,
  *     G = K / group_size groups per row.  Requirements: M, N, K > 0;
- *     group_size in {32, 64, 128}; K % group_size == 0; N % 8 == 0.
+ *     group_size in {32, 64, 128}, or group_size == K for one scale (and zero point)
+ *     per output row ("LLM Quantization: INT8, GPTQ, and AWQ Explained", What
+ *     quantization actually does: per-channel); K % group_size == 0; K % 32 == 0;
+ *     N % 8 == 0.
  *   - the caller owns every buffer.  The library keeps no pointer after a call
  *     returns.  Host entry points are synchronous.  Device entry points are
  *     asynchronous and stream-ordered: inputs must stay alive, and outputs are

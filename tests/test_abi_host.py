@@ -184,6 +184,23 @@ def test_pack_unpack_round_trip(shape, act):
         assert np.array_equal(packed[N * K // 8:], oracle.sorted_k_order(g_idx))
 
 
+@pytest.mark.parametrize("K", [96, 1536])
+def test_per_channel_quantize_pack_bit_exact(K):
+    """group_size = K: one scale (and zero point) per output row."""
+    cfg = wl.custom_config("perch", 500 + K, K=K, N=24, group_size=K)
+    w = wl.weights(cfg)
+    _assert_same_quant(w4.w4a16_quantize(w, K), oracle.rtn_quantize(w, K))
+    c, S = w4.w4a16_quantize_sym(w, K)
+    co, So = oracle.rtn_quantize_sym(w, K)
+    assert np.array_equal(c, co) and np.array_equal(S.view(np.uint16), So.view(np.uint16))
+    assert S.shape == (1, 24)
+    codes = w4.w4a16_quantize(w, K)[0]
+    g_idx = np.zeros(K, np.int32)                 # act order with one group: identity order
+    for gi in (None, g_idx):
+        packed = w4.w4a16_pack(codes, gi, K)
+        assert np.array_equal(w4.w4a16_unpack(packed, gi, K, 24, K), codes)
+
+
 def test_identity_gidx_packs_like_contiguous():
     codes = wl.random_codes(16, 128, seed=3)
     ident = (np.arange(128) // 32).astype(np.int32)
@@ -211,6 +228,8 @@ def _status(fn, *args):
 def test_error_codes_host():
     codes = wl.random_codes(8, 64, seed=1)
     assert _status(w4.w4a16_pack, codes, None, 48) == w4.ERR_UNSUPPORTED
+    assert _status(w4.w4a16_pack, codes[:, :48], None, 48) == w4.ERR_INVALID_ARG   # per-channel, K % 32
+    assert _status(w4.w4a16_pack, codes, None, 256) == w4.ERR_UNSUPPORTED          # neither g nor K
     assert _status(w4.w4a16_pack, codes[:, :48], None, 32) == w4.ERR_INVALID_ARG   # K % g
     assert _status(w4.w4a16_pack, codes[:4], None, 32) == w4.ERR_INVALID_ARG       # N % 8
     bad = codes.copy()

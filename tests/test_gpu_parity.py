@@ -217,14 +217,31 @@ SYM = [
 ]
 
 
-@pytest.mark.parametrize("case", range(len(SYM)))
-def test_symmetric_layers_match_oracle(case):
+# per-channel scales (group size = K: one scale and zero point per output row), with
+# and without zero points
+PERCH = [
+    # name, M, N, K, act_order, sym
+    ("p1", 1, 264, 1536, False, False),   # GEMV
+    ("p2", 1, 136, 12288, False, True),   # GEMV, split rows, symmetric
+    ("p3", 4, 392, 2048, False, False),   # skinny (dequantised path)
+    ("p4", 5, 264, 12288, True, False),   # skinny, two K slices, act order (one group)
+    ("p5", 40, 264, 1024, False, True),   # large-tile kernel, 64-row tiles, symmetric
+    ("p6", 300, 520, 640, False, False),  # large-tile kernel, 256-row tiles
+    ("p7", 3, 72, 96, False, False),      # tiled fallback kernel
+]
+
+VARIANT_CASES = ([(name, M, N, K, g, act, True) for name, M, N, K, g, act in SYM] +
+                 [(name, M, N, K, K, act, sym) for name, M, N, K, act, sym in PERCH])
+
+
+@pytest.mark.parametrize("case", range(len(VARIANT_CASES)))
+def test_symmetric_and_per_channel_layers_match_oracle(case):
     import torch
-    name, M, N, K, g, act = SYM[case]
-    cfg = wl.custom_config(name, 400 + case, K=K, N=N, group_size=g, M_list=(M,), act_order=act, sym=True)
-    note(f"symmetric {name} M={M} N={N} K={K} g={g} act={act}")
+    name, M, N, K, g, act, sym = VARIANT_CASES[case]
+    cfg = wl.custom_config(name, 400 + case, K=K, N=N, group_size=g, M_list=(M,), act_order=act, sym=sym)
+    note(f"variant {name} M={M} N={N} K={K} g={g} act={act} sym={sym}")
     prod = product_layer(cfg, M)
-    assert prod["qzeros"] is None
+    assert (prod["qzeros"] is None) == sym
     ref = oracle_layer(cfg, M, np.arange(N))
     assert np.array_equal(prod["codes"], ref["codes"])
     paths = ["gemv", "gemm"] if M == 1 else ["gemm"]
@@ -234,7 +251,7 @@ def test_symmetric_layers_match_oracle(case):
         y = run_gemm(prod).cpu().numpy()
         assert oracle.rel_err(y, ref["y_ref"]) <= TOL, path
     os.environ.pop("W4A16_FORCE_PATH", None)
-    W16 = w4.w4a16_dequant(prod["qweight"], prod["scales"], None, prod["g_idx"], g, K).cpu().numpy()
+    W16 = w4.w4a16_dequant(prod["qweight"], prod["scales"], prod["qzeros"], prod["g_idx"], g, K).cpu().numpy()
     assert np.array_equal(W16.view(np.uint16), ref["W16"].view(np.uint16))
     # unit-vector probes select binary16((code - 8) * S) exactly
     ks = np.unique(np.concatenate([[0, K - 1], np.random.default_rng(case).integers(0, K, 6)]))

@@ -19,7 +19,13 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : 7; }
+// Group of input channel k: k >> gshift.  Groups of 32 / 64 / 128 channels, or one
+// group per row (g = K, any multiple of 32): a shift that sends every channel to group 0.
+constexpr int kPerChannelShift = 30;
+int log2_group(int g) { return g == 32 ? 5 : g == 64 ? 6 : g == 128 ? 7 : kPerChannelShift; }
+
+// Groups covering channels [k0, k0 + len) (len > 0).
+int groups_in(int k0, int len, int gshift) { return ((k0 + len - 1) >> gshift) - (k0 >> gshift) + 1; }
 
 int env_int(const char* name, int fallback) {
   const char* v = std::getenv(name);
@@ -206,7 +212,7 @@ GemvPlan plan_gemv(int N, int K, int gshift, bool act) {
   if (p.sh.wpr == 1 && (lpr == 8 || lpr == 16 || lpr == 32 || lpr == 64) && (C + lpr - 1) / lpr <= 4)
     p.sh = {lpr, (C + lpr - 1) / lpr, C % lpr == 0, 1};
   if (static_cast<long long>(N) * K / 2 >= (1LL << 31)) return p;   // 32-bit byte offsets into the codes
-  const int G = K >> gshift;
+  const int G = groups_in(0, K, gshift);
   const int unit = kGemvWaves * (64 / p.sh.lpr);                    // rows per unit
   if ((unit / 8) * G > kGemvWaves * 64) return p;                   // one staging item per thread and step
   p.ept = unit * G <= kGemvWaves * 64 ? 1 : 8;                      // staging rows per thread
@@ -269,7 +275,7 @@ SkinnyShape pick_skinny_shape(int M, int K, int gshift) {
     for (int t : {1, 2, 4}) {
       if (kc % t != 0 || kc / t > 16) continue;
       const int waves = kc / t;
-      const int entries = 16 * (Ks >> gshift);
+      const int entries = 16 * groups_in(0, Ks, gshift);
       const int se = (entries + 64 * waves - 1) / (64 * waves);
       if (se > 4) break;
       sh.waves = waves;
@@ -290,7 +296,7 @@ int launch_skinny_t(const SkinnyShape& sh, hipStream_t st, const half_t* x, cons
       hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_skinny_kernel<T, SE, ACT, SUB>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (int rc = hip_status(lds_ok, "hipFuncSetAttribute")) return rc;
-  const size_t lds = skinny_lds_bytes(sh.waves, (K / sh.ks) >> gshift);
+  const size_t lds = skinny_lds_bytes(sh.waves, groups_in(0, K / sh.ks, gshift));
   const int nblk = (N + 15) / 16;
   const int per_cu = std::max(1, 16 / sh.waves);
   const int per_slice = std::min(nblk, std::max(1, device_cus() * per_cu / sh.ks));

@@ -96,10 +96,12 @@ void clear_error() { t_last_error.clear(); }
 
 int check_shape(int N, int K, int group_size) {
   if (N <= 0 || K <= 0) return fail(W4A16_ERR_INVALID_ARG, "N and K must be positive (N=%d K=%d)", N, K);
-  if (group_size != 32 && group_size != 64 && group_size != 128)
-    return fail(W4A16_ERR_UNSUPPORTED, "group_size %d is not supported (32, 64 or 128)", group_size);
+  // groups of 32, 64 or 128 input channels, or one group per row (per-channel, g = K)
+  if (group_size != 32 && group_size != 64 && group_size != 128 && group_size != K)
+    return fail(W4A16_ERR_UNSUPPORTED, "group_size %d is not supported (32, 64, 128 or K=%d)", group_size, K);
   if (K % group_size != 0)
     return fail(W4A16_ERR_INVALID_ARG, "K=%d is not a multiple of group_size=%d", K, group_size);
+  if (K % 32 != 0) return fail(W4A16_ERR_INVALID_ARG, "K=%d is not a multiple of 32", K);
   if (N % 8 != 0) return fail(W4A16_ERR_INVALID_ARG, "N=%d is not a multiple of 8", N);
   return W4A16_OK;
 }

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   const int CS = (C + WPR - 1) / WPR;    // chunks per slice
   const int h = WPR == 1 ? 0 : wave % WPR;   // this wavefront's slice
   const int W = K >> 3;                  // words per row
-  const int G = K >> gshift;
+  const int G = ((K - 1) >> gshift) + 1;  // groups per row (one per row when per-channel)
   const int GP = G + 1;                  // padded ring row (float2)
   const int nblk = gridDim.x;
   const int blk = xcd_block(blockIdx.x, nblk);

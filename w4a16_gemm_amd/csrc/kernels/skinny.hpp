@@ -84,8 +84,8 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
   const int gs = gridDim.x / ks;                  // workgroups per slice
   const int slice = blockIdx.x / gs;
   const int Ks = K / ks;                          // channels per slice
-  const int G = Ks >> gshift;                     // groups per slice (slab rows)
-  const int g0 = slice * G;                       // first group of the slice
+  const int g0 = (slice * Ks) >> gshift;                    // first group of the slice
+  const int G = ((slice * Ks + Ks - 1) >> gshift) - g0 + 1;  // groups of the slice (slab rows)
   const int slab_n = 16 * G;
   const int nblk = (N + 15) >> 4;
   const int kw = slice * Ks + wave * 128 * T;
