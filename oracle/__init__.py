@@ -25,7 +25,10 @@ What it computes, in plain numpy float64 (slow and obviously correct):
 * ``act_order``      GPTQ act-order group assignment g_idx from the calibration
                      activations (same page and section).
 * ``pack_codes`` / ``unpack_codes`` / ``pack_zeros`` / ``unpack_zeros``
-                     eight 4-bit values per 32-bit word.
+                     eight 4-bit values per 32-bit word; the ``...8`` variants
+                     four 8-bit values per word.  ``rtn_quantize`` and
+                     ``rtn_quantize_sym`` take bits=8 for 8-bit weights ("AWQ +
+                     GPTQ Quantization, in depth", 4-bit bigger or 8-bit smaller).
 * ``dequant`` / ``linear``   W^ = (q - Z)*S and y = x W^T in float64.
 * ``layer_bytes`` / ``bits_per_weight``   storage cost of a packed layer.
 
@@ -43,7 +46,8 @@ from .quant import (round_half_even, fp16_ceil, group_index, rtn_quantize,
                     awq_scales, awq_fold_weights, awq_fold_activations,
                     act_order_h, act_order)
 from .packing import (pack_codes, unpack_codes, pack_zeros, unpack_zeros,
-                      sorted_k_order, pack_codes_act_order)
+                      sorted_k_order, pack_codes_act_order,
+                      pack_codes8, unpack_codes8, pack_zeros8, unpack_zeros8)
 from .layer import dequant, dequant_fp16, linear, rel_err
 from .storage import layer_bytes, bits_per_weight
 

@@ -69,3 +69,46 @@ def pack_codes_act_order(codes, g_idx) -> np.ndarray:
     perm = sorted_k_order(g_idx)
     c = np.asarray(codes)[:, perm]
     return np.concatenate([pack_codes(c).reshape(-1), perm.astype(np.int32)])
+
+
+# --- 8-bit weights: four 8-bit values per 32-bit word ------------------------------
+# byte j (bits 8j..8j+7) of word w holds element 4w + j of the packed axis.
+
+def _pack4_last_axis(vals: np.ndarray) -> np.ndarray:
+    v = np.asarray(vals)
+    assert v.ndim == 2 and v.shape[1] % 4 == 0
+    assert v.min(initial=0) >= 0 and v.max(initial=0) <= 255
+    u = v.astype(np.uint64).reshape(v.shape[0], v.shape[1] // 4, 4)
+    words = np.zeros(u.shape[:2], dtype=np.uint64)
+    for j in range(4):
+        words |= u[:, :, j] << np.uint64(8 * j)
+    return words.astype(np.uint32).view(np.int32)
+
+
+def _unpack4_last_axis(words: np.ndarray) -> np.ndarray:
+    w = np.asarray(words).view(np.uint32).astype(np.uint64)
+    out = np.empty((w.shape[0], w.shape[1], 4), dtype=np.uint8)
+    for j in range(4):
+        out[:, :, j] = ((w >> np.uint64(8 * j)) & np.uint64(0xFF)).astype(np.uint8)
+    return out.reshape(w.shape[0], w.shape[1] * 4)
+
+
+def pack_codes8(codes) -> np.ndarray:
+    """8-bit codes uint8 [N][K] -> int32 [N][K/4]."""
+    return _pack4_last_axis(codes)
+
+
+def unpack_codes8(qweight) -> np.ndarray:
+    """int32 [N][K/4] -> 8-bit codes uint8 [N][K]."""
+    return _unpack4_last_axis(qweight)
+
+
+def pack_zeros8(zeros) -> np.ndarray:
+    """8-bit zeros uint8 [G][N] -> int32 [G][N/4]."""
+    return _pack4_last_axis(zeros)
+
+
+def unpack_zeros8(qzeros) -> np.ndarray:
+    """int32 [G][N/4] -> 8-bit zeros uint8 [G][N]."""
+    return _unpack4_last_axis(qzeros)
+

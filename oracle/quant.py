@@ -55,8 +55,9 @@ def group_index(K: int, group_size: int, g_idx=None) -> np.ndarray:
     return np.asarray(g_idx, dtype=np.int64)
 
 
-def rtn_quantize(w, group_size: int, g_idx=None, in_scale=None):
-    """Asymmetric 4-bit round-to-nearest group quantiser.
+def rtn_quantize(w, group_size: int, g_idx=None, in_scale=None, bits: int = 4):
+    """Asymmetric round-to-nearest group quantiser, 4-bit (16 levels) or 8-bit (256
+    levels: "AWQ + GPTQ Quantization, in depth", 4-bit bigger or 8-bit smaller).
 
     w        binary16 [N][K] weights (out x in).
     g_idx    optional int [K]: group of every input channel (act order).
@@ -65,13 +66,15 @@ def rtn_quantize(w, group_size: int, g_idx=None, in_scale=None):
 
     Returns codes uint8 [N][K], scales binary16 [G][N], zeros uint8 [G][N]
     with G = K / group_size.  Per (row n, group gamma), over the members
-    {k : group(k) = gamma}:
+    {k : group(k) = gamma}, with L = 2**bits - 1 (15 or 255):
         w_lo = min(0, min w), w_hi = max(0, max w)
-        S = smallest binary16 >= (w_hi - w_lo)/15       (S = 1 if w_hi = w_lo)
-        Z = clamp(round(-w_lo/S), 0, 15)
-        q = clamp(round(w/S) + Z, 0, 15)
+        S = smallest binary16 >= (w_hi - w_lo)/L        (S = 1 if w_hi = w_lo)
+        Z = clamp(round(-w_lo/S), 0, L)
+        q = clamp(round(w/S) + Z, 0, L)
     All arithmetic is float64 on the binary16 inputs.
     """
+    assert bits in (4, 8)
+    levels = (1 << bits) - 1
     w = np.asarray(w)
     assert w.dtype == np.float16 and w.ndim == 2
     N, K = w.shape
@@ -92,12 +95,12 @@ def rtn_quantize(w, group_size: int, g_idx=None, in_scale=None):
         lo = np.minimum(Wg.min(axis=1), 0.0)
         hi = np.maximum(Wg.max(axis=1), 0.0)
         flat = hi == lo
-        S16 = fp16_ceil(np.where(flat, 1.0, (hi - lo) / LEVELS))
+        S16 = fp16_ceil(np.where(flat, 1.0, (hi - lo) / levels))
         S16[flat] = np.float16(1.0)
         S = S16.astype(np.float64)
-        Z = np.clip(round_half_even(-lo / S), 0, LEVELS)
+        Z = np.clip(round_half_even(-lo / S), 0, levels)
         Z[flat] = 0
-        q = np.clip(round_half_even(Wg / S[:, None]) + Z[:, None], 0, LEVELS)
+        q = np.clip(round_half_even(Wg / S[:, None]) + Z[:, None], 0, levels)
         codes[:, cols] = q.astype(np.uint8)
         scales[gamma] = S16
         zeros[gamma] = Z.astype(np.uint8)
@@ -108,21 +111,26 @@ SYM_LEVELS = 7              # 2**(4-1) - 1: the symmetric grid is -7 .. 7
 SYM_ZERO = 8                # stored code of 0 (the implicit zero point)
 
 
-def rtn_quantize_sym(w, group_size: int, g_idx=None, in_scale=None):
+def rtn_quantize_sym(w, group_size: int, g_idx=None, in_scale=None, bits: int = 4):
     """Symmetric 4-bit round-to-nearest group quantiser: the absmax scheme of "LLM
     Quantization: INT8, GPTQ, and AWQ Explained", What quantization actually does
     (one scale from the block's largest magnitude, round, clamp to the symmetric
     range), on the 4-bit grid -7 .. 7; the GPTQ recipe of "AWQ + GPTQ Quantization, in
     depth", Running it, uses the symmetric W4A16 scheme where the AWQ one is asymmetric.
 
-    Returns codes uint8 [N][K] (the signed value plus 8, so the implicit zero point
-    is 8) and scales binary16 [G][N].  Per (row n, group gamma):
+    Returns codes uint8 [N][K] (the signed value plus 2**(bits-1), so the implicit
+    zero point is 8 at 4 bits and 128 at 8 bits) and scales binary16 [G][N].  Per
+    (row n, group gamma), with L = 2**(bits-1) - 1 (7, or 127 as in the pages' int8
+    absmax code):
         a = max |w|
-        S = smallest binary16 >= a / 7                  (S = 1 if a = 0)
-        q = clamp(round(w / S), -7, 7),  code = q + 8
-    and w ~ (code - 8) * S.  Same group membership, AWQ factor and float64
+        S = smallest binary16 >= a / L                  (S = 1 if a = 0)
+        q = clamp(round(w / S), -L, L),  code = q + L + 1
+    and w ~ (code - L - 1) * S.  Same group membership, AWQ factor and float64
     arithmetic as rtn_quantize.
     """
+    assert bits in (4, 8)
+    levels = (1 << (bits - 1)) - 1
+    zero = levels + 1
     w = np.asarray(w)
     assert w.dtype == np.float16 and w.ndim == 2
     N, K = w.shape
@@ -141,18 +149,19 @@ def rtn_quantize_sym(w, group_size: int, g_idx=None, in_scale=None):
         Wg = W[:, cols]
         a = np.abs(Wg).max(axis=1)
         flat = a == 0.0
-        S16 = fp16_ceil(np.where(flat, 1.0, a / SYM_LEVELS))
+        S16 = fp16_ceil(np.where(flat, 1.0, a / levels))
         S16[flat] = np.float16(1.0)
         S = S16.astype(np.float64)
-        q = np.clip(round_half_even(Wg / S[:, None]), -SYM_LEVELS, SYM_LEVELS)
-        codes[:, cols] = (q + SYM_ZERO).astype(np.uint8)
+        q = np.clip(round_half_even(Wg / S[:, None]), -levels, levels)
+        codes[:, cols] = (q + zero).astype(np.uint8)
         scales[gamma] = S16
     return codes, scales
 
 
-def sym_zeros(G: int, N: int) -> np.ndarray:
-    """The implicit zero points of a symmetric layer, uint8 [G][N], all 8."""
-    return np.full((G, N), SYM_ZERO, dtype=np.uint8)
+def sym_zeros(G: int, N: int, bits: int = 4) -> np.ndarray:
+    """The implicit zero points of a symmetric layer, uint8 [G][N]: 8 (4-bit) or
+    128 (8-bit)."""
+    return np.full((G, N), 1 << (bits - 1), dtype=np.uint8)
 
 
 # --- AWQ ------------------------------------------------------------------------

@@ -48,22 +48,22 @@ def _nearest_int_in(lo: int, hi: int, target: Fraction, parity_offset: int = 0) 
     return best[1]
 
 
-def quantize_group_exact(ws):
-    """Exact RTN of one group (list of Fractions) -> (S, Z, [q...])."""
+def quantize_group_exact(ws, top: int = 15):
+    """Exact RTN of one group (list of Fractions) on the grid 0..top -> (S, Z, [q...])."""
     lo = min([Fraction(0)] + list(ws))
     hi = max([Fraction(0)] + list(ws))
     if lo == hi:
         return Fraction(1), 0, [0] * len(ws)
-    S = fp16_ceil_exact((hi - lo) / 15)
-    Z = _nearest_int_in(0, 15, -lo / S)
+    S = fp16_ceil_exact((hi - lo) / top)
+    Z = _nearest_int_in(0, top, -lo / S)
     qs = []
     for w in ws:
         # grid point (j - Z)*S nearest to w  <=>  j nearest to w/S + Z
-        qs.append(_nearest_int_in(0, 15, w / S + Z, parity_offset=Z))
+        qs.append(_nearest_int_in(0, top, w / S + Z, parity_offset=Z))
     return S, Z, qs
 
 
-def quantize_exact(w: np.ndarray, group_size: int, g_idx=None, in_scale=None):
+def quantize_exact(w: np.ndarray, group_size: int, g_idx=None, in_scale=None, top: int = 15):
     """Exact RTN of a small matrix; same return shapes as the oracle (but Fractions
     for the scales).  in_scale multiplies the float64 columns (its float64
     products are what gets quantised, as in the oracle's definition)."""
@@ -79,7 +79,7 @@ def quantize_exact(w: np.ndarray, group_size: int, g_idx=None, in_scale=None):
     for n in range(N):
         for gam in range(G):
             ks = [k for k in range(K) if gid[k] == gam]
-            s, z, qs = quantize_group_exact([Fraction(float(W[n, k])) for k in ks])
+            s, z, qs = quantize_group_exact([Fraction(float(W[n, k])) for k in ks], top)
             S[gam][n] = s
             Z[gam, n] = z
             for k, q in zip(ks, qs):
@@ -105,18 +105,19 @@ def linear_exact(x: np.ndarray, codes, S, Z, group_size: int, g_idx=None):
     return y
 
 
-def quantize_group_exact_sym(ws):
+def quantize_group_exact_sym(ws, half: int = 8):
     """Exact symmetric RTN of one group (list of Fractions) -> (S, [code...]): S is
-    the smallest binary16 with 7 S >= max |w| (found by scan), each code the grid
-    index j in [1, 15] whose point (j - 8) S is nearest to w, ties to even j - 8."""
+    the smallest binary16 with (half - 1) S >= max |w| (found by scan), each code the
+    grid index j in [1, 2 half - 1] whose point (j - half) S is nearest to w, ties to
+    even j - half (half = 8 at 4 bits, 128 at 8 bits)."""
     a = max([abs(w) for w in ws] + [Fraction(0)])
     if a == 0:
-        return Fraction(1), [8] * len(ws)
-    S = fp16_ceil_exact(a / 7)
-    return S, [_nearest_int_in(1, 15, w / S + 8, parity_offset=8) for w in ws]
+        return Fraction(1), [half] * len(ws)
+    S = fp16_ceil_exact(a / (half - 1))
+    return S, [_nearest_int_in(1, 2 * half - 1, w / S + half, parity_offset=half) for w in ws]
 
 
-def quantize_exact_sym(w: np.ndarray, group_size: int, g_idx=None, in_scale=None):
+def quantize_exact_sym(w: np.ndarray, group_size: int, g_idx=None, in_scale=None, half: int = 8):
     """Exact symmetric RTN of a small matrix: (codes uint8 [N][K], scales [G][N] as
     Fractions)."""
     N, K = w.shape
@@ -130,7 +131,7 @@ def quantize_exact_sym(w: np.ndarray, group_size: int, g_idx=None, in_scale=None
     for n in range(N):
         for gam in range(G):
             members = np.nonzero(gid == gam)[0]
-            s, qs = quantize_group_exact_sym([Fraction(float(W[n, k])) for k in members])
+            s, qs = quantize_group_exact_sym([Fraction(float(W[n, k])) for k in members], half)
             S[gam][n] = s
             for k, q in zip(members, qs):
                 codes[n, k] = q

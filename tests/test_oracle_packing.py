@@ -55,3 +55,15 @@ def test_act_order_packing():
     packed_id = oracle.pack_codes_act_order(c, ident)
     assert np.array_equal(packed_id[:-K].reshape(5, K // 8), oracle.pack_codes(c))
     assert np.array_equal(packed_id[-K:], np.arange(K))
+
+
+def test_pack8_known_words_and_round_trip():
+    codes = np.array([[0x01, 0x23, 0x45, 0x67, 0x89, 0xAB, 0xCD, 0xEF]], dtype=np.uint8)
+    words = oracle.pack_codes8(codes).view(np.uint32)
+    assert words.tolist() == [[0x67452301, 0xEFCDAB89]]      # byte j of a word = element 4w + j
+    rng = np.random.default_rng(5)
+    c = rng.integers(0, 256, size=(8, 64), dtype=np.uint8)
+    assert np.array_equal(oracle.unpack_codes8(oracle.pack_codes8(c)), c)
+    z = rng.integers(0, 256, size=(3, 32), dtype=np.uint8)
+    assert np.array_equal(oracle.unpack_zeros8(oracle.pack_zeros8(z)), z)
+

@@ -211,6 +211,64 @@ def test_sym_rtn_invariants_on_configs(name):
     assert np.array_equal(c_neg.astype(int), 16 - codes.astype(int))
 
 
+# --- 8-bit weights ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("g", [4, 8])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_rtn8_matches_exact_search(g, seed):
+    w = _plant_special_groups(_tile(seed, 8, 8), g, None)
+    c, S, Z = oracle.rtn_quantize(w, g, bits=8)
+    ce, Se, Ze = quantize_exact(w, g, top=255)
+    assert np.array_equal(c, ce) and np.array_equal(Z, Ze)
+    assert all(Fraction(float(S[a, n])) == Se[a][n] for a in range(S.shape[0]) for n in range(8))
+    c, S = oracle.rtn_quantize_sym(w, g, bits=8)
+    ce, Se = quantize_exact_sym(w, g, half=128)
+    assert np.array_equal(c, ce)
+    assert all(Fraction(float(S[a, n])) == Se[a][n] for a in range(S.shape[0]) for n in range(8))
+
+
+def test_sym8_is_the_int8_absmax_grid():
+    """At 8 bits the symmetric scheme is the pages' int8 absmax code on each group
+    (scale absmax / 127, round half even, clamp to -127..127), with the scale held in
+    binary16 rounded up: on groups whose absmax / 127 is a binary16 value the codes are
+    exactly round(w / (absmax / 127)) + 128."""
+    w = np.zeros((4, 16), np.float16)
+    w[0] = np.float16(127.0) * np.linspace(-1, 1, 16).astype(np.float16)   # absmax 127: scale 1
+    w[1] = np.float16(0.5) * w[0]                                         # scale 0.5 (power of two)
+    w[2] = -w[0]
+    w[3, :] = 0
+    codes, S = oracle.rtn_quantize_sym(w, 16, bits=8)
+    assert S[0, :3].tolist() == [1.0, 0.5, 1.0] and float(S[0, 3]) == 1.0
+    a = np.abs(w.astype(np.float64)).max(1)
+    for r in range(3):
+        expect = np.clip(np.rint(w[r].astype(np.float64) / (a[r] / 127.0)), -127, 127) + 128
+        assert np.array_equal(codes[r], expect.astype(np.uint8))
+    assert np.all(codes[3] == 128)
+
+
+@pytest.mark.parametrize("name", ["c1", "c3"])
+def test_rtn8_invariants_on_configs(name):
+    cfg = wl.CONFIGS[name]
+    rows = np.linspace(0, cfg.N - 1, 16).astype(np.int64)
+    w = wl.weights(cfg, rows)
+    W = w.astype(np.float64)
+    g = cfg.group_size
+    gid = oracle.group_index(cfg.K, g)
+    for sym in (False, True):
+        if sym:
+            codes, S = oracle.rtn_quantize_sym(w, g, bits=8)
+            Z = oracle.sym_zeros(cfg.G, len(rows), bits=8)
+        else:
+            codes, S, Z = oracle.rtn_quantize(w, g, bits=8)
+        Sk = S.astype(np.float64)[gid, :].T
+        What = oracle.dequant(codes, S, Z, g)
+        assert np.all(np.abs(W - What) <= Sk / 2)
+        # 8 bits: at most 1/16 of the 4-bit step on the same group's range
+        c4, S4, Z4 = oracle.rtn_quantize(w, g)
+        assert np.all(S.astype(np.float64) <= S4.astype(np.float64) * (15.0 / 127.0) * 1.01 if sym
+                      else S.astype(np.float64) <= S4.astype(np.float64) * (15.0 / 255.0) * 1.01)
+
+
 # --- AWQ scale and fold -------------------------------------------------------------
 
 def test_awq_scales_exact_mean_and_sqrt():
