@@ -196,6 +196,56 @@ int w4a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t*
                   const int32_t* g_idx, int group_size, int N, int K, uint16_t* w_out,
                   void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * 8-bit weights (W8A16): the same layer with 256-level codes ("AWQ + GPTQ
+ * Quantization, in depth", 4-bit bigger or 8-bit smaller).  Same conventions,
+ * shapes, error codes and act order as above; codes and zero points are bytes.
+ *   qweight  int32 buffer of w8a16_qweight_words(N, K, act_order) words (private
+ *            layout: four codes per word; the act-order tail as above)
+ *   qzeros   int32 [G][N/4] or NULL (symmetric: every zero point 128): zero point of
+ *            (group, n) in bits 8j..8j+7 of word [group][n/4], j = n % 4
+ * ------------------------------------------------------------------------------ */
+
+size_t w8a16_qweight_words(int N, int K, int act_order);
+
+/* Asymmetric round-to-nearest on 256 levels: as w4a16_quantize with 255 for 15
+ * (S = smallest binary16 >= (w_hi - w_lo) / 255, Z and q clamped to [0, 255]).
+ * Errors as w4a16_quantize. */
+int w8a16_quantize(const uint16_t* w, int N, int K, int group_size, const int32_t* g_idx,
+                   const double* in_scale, uint8_t* codes, uint16_t* scales, uint8_t* zeros);
+
+/* Symmetric: the int8 absmax scheme of "LLM Quantization: INT8, GPTQ, and AWQ
+ * Explained", What quantization actually does, per group: S = smallest binary16 >=
+ * max |w| / 127, q = clamp(round(w / S), -127, 127), codes = q + 128 (1 .. 255); pass
+ * qzeros = NULL to the device calls.  Errors as w4a16_quantize. */
+int w8a16_quantize_sym(const uint16_t* w, int N, int K, int group_size, const int32_t* g_idx,
+                       const double* in_scale, uint8_t* codes, uint16_t* scales);
+
+/* Pack / unpack codes uint8 [N][K] (0..255) to / from the 8-bit weight buffer; g_idx as
+ * for w4a16_pack.  Errors: INVALID_ARG, UNSUPPORTED, BAD_GIDX. */
+int w8a16_pack(const uint8_t* codes, const int32_t* g_idx, int group_size, int N, int K,
+               int32_t* qweight);
+int w8a16_unpack(const int32_t* qweight, const int32_t* g_idx, int group_size, int N, int K,
+                 uint8_t* codes);
+
+/* Zero points: zeros uint8 [G][N] <-> qzeros int32 [G][N/4].  Errors: INVALID_ARG. */
+int w8a16_pack_zeros(const uint8_t* zeros, int G, int N, int32_t* qzeros);
+int w8a16_unpack_zeros(const int32_t* qzeros, int G, int N, uint8_t* zeros);
+
+/* y = x * W^T for 8-bit weights, device memory, asynchronous on `stream`.  M == 1
+ * runs the split-K GEMV (K <= 32768, at most 512 groups per row, N*K < 2^31), larger M
+ * the tiled MFMA kernel (act order: x gathered into stream-ordered scratch memory
+ * first).  qzeros NULL = symmetric.  Errors as w4a16_gemm. */
+int w8a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+               const int32_t* qzeros, const int32_t* g_idx, int group_size, int M, int N,
+               int K, uint16_t* y, void* stream);
+
+/* binary16((q - Z) * S) of an 8-bit weight buffer, [N][K] in the original channel
+ * order (debug/parity view).  Errors as w4a16_gemm. */
+int w8a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
+                  const int32_t* g_idx, int group_size, int N, int K, uint16_t* w_out,
+                  void* stream);
+
 #ifdef __cplusplus
 }
 #endif

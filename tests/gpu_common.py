@@ -44,11 +44,12 @@ def product_layer(cfg: wl.LayerConfig, M: int, x=None):
         if cfg.awq:
             s = w4.w4a16_awq_scales(X)
     w = wl.weights(cfg)
+    eight = cfg.bits == 8
     if cfg.sym:
-        codes, S = w4.w4a16_quantize_sym(w, g, g_idx, s)
+        codes, S = (w4.w8a16_quantize_sym if eight else w4.w4a16_quantize_sym)(w, g, g_idx, s)
         Z = None
     else:
-        codes, S, Z = w4.w4a16_quantize(w, g, g_idx, s)
+        codes, S, Z = (w4.w8a16_quantize if eight else w4.w4a16_quantize)(w, g, g_idx, s)
     if x is None:
         x = wl.activations(cfg, M)
         if s is not None:
@@ -56,9 +57,10 @@ def product_layer(cfg: wl.LayerConfig, M: int, x=None):
     layer = {
         "cfg": cfg, "M": M, "codes": codes, "g_idx_np": g_idx,
         "x": torch.from_numpy(np.ascontiguousarray(x)).to(dev),
-        "qweight": torch.from_numpy(w4.w4a16_pack(codes, g_idx, g)).to(dev),
+        "qweight": torch.from_numpy((w4.w8a16_pack if eight else w4.w4a16_pack)(codes, g_idx, g)).to(dev),
         "scales": torch.from_numpy(S).to(dev),
-        "qzeros": None if Z is None else torch.from_numpy(w4.w4a16_pack_zeros(Z)).to(dev),
+        "qzeros": None if Z is None else torch.from_numpy(
+            (w4.w8a16_pack_zeros if eight else w4.w4a16_pack_zeros)(Z)).to(dev),
         "g_idx": None if g_idx is None else torch.from_numpy(g_idx).to(dev),
     }
     return layer
@@ -76,10 +78,10 @@ def oracle_layer(cfg: wl.LayerConfig, M: int, rows, x=None):
             s = oracle.awq_scales(X)
     w = wl.weights(cfg, rows)
     if cfg.sym:
-        codes, S = oracle.rtn_quantize_sym(w, g, g_idx, s)
-        Z = oracle.sym_zeros(S.shape[0], S.shape[1])
+        codes, S = oracle.rtn_quantize_sym(w, g, g_idx, s, bits=cfg.bits)
+        Z = oracle.sym_zeros(S.shape[0], S.shape[1], bits=cfg.bits)
     else:
-        codes, S, Z = oracle.rtn_quantize(w, g, g_idx, s)
+        codes, S, Z = oracle.rtn_quantize(w, g, g_idx, s, bits=cfg.bits)
     if x is None:
         x = wl.activations(cfg, M)
         if s is not None:
@@ -91,8 +93,9 @@ def oracle_layer(cfg: wl.LayerConfig, M: int, rows, x=None):
 
 def run_gemm(layer, x=None, y=None):
     import torch
-    out = w4.w4a16_gemm(layer["x"] if x is None else x, layer["qweight"], layer["scales"], layer["qzeros"],
-                        layer["g_idx"], layer["cfg"].group_size, y=y)
+    gemm = w4.w8a16_gemm if layer["cfg"].bits == 8 else w4.w4a16_gemm
+    out = gemm(layer["x"] if x is None else x, layer["qweight"], layer["scales"], layer["qzeros"],
+               layer["g_idx"], layer["cfg"].group_size, y=y)
     torch.cuda.synchronize()
     return out
 

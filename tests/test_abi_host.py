@@ -20,13 +20,13 @@ HEADER = os.path.join(ROOT, "include", "w4a16.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(w4a16_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(w[48]a16_\w+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
     lib = w4.lib()
     declared = _declared_functions()
-    assert len(declared) == 14
+    assert len(declared) == 23
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(w4.EXPORTS) == declared
@@ -199,6 +199,63 @@ def test_per_channel_quantize_pack_bit_exact(K):
     for gi in (None, g_idx):
         packed = w4.w4a16_pack(codes, gi, K)
         assert np.array_equal(w4.w4a16_unpack(packed, gi, K, 24, K), codes)
+
+
+# --- 8-bit weights -----------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["c1", "c2up", "c3", "c5"])
+def test_quantize8_bit_exact_on_config_rows(name):
+    cfg = wl.CONFIGS[name]
+    rows = np.linspace(0, cfg.N - 1, 16).astype(np.int64)
+    w = wl.weights(cfg, rows)
+    g_idx = s = None
+    if cfg.act_order:
+        g_idx, _ = oracle.act_order(wl.calibration(cfg), cfg.group_size)
+    if cfg.awq:
+        s = oracle.awq_scales(wl.calibration(cfg))
+    _assert_same_quant(w4.w8a16_quantize(w, cfg.group_size, g_idx, s),
+                       oracle.rtn_quantize(w, cfg.group_size, g_idx, s, bits=8))
+    c, S = w4.w8a16_quantize_sym(w, cfg.group_size, g_idx, s)
+    co, So = oracle.rtn_quantize_sym(w, cfg.group_size, g_idx, s, bits=8)
+    assert np.array_equal(c, co) and np.array_equal(S.view(np.uint16), So.view(np.uint16))
+
+
+def test_quantize8_bit_exact_on_special_groups():
+    rng = np.random.default_rng(2)
+    for scale in (1e-6, 1e-3, 1.0, 300.0):
+        w = (rng.standard_normal((16, 128)) * scale).astype(np.float16)
+        w[3, :32] = 0
+        w[4, 32:64] = np.abs(w[4, 32:64])
+        w[5, 64:96] = -np.abs(w[5, 64:96])
+        for g in (32, 64, 128):
+            _assert_same_quant(w4.w8a16_quantize(w, g), oracle.rtn_quantize(w, g, bits=8))
+            c, S = w4.w8a16_quantize_sym(w, g)
+            co, So = oracle.rtn_quantize_sym(w, g, bits=8)
+            assert np.array_equal(c, co) and np.array_equal(S.view(np.uint16), So.view(np.uint16))
+
+
+def test_pack8_private_layout_and_round_trip():
+    codes = np.tile(np.array([0x01, 0x23, 0x45, 0x67], np.uint8), (8, 8))   # K = 32
+    words = w4.w8a16_pack(codes, None, 32).view(np.uint32)
+    # element e of a word sits in byte (0, 2, 1, 3)[e]
+    assert np.all(words == 0x67234501)
+    for act in (False, True):
+        N, K, g = 24, 256, 64
+        c = np.random.default_rng(7).integers(0, 256, size=(N, K), dtype=np.uint8)
+        g_idx = None
+        if act:
+            perm = np.random.default_rng(8).permutation(K)
+            g_idx = np.empty(K, np.int32)
+            g_idx[perm] = np.arange(K) // g
+        packed = w4.w8a16_pack(c, g_idx, g)
+        assert packed.size == w4.w8a16_qweight_words(N, K, act)
+        assert np.array_equal(w4.w8a16_unpack(packed, g_idx, g, N, K), c)
+        if act:
+            assert np.array_equal(packed[N * K // 4:], oracle.sorted_k_order(g_idx))
+    z = np.random.default_rng(9).integers(0, 256, size=(6, 32), dtype=np.uint8)
+    q = w4.w8a16_pack_zeros(z)
+    assert np.array_equal(q, oracle.pack_zeros8(z))
+    assert np.array_equal(w4.w8a16_unpack_zeros(q, 6, 32), z)
 
 
 def test_identity_gidx_packs_like_contiguous():

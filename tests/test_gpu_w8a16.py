@@ -1,0 +1,90 @@
+"""GPU parity of the 8-bit weight path against the oracle (needs an MI355X).
+
+8-bit weights: "AWQ + GPTQ Quantization, in depth", 4-bit bigger or 8-bit smaller; the
+symmetric variant is the int8 absmax scheme of "LLM Quantization: INT8, GPTQ, and AWQ
+Explained", What quantization actually does, per group.  Same bars as the 4-bit
+parity tests: codes bit-exact, the device weight view bit-exact, unit-vector probes
+bit-exact, outputs within max|y - y_ref| / rms(y_ref) <= 1e-2.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import w4a16_gemm_amd as w4
+import workloads as wl
+from gpu_common import device, note, oracle_layer, product_layer, run_gemm, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+CASES = [
+    # name, M, N, K, group, act_order, sym
+    ("e1", 1, 264, 1536, 128, False, False),    # GEMV, exact split
+    ("e2", 1, 520, 8192, 64, True, False),      # GEMV, rows split over two wavefronts, act order
+    ("e3", 1, 136, 12288, 128, False, True),    # GEMV, four slices, symmetric
+    ("e4", 1, 72, 1056, 32, False, False),      # GEMV, inexact split
+    ("e5", 4, 392, 2048, 128, False, False),    # tiled MFMA, 16-row blocks
+    ("e6", 20, 264, 1024, 64, True, True),      # tiled, 32-row blocks, act order, symmetric
+    ("e7", 100, 136, 640, 128, False, False),   # tiled, 128-row blocks
+    ("e8", 300, 264, 1536, 1536, False, False), # per-channel, three 128-row blocks
+    ("e9", 1, 40, 96, 96, False, True),         # per-channel, tiny K, symmetric
+]
+
+
+@pytest.fixture(autouse=True)
+def _clear_env():
+    os.environ.pop("W4A16_FORCE_PATH", None)
+    yield
+    os.environ.pop("W4A16_FORCE_PATH", None)
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_w8a16_layers_match_oracle(case):
+    import torch
+    name, M, N, K, g, act, sym = CASES[case]
+    cfg = wl.custom_config(name, 600 + case, K=K, N=N, group_size=g, M_list=(M,), act_order=act, sym=sym, bits=8)
+    note(f"8-bit {name} M={M} N={N} K={K} g={g} act={act} sym={sym}")
+    prod = product_layer(cfg, M)
+    ref = oracle_layer(cfg, M, np.arange(N))
+    assert np.array_equal(prod["codes"], ref["codes"])
+    for path in (["gemv", "gemm"] if M == 1 else ["gemm"]):
+        os.environ["W4A16_FORCE_PATH"] = path
+        note(f"  path={path}")
+        y = run_gemm(prod).cpu().numpy()
+        assert oracle.rel_err(y, ref["y_ref"]) <= TOL, path
+    os.environ.pop("W4A16_FORCE_PATH")
+    W16 = w4.w8a16_dequant(prod["qweight"], prod["scales"], prod["qzeros"], prod["g_idx"], g, K).cpu().numpy()
+    assert np.array_equal(W16.view(np.uint16), ref["W16"].view(np.uint16))
+    back = w4.w8a16_unpack(prod["qweight"].cpu().numpy(), prod["g_idx_np"], g, N, K)
+    assert np.array_equal(back, ref["codes"])
+    # unit-vector probes: x = e_k gives binary16(W^[:, k]) exactly, on both kernels
+    ks = np.unique(np.concatenate([[0, K - 1], np.random.default_rng(case).integers(0, K, 6)]))
+    E = torch.from_numpy(wl.unit_vectors(K, ks)).to(device())
+    expect = ref["W16"][:, ks].T.copy()
+    os.environ["W4A16_FORCE_PATH"] = "gemm"
+    ye = run_gemm(prod, x=E).cpu().numpy()
+    assert np.array_equal(ye.view(np.uint16), expect.view(np.uint16))
+    os.environ["W4A16_FORCE_PATH"] = "gemv"
+    for i in (0, len(ks) - 1):
+        yi = run_gemm(prod, x=E[i:i + 1].contiguous()).cpu().numpy()
+        assert np.array_equal(yi[0].view(np.uint16), expect[i].view(np.uint16))
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_w8a16_full_size_layer_on_sampled_rows(M):
+    import torch
+    cfg = wl.config("c3w8")
+    note(f"8-bit full-size {cfg.name} M={M} (N={cfg.N} K={cfg.K})")
+    prod = product_layer(cfg, 16)
+    rows = np.unique(np.concatenate([sample_rows(cfg.N, 96), np.arange(cfg.N - 8, cfg.N)]))
+    ref = oracle_layer(cfg, M, rows)
+    assert np.array_equal(prod["codes"][rows], ref["codes"])
+    x = prod["x"][:M].contiguous()
+    y = torch.full((M, cfg.N), float("nan"), dtype=torch.float16, device=x.device)
+    run_gemm(prod, x=x, y=y)
+    assert not bool(torch.isnan(y).any())
+    assert oracle.rel_err(y.cpu().numpy()[:, rows], ref["y_ref"]) <= TOL

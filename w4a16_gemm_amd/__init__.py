@@ -40,6 +40,19 @@ _SIGNATURES = {
                             _c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
     "w4a16_dequant": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                _c_int, _c_void_p, _c_void_p]),
+    "w8a16_qweight_words": (ctypes.c_size_t, [_c_int, _c_int, _c_int]),
+    "w8a16_quantize": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
+                                _c_void_p, _c_void_p, _c_void_p]),
+    "w8a16_quantize_sym": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
+                                    _c_void_p, _c_void_p]),
+    "w8a16_pack": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p]),
+    "w8a16_unpack": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_void_p]),
+    "w8a16_pack_zeros": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p]),
+    "w8a16_unpack_zeros": (_c_int, [_c_void_p, _c_int, _c_int, _c_void_p]),
+    "w8a16_gemm": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
+                            _c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
+    "w8a16_dequant": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
+                               _c_int, _c_void_p, _c_void_p]),
 }
 EXPORTS = tuple(_SIGNATURES)
 
@@ -249,3 +262,120 @@ def w4a16_dequant(qweight, scales, qzeros, g_idx, group_size: int, K: int, out=N
 
 
 __all__ = ["LIB_PATH", "EXPORTS", "W4A16Error", "lib"] + [n for n in EXPORTS if n != "w4a16_last_error"]
+
+
+# --- 8-bit weights (same conventions; codes and zero points are bytes) --------------
+
+def w8a16_qweight_words(N: int, K: int, act_order: bool) -> int:
+    return int(lib().w8a16_qweight_words(N, K, int(bool(act_order))))
+
+
+def w8a16_quantize(w, group_size: int, g_idx=None, in_scale=None):
+    """binary16 w [N][K] -> (codes uint8 [N][K], scales binary16 [G][N], zeros uint8 [G][N]),
+    256 levels."""
+    w = _np(w, np.float16, 2)
+    N, K = w.shape
+    G = K // group_size if group_size else 0
+    gi = None if g_idx is None else _np(g_idx, np.int32, 1)
+    sc = None if in_scale is None else _np(in_scale, np.float64, 1)
+    codes = np.empty((N, K), np.uint8)
+    scales = np.empty((max(G, 1), N), np.float16)
+    zeros = np.empty((max(G, 1), N), np.uint8)
+    _check(lib().w8a16_quantize(_ptr(w), N, K, group_size, _ptr(gi), _ptr(sc), _ptr(codes),
+                                _ptr(scales), _ptr(zeros)))
+    return codes, scales, zeros
+
+
+def w8a16_quantize_sym(w, group_size: int, g_idx=None, in_scale=None):
+    """Symmetric 8-bit (int8 absmax per group): (codes uint8 [N][K] in 1..255, scales
+    binary16 [G][N]); the zero point is 128 everywhere (qzeros=None on the device)."""
+    w = _np(w, np.float16, 2)
+    N, K = w.shape
+    G = K // group_size if group_size else 0
+    gi = None if g_idx is None else _np(g_idx, np.int32, 1)
+    sc = None if in_scale is None else _np(in_scale, np.float64, 1)
+    codes = np.empty((N, K), np.uint8)
+    scales = np.empty((max(G, 1), N), np.float16)
+    _check(lib().w8a16_quantize_sym(_ptr(w), N, K, group_size, _ptr(gi), _ptr(sc), _ptr(codes), _ptr(scales)))
+    return codes, scales
+
+
+def w8a16_pack(codes, g_idx, group_size: int) -> np.ndarray:
+    codes = _np(codes, np.uint8, 2)
+    N, K = codes.shape
+    gi = None if g_idx is None else _np(g_idx, np.int32, 1)
+    out = np.empty(max(w8a16_qweight_words(N, K, gi is not None), 1), np.int32)
+    _check(lib().w8a16_pack(_ptr(codes), _ptr(gi), group_size, N, K, _ptr(out)))
+    return out
+
+
+def w8a16_unpack(qweight, g_idx, group_size: int, N: int, K: int) -> np.ndarray:
+    qweight = _np(qweight, np.int32).reshape(-1)
+    gi = None if g_idx is None else _np(g_idx, np.int32, 1)
+    if qweight.size < w8a16_qweight_words(N, K, gi is not None):
+        raise ValueError("qweight is smaller than the packed size of an N x K 8-bit layer")
+    codes = np.empty((N, K), np.uint8)
+    _check(lib().w8a16_unpack(_ptr(qweight), _ptr(gi), group_size, N, K, _ptr(codes)))
+    return codes
+
+
+def w8a16_pack_zeros(zeros) -> np.ndarray:
+    zeros = _np(zeros, np.uint8, 2)
+    G, N = zeros.shape
+    out = np.empty((G, max(N // 4, 1)), np.int32)
+    _check(lib().w8a16_pack_zeros(_ptr(zeros), G, N, _ptr(out)))
+    return out
+
+
+def w8a16_unpack_zeros(qzeros, G: int, N: int) -> np.ndarray:
+    qzeros = _np(qzeros, np.int32, 2)
+    if qzeros.shape != (G, N // 4):
+        raise ValueError(f"qzeros shape {qzeros.shape} != {(G, N // 4)}")
+    out = np.empty((G, N), np.uint8)
+    _check(lib().w8a16_unpack_zeros(_ptr(qzeros), G, N, _ptr(out)))
+    return out
+
+
+def w8a16_gemm(x, qweight, scales, qzeros, g_idx, group_size: int, y=None, stream=None):
+    """y = x W^T for 8-bit weights on the device (qzeros int32 [G][N/4] or None)."""
+    import torch
+    _dev(x, torch.float16, "x")
+    _dev(qweight, torch.int32, "qweight")
+    _dev(scales, torch.float16, "scales")
+    if qzeros is not None:
+        _dev(qzeros, torch.int32, "qzeros")
+    if g_idx is not None:
+        _dev(g_idx, torch.int32, "g_idx")
+    M, K = x.shape
+    G, N = scales.shape
+    if qweight.numel() < w8a16_qweight_words(N, K, g_idx is not None):
+        raise ValueError("qweight is smaller than the packed size of an N x K 8-bit layer")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _dev(y, torch.float16, "y")
+    if tuple(y.shape) != (M, N):
+        raise ValueError(f"y shape {tuple(y.shape)} != {(M, N)}")
+    _check(lib().w8a16_gemm(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(),
+                            None if qzeros is None else qzeros.data_ptr(),
+                            None if g_idx is None else g_idx.data_ptr(), group_size, M, N, K,
+                            y.data_ptr(), _stream_handle(stream, x.device)))
+    return y
+
+
+def w8a16_dequant(qweight, scales, qzeros, g_idx, group_size: int, K: int, out=None, stream=None):
+    """binary16 (q - Z) * S of an 8-bit weight buffer as [N][K] in the original order."""
+    import torch
+    _dev(qweight, torch.int32, "qweight")
+    _dev(scales, torch.float16, "scales")
+    if qzeros is not None:
+        _dev(qzeros, torch.int32, "qzeros")
+    if g_idx is not None:
+        _dev(g_idx, torch.int32, "g_idx")
+    G, N = scales.shape
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.float16, device=qweight.device)
+    _dev(out, torch.float16, "out")
+    _check(lib().w8a16_dequant(qweight.data_ptr(), scales.data_ptr(), None if qzeros is None else qzeros.data_ptr(),
+                               None if g_idx is None else g_idx.data_ptr(), group_size, N, K,
+                               out.data_ptr(), _stream_handle(stream, qweight.device)))
+    return out

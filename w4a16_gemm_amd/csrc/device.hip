@@ -59,16 +59,13 @@ int check_device_args(const void* const* ptrs, int nptrs, int N, int K, int grou
 
 // Optional (W4A16_DEBUG_CHECKS=1) check of a device-resident g_idx against the order
 // stored in the weight buffer.  Synchronous.
-int debug_check_gidx(const int32_t* g_idx, const int32_t* qweight, int N, int K, int group_size,
-                     hipStream_t stream) {
+int debug_check_gidx(const int32_t* g_idx, const int32_t* tail_dev, int K, int group_size, hipStream_t stream) {
   if (env_int("W4A16_DEBUG_CHECKS", 0) == 0) return W4A16_OK;
   if (int st = hip_status(hipStreamSynchronize(stream), "hipStreamSynchronize")) return st;
   std::vector<int32_t> h(K), tail(K), perm(K);
   if (int st = hip_status(hipMemcpy(h.data(), g_idx, sizeof(int32_t) * K, hipMemcpyDeviceToHost), "hipMemcpy"))
     return st;
-  if (int st = hip_status(hipMemcpy(tail.data(), qweight + qweight_words(N, K, false),
-                                    sizeof(int32_t) * K, hipMemcpyDeviceToHost),
-                          "hipMemcpy"))
+  if (int st = hip_status(hipMemcpy(tail.data(), tail_dev, sizeof(int32_t) * K, hipMemcpyDeviceToHost), "hipMemcpy"))
     return st;
   if (int st = check_gidx_and_sort(h.data(), K, group_size, perm.data())) return st;
   for (int p = 0; p < K; ++p)
@@ -89,12 +86,11 @@ struct GemvShape {
   int wpr = 1;  // wavefronts per row: slices of a long row
 };
 
-// Lanes per row, chunks per lane and slices for K/32 chunks per row.  Up to 256
-// chunks (K <= 8192): an exact split with the widest rows first, else the widest
+// Lanes per row, chunks per lane and slices for C 16-byte chunks per row (K / 32 at
+// 4 bits, K / 16 at 8 bits).  Up to 256 chunks (K <= 8192 at 4 bits): an exact split with the widest rows first, else the widest
 // split, at most 4 chunks per lane (more spill the activations out of registers).
 // Longer rows: one wavefront per slice, 2, 4 or 8 slices of at most 256 chunks.
-GemvShape pick_gemv_shape(int K) {
-  const int C = K / 32;
+GemvShape pick_gemv_shape(int C) {
   if (C <= 256) {
     for (int lpr : {64, 32, 16, 8})
       if (C % lpr == 0 && C / lpr <= 4) return {lpr, C / lpr, true, 1};
@@ -123,10 +119,10 @@ int device_cus() {
 // Register-pipeline depth: about 8 KB of codes in flight per wavefront.
 constexpr int gemv_depth(int cpl) { return cpl >= 3 ? 2 : 8 / cpl; }
 
-template <int LPR, int CPL, bool EXACT, bool ACT, int EPT, int WPR>
+template <int LPR, int CPL, bool EXACT, bool ACT, int EPT, int WPR, int BITS>
 void launch_gemv_e(dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
                    const uint16_t* s, Zeros z, half_t* y, int N, int K, int gshift, int steps) {
-  auto kern = gemv_m1_kernel<LPR, CPL, kGemvWaves, gemv_depth(CPL), EXACT, ACT, EPT, WPR>;
+  auto kern = gemv_m1_kernel<LPR, CPL, kGemvWaves, gemv_depth(CPL), EXACT, ACT, EPT, WPR, BITS>;
   // Dynamic LDS above 64 KB has to be allowed per kernel (once per process).
   static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -138,51 +134,52 @@ void launch_gemv_e(dim3 grid, size_t shmem, hipStream_t st, const half_t* x, con
 // Staging rows per thread: one row (EPT = 1) is compiled only for exact splits
 // without act order, the decode shapes of large layers; everything else stages
 // whole 8-row items.
-template <int LPR, int CPL, bool EXACT, bool ACT>
+template <int LPR, int CPL, bool EXACT, bool ACT, int BITS>
 void launch_gemv_t(int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
                    const uint16_t* s, Zeros z, half_t* y, int N, int K, int gshift, int steps) {
   if constexpr (EXACT && !ACT)
-    if (ept == 1) return launch_gemv_e<LPR, CPL, EXACT, ACT, 1, 1>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
-  launch_gemv_e<LPR, CPL, EXACT, ACT, 8, 1>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+    if (ept == 1)
+      return launch_gemv_e<LPR, CPL, EXACT, ACT, 1, 1, BITS>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+  launch_gemv_e<LPR, CPL, EXACT, ACT, 8, 1, BITS>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
 }
 
-template <int LPR, bool EXACT, bool ACT>
+template <int LPR, bool EXACT, bool ACT, int BITS>
 void launch_gemv_cpl(int cpl, int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
                      const uint16_t* s, Zeros z, half_t* y, int N, int K, int gshift, int steps) {
   switch (cpl) {
-    case 1: launch_gemv_t<LPR, 1, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 2: launch_gemv_t<LPR, 2, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 3: launch_gemv_t<LPR, 3, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    default: launch_gemv_t<LPR, 4, EXACT, ACT>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 1: launch_gemv_t<LPR, 1, EXACT, ACT, BITS>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 2: launch_gemv_t<LPR, 2, EXACT, ACT, BITS>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 3: launch_gemv_t<LPR, 3, EXACT, ACT, BITS>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    default: launch_gemv_t<LPR, 4, EXACT, ACT, BITS>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
   }
 }
 
 // Split rows (K > 8192): 64 lanes per row slice, 3 or 4 chunks per lane, whole 8-row
 // staging items (a row has more than 64 groups).
-template <int WPR, bool EXACT, bool ACT>
+template <int WPR, bool EXACT, bool ACT, int BITS>
 void launch_gemv_split(int cpl, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
                        const uint16_t* s, Zeros z, half_t* y, int N, int K, int gshift, int steps) {
-  if (cpl == 3) launch_gemv_e<64, 3, EXACT, ACT, 8, WPR>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
-  else launch_gemv_e<64, 4, EXACT, ACT, 8, WPR>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+  if (cpl == 3) launch_gemv_e<64, 3, EXACT, ACT, 8, WPR, BITS>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+  else launch_gemv_e<64, 4, EXACT, ACT, 8, WPR, BITS>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
 }
 
-template <bool EXACT, bool ACT>
+template <bool EXACT, bool ACT, int BITS>
 void launch_gemv_lpr(const GemvShape& sh, int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x,
                      const uint32_t* qw, const uint16_t* s, Zeros z, half_t* y, int N, int K,
                      int gshift, int steps) {
   if (sh.wpr > 1) {
     switch (sh.wpr) {
-      case 2: launch_gemv_split<2, EXACT, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-      case 4: launch_gemv_split<4, EXACT, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-      default: launch_gemv_split<8, EXACT, ACT>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+      case 2: launch_gemv_split<2, EXACT, ACT, BITS>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+      case 4: launch_gemv_split<4, EXACT, ACT, BITS>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+      default: launch_gemv_split<8, EXACT, ACT, BITS>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
     }
     return;
   }
   switch (sh.lpr) {
-    case 64: launch_gemv_cpl<64, EXACT, ACT>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 32: launch_gemv_cpl<32, EXACT, ACT>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 16: launch_gemv_cpl<16, EXACT, ACT>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    default: launch_gemv_cpl<8, EXACT, ACT>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 64: launch_gemv_cpl<64, EXACT, ACT, BITS>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 32: launch_gemv_cpl<32, EXACT, ACT, BITS>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 16: launch_gemv_cpl<16, EXACT, ACT, BITS>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    default: launch_gemv_cpl<8, EXACT, ACT, BITS>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
   }
 }
 
@@ -202,16 +199,16 @@ struct GemvPlan {
   size_t shmem = 0;
 };
 
-GemvPlan plan_gemv(int N, int K, int gshift, bool act) {
+GemvPlan plan_gemv(int N, int K, int gshift, bool act, int bits = 4) {
   GemvPlan p;
-  p.sh = pick_gemv_shape(K);
+  const int C = K / (bits == 4 ? 32 : 16);   // 16-byte chunks per row
+  p.sh = pick_gemv_shape(C);
   if (p.sh.lpr == 0) return p;
   // measurements only: lanes per row forced (rows of at most 256 chunks)
   const int lpr = env_int("W4A16_TUNE_GEMV_LPR", 0);
-  const int C = K / 32;
   if (p.sh.wpr == 1 && (lpr == 8 || lpr == 16 || lpr == 32 || lpr == 64) && (C + lpr - 1) / lpr <= 4)
     p.sh = {lpr, (C + lpr - 1) / lpr, C % lpr == 0, 1};
-  if (static_cast<long long>(N) * K / 2 >= (1LL << 31)) return p;   // 32-bit byte offsets into the codes
+  if (static_cast<long long>(N) * K * bits / 8 >= (1LL << 31)) return p;   // 32-bit byte offsets into the codes
   const int G = groups_in(0, K, gshift);
   const int unit = kGemvWaves * (64 / p.sh.lpr);                    // rows per unit
   if ((unit / 8) * G > kGemvWaves * 64) return p;                   // one staging item per thread and step
@@ -230,26 +227,42 @@ GemvPlan plan_gemv(int N, int K, int gshift, bool act) {
   return p;
 }
 
+template <int BITS = 4>
 int run_gemv(const GemvPlan& p, bool act, const half_t* x, const uint32_t* qw, const uint16_t* s,
              Zeros z, half_t* y, int N, int K, int gshift, hipStream_t st) {
   const dim3 grid(p.blocks);
   if (p.sh.exact) {
-    if (act) launch_gemv_lpr<true, true>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
-    else launch_gemv_lpr<true, false>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
+    if (act) launch_gemv_lpr<true, true, BITS>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
+    else launch_gemv_lpr<true, false, BITS>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
   } else {
-    if (act) launch_gemv_lpr<false, true>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
-    else launch_gemv_lpr<false, false>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
+    if (act) launch_gemv_lpr<false, true, BITS>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
+    else launch_gemv_lpr<false, false, BITS>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
   }
   return check_launch("gemv launch");
 }
 
 // --- GEMM (M > 1) ---------------------------------------------------------------
 
-template <int BM>
+template <int BM, int BITS = 4>
 void launch_gemm_bm(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, Zeros z,
                     half_t* y, int M, int N, int K, int gshift) {
   const dim3 grid((N + 255) / 256, (M + BM - 1) / BM);
-  hipLaunchKernelGGL((gemm_mfma_kernel<BM>), grid, dim3(256), 0, st, x, qw, s, z, y, M, N, K, gshift);
+  hipLaunchKernelGGL((gemm_mfma_kernel<BM, BITS>), grid, dim3(256), 0, st, x, qw, s, z, y, M, N, K, gshift);
+}
+
+// The tiled MFMA kernel with the row-block height for M.
+template <int BITS>
+int run_gemm_tiled(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, Zeros z, half_t* y,
+                   int M, int N, int K, int gshift) {
+  if (M <= 16)
+    launch_gemm_bm<16, BITS>(st, x, qw, s, z, y, M, N, K, gshift);
+  else if (M <= 32)
+    launch_gemm_bm<32, BITS>(st, x, qw, s, z, y, M, N, K, gshift);
+  else if (M <= 64)
+    launch_gemm_bm<64, BITS>(st, x, qw, s, z, y, M, N, K, gshift);
+  else
+    launch_gemm_bm<128, BITS>(st, x, qw, s, z, y, M, N, K, gshift);
+  return check_launch("gemm launch");
 }
 
 // Skinny-batch kernel shape: W wavefronts of T 128-channel steps (K = 128 T W), SE
@@ -416,15 +429,7 @@ int run_gemm(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* 
       static_cast<long long>(M) * K < (1LL << 31) &&
       env_int("W4A16_TUNE_GEMM_BIG", 1) != 0)
     return run_gemm_big(st, x, qw, s, z, y, M, N, K, gshift);
-  if (M <= 16)
-    launch_gemm_bm<16>(st, x, qw, s, z, y, M, N, K, gshift);
-  else if (M <= 32)
-    launch_gemm_bm<32>(st, x, qw, s, z, y, M, N, K, gshift);
-  else if (M <= 64)
-    launch_gemm_bm<64>(st, x, qw, s, z, y, M, N, K, gshift);
-  else
-    launch_gemm_bm<128>(st, x, qw, s, z, y, M, N, K, gshift);
-  return check_launch("gemm launch");
+  return run_gemm_tiled<4>(st, x, qw, s, z, y, M, N, K, gshift);
 }
 
 enum class Path { kAuto, kGemv, kGemm };
@@ -453,7 +458,7 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
   const bool act = g_idx != nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (act)
-    if (int s = debug_check_gidx(g_idx, qweight, N, K, group_size, st)) return s;
+    if (int s = debug_check_gidx(g_idx, qweight + qweight_words(N, K, false), K, group_size, st)) return s;
 
   const int gshift = log2_group(group_size);
   const auto* hx = reinterpret_cast<const half_t*>(x);
@@ -526,7 +531,7 @@ int w4a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t*
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool act = g_idx != nullptr;
   if (act)
-    if (int s = debug_check_gidx(g_idx, qweight, N, K, group_size, st)) return s;
+    if (int s = debug_check_gidx(g_idx, qweight + qweight_words(N, K, false), K, group_size, st)) return s;
   const size_t words = static_cast<size_t>(N) * (K / 8);
   const dim3 grid(static_cast<unsigned>((words + 255) / 256));
   const auto* hq = reinterpret_cast<const uint32_t*>(qweight);
@@ -538,6 +543,75 @@ int w4a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t*
     hipLaunchKernelGGL(dequant_kernel<true>, grid, dim3(256), 0, st, hq, hs, hz, hw, N, K, gshift);
   else
     hipLaunchKernelGGL(dequant_kernel<false>, grid, dim3(256), 0, st, hq, hs, hz, hw, N, K, gshift);
+  return check_launch("dequant launch");
+}
+
+// 8-bit weights ("AWQ + GPTQ Quantization, in depth", 4-bit bigger or 8-bit smaller):
+// M == 1 on the GEMV, larger M on the tiled MFMA kernel (the skinny-batch and
+// large-tile kernels are 4-bit only).
+int w8a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
+               const int32_t* g_idx, int group_size, int M, int N, int K, uint16_t* y, void* stream) {
+  clear_error();
+  if (M <= 0) return fail(W4A16_ERR_INVALID_ARG, "M must be positive (M=%d)", M);
+  const void* ptrs[] = {x, qweight, scales, y, qzeros};   // qzeros may be NULL: symmetric
+  if (int st = check_device_args(ptrs, qzeros ? 5 : 4, N, K, group_size)) return st;
+  const bool act = g_idx != nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (act)
+    if (int s = debug_check_gidx(g_idx, qweight + qweight8_words(N, K, false), K, group_size, st)) return s;
+  const int gshift = log2_group(group_size);
+  const auto* hx = reinterpret_cast<const half_t*>(x);
+  const auto* hq = reinterpret_cast<const uint32_t*>(qweight);
+  const auto* hs = reinterpret_cast<const half_t*>(scales);
+  const Zeros hz = layer_zeros(qzeros, scales);
+  auto* hy = reinterpret_cast<half_t*>(y);
+
+  const Path forced = forced_path();
+  const GemvPlan gp = M == 1 ? plan_gemv(N, K, gshift, act, 8) : GemvPlan{};
+  if (forced == Path::kGemv && !gp.ok)
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "the 8-bit GEMV path needs M == 1, K <= 32768, N*K < 2^31 and at most 512 groups per row "
+                "(M=%d N=%d K=%d group_size=%d)",
+                M, N, K, group_size);
+  if (gp.ok && forced != Path::kGemm)
+    return run_gemv<8>(gp, act, hx, hq, reinterpret_cast<const uint16_t*>(scales), hz, hy, N, K, gshift, st);
+  if (static_cast<long long>(M) * K >= (1LL << 31) || static_cast<long long>(N) * (K / 4) >= (1LL << 31))
+    return fail(W4A16_ERR_UNSUPPORTED, "8-bit layer too large for 32-bit element offsets (M=%d N=%d K=%d)", M, N, K);
+  if (!act) return run_gemm_tiled<8>(st, hx, hq, hs, hz, hy, M, N, K, gshift);
+
+  half_t* xs = nullptr;   // act order: x gathered into stored order (stream-ordered scratch)
+  const size_t bytes = static_cast<size_t>(M) * K * sizeof(half_t);
+  if (int s = hip_status(hipMallocAsync(reinterpret_cast<void**>(&xs), bytes, st), "hipMallocAsync")) return s;
+  const int32_t* perm = qweight + qweight8_words(N, K, false);
+  const size_t total = static_cast<size_t>(M) * K;
+  hipLaunchKernelGGL(gather_x_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, hx,
+                     perm, xs, M, K);
+  int rc = check_launch("gather launch");
+  if (rc == W4A16_OK) rc = run_gemm_tiled<8>(st, xs, hq, hs, hz, hy, M, N, K, gshift);
+  const int rf = hip_status(hipFreeAsync(xs, st), "hipFreeAsync");
+  return rc != W4A16_OK ? rc : rf;
+}
+
+int w8a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros, const int32_t* g_idx,
+                  int group_size, int N, int K, uint16_t* w_out, void* stream) {
+  clear_error();
+  const void* ptrs[] = {qweight, scales, w_out, qzeros};   // qzeros may be NULL: symmetric
+  if (int st = check_device_args(ptrs, qzeros ? 4 : 3, N, K, group_size)) return st;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool act = g_idx != nullptr;
+  if (act)
+    if (int s = debug_check_gidx(g_idx, qweight + qweight8_words(N, K, false), K, group_size, st)) return s;
+  const size_t words = static_cast<size_t>(N) * (K / 4);
+  const dim3 grid(static_cast<unsigned>((words + 255) / 256));
+  const auto* hq = reinterpret_cast<const uint32_t*>(qweight);
+  const auto* hs = reinterpret_cast<const half_t*>(scales);
+  const Zeros hz = layer_zeros(qzeros, scales);
+  auto* hw = reinterpret_cast<half_t*>(w_out);
+  const int gshift = log2_group(group_size);
+  if (act)
+    hipLaunchKernelGGL(dequant8_kernel<true>, grid, dim3(256), 0, st, hq, hs, hz, hw, N, K, gshift);
+  else
+    hipLaunchKernelGGL(dequant8_kernel<false>, grid, dim3(256), 0, st, hq, hs, hz, hw, N, K, gshift);
   return check_launch("dequant launch");
 }
 

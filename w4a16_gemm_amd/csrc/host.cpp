@@ -17,8 +17,9 @@ namespace {
 thread_local std::string t_last_error;
 
 constexpr int kLevels = 15;  // 16 grid points, "4 bits ... 16 levels"
-constexpr int kSymLevels = 7;    // symmetric grid -7 .. 7
-constexpr uint8_t kSymZero = 8;  // stored code of 0: the implicit zero point
+constexpr int kSymLevels = 7;    // symmetric grid -7 .. 7 (stored code of 0: 8)
+constexpr int kLevels8 = 255;    // 8-bit weights: 256 grid points
+constexpr int kSymLevels8 = 127; // symmetric 8-bit grid -127 .. 127 (stored code of 0: 128)
 
 // Exact binary16 -> binary64.
 double half_to_double(uint16_t h) {
@@ -79,6 +80,124 @@ int group_members(const int32_t* g_idx, int K, int group_size, std::vector<int32
     return W4A16_OK;
   }
   return check_gidx_and_sort(g_idx, K, group_size, order.data());
+}
+// Checks shared by the quantisers.
+int check_quantize_args(const uint16_t* w, int N, int K, int group_size, const int32_t* g_idx,
+                        const double* in_scale, std::vector<int32_t>& order) {
+  if (int st = check_shape(N, K, group_size)) return st;
+  if (int st = group_members(g_idx, K, group_size, order)) return st;
+  if (in_scale)
+    for (int k = 0; k < K; ++k)
+      if (!(in_scale[k] > 0.0) || !std::isfinite(in_scale[k]))
+        return fail(W4A16_ERR_INVALID_ARG, "in_scale[%d] is not a positive finite number", k);
+  const size_t nk = static_cast<size_t>(N) * K;
+  for (size_t i = 0; i < nk; ++i)
+    if (!half_is_finite(w[i])) return fail(W4A16_ERR_INVALID_ARG, "weight %zu is not finite", i);
+  return W4A16_OK;
+}
+
+// Row n of the weights, times the per-input-channel factor if any, in binary64.
+void load_row(const uint16_t* w, int K, int n, const double* in_scale, std::vector<double>& row) {
+  for (int k = 0; k < K; ++k) {
+    const double v = half_to_double(w[static_cast<size_t>(n) * K + k]);
+    row[k] = in_scale ? v * in_scale[k] : v;
+  }
+}
+
+// The stored channel order of a weight buffer: its act-order tail, checked to be a
+// permutation that agrees with g_idx, or the identity.
+int stored_order(const int32_t* tail, const int32_t* g_idx, int K, int group_size, std::vector<int32_t>& perm) {
+  if (!g_idx) {
+    for (int p = 0; p < K; ++p) perm[p] = p;
+    return W4A16_OK;
+  }
+  std::vector<char> seen(K, 0);
+  for (int p = 0; p < K; ++p) {
+    const int32_t k = tail[p];
+    if (k < 0 || k >= K || seen[k])
+      return fail(W4A16_ERR_BAD_GIDX, "stored order is not a permutation at position %d", p);
+    seen[k] = 1;
+    if (g_idx[k] != p / group_size)
+      return fail(W4A16_ERR_BAD_GIDX, "stored order disagrees with g_idx at position %d", p);
+    perm[p] = k;
+  }
+  return W4A16_OK;
+}
+
+// Asymmetric round-to-nearest on the grid 0 .. levels (15 or 255).
+int quantize_asym(const uint16_t* w, int N, int K, int group_size, const int32_t* g_idx, const double* in_scale,
+                  int levels, uint8_t* codes, uint16_t* scales, uint8_t* zeros) {
+  if (!w || !codes || !scales || !zeros) return fail(W4A16_ERR_INVALID_ARG, "NULL buffer");
+  std::vector<int32_t> order;
+  if (int st = check_quantize_args(w, N, K, group_size, g_idx, in_scale, order)) return st;
+  const int G = K / group_size;
+  const double L = static_cast<double>(levels);
+  std::vector<double> row(K);
+  for (int n = 0; n < N; ++n) {
+    load_row(w, K, n, in_scale, row);
+    for (int g = 0; g < G; ++g) {
+      const int32_t* members = order.data() + static_cast<size_t>(g) * group_size;
+      double lo = 0.0, hi = 0.0;
+      for (int i = 0; i < group_size; ++i) {
+        lo = std::min(lo, row[members[i]]);
+        hi = std::max(hi, row[members[i]]);
+      }
+      uint8_t* qrow = codes + static_cast<size_t>(n) * K;
+      const size_t gi = static_cast<size_t>(g) * N + n;
+      if (hi == lo) {  // all-zero group
+        scales[gi] = 0x3C00;  // 1.0
+        zeros[gi] = 0;
+        for (int i = 0; i < group_size; ++i) qrow[members[i]] = 0;
+        continue;
+      }
+      const uint16_t sbits = half_ceil((hi - lo) / L);
+      const double S = half_to_double(sbits);
+      const double Z = std::min(std::max(std::nearbyint(-lo / S), 0.0), L);
+      scales[gi] = sbits;
+      zeros[gi] = static_cast<uint8_t>(Z);
+      for (int i = 0; i < group_size; ++i) {
+        const double q = std::nearbyint(row[members[i]] / S) + Z;
+        qrow[members[i]] = static_cast<uint8_t>(std::min(std::max(q, 0.0), L));
+      }
+    }
+  }
+  return W4A16_OK;
+}
+
+// Symmetric round-to-nearest on the grid -levels .. levels (7 or 127), stored as
+// code = q + levels + 1.
+int quantize_sym(const uint16_t* w, int N, int K, int group_size, const int32_t* g_idx, const double* in_scale,
+                 int levels, uint8_t* codes, uint16_t* scales) {
+  if (!w || !codes || !scales) return fail(W4A16_ERR_INVALID_ARG, "NULL buffer");
+  std::vector<int32_t> order;
+  if (int st = check_quantize_args(w, N, K, group_size, g_idx, in_scale, order)) return st;
+  const int G = K / group_size;
+  const double L = static_cast<double>(levels);
+  const uint8_t zero = static_cast<uint8_t>(levels + 1);
+  std::vector<double> row(K);
+  for (int n = 0; n < N; ++n) {
+    load_row(w, K, n, in_scale, row);
+    for (int g = 0; g < G; ++g) {
+      const int32_t* members = order.data() + static_cast<size_t>(g) * group_size;
+      double a = 0.0;
+      for (int i = 0; i < group_size; ++i) a = std::max(a, std::fabs(row[members[i]]));
+      uint8_t* qrow = codes + static_cast<size_t>(n) * K;
+      const size_t gi = static_cast<size_t>(g) * N + n;
+      if (a == 0.0) {  // all-zero group: S = 1, every code the zero
+        scales[gi] = 0x3C00;
+        for (int i = 0; i < group_size; ++i) qrow[members[i]] = zero;
+        continue;
+      }
+      const uint16_t sbits = half_ceil(a / L);
+      const double S = half_to_double(sbits);
+      scales[gi] = sbits;
+      for (int i = 0; i < group_size; ++i) {
+        const double q = std::min(std::max(std::nearbyint(row[members[i]] / S), -L), L);
+        qrow[members[i]] = static_cast<uint8_t>(q + zero);
+      }
+    }
+  }
+  return W4A16_OK;
 }
 }  // namespace
 
@@ -172,27 +291,81 @@ int w4a16_unpack(const int32_t* qweight, const int32_t* g_idx, int group_size, i
   if (int st = check_shape(N, K, group_size)) return st;
   const int W = K / 8;
   std::vector<int32_t> perm(K);
-  if (g_idx) {
-    const int32_t* tail = qweight + static_cast<size_t>(N) * W;
-    std::vector<char> seen(K, 0);
-    for (int p = 0; p < K; ++p) {
-      const int32_t k = tail[p];
-      if (k < 0 || k >= K || seen[k])
-        return fail(W4A16_ERR_BAD_GIDX, "stored order is not a permutation at position %d", p);
-      seen[k] = 1;
-      if (g_idx[k] != p / group_size)
-        return fail(W4A16_ERR_BAD_GIDX, "stored order disagrees with g_idx at position %d", p);
-      perm[p] = k;
-    }
-  } else {
-    for (int p = 0; p < K; ++p) perm[p] = p;
-  }
+  if (int st = stored_order(qweight + static_cast<size_t>(N) * W, g_idx, K, group_size, perm)) return st;
   for (int n = 0; n < N; ++n) {
     const uint32_t* in = reinterpret_cast<const uint32_t*>(qweight) + static_cast<size_t>(n) * W;
     uint8_t* row = codes + static_cast<size_t>(n) * K;
     for (int w = 0; w < W; ++w)
       for (int e = 0; e < 8; ++e) row[perm[8 * w + e]] = (in[w] >> (4 * kNibbleOf[e])) & 0xF;
   }
+  return W4A16_OK;
+}
+
+size_t w8a16_qweight_words(int N, int K, int act_order) {
+  if (N <= 0 || K <= 0 || K % 8 != 0) return 0;
+  return qweight8_words(N, K, act_order != 0);
+}
+
+int w8a16_pack(const uint8_t* codes, const int32_t* g_idx, int group_size, int N, int K, int32_t* qweight) {
+  clear_error();
+  if (!codes || !qweight) return fail(W4A16_ERR_INVALID_ARG, "NULL buffer");
+  if (int st = check_shape(N, K, group_size)) return st;
+  std::vector<int32_t> perm;
+  if (int st = group_members(g_idx, K, group_size, perm)) return st;
+  const int W = K / 4;
+  for (int n = 0; n < N; ++n) {
+    const uint8_t* row = codes + static_cast<size_t>(n) * K;
+    uint32_t* out = reinterpret_cast<uint32_t*>(qweight) + static_cast<size_t>(n) * W;
+    for (int w = 0; w < W; ++w) {
+      uint32_t word = 0;
+      for (int e = 0; e < 4; ++e) word |= static_cast<uint32_t>(row[perm[4 * w + e]]) << (8 * kByteOf[e]);
+      out[w] = word;
+    }
+  }
+  if (g_idx)
+    for (int p = 0; p < K; ++p) qweight[static_cast<size_t>(N) * W + p] = perm[p];
+  return W4A16_OK;
+}
+
+int w8a16_unpack(const int32_t* qweight, const int32_t* g_idx, int group_size, int N, int K, uint8_t* codes) {
+  clear_error();
+  if (!codes || !qweight) return fail(W4A16_ERR_INVALID_ARG, "NULL buffer");
+  if (int st = check_shape(N, K, group_size)) return st;
+  const int W = K / 4;
+  std::vector<int32_t> perm(K);
+  if (int st = stored_order(qweight + static_cast<size_t>(N) * W, g_idx, K, group_size, perm)) return st;
+  for (int n = 0; n < N; ++n) {
+    const uint32_t* in = reinterpret_cast<const uint32_t*>(qweight) + static_cast<size_t>(n) * W;
+    uint8_t* row = codes + static_cast<size_t>(n) * K;
+    for (int w = 0; w < W; ++w)
+      for (int e = 0; e < 4; ++e) row[perm[4 * w + e]] = (in[w] >> (8 * kByteOf[e])) & 0xFF;
+  }
+  return W4A16_OK;
+}
+
+int w8a16_pack_zeros(const uint8_t* zeros, int G, int N, int32_t* qzeros) {
+  clear_error();
+  if (!zeros || !qzeros) return fail(W4A16_ERR_INVALID_ARG, "NULL buffer");
+  if (G <= 0 || N <= 0 || N % 8 != 0)
+    return fail(W4A16_ERR_INVALID_ARG, "bad zero-point shape G=%d N=%d", G, N);
+  for (int g = 0; g < G; ++g)
+    for (int w = 0; w < N / 4; ++w) {
+      uint32_t word = 0;
+      for (int j = 0; j < 4; ++j) word |= static_cast<uint32_t>(zeros[static_cast<size_t>(g) * N + 4 * w + j]) << (8 * j);
+      qzeros[static_cast<size_t>(g) * (N / 4) + w] = static_cast<int32_t>(word);
+    }
+  return W4A16_OK;
+}
+
+int w8a16_unpack_zeros(const int32_t* qzeros, int G, int N, uint8_t* zeros) {
+  clear_error();
+  if (!zeros || !qzeros) return fail(W4A16_ERR_INVALID_ARG, "NULL buffer");
+  if (G <= 0 || N <= 0 || N % 8 != 0)
+    return fail(W4A16_ERR_INVALID_ARG, "bad zero-point shape G=%d N=%d", G, N);
+  for (int g = 0; g < G; ++g)
+    for (int n = 0; n < N; ++n)
+      zeros[static_cast<size_t>(g) * N + n] =
+          (static_cast<uint32_t>(qzeros[static_cast<size_t>(g) * (N / 4) + n / 4]) >> (8 * (n % 4))) & 0xFF;
   return W4A16_OK;
 }
 
@@ -229,98 +402,25 @@ int w4a16_unpack_zeros(const int32_t* qzeros, int G, int N, uint8_t* zeros) {
 int w4a16_quantize(const uint16_t* w, int N, int K, int group_size, const int32_t* g_idx,
                    const double* in_scale, uint8_t* codes, uint16_t* scales, uint8_t* zeros) {
   clear_error();
-  if (!w || !codes || !scales || !zeros) return fail(W4A16_ERR_INVALID_ARG, "NULL buffer");
-  if (int st = check_shape(N, K, group_size)) return st;
-  std::vector<int32_t> order;
-  if (int st = group_members(g_idx, K, group_size, order)) return st;
-  if (in_scale)
-    for (int k = 0; k < K; ++k)
-      if (!(in_scale[k] > 0.0) || !std::isfinite(in_scale[k]))
-        return fail(W4A16_ERR_INVALID_ARG, "in_scale[%d] is not a positive finite number", k);
-  const size_t nk = static_cast<size_t>(N) * K;
-  for (size_t i = 0; i < nk; ++i)
-    if (!half_is_finite(w[i])) return fail(W4A16_ERR_INVALID_ARG, "weight %zu is not finite", i);
-
-  const int G = K / group_size;
-  std::vector<double> row(K);
-  for (int n = 0; n < N; ++n) {
-    for (int k = 0; k < K; ++k) {
-      const double v = half_to_double(w[static_cast<size_t>(n) * K + k]);
-      row[k] = in_scale ? v * in_scale[k] : v;
-    }
-    for (int g = 0; g < G; ++g) {
-      const int32_t* members = order.data() + static_cast<size_t>(g) * group_size;
-      double lo = 0.0, hi = 0.0;
-      for (int i = 0; i < group_size; ++i) {
-        lo = std::min(lo, row[members[i]]);
-        hi = std::max(hi, row[members[i]]);
-      }
-      uint8_t* qrow = codes + static_cast<size_t>(n) * K;
-      const size_t gi = static_cast<size_t>(g) * N + n;
-      if (hi == lo) {  // all-zero group
-        scales[gi] = 0x3C00;  // 1.0
-        zeros[gi] = 0;
-        for (int i = 0; i < group_size; ++i) qrow[members[i]] = 0;
-        continue;
-      }
-      const uint16_t sbits = half_ceil((hi - lo) / kLevels);
-      const double S = half_to_double(sbits);
-      const double Z = std::min(std::max(std::nearbyint(-lo / S), 0.0), static_cast<double>(kLevels));
-      scales[gi] = sbits;
-      zeros[gi] = static_cast<uint8_t>(Z);
-      for (int i = 0; i < group_size; ++i) {
-        const double q = std::nearbyint(row[members[i]] / S) + Z;
-        qrow[members[i]] = static_cast<uint8_t>(std::min(std::max(q, 0.0), static_cast<double>(kLevels)));
-      }
-    }
-  }
-  return W4A16_OK;
+  return quantize_asym(w, N, K, group_size, g_idx, in_scale, kLevels, codes, scales, zeros);
 }
 
 int w4a16_quantize_sym(const uint16_t* w, int N, int K, int group_size, const int32_t* g_idx,
                        const double* in_scale, uint8_t* codes, uint16_t* scales) {
   clear_error();
-  if (!w || !codes || !scales) return fail(W4A16_ERR_INVALID_ARG, "NULL buffer");
-  if (int st = check_shape(N, K, group_size)) return st;
-  std::vector<int32_t> order;
-  if (int st = group_members(g_idx, K, group_size, order)) return st;
-  if (in_scale)
-    for (int k = 0; k < K; ++k)
-      if (!(in_scale[k] > 0.0) || !std::isfinite(in_scale[k]))
-        return fail(W4A16_ERR_INVALID_ARG, "in_scale[%d] is not a positive finite number", k);
-  const size_t nk = static_cast<size_t>(N) * K;
-  for (size_t i = 0; i < nk; ++i)
-    if (!half_is_finite(w[i])) return fail(W4A16_ERR_INVALID_ARG, "weight %zu is not finite", i);
+  return quantize_sym(w, N, K, group_size, g_idx, in_scale, kSymLevels, codes, scales);
+}
 
-  const int G = K / group_size;
-  std::vector<double> row(K);
-  for (int n = 0; n < N; ++n) {
-    for (int k = 0; k < K; ++k) {
-      const double v = half_to_double(w[static_cast<size_t>(n) * K + k]);
-      row[k] = in_scale ? v * in_scale[k] : v;
-    }
-    for (int g = 0; g < G; ++g) {
-      const int32_t* members = order.data() + static_cast<size_t>(g) * group_size;
-      double a = 0.0;
-      for (int i = 0; i < group_size; ++i) a = std::max(a, std::fabs(row[members[i]]));
-      uint8_t* qrow = codes + static_cast<size_t>(n) * K;
-      const size_t gi = static_cast<size_t>(g) * N + n;
-      if (a == 0.0) {  // all-zero group: S = 1, every code 8
-        scales[gi] = 0x3C00;
-        for (int i = 0; i < group_size; ++i) qrow[members[i]] = kSymZero;
-        continue;
-      }
-      const uint16_t sbits = half_ceil(a / kSymLevels);
-      const double S = half_to_double(sbits);
-      scales[gi] = sbits;
-      for (int i = 0; i < group_size; ++i) {
-        const double q = std::min(std::max(std::nearbyint(row[members[i]] / S), -static_cast<double>(kSymLevels)),
-                                  static_cast<double>(kSymLevels));
-        qrow[members[i]] = static_cast<uint8_t>(q + kSymZero);
-      }
-    }
-  }
-  return W4A16_OK;
+int w8a16_quantize(const uint16_t* w, int N, int K, int group_size, const int32_t* g_idx,
+                   const double* in_scale, uint8_t* codes, uint16_t* scales, uint8_t* zeros) {
+  clear_error();
+  return quantize_asym(w, N, K, group_size, g_idx, in_scale, kLevels8, codes, scales, zeros);
+}
+
+int w8a16_quantize_sym(const uint16_t* w, int N, int K, int group_size, const int32_t* g_idx,
+                       const double* in_scale, uint8_t* codes, uint16_t* scales) {
+  clear_error();
+  return quantize_sym(w, N, K, group_size, g_idx, in_scale, kSymLevels8, codes, scales);
 }
 
 int w4a16_awq_scales(const uint16_t* xcal, int T, int K, double alpha, double* s) {

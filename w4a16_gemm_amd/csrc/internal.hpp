@@ -13,7 +13,8 @@ namespace w4a16 {
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 void clear_error();
 
-// M/N/K > 0, group_size in {32, 64, 128}, K % group_size == 0, N % 8 == 0.
+// N/K > 0, group_size in {32, 64, 128} or K, K % group_size == 0, K % 32 == 0,
+// N % 8 == 0.
 int check_shape(int N, int K, int group_size);
 
 // g_idx (host memory): every value in [0, G) and every group exactly group_size
@@ -33,6 +34,16 @@ constexpr int kNibbleOf[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 
 inline size_t qweight_words(int N, int K, bool act_order) {
   return static_cast<size_t>(N) * static_cast<size_t>(K / 8) + (act_order ? static_cast<size_t>(K) : 0);
+}
+
+// 8-bit weights: words [N][K/4], element e of a word (stored position 4w+e) in byte
+// kByteOf[e], so that masking with 0x00FF00FF (and the same after a shift by 8) gives
+// the pairs (e0,e1), (e2,e3) of consecutive input channels.  Same act-order tail.
+// Zero points [G][N/4]: byte j of word [g][n/4] is Z of (g, 4 (n/4) + j).
+constexpr int kByteOf[4] = {0, 2, 1, 3};
+
+inline size_t qweight8_words(int N, int K, bool act_order) {
+  return static_cast<size_t>(N) * static_cast<size_t>(K / 4) + (act_order ? static_cast<size_t>(K) : 0);
 }
 
 }  // namespace w4a16

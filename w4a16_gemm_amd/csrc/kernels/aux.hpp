@@ -34,6 +34,31 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint32_t* __restrict
   }
 }
 
+// 8-bit weights: w_out[n][k] = binary16((q - Z) * S) with dequant_word8, one thread per
+// packed word (four channels).
+template <bool ACT>
+__global__ __launch_bounds__(256) void dequant8_kernel(const uint32_t* __restrict__ qw,
+                                                      const half_t* __restrict__ scales, Zeros qzeros,
+                                                      half_t* __restrict__ w_out, int N, int K, int gshift) {
+  const int W = K >> 2;
+  const size_t idx = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= static_cast<size_t>(N) * W) return;
+  const int n = static_cast<int>(idx / W);
+  const int wd = static_cast<int>(idx % W);
+  const int p0 = wd * 4;
+  const int gi = p0 >> gshift;
+  const DequantConsts dc = make_consts(load_zero<8>(qzeros, gi, N, n), scales[static_cast<size_t>(gi) * N + n]);
+  const half4_t d = dequant_word8(qw[idx], dc);
+  half_t* row = w_out + static_cast<size_t>(n) * K;
+  if constexpr (!ACT) {
+    *reinterpret_cast<half4_t*>(row + p0) = d;
+  } else {
+    const int32_t* perm = reinterpret_cast<const int32_t*>(qw + static_cast<size_t>(N) * W);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) row[perm[p0 + e]] = d[e];
+  }
+}
+
 // Act order, M > 1: xs[m][p] = x[m][perm[p]], so that the GEMM sees every group as
 // a contiguous run of input channels.
 __global__ __launch_bounds__(256) void gather_x_kernel(const half_t* __restrict__ x,

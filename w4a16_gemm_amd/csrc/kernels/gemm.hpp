@@ -24,11 +24,15 @@
 
 namespace w4a16 {
 
-template <int BM>
+// BITS = 8: 8-bit weights (four per word, byte order 0, 2, 1, 3); a lane's 32 channels
+// are 32 bytes, and the s-th MFMA of the tile takes its words 2s and 2s + 1.
+template <int BM, int BITS = 4>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const half_t* __restrict__ scales,
     Zeros qzeros, half_t* __restrict__ y, int M, int N, int K, int gshift) {
   static_assert(BM % 16 == 0 && BM >= 16, "BM must be a multiple of 16");
+  static_assert(BITS == 4 || BITS == 8, "4- or 8-bit weights");
+  constexpr int NQ = BITS / 4;                    // 16-byte pieces of a lane's 32 channels
   constexpr int MB = BM / 16;                     // 16-row blocks per wavefront
   constexpr int ACH = BM * 16;                    // 16-byte activation chunks per K tile
   constexpr int APT = (ACH + 255) / 256;          // chunks per thread
@@ -41,7 +45,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
   const int lq = lane >> 4;  // which 32-channel quarter of the K tile
   const int m0 = blockIdx.y * BM;
   const int nw = blockIdx.x * 256 + wave * 64;
-  const int W = K >> 3;
+  const int W = K >> (BITS == 4 ? 3 : 2);         // words per row
   const int KT = (K + 127) >> 7;
 
   uint4 areg[APT];
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     }
   };
 
-  uint4 bw[4];
+  uint4 bw[4][NQ];
   half_t bs[4];
   uint32_t bz[4];
   auto load_b = [&](int t) {
@@ -78,10 +82,11 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int n = min(nw + 16 * nb + lr, N - 1);
-      bw[nb] = kin ? *reinterpret_cast<const uint4*>(qw + static_cast<size_t>(n) * W + (k >> 3))
-                   : uint4{0, 0, 0, 0};
+      const uint4* src = reinterpret_cast<const uint4*>(qw + static_cast<size_t>(n) * W + (k >> (BITS == 4 ? 3 : 2)));
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) bw[nb][q] = kin ? src[q] : uint4{0, 0, 0, 0};
       bs[nb] = scales[static_cast<size_t>(gi) * N + n];
-      bz[nb] = load_zero(qzeros, gi, N, n);
+      bz[nb] = load_zero<BITS>(qzeros, gi, N, n);
     }
   };
 
@@ -97,11 +102,12 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
   __syncthreads();
 
   for (int t = 0; t < KT; ++t) {
-    uint4 cw[4];
+    uint4 cw[4][NQ];
     DequantConsts dc[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      cw[nb] = bw[nb];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) cw[nb][q] = bw[nb][q];
       dc[nb] = make_consts(bz[nb], bs[nb]);
     }
     if (t + 1 < KT) {
@@ -114,8 +120,16 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
       half8_t bf[4];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        const uint32_t word = s == 0 ? cw[nb].x : s == 1 ? cw[nb].y : s == 2 ? cw[nb].z : cw[nb].w;
-        bf[nb] = dequant_word(word, dc[nb]);
+        if constexpr (BITS == 4) {
+          const uint4 c = cw[nb][0];
+          const uint32_t word = s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;
+          bf[nb] = dequant_word(word, dc[nb]);
+        } else {
+          const uint4 c = cw[nb][s >> 1];
+          const half4_t lo = dequant_word8((s & 1) ? c.z : c.x, dc[nb]);
+          const half4_t hi = dequant_word8((s & 1) ? c.w : c.y, dc[nb]);
+          bf[nb] = half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {

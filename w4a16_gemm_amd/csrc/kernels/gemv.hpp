@@ -82,7 +82,12 @@ __device__ __forceinline__ float lane_group_sum(float v) {
 // LDS: scale/zero ring 2 * STRIDE * (G + 1) float2, row results steps * STRIDE * WPR floats,
 // and under act order the gathered activations, K binary16.  Needs 8 OCT G / EPT <=
 // WAVES * 64 (at most one staging task per thread and step) and an even DEPTH.
-template <int LPR, int CPL, int WAVES, int DEPTH, bool EXACT, bool ACT, int EPT, int WPR>
+//
+// BITS = 8 (8-bit weights, four codes per word in the byte order 0, 2, 1, 3): a 16-byte
+// chunk is 16 channels, the pairs of a word are its bytes 0 and 2 and (after a shift by
+// 8) 1 and 3 as subnormals q * 2^-24 (q < 256 fits the mantissa), both accumulated
+// with weight 1, and the zero points are bytes.
+template <int LPR, int CPL, int WAVES, int DEPTH, bool EXACT, bool ACT, int EPT, int WPR, int BITS = 4>
 __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
     const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
     Zeros qzeros, half_t* __restrict__ y, int N, int K, int gshift, int steps) {
@@ -90,6 +95,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   static_assert(DEPTH % 2 == 0, "the ring slot of row t is t % 2, the unrolled slot index");
   static_assert(WPR == 1 || (LPR == 64 && WAVES % WPR == 0 && WPR % DEPTH == 0),
                 "split rows: one row per wavefront, whole register slots per step");
+  static_assert(BITS == 4 || BITS == 8, "4- or 8-bit weights");
+  constexpr int CSH = BITS == 4 ? 5 : 4;   // log2 channels per 16-byte chunk
+  constexpr int XQ = 1 << (CSH - 3);       // 16-byte pieces of activations per chunk
+  constexpr int XP = 4 * XQ;               // activation pairs per chunk
   constexpr int RPW = 64 / LPR;          // rows per wavefront per step
   constexpr int STRIDE = WAVES * RPW;    // rows per unit
   static_assert(STRIDE % 8 == 0, "a unit must cover whole 8-row groups of zero points");
@@ -102,10 +111,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   const int wave = tid >> 6;
   const int rr = lane / LPR;
   const int j = lane % LPR;
-  const int C = K >> 5;                  // 32-channel chunks per row
+  const int C = K >> CSH;                // 16-byte chunks per row
   const int CS = (C + WPR - 1) / WPR;    // chunks per slice
   const int h = WPR == 1 ? 0 : wave % WPR;   // this wavefront's slice
-  const int W = K >> 3;                  // words per row
+  const int W = K >> (BITS == 4 ? 3 : 2);  // words per row
   const int G = ((K - 1) >> gshift) + 1;  // groups per row (one per row when per-channel)
   const int GP = G + 1;                  // padded ring row (float2)
   const int nblk = gridDim.x;
@@ -129,7 +138,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
     const int local = j + LPR * i;
     chunk[i] = EXACT ? h * CS + local : min(h * CS + min(local, CS - 1), C - 1);
     live[i] = EXACT || (local < CS && h * CS + local < C);
-    gcol[i] = (chunk[i] << 5) >> gshift;
+    gcol[i] = (chunk[i] << CSH) >> gshift;
   }
 
   // Staging task of this thread: rows [8 o + r0, 8 o + r0 + EPT) of the unit, group g
@@ -143,15 +152,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   const int it_o = it_c / G;
   const int st_r0 = (ts_c % TPI) * EPT;
   using ScaleBits = std::conditional_t<EPT == 8, uint4, uint16_t>;
+  using ZeroBits = std::conditional_t<BITS == 4, uint32_t, uint2>;   // the zero points of 8 rows
   ScaleBits zs_s[2];
-  uint32_t zs_z[2];
+  ZeroBits zs_z[2];
   auto load_item = [&](int t, int set) {   // unconditional: rows and steps clamped
     const int n8 = min((blk + min(t, steps - 1) * nblk) * STRIDE + 8 * it_o, N - 8);
     if constexpr (EPT == 8)
       zs_s[set] = *reinterpret_cast<const uint4*>(scales + static_cast<size_t>(it_g) * N + n8);
     else
       zs_s[set] = scales[static_cast<size_t>(it_g) * N + n8 + st_r0];
-    zs_z[set] = *qzeros.at(static_cast<size_t>(it_g) * (N >> 3) + (n8 >> 3));
+    if constexpr (BITS == 4)
+      zs_z[set] = *qzeros.at(static_cast<size_t>(it_g) * (N >> 3) + (n8 >> 3));
+    else
+      zs_z[set] = *reinterpret_cast<const uint2*>(qzeros.at(static_cast<size_t>(it_g) * (N >> 2) + (n8 >> 2)));
   };
   auto put_item = [&](int set, int slot) {
     if (tid < tasks) {
@@ -166,7 +179,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
           bits = zs_s[set];
         }
         const float S = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(bits)));
-        const float Z = static_cast<float>((qzeros.word(zs_z[set]) >> (4 * (st_r0 + r))) & 0xFu);
+        float Z;
+        if constexpr (BITS == 4) {
+          Z = static_cast<float>((qzeros.word(zs_z[set]) >> (4 * (st_r0 + r))) & 0xFu);
+        } else {
+          const int zr = st_r0 + r;
+          const uint32_t zw = qzeros.word8(zr < 4 ? zs_z[set].x : zs_z[set].y);
+          Z = static_cast<float>((zw >> (8 * (zr & 3))) & 0xFFu);
+        }
         dst[r * GP] = make_float2(S * 16777216.0f, -Z * S);   // both exact in fp32
       }
     }
@@ -176,10 +196,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   // activations of this lane's chunks (without act order straight into registers;
   // under act order the stored channel order, 16 bytes per load, all at once), the
   // staging items of steps 0 and 1, then the first DEPTH rows of codes.
-  uint4 xv[CPL][4];
+  uint4 xv[CPL][XQ];
   // Under act order the stored order is read in 4-entry pieces, PPT per thread to
   // cover the whole row, PB of them in flight per round.
-  constexpr int PPT = (WPR * LPR * CPL + 63) / 64;
+  constexpr int PPT = (WPR * LPR * CPL * (1 << CSH) / 4 + NT - 1) / NT;
   constexpr int PB = PPT < 4 ? PPT : 4;
   const int4* perm4 = reinterpret_cast<const int4*>(qw + static_cast<size_t>(N) * W);
   int4 pv[PB];
@@ -187,7 +207,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) xv[i][q] = reinterpret_cast<const uint4*>(x)[4 * chunk[i] + q];
+      for (int q = 0; q < XQ; ++q) xv[i][q] = reinterpret_cast<const uint4*>(x)[XQ * chunk[i] + q];
   } else {
 #pragma unroll
     for (int u = 0; u < PB; ++u) pv[u] = perm4[min(tid + u * NT, (K >> 2) - 1)];
@@ -240,19 +260,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) xv[i][q] = reinterpret_cast<const uint4*>(xs)[4 * chunk[i] + q];
+      for (int q = 0; q < XQ; ++q) xv[i][q] = reinterpret_cast<const uint4*>(xs)[XQ * chunk[i] + q];
   }
 
   // 3. this lane's activations as pairs, and the per-chunk sums (dot2 with ones);
   // chunks past the end of the row (inexact split) contribute nothing.
-  half2_t xr[CPL][16];
+  half2_t xr[CPL][XP];
   float xsum[CPL];
   const half2_t ones = half2_t{static_cast<half_t>(1.0f), static_cast<half_t>(1.0f)};
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     float sx = 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < XQ; ++q) {
       const uint4 v = xv[i][q];
       xr[i][4 * q + 0] = live[i] ? as_h2(v.x) : half2_t{0, 0};
       xr[i][4 * q + 1] = live[i] ? as_h2(v.y) : half2_t{0, 0};
@@ -260,7 +280,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
       xr[i][4 * q + 3] = live[i] ? as_h2(v.w) : half2_t{0, 0};
     }
 #pragma unroll
-    for (int q = 0; q < 16; ++q) sx = __builtin_amdgcn_fdot2(xr[i][q], ones, sx, false);
+    for (int q = 0; q < XP; ++q) sx = __builtin_amdgcn_fdot2(xr[i][q], ones, sx, false);
     xsum[i] = sx;
   }
 
@@ -288,17 +308,22 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
         const uint32_t word = q == 0 ? w[i].x : q == 1 ? w[i].y : q == 2 ? w[i].z : w[i].w;
-        const SubPairs p = expand_word_subnormal(word);
-        aa[i] = __builtin_amdgcn_fdot2(as_h2(p.a0), xr[i][4 * q + 0], aa[i], false);
-        ab[i] = __builtin_amdgcn_fdot2(as_h2(p.b0), xr[i][4 * q + 1], ab[i], false);
-        aa[i] = __builtin_amdgcn_fdot2(as_h2(p.a1), xr[i][4 * q + 2], aa[i], false);
-        ab[i] = __builtin_amdgcn_fdot2(as_h2(p.b1), xr[i][4 * q + 3], ab[i], false);
+        if constexpr (BITS == 4) {
+          const SubPairs p = expand_word_subnormal(word);
+          aa[i] = __builtin_amdgcn_fdot2(as_h2(p.a0), xr[i][4 * q + 0], aa[i], false);
+          ab[i] = __builtin_amdgcn_fdot2(as_h2(p.b0), xr[i][4 * q + 1], ab[i], false);
+          aa[i] = __builtin_amdgcn_fdot2(as_h2(p.a1), xr[i][4 * q + 2], aa[i], false);
+          ab[i] = __builtin_amdgcn_fdot2(as_h2(p.b1), xr[i][4 * q + 3], ab[i], false);
+        } else {   // bytes 0, 2 and 1, 3: elements (e0, e1) and (e2, e3)
+          aa[i] = __builtin_amdgcn_fdot2(as_h2(word & 0x00FF00FFu), xr[i][2 * q + 0], aa[i], false);
+          ab[i] = __builtin_amdgcn_fdot2(as_h2((word >> 8) & 0x00FF00FFu), xr[i][2 * q + 1], ab[i], false);
+        }
       }
     }
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
-      const float tq = fmaf(ab[i], 0.0625f, aa[i]);  // 2^-24 * sum x q
+      const float tq = fmaf(ab[i], BITS == 4 ? 0.0625f : 1.0f, aa[i]);  // 2^-24 * sum x q
       acc = fmaf(tq, sc[i].x, acc);                  // + S * sum x q
       acc = fmaf(sc[i].y, xsum[i], acc);             // - Z * S * sum x
     }

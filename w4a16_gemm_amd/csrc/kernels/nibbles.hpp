@@ -26,6 +26,7 @@ namespace w4a16 {
 typedef _Float16 half_t;
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -135,6 +136,16 @@ __device__ __forceinline__ half8_t dequant_word(uint32_t w, const DequantConsts&
   return half8_t{d0.x, d0.y, d1.x, d1.y, d2.x, d2.y, d3.x, d3.y};
 }
 
+// 8-bit weights: four binary16 weights binary16((q_e - Z) * S), e = 0..3, of a word in
+// the private byte order (element e in byte 0, 2, 1, 3): OR-ing a byte pair into the
+// mantissas of 1024 gives (1024 + q) exactly, and (1024 + q) - (1024 + Z) = q - Z is
+// exact, so the product with S is the only rounding.
+__device__ __forceinline__ half4_t dequant_word8(uint32_t w, const DequantConsts& c) {
+  const half2_t d0 = (as_h2((w & 0x00FF00FFu) | 0x64006400u) + c.neg_1024_z) * c.scale;
+  const half2_t d1 = (as_h2(((w >> 8) & 0x00FF00FFu) | 0x64006400u) + c.neg_1024_z) * c.scale;
+  return half4_t{d0.x, d0.y, d1.x, d1.y};
+}
+
 // Workgroup -> position in a sweep over row units, so that the workgroups of one XCD
 // (dispatch is round-robin over the 8 XCDs) own neighbouring units: the streams of
 // one XCD's L2 then cover one contiguous stretch of the weights.
@@ -150,19 +161,29 @@ __device__ __forceinline__ int xcd_block(int bid, int nblk) {
 // then points at any readable word, every zero-point load of the kernels reads that one
 // word (so the loads keep their place in the wait counts but stay in the cache), and
 // the loaded words are replaced by kSymZeroWord.
+// 8-bit weights: packed words [G][N/4], Z of (g, n) in byte n % 4 of word [g][n / 4]
+// (so byte g N + n of the buffer); symmetric: every Z is 128.
 constexpr uint32_t kSymZeroWord = 0x88888888u;
+constexpr uint32_t kSymZeroWord8 = 0x80808080u;
 
 struct Zeros {
   const uint32_t* words;
   int sym;
   __device__ __forceinline__ const uint32_t* at(size_t idx) const { return words + (sym ? 0 : idx); }
   __device__ __forceinline__ uint32_t word(uint32_t loaded) const { return sym ? kSymZeroWord : loaded; }
+  __device__ __forceinline__ uint32_t word8(uint32_t loaded) const { return sym ? kSymZeroWord8 : loaded; }
 };
 
 // Zero point of (group gi, output n).
+template <int BITS = 4>
 __device__ __forceinline__ uint32_t load_zero(Zeros z, int gi, int N, int n) {
-  if (z.sym) return 8u;
-  return (z.words[static_cast<size_t>(gi) * (N >> 3) + (n >> 3)] >> ((n & 7) * 4)) & 0xFu;
+  if constexpr (BITS == 4) {
+    if (z.sym) return 8u;
+    return (z.words[static_cast<size_t>(gi) * (N >> 3) + (n >> 3)] >> ((n & 7) * 4)) & 0xFu;
+  } else {
+    if (z.sym) return 128u;
+    return (z.words[static_cast<size_t>(gi) * (N >> 2) + (n >> 2)] >> ((n & 3) * 8)) & 0xFFu;
+  }
 }
 
 }  // namespace w4a16

@@ -52,6 +52,7 @@ class LayerConfig:
     act_order: bool = False     # calibration-derived input-channel ordering (g_idx)
     note: str = ""
     sym: bool = False           # symmetric quantisation (no zero points)
+    bits: int = 4               # weight bits: 4 or 8
 
     @property
     def n_outliers(self) -> int:
@@ -90,6 +91,9 @@ CONFIGS = {
 VARIANTS = {
     "c3s": replace(CONFIGS["c3"], name="c3s", sym=True,
                    note="70B-class MLP up-projection, symmetric int4 (no zero points), decode"),
+    # the same layer with 8-bit weights ("in depth", 4-bit bigger or 8-bit smaller)
+    "c3w8": replace(CONFIGS["c3"], name="c3w8", bits=8,
+                    note="70B-class MLP up-projection, asymmetric 8-bit weights, decode"),
 }
 
 
@@ -101,12 +105,12 @@ def config(name: str) -> LayerConfig:
 def custom_config(name: str, cfg_id: int, K: int, N: int, group_size: int, *,
                   w_std: float = 0.02, outlier_frac: float = 0.005,
                   outlier_mult: float = 20.0, M_list=(1,), awq=False, act_order=False,
-                  sym=False) -> LayerConfig:
+                  sym=False, bits=4) -> LayerConfig:
     """A layer of arbitrary shape with the same distributions (used for small
     parity cases that span several tiles and a ragged tail)."""
     return LayerConfig(name, cfg_id, K=K, N=N, group_size=group_size, w_std=w_std,
                        outlier_frac=outlier_frac, outlier_mult=outlier_mult,
-                       M_list=tuple(M_list), awq=awq, act_order=act_order, sym=sym)
+                       M_list=tuple(M_list), awq=awq, act_order=act_order, sym=sym, bits=bits)
 
 
 def _rng(cfg: LayerConfig, stream: int, *sub: int) -> np.random.Generator:
