@@ -45,7 +45,7 @@ MAX_COPIES = 64
 METRIC = "W4A16 GEMV HBM GB/s (% of peak) at M=1; prefill GEMM TFLOP/s (% MFMA)"
 HEADLINE = ("c3", 1)
 SECONDARY = [("c1", 1), ("c2up", 1), ("c2down", 1), ("c3", 2), ("c3", 4), ("c3", 8), ("c3", 16),
-             ("c3s", 1), ("c4", 2048), ("c5", 1), ("c5", 512)]
+             ("c3s", 1), ("c3w8", 1), ("c3w8", 16), ("c4", 2048), ("c5", 1), ("c5", 512)]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = ["w4a16_gemm_amd/csrc/kernels/nibbles.hpp", "w4a16_gemm_amd/csrc/kernels/gemv.hpp",
                   "w4a16_gemm_amd/csrc/kernels/gemm.hpp", "w4a16_gemm_amd/csrc/kernels/skinny.hpp",
@@ -53,9 +53,9 @@ KERNEL_SOURCES = ["w4a16_gemm_amd/csrc/kernels/nibbles.hpp", "w4a16_gemm_amd/csr
 
 
 def algo_bytes(cfg: wl.LayerConfig, M: int) -> int:
-    N, K, G = cfg.N, cfg.K, cfg.G
-    zeros = 0 if cfg.sym else G * N // 2
-    return N * K // 2 + 2 * G * N + zeros + (4 * K if cfg.act_order else 0) + 2 * M * K + 2 * M * N
+    N, K, G, b = cfg.N, cfg.K, cfg.G, cfg.bits
+    zeros = 0 if cfg.sym else G * N * b // 8
+    return N * K * b // 8 + 2 * G * N + zeros + (4 * K if cfg.act_order else 0) + 2 * M * K + 2 * M * N
 
 
 def algo_flops(cfg: wl.LayerConfig, M: int) -> int:
@@ -88,19 +88,20 @@ def prepare_layer(cfg: wl.LayerConfig, M_max: int):
         X = wl.calibration(cfg)
         g_idx = w4.w4a16_act_order(X, g) if cfg.act_order else None
         s = w4.w4a16_awq_scales(X) if cfg.awq else None
+    eight = cfg.bits == 8
     if cfg.sym:
-        codes, S = w4.w4a16_quantize_sym(wl.weights(cfg), g, g_idx, s)
+        codes, S = (w4.w8a16_quantize_sym if eight else w4.w4a16_quantize_sym)(wl.weights(cfg), g, g_idx, s)
         Z = None
     else:
-        codes, S, Z = w4.w4a16_quantize(wl.weights(cfg), g, g_idx, s)
+        codes, S, Z = (w4.w8a16_quantize if eight else w4.w4a16_quantize)(wl.weights(cfg), g, g_idx, s)
     x = wl.activations(cfg, M_max)
     if s is not None:
         x = w4.w4a16_awq_fold_activations(x, s)
     return {
         "x": torch.from_numpy(x).to(dev),
-        "qweight": torch.from_numpy(w4.w4a16_pack(codes, g_idx, g)).to(dev),
+        "qweight": torch.from_numpy((w4.w8a16_pack if eight else w4.w4a16_pack)(codes, g_idx, g)).to(dev),
         "scales": torch.from_numpy(S).to(dev),
-        "qzeros": None if Z is None else torch.from_numpy(w4.w4a16_pack_zeros(Z)).to(dev),
+        "qzeros": None if Z is None else torch.from_numpy((w4.w8a16_pack_zeros if eight else w4.w4a16_pack_zeros)(Z)).to(dev),
         "g_idx": None if g_idx is None else torch.from_numpy(g_idx).to(dev),
     }
 
@@ -123,8 +124,10 @@ def time_layer(cfg: wl.LayerConfig, M: int, layer, steps: int, warmup: int):
     args = [(x.data_ptr(), q.data_ptr(), s.data_ptr(), None if z is None else z.data_ptr(), gptr, cfg.group_size,
              M, cfg.N, cfg.K, y.data_ptr(), stream.cuda_stream) for q, s, z in pool]
 
+    gemm = lib.w8a16_gemm if cfg.bits == 8 else lib.w4a16_gemm
+
     def launch(i):
-        rc = lib.w4a16_gemm(*args[i % len(args)])
+        rc = gemm(*args[i % len(args)])
         if rc != 0:
             raise RuntimeError(f"w4a16_gemm failed ({rc}): {lib.w4a16_last_error().decode()}")
 
@@ -169,7 +172,7 @@ def summarize(cfg, M, t):
     f = algo_flops(cfg, M)
     out = {
         "workload": f"{cfg.name}: {cfg.note}", "M": M, "N": cfg.N, "K": cfg.K, "group": cfg.group_size,
-        "act_order": cfg.act_order, "awq": cfg.awq, "sym": cfg.sym,
+        "act_order": cfg.act_order, "awq": cfg.awq, "sym": cfg.sym, "bits": cfg.bits,
         "us_per_layer": round(ur, 3),
         "event_pair_us_mean": round(us, 3), "event_pair_us_median": round(t["kernel_us_median"], 3),
         "region_us_per_step": round(ur, 3),
