@@ -22,6 +22,8 @@ What it computes, in plain numpy float64 (slow and obviously correct):
                      the AWQ per-input-channel scale s = mean|X|^alpha and its
                      fold W*diag(s), x*diag(1/s) ("AWQ + GPTQ Quantization, in
                      depth", The two algorithms, compactly).
+* ``awq_search``     the AWQ grid search over alpha: loss of every alpha on the
+                     calibration activations, best alpha (same page and section).
 * ``act_order``      GPTQ act-order group assignment g_idx from the calibration
                      activations (same page and section).
 * ``pack_codes`` / ``unpack_codes`` / ``pack_zeros`` / ``unpack_zeros``
@@ -45,6 +47,7 @@ from .quant import (round_half_even, fp16_ceil, group_index, rtn_quantize,
                     rtn_quantize_sym, sym_zeros,
                     awq_scales, awq_fold_weights, awq_fold_activations,
                     act_order_h, act_order)
+from .awq_search import awq_search
 from .packing import (pack_codes, unpack_codes, pack_zeros, unpack_zeros,
                       sorted_k_order, pack_codes_act_order,
                       pack_codes8, unpack_codes8, pack_zeros8, unpack_zeros8)
