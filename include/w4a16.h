@@ -196,6 +196,21 @@ int w4a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t*
                   const int32_t* g_idx, int group_size, int N, int K, uint16_t* w_out,
                   void* stream);
 
+/* AWQ scale search ("AWQ + GPTQ Quantization, in depth", The two algorithms,
+ * compactly: s = (mean over tokens of |X|) ** alpha for alpha on a grid in [0, 1], loss
+ * = norm(W X - Wq X), keep the best).  For every alphas[i]: s = w4a16_awq_scales(xcal,
+ * alpha), the layer quantised with w4a16_quantize(w, in_scale = s), and
+ *   losses[i] = || xcal W^T - binary16(xcal / s) W^_alpha^T ||_F
+ * over the T calibration rows, with the reference product on binary16 weights and the
+ * candidate on w4a16_gemm (both on the device, fp32 accumulation, binary16 outputs),
+ * squared differences summed in fp32 per workgroup and in binary64 in a fixed order.
+ * *best = the first index of the smallest loss.  Host inputs w binary16 [N][K], xcal
+ * binary16 [T][K]; device memory is allocated for the call and freed before it returns;
+ * the work runs on `stream` and the call returns when the losses are on the host.
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+int w4a16_awq_search(const uint16_t* w, const uint16_t* xcal, int N, int K, int T, int group_size,
+                     const double* alphas, int n_alpha, double* losses, int* best, void* stream);
+
 /* ---------------------------------------------------------------------------------
  * 8-bit weights (W8A16): the same layer with 256-level codes ("AWQ + GPTQ
  * Quantization, in depth", 4-bit bigger or 8-bit smaller).  Same conventions,

@@ -40,6 +40,8 @@ _SIGNATURES = {
                             _c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
     "w4a16_dequant": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                _c_int, _c_void_p, _c_void_p]),
+    "w4a16_awq_search": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p,
+                                  _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "w8a16_qweight_words": (ctypes.c_size_t, [_c_int, _c_int, _c_int]),
     "w8a16_quantize": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
                                 _c_void_p, _c_void_p, _c_void_p]),
@@ -379,3 +381,22 @@ def w8a16_dequant(qweight, scales, qzeros, g_idx, group_size: int, K: int, out=N
                                None if g_idx is None else g_idx.data_ptr(), group_size, N, K,
                                out.data_ptr(), _stream_handle(stream, qweight.device)))
     return out
+
+
+def w4a16_awq_search(w, xcal, group_size: int, alphas, stream=None):
+    """AWQ alpha search on the device: (losses float64 [len(alphas)], best index).
+    w binary16 [N][K] and xcal binary16 [T][K] on the host."""
+    import torch
+    w = _np(w, np.float16, 2)
+    X = _np(xcal, np.float16, 2)
+    N, K = w.shape
+    T = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError("xcal must have K columns")
+    a = _np(alphas, np.float64, 1)
+    losses = np.empty(a.size, np.float64)
+    best = ctypes.c_int(-1)
+    _check(lib().w4a16_awq_search(_ptr(w), _ptr(X), N, K, T, group_size, _ptr(a), a.size, _ptr(losses),
+                                  ctypes.addressof(best), _stream_handle(stream, torch.device("cuda:0"))))
+    return losses, best.value
+

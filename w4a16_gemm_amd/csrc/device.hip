@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <vector>
@@ -613,6 +614,91 @@ int w8a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t*
   else
     hipLaunchKernelGGL(dequant8_kernel<false>, grid, dim3(256), 0, st, hq, hs, hz, hw, N, K, gshift);
   return check_launch("dequant launch");
+}
+
+// AWQ alpha search: the W4A16 GEMM of every candidate against the binary16 product of
+// the unquantised layer, on the calibration activations.  Host inputs, device work on
+// `stream`, returns when the losses are on the host.
+int w4a16_awq_search(const uint16_t* w, const uint16_t* xcal, int N, int K, int T, int group_size,
+                     const double* alphas, int n_alpha, double* losses, int* best, void* stream) {
+  clear_error();
+  if (!w || !xcal || !alphas || !losses || !best) return fail(W4A16_ERR_INVALID_ARG, "NULL buffer");
+  if (T <= 0 || n_alpha <= 0) return fail(W4A16_ERR_INVALID_ARG, "T and the grid size must be positive");
+  if (int rc = check_shape(N, K, group_size)) return rc;
+  for (int i = 0; i < n_alpha; ++i)
+    if (!(alphas[i] >= 0.0) || !std::isfinite(alphas[i]))
+      return fail(W4A16_ERR_INVALID_ARG, "alpha[%d] is not a finite number >= 0", i);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int G = K / group_size;
+  const size_t nk = static_cast<size_t>(N) * K, tk = static_cast<size_t>(T) * K, tn = static_cast<size_t>(T) * N;
+  const int parts = static_cast<int>(std::min<size_t>(1024, (tn + 255) / 256));
+
+  std::vector<void*> dev;
+  auto release = [&](int rc) {
+    for (void* p : dev) (void)hipFree(p);
+    return rc;
+  };
+  auto alloc = [&](size_t bytes) -> void* {
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) return nullptr;
+    dev.push_back(p);
+    return p;
+  };
+  auto* dw = static_cast<half_t*>(alloc(nk * 2));
+  auto* dx = static_cast<half_t*>(alloc(tk * 2));
+  auto* dxs = static_cast<uint16_t*>(alloc(tk * 2));
+  auto* dq = static_cast<int32_t*>(alloc(nk / 2));
+  auto* ds = static_cast<uint16_t*>(alloc(static_cast<size_t>(G) * N * 2));
+  auto* dz = static_cast<int32_t*>(alloc(static_cast<size_t>(G) * N / 2));
+  auto* dyref = static_cast<half_t*>(alloc(tn * 2));
+  auto* dy = static_cast<uint16_t*>(alloc(tn * 2));
+  auto* dpart = static_cast<float*>(alloc(static_cast<size_t>(parts) * sizeof(float)));
+  if (dev.size() != 9) return release(fail(W4A16_ERR_HIP, "hipMalloc failed for the search buffers"));
+  if (int rc = hip_status(hipMemcpyAsync(dw, w, nk * 2, hipMemcpyHostToDevice, st), "hipMemcpyAsync")) return release(rc);
+  if (int rc = hip_status(hipMemcpyAsync(dx, xcal, tk * 2, hipMemcpyHostToDevice, st), "hipMemcpyAsync"))
+    return release(rc);
+  // the unquantised layer's outputs: binary16 weights on the tiled MFMA kernel
+  if (int rc = run_gemm_tiled<16>(st, dx, reinterpret_cast<const uint32_t*>(dw), nullptr, Zeros{nullptr, 0}, dyref,
+                                  T, N, K, 0))
+    return release(rc);
+
+  std::vector<double> s(K);
+  std::vector<uint8_t> codes(nk), zeros(static_cast<size_t>(G) * N);
+  std::vector<uint16_t> scales(static_cast<size_t>(G) * N), xs(tk);
+  std::vector<int32_t> qw(nk / 8), qz(static_cast<size_t>(G) * N / 8);
+  std::vector<float> part(parts);
+  for (int i = 0; i < n_alpha; ++i) {
+    int rc = w4a16_awq_scales(xcal, T, K, alphas[i], s.data());
+    if (rc == W4A16_OK) rc = w4a16_quantize(w, N, K, group_size, nullptr, s.data(), codes.data(), scales.data(), zeros.data());
+    if (rc == W4A16_OK) rc = w4a16_pack(codes.data(), nullptr, group_size, N, K, qw.data());
+    if (rc == W4A16_OK) rc = w4a16_pack_zeros(zeros.data(), G, N, qz.data());
+    if (rc == W4A16_OK) rc = w4a16_awq_fold_activations(xcal, T, K, s.data(), xs.data());
+    if (rc != W4A16_OK) return release(rc);
+    const hipError_t e[4] = {
+        hipMemcpyAsync(dq, qw.data(), nk / 2, hipMemcpyHostToDevice, st),
+        hipMemcpyAsync(ds, scales.data(), scales.size() * 2, hipMemcpyHostToDevice, st),
+        hipMemcpyAsync(dz, qz.data(), qz.size() * 4, hipMemcpyHostToDevice, st),
+        hipMemcpyAsync(dxs, xs.data(), tk * 2, hipMemcpyHostToDevice, st)};
+    for (hipError_t ei : e)
+      if (int r = hip_status(ei, "hipMemcpyAsync")) return release(r);
+    rc = w4a16_gemm(dxs, dq, ds, dz, nullptr, group_size, T, N, K, dy, st);
+    if (rc != W4A16_OK) return release(rc);
+    hipLaunchKernelGGL(sq_diff_kernel, dim3(parts), dim3(256), 0, st, dyref, reinterpret_cast<const half_t*>(dy), tn,
+                       dpart);
+    if (int r = check_launch("squared-difference launch")) return release(r);
+    if (int r = hip_status(hipMemcpyAsync(part.data(), dpart, parts * sizeof(float), hipMemcpyDeviceToHost, st),
+                           "hipMemcpyAsync"))
+      return release(r);
+    if (int r = hip_status(hipStreamSynchronize(st), "hipStreamSynchronize")) return release(r);
+    double total = 0.0;
+    for (int p = 0; p < parts; ++p) total += part[p];
+    losses[i] = std::sqrt(total);
+  }
+  int b = 0;
+  for (int i = 1; i < n_alpha; ++i)
+    if (losses[i] < losses[b]) b = i;
+  *best = b;
+  return release(W4A16_OK);
 }
 
 }  // extern "C"

@@ -82,4 +82,24 @@ __global__ __launch_bounds__(256) void sum_slices_kernel(const float* __restrict
   y[idx] = static_cast<half_t>(v);
 }
 
+// Sum of squared differences of two binary16 arrays, one fp32 partial per workgroup
+// (grid-stride, then a fixed-order tree in LDS); the host adds the partials in order.
+__global__ __launch_bounds__(256) void sq_diff_kernel(const half_t* __restrict__ a, const half_t* __restrict__ b,
+                                                      size_t count, float* __restrict__ partial) {
+  __shared__ float red[256];
+  float acc = 0.f;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < count;
+       i += static_cast<size_t>(gridDim.x) * 256) {
+    const float d = static_cast<float>(a[i]) - static_cast<float>(b[i]);
+    acc = fmaf(d, d, acc);
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
+}
+
 }  // namespace w4a16

@@ -26,12 +26,14 @@ namespace w4a16 {
 
 // BITS = 8: 8-bit weights (four per word, byte order 0, 2, 1, 3); a lane's 32 channels
 // are 32 bytes, and the s-th MFMA of the tile takes its words 2s and 2s + 1.
+// BITS = 16: dense binary16 weights [N][K] (scales and zero points unused): the
+// reference product of the AWQ search.
 template <int BM, int BITS = 4>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const half_t* __restrict__ scales,
     Zeros qzeros, half_t* __restrict__ y, int M, int N, int K, int gshift) {
   static_assert(BM % 16 == 0 && BM >= 16, "BM must be a multiple of 16");
-  static_assert(BITS == 4 || BITS == 8, "4- or 8-bit weights");
+  static_assert(BITS == 4 || BITS == 8 || BITS == 16, "4-, 8- or 16-bit weights");
   constexpr int NQ = BITS / 4;                    // 16-byte pieces of a lane's 32 channels
   constexpr int MB = BM / 16;                     // 16-row blocks per wavefront
   constexpr int ACH = BM * 16;                    // 16-byte activation chunks per K tile
@@ -45,7 +47,8 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
   const int lq = lane >> 4;  // which 32-channel quarter of the K tile
   const int m0 = blockIdx.y * BM;
   const int nw = blockIdx.x * 256 + wave * 64;
-  const int W = K >> (BITS == 4 ? 3 : 2);         // words per row
+  constexpr int WSH = BITS == 4 ? 3 : BITS == 8 ? 2 : 1;   // log2 channels per word
+  const int W = K >> WSH;                         // words per row
   const int KT = (K + 127) >> 7;
 
   uint4 areg[APT];
@@ -82,11 +85,13 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
       const int n = min(nw + 16 * nb + lr, N - 1);
-      const uint4* src = reinterpret_cast<const uint4*>(qw + static_cast<size_t>(n) * W + (k >> (BITS == 4 ? 3 : 2)));
+      const uint4* src = reinterpret_cast<const uint4*>(qw + static_cast<size_t>(n) * W + (k >> WSH));
 #pragma unroll
       for (int q = 0; q < NQ; ++q) bw[nb][q] = kin ? src[q] : uint4{0, 0, 0, 0};
-      bs[nb] = scales[static_cast<size_t>(gi) * N + n];
-      bz[nb] = load_zero<BITS>(qzeros, gi, N, n);
+      if constexpr (BITS != 16) {
+        bs[nb] = scales[static_cast<size_t>(gi) * N + n];
+        bz[nb] = load_zero<BITS>(qzeros, gi, N, n);
+      }
     }
   };
 
@@ -108,7 +113,7 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
     for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
       for (int q = 0; q < NQ; ++q) cw[nb][q] = bw[nb][q];
-      dc[nb] = make_consts(bz[nb], bs[nb]);
+      if constexpr (BITS != 16) dc[nb] = make_consts(bz[nb], bs[nb]);
     }
     if (t + 1 < KT) {
       load_a(t + 1);
@@ -120,7 +125,9 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(
       half8_t bf[4];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
-        if constexpr (BITS == 4) {
+        if constexpr (BITS == 16) {
+          bf[nb] = __builtin_bit_cast(half8_t, cw[nb][s]);
+        } else if constexpr (BITS == 4) {
           const uint4 c = cw[nb][0];
           const uint32_t word = s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w;
           bf[nb] = dequant_word(word, dc[nb]);
