@@ -355,6 +355,37 @@ def decode_step_bench(step: wl.DecodeStep, steps: int = 100, warmup: int = 10):
     }
 
 
+def awq_search_bench(cfg: wl.LayerConfig, n_alpha: int = 11):
+    """The AWQ alpha search on one layer with its calibration activations: wall time of
+    the whole search and the device time of one candidate's W4A16 GEMM at M = T (the
+    hot path inside it)."""
+    import torch
+    import w4a16_gemm_amd as w4
+    w = wl.weights(cfg)
+    X = wl.calibration(cfg)
+    alphas = np.linspace(0.0, 1.0, n_alpha)
+    w4.w4a16_awq_search(w, X[:8], cfg.group_size, alphas[:1])      # load, first-touch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    losses, best = w4.w4a16_awq_search(w, X, cfg.group_size, alphas)
+    wall = time.perf_counter() - t0
+    T = X.shape[0]
+    layer = prepare_layer(wl.custom_config(cfg.name + "_cal", cfg.cfg_id, K=cfg.K, N=cfg.N,
+                                           group_size=cfg.group_size, M_list=(T,)), T)
+    t = time_layer(wl.custom_config(cfg.name + "_cal", cfg.cfg_id, K=cfg.K, N=cfg.N, group_size=cfg.group_size,
+                                    M_list=(T,)), T, layer, 20, 5)
+    return {
+        "workload": f"AWQ alpha search on the {cfg.name} layer (N={cfg.N}, K={cfg.K}, group {cfg.group_size}) "
+                    f"with its {T} calibration tokens, {n_alpha} alphas on [0, 1]",
+        "best_alpha": float(alphas[best]), "loss_best": float(losses[best]), "loss_alpha0": float(losses[0]),
+        "wall_s": round(wall, 3), "wall_ms_per_alpha": round(1e3 * wall / n_alpha, 2),
+        "gemm_us_per_alpha_M_T": round(t["region_us_per_step"], 2),
+        "note": "per candidate: the scale on the host (exact mean over the calibration tokens), then "
+                "quantisation and packing, the activation fold, one W4A16 GEMM at M = T and the reduction "
+                "on the device",
+    }
+
+
 def traffic_for(hash_now: str, key: str):
     try:
         with open(TRAFFIC_FILE) as f:
@@ -377,6 +408,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-ref", action="store_true",
                     help="skip timing the dense binary16 library GEMM of the same shapes")
+    ap.add_argument("--no-awq-search", action="store_true", help="skip timing the AWQ alpha search")
     ap.add_argument("--no-decode-step", action="store_true",
                     help="skip the whole-decode-step workload of the 1.5B example")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -490,6 +522,9 @@ def main() -> int:
     if not args.no_decode_step and args.configs in ("all", "headline"):
         log("timing the decode step of the 1.5B example (eager and graph replay)")
         line["decode_step"] = decode_step_bench(wl.DECODE_1P5B)
+    if not args.no_awq_search and args.configs in ("all", "headline"):
+        log("timing the AWQ alpha search on the c2 up-projection layer")
+        line["awq_search"] = awq_search_bench(wl.CONFIGS["c2up"])
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (cpu_baseline)")
         line["cpu_baseline"] = cpu_baseline(hcfg, args.cpu_rows)

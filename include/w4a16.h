@@ -196,10 +196,23 @@ int w4a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t*
                   const int32_t* g_idx, int group_size, int N, int K, uint16_t* w_out,
                   void* stream);
 
+/* The round-to-nearest quantiser and packing on the device, for contiguous groups:
+ * writes exactly what w4a16_quantize (sym == 0) or w4a16_quantize_sym (sym != 0)
+ * followed by w4a16_pack and w4a16_pack_zeros write on the host (every decision taken
+ * in binary64 with the same operations), directly into the device buffers.
+ *   w         binary16 [N][K] (device);  in_scale binary64 [K] (device) or NULL, must be
+ *             positive and finite (not checked)
+ *   qweight   out int32 [N][K/8];  scales out binary16 [G][N];  qzeros out int32 [G][N/8]
+ *             (unused and may be NULL when sym != 0)
+ * Asynchronous on `stream`.  Errors: INVALID_ARG, UNSUPPORTED, HIP. */
+int w4a16_quantize_device(const uint16_t* w, int N, int K, int group_size, const double* in_scale,
+                          int sym, int32_t* qweight, uint16_t* scales, int32_t* qzeros, void* stream);
+
 /* AWQ scale search ("AWQ + GPTQ Quantization, in depth", The two algorithms,
  * compactly: s = (mean over tokens of |X|) ** alpha for alpha on a grid in [0, 1], loss
  * = norm(W X - Wq X), keep the best).  For every alphas[i]: s = w4a16_awq_scales(xcal,
- * alpha), the layer quantised with w4a16_quantize(w, in_scale = s), and
+ * alpha), the layer quantised as w4a16_quantize(w, in_scale = s) does (on the device,
+ * w4a16_quantize_device), and
  *   losses[i] = || xcal W^T - binary16(xcal / s) W^_alpha^T ||_F
  * over the T calibration rows, with the reference product on binary16 weights and the
  * candidate on w4a16_gemm (both on the device, fp32 accumulation, binary16 outputs),

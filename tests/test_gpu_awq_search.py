@@ -45,3 +45,26 @@ def test_awq_search_rejects_bad_arguments():
     with pytest.raises(w4.W4A16Error) as e:
         w4.w4a16_awq_search(w, X, 48, [0.5])
     assert e.value.status == w4.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("N,K,g,sym,scaled", [(264, 1024, 128, False, False), (136, 2048, 64, True, True),
+                                              (72, 1536, 32, False, True), (40, 1536, 1536, True, False)])
+def test_device_quantiser_is_bit_exact_with_the_host(N, K, g, sym, scaled):
+    import torch
+    cfg = wl.custom_config("qdev", 900 + K + g, K=K, N=N, group_size=g)
+    w = wl.weights(cfg)
+    w[3, :g] = 0                                          # an all-zero group
+    s = oracle.awq_scales(wl.calibration(cfg, 64), 0.4) if scaled else None
+    note(f"device quantiser N={N} K={K} g={g} sym={sym} scaled={scaled}")
+    dev = torch.device("cuda:0")
+    qw, S, qz = w4.w4a16_quantize_device(torch.from_numpy(w).to(dev), g,
+                                         None if s is None else torch.from_numpy(s).to(dev), sym)
+    torch.cuda.synchronize()
+    if sym:
+        codes, Sh = w4.w4a16_quantize_sym(w, g, None, s)
+        assert qz is None
+    else:
+        codes, Sh, Zh = w4.w4a16_quantize(w, g, None, s)
+        assert np.array_equal(qz.cpu().numpy(), w4.w4a16_pack_zeros(Zh))
+    assert np.array_equal(qw.cpu().numpy(), w4.w4a16_pack(codes, None, g))
+    assert np.array_equal(S.cpu().numpy().view(np.uint16), Sh.view(np.uint16))

@@ -40,6 +40,8 @@ _SIGNATURES = {
                             _c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
     "w4a16_dequant": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                _c_int, _c_void_p, _c_void_p]),
+    "w4a16_quantize_device": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_int, _c_void_p,
+                                       _c_void_p, _c_void_p, _c_void_p]),
     "w4a16_awq_search": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p,
                                   _c_int, _c_void_p, _c_void_p, _c_void_p]),
     "w8a16_qweight_words": (ctypes.c_size_t, [_c_int, _c_int, _c_int]),
@@ -399,4 +401,24 @@ def w4a16_awq_search(w, xcal, group_size: int, alphas, stream=None):
     _check(lib().w4a16_awq_search(_ptr(w), _ptr(X), N, K, T, group_size, _ptr(a), a.size, _ptr(losses),
                                   ctypes.addressof(best), _stream_handle(stream, torch.device("cuda:0"))))
     return losses, best.value
+
+
+def w4a16_quantize_device(w, group_size: int, in_scale=None, sym: bool = False, stream=None):
+    """Quantise and pack binary16 w [N][K] (a device tensor) on the device: (qweight int32
+    [N*K/8], scales binary16 [G][N], qzeros int32 [G][N/8] or None when symmetric), the
+    same bits as the host quantiser and packing.  in_scale: float64 device tensor [K]."""
+    import torch
+    _dev(w, torch.float16, "w")
+    if in_scale is not None:
+        _dev(in_scale, torch.float64, "in_scale")
+    N, K = w.shape
+    G = K // group_size
+    qweight = torch.empty(N * K // 8, dtype=torch.int32, device=w.device)
+    scales = torch.empty((G, N), dtype=torch.float16, device=w.device)
+    qzeros = None if sym else torch.empty((G, N // 8), dtype=torch.int32, device=w.device)
+    _check(lib().w4a16_quantize_device(w.data_ptr(), N, K, group_size,
+                                       None if in_scale is None else in_scale.data_ptr(), int(bool(sym)),
+                                       qweight.data_ptr(), scales.data_ptr(),
+                                       None if qzeros is None else qzeros.data_ptr(), _stream_handle(stream, w.device)))
+    return qweight, scales, qzeros
 

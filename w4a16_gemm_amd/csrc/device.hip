@@ -13,6 +13,7 @@
 #include "kernels/aux.hpp"
 #include "kernels/gemm.hpp"
 #include "kernels/gemv.hpp"
+#include "kernels/quantize.hpp"
 #include "kernels/skinny.hpp"
 
 namespace w4a16 {
@@ -616,6 +617,24 @@ int w8a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t*
   return check_launch("dequant launch");
 }
 
+int w4a16_quantize_device(const uint16_t* w, int N, int K, int group_size, const double* in_scale, int sym,
+                          int32_t* qweight, uint16_t* scales, int32_t* qzeros, void* stream) {
+  clear_error();
+  if (!w || !qweight || !scales || (!sym && !qzeros)) return fail(W4A16_ERR_INVALID_ARG, "NULL buffer");
+  if (int rc = check_shape(N, K, group_size)) return rc;
+  const long long threads = static_cast<long long>(N) * (K / group_size);
+  const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  auto* qw = reinterpret_cast<uint32_t*>(qweight);
+  auto* qz = reinterpret_cast<uint32_t*>(qzeros);
+  if (sym)
+    hipLaunchKernelGGL(quantize_rtn_kernel<true>, grid, dim3(256), 0, st, w, in_scale, N, K, group_size, qw, scales, qz);
+  else
+    hipLaunchKernelGGL(quantize_rtn_kernel<false>, grid, dim3(256), 0, st, w, in_scale, N, K, group_size, qw, scales,
+                       qz);
+  return check_launch("quantize launch");
+}
+
 // AWQ alpha search: the W4A16 GEMM of every candidate against the binary16 product of
 // the unquantised layer, on the calibration activations.  Host inputs, device work on
 // `stream`, returns when the losses are on the host.
@@ -653,7 +672,8 @@ int w4a16_awq_search(const uint16_t* w, const uint16_t* xcal, int N, int K, int 
   auto* dyref = static_cast<half_t*>(alloc(tn * 2));
   auto* dy = static_cast<uint16_t*>(alloc(tn * 2));
   auto* dpart = static_cast<float*>(alloc(static_cast<size_t>(parts) * sizeof(float)));
-  if (dev.size() != 9) return release(fail(W4A16_ERR_HIP, "hipMalloc failed for the search buffers"));
+  auto* dsc = static_cast<double*>(alloc(static_cast<size_t>(K) * sizeof(double)));
+  if (dev.size() != 10) return release(fail(W4A16_ERR_HIP, "hipMalloc failed for the search buffers"));
   if (int rc = hip_status(hipMemcpyAsync(dw, w, nk * 2, hipMemcpyHostToDevice, st), "hipMemcpyAsync")) return release(rc);
   if (int rc = hip_status(hipMemcpyAsync(dx, xcal, tk * 2, hipMemcpyHostToDevice, st), "hipMemcpyAsync"))
     return release(rc);
@@ -663,24 +683,19 @@ int w4a16_awq_search(const uint16_t* w, const uint16_t* xcal, int N, int K, int 
     return release(rc);
 
   std::vector<double> s(K);
-  std::vector<uint8_t> codes(nk), zeros(static_cast<size_t>(G) * N);
-  std::vector<uint16_t> scales(static_cast<size_t>(G) * N), xs(tk);
-  std::vector<int32_t> qw(nk / 8), qz(static_cast<size_t>(G) * N / 8);
   std::vector<float> part(parts);
   for (int i = 0; i < n_alpha; ++i) {
+    // the candidate's scale on the host (exact mean), quantisation and fold on the device
     int rc = w4a16_awq_scales(xcal, T, K, alphas[i], s.data());
-    if (rc == W4A16_OK) rc = w4a16_quantize(w, N, K, group_size, nullptr, s.data(), codes.data(), scales.data(), zeros.data());
-    if (rc == W4A16_OK) rc = w4a16_pack(codes.data(), nullptr, group_size, N, K, qw.data());
-    if (rc == W4A16_OK) rc = w4a16_pack_zeros(zeros.data(), G, N, qz.data());
-    if (rc == W4A16_OK) rc = w4a16_awq_fold_activations(xcal, T, K, s.data(), xs.data());
     if (rc != W4A16_OK) return release(rc);
-    const hipError_t e[4] = {
-        hipMemcpyAsync(dq, qw.data(), nk / 2, hipMemcpyHostToDevice, st),
-        hipMemcpyAsync(ds, scales.data(), scales.size() * 2, hipMemcpyHostToDevice, st),
-        hipMemcpyAsync(dz, qz.data(), qz.size() * 4, hipMemcpyHostToDevice, st),
-        hipMemcpyAsync(dxs, xs.data(), tk * 2, hipMemcpyHostToDevice, st)};
-    for (hipError_t ei : e)
-      if (int r = hip_status(ei, "hipMemcpyAsync")) return release(r);
+    if (int r = hip_status(hipMemcpyAsync(dsc, s.data(), K * sizeof(double), hipMemcpyHostToDevice, st),
+                           "hipMemcpyAsync"))
+      return release(r);
+    rc = w4a16_quantize_device(reinterpret_cast<const uint16_t*>(dw), N, K, group_size, dsc, 0, dq, ds, dz, st);
+    if (rc != W4A16_OK) return release(rc);
+    hipLaunchKernelGGL(fold_activations_kernel, dim3(static_cast<unsigned>((tk + 255) / 256)), dim3(256), 0, st,
+                       reinterpret_cast<const uint16_t*>(dx), dsc, tk, K, dxs);
+    if (int r = check_launch("fold launch")) return release(r);
     rc = w4a16_gemm(dxs, dq, ds, dz, nullptr, group_size, T, N, K, dy, st);
     if (rc != W4A16_OK) return release(rc);
     hipLaunchKernelGGL(sq_diff_kernel, dim3(parts), dim3(256), 0, st, dyref, reinterpret_cast<const half_t*>(dy), tn,
