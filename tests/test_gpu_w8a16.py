@@ -88,3 +88,28 @@ def test_w8a16_full_size_layer_on_sampled_rows(M):
     run_gemm(prod, x=x, y=y)
     assert not bool(torch.isnan(y).any())
     assert oracle.rel_err(y.cpu().numpy()[:, rows], ref["y_ref"]) <= TOL
+
+
+# skinny batches (2 <= M <= 32): the 8-bit skinny kernel, every shape family
+SKINNY = [
+    # name, M, N, K, group, act_order, sym
+    ("f1", 4, 264, 2048, 128, False, False),    # one slice, subnormal path
+    ("f2", 9, 136, 1024, 32, True, False),      # dequantised path, act order
+    ("f3", 16, 392, 8192, 128, False, True),    # two K slices, symmetric
+    ("f4", 20, 72, 4096, 64, False, False),     # two launches (16 + 4 rows)
+    ("f5", 2, 40, 1536, 1536, False, False),    # per-channel
+]
+
+
+@pytest.mark.parametrize("case", range(len(SKINNY)))
+def test_w8a16_skinny_batches_match_oracle(case):
+    name, M, N, K, g, act, sym = SKINNY[case]
+    cfg = wl.custom_config(name, 650 + case, K=K, N=N, group_size=g, M_list=(M,), act_order=act, sym=sym, bits=8)
+    note(f"8-bit skinny {name} M={M} N={N} K={K} g={g} act={act} sym={sym}")
+    prod = product_layer(cfg, M)
+    ref = oracle_layer(cfg, M, np.arange(N))
+    for tiled in ("1", "0"):
+        os.environ["W4A16_TUNE_GEMM_SKINNY"] = tiled
+        y = run_gemm(prod).cpu().numpy()
+        assert oracle.rel_err(y, ref["y_ref"]) <= TOL, tiled
+    os.environ.pop("W4A16_TUNE_GEMM_SKINNY")

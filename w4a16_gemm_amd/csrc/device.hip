@@ -280,7 +280,7 @@ constexpr int kBigMinM = 33;          // the large-tile kernel from here on (whe
 
 // The whole row in one workgroup when it fits (K <= 8192), else the fewest K slices
 // that fit; per slice the most wavefronts (fewest slab entries per thread).
-SkinnyShape pick_skinny_shape(int M, int K, int gshift) {
+SkinnyShape pick_skinny_shape(int M, int K, int gshift, int bits = 4) {
   SkinnyShape sh;
   if (M > kSkinnyMaxM) return sh;
   for (int ks : {1, 2, 4, 8}) {
@@ -288,6 +288,7 @@ SkinnyShape pick_skinny_shape(int M, int K, int gshift) {
     const int Ks = K / ks;
     const int kc = Ks / 128;
     for (int t : {1, 2, 4}) {
+      if (bits == 8 && t > 2) break;   // 8-bit codes take twice the registers per step
       if (kc % t != 0 || kc / t > 16) continue;
       const int waves = kc / t;
       const int entries = 16 * groups_in(0, Ks, gshift);
@@ -304,18 +305,18 @@ SkinnyShape pick_skinny_shape(int M, int K, int gshift) {
 }
 
 // ks > 1: partial sums to part [ks][M][N] fp32, then sum_slices_kernel into y.
-template <int T, int SE, bool ACT, bool SUB>
+template <int T, int SE, bool ACT, bool SUB, int BITS = 4>
 int launch_skinny_t(const SkinnyShape& sh, hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s,
                     Zeros z, half_t* y, float* part, int M, int N, int K, int gshift) {
   static const hipError_t lds_ok =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_skinny_kernel<T, SE, ACT, SUB>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_skinny_kernel<T, SE, ACT, SUB, BITS>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (int rc = hip_status(lds_ok, "hipFuncSetAttribute")) return rc;
   const size_t lds = skinny_lds_bytes(sh.waves, groups_in(0, K / sh.ks, gshift));
   const int nblk = (N + 15) / 16;
   const int per_cu = std::max(1, 16 / sh.waves);
   const int per_slice = std::min(nblk, std::max(1, device_cus() * per_cu / sh.ks));
-  hipLaunchKernelGGL((gemm_skinny_kernel<T, SE, ACT, SUB>), dim3(per_slice * sh.ks), dim3(64 * sh.waves), lds, st, x,
+  hipLaunchKernelGGL((gemm_skinny_kernel<T, SE, ACT, SUB, BITS>), dim3(per_slice * sh.ks), dim3(64 * sh.waves), lds, st, x,
                      qw, s, z, y, part, M, N, K, gshift, sh.ks);
   if (int rc = check_launch("skinny gemm launch")) return rc;
   if (sh.ks == 1) return W4A16_OK;
@@ -325,18 +326,45 @@ int launch_skinny_t(const SkinnyShape& sh, hipStream_t st, const half_t* x, cons
   return check_launch("slice sum launch");
 }
 
-template <bool ACT>
+template <bool ACT, int BITS = 4>
 int launch_skinny(const SkinnyShape& sh, hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s,
                   Zeros z, half_t* y, float* part, int M, int N, int K, int gshift) {
-#define W4A16_SKINNY(T_, SE_)                                                                              \
-  if (sh.t == T_ && sh.se == SE_)                                                                        \
-    return gshift == 7 ? launch_skinny_t<T_, SE_, ACT, true>(sh, st, x, qw, s, z, y, part, M, N, K, gshift) \
-                       : launch_skinny_t<T_, SE_, ACT, false>(sh, st, x, qw, s, z, y, part, M, N, K, gshift);
+#define W4A16_SKINNY(T_, SE_)                                                                                    \
+  if (sh.t == T_ && sh.se == SE_)                                                                              \
+    return gshift == 7 ? launch_skinny_t<T_, SE_, ACT, true, BITS>(sh, st, x, qw, s, z, y, part, M, N, K, gshift) \
+                       : launch_skinny_t<T_, SE_, ACT, false, BITS>(sh, st, x, qw, s, z, y, part, M, N, K, gshift);
   W4A16_SKINNY(1, 1) W4A16_SKINNY(1, 2) W4A16_SKINNY(1, 4)
   W4A16_SKINNY(2, 1) W4A16_SKINNY(2, 2) W4A16_SKINNY(2, 4)
-  W4A16_SKINNY(4, 1) W4A16_SKINNY(4, 2) W4A16_SKINNY(4, 4)
+  if constexpr (BITS == 4) {
+    W4A16_SKINNY(4, 1) W4A16_SKINNY(4, 2) W4A16_SKINNY(4, 4)
+  }
 #undef W4A16_SKINNY
   return fail(W4A16_ERR_UNSUPPORTED, "no skinny kernel for T=%d SE=%d", sh.t, sh.se);
+}
+
+// The skinny kernel once per 16 rows of x and y; K slices keep their fp32 partial
+// tiles in stream-ordered scratch memory, reused by the launches of every 16 rows.
+template <int BITS>
+int run_skinny(const SkinnyShape& sk, bool act, hipStream_t st, const half_t* hx, const uint32_t* hq,
+               const half_t* hs, Zeros hz, half_t* hy, int M, int N, int K, int gshift) {
+  float* part = nullptr;
+  if (sk.ks > 1) {
+    const size_t bytes = static_cast<size_t>(sk.ks) * std::min(M, kSkinnyMaxM) * N * sizeof(float);
+    if (int s = hip_status(hipMallocAsync(reinterpret_cast<void**>(&part), bytes, st), "hipMallocAsync")) return s;
+  }
+  int rc = W4A16_OK;
+  for (int m0 = 0; m0 < M && rc == W4A16_OK; m0 += kSkinnyMaxM) {
+    const int mc = std::min(kSkinnyMaxM, M - m0);
+    const half_t* xc = hx + static_cast<size_t>(m0) * K;
+    half_t* yc = hy + static_cast<size_t>(m0) * N;
+    rc = act ? launch_skinny<true, BITS>(sk, st, xc, hq, hs, hz, yc, part, mc, N, K, gshift)
+             : launch_skinny<false, BITS>(sk, st, xc, hq, hs, hz, yc, part, mc, N, K, gshift);
+  }
+  if (part) {
+    const int rf = hip_status(hipFreeAsync(part, st), "hipFreeAsync");
+    if (rc == W4A16_OK) rc = rf;
+  }
+  return rc;
 }
 
 // Large-M GEMM.  BM x 256 tiles (BM = 256 rows; 128 or 64 when the whole batch fits in
@@ -487,26 +515,7 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
   if (sk.waves != 0 && static_cast<long long>(N) * K / 2 < (1LL << 31) &&
       M <= env_int("W4A16_TUNE_SKINNY_CHUNK_MAX_M", kSkinnyChunkMaxM) &&
       env_int("W4A16_TUNE_GEMM_SKINNY", 1) != 0) {
-    // K slices: fp32 partial tiles in stream-ordered scratch memory, reused by the
-    // launches of every 16 rows
-    float* part = nullptr;
-    if (sk.ks > 1) {
-      const size_t bytes = static_cast<size_t>(sk.ks) * std::min(M, kSkinnyMaxM) * N * sizeof(float);
-      if (int s = hip_status(hipMallocAsync(reinterpret_cast<void**>(&part), bytes, st), "hipMallocAsync")) return s;
-    }
-    int rc = W4A16_OK;
-    for (int m0 = 0; m0 < M && rc == W4A16_OK; m0 += kSkinnyMaxM) {
-      const int mc = std::min(kSkinnyMaxM, M - m0);
-      const half_t* xc = hx + static_cast<size_t>(m0) * K;
-      half_t* yc = hy + static_cast<size_t>(m0) * N;
-      rc = act ? launch_skinny<true>(sk, st, xc, hq, hs, hz, yc, part, mc, N, K, gshift)
-               : launch_skinny<false>(sk, st, xc, hq, hs, hz, yc, part, mc, N, K, gshift);
-    }
-    if (part) {
-      const int rf = hip_status(hipFreeAsync(part, st), "hipFreeAsync");
-      if (rc == W4A16_OK) rc = rf;
-    }
-    return rc;
+    return run_skinny<4>(sk, act, st, hx, hq, hs, hz, hy, M, N, K, gshift);
   }
 
   if (!act) return run_gemm(st, hx, hq, hs, hz, hy, M, N, K, gshift);
@@ -577,6 +586,11 @@ int w8a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
                 M, N, K, group_size);
   if (gp.ok && forced != Path::kGemm)
     return run_gemv<8>(gp, act, hx, hq, reinterpret_cast<const uint16_t*>(scales), hz, hy, N, K, gshift, st);
+  // up to kSkinnyChunkMaxM rows: the skinny kernel (32-bit byte offsets into the codes)
+  const SkinnyShape sk = pick_skinny_shape(std::min(M, kSkinnyMaxM), K, gshift, 8);
+  if (sk.waves != 0 && static_cast<long long>(N) * K < (1LL << 31) && M <= kSkinnyChunkMaxM &&
+      env_int("W4A16_TUNE_GEMM_SKINNY", 1) != 0)
+    return run_skinny<8>(sk, act, st, hx, hq, hs, hz, hy, M, N, K, gshift);
   if (static_cast<long long>(M) * K >= (1LL << 31) || static_cast<long long>(N) * (K / 4) >= (1LL << 31))
     return fail(W4A16_ERR_UNSUPPORTED, "8-bit layer too large for 32-bit element offsets (M=%d N=%d K=%d)", M, N, K);
   if (!act) return run_gemm_tiled<8>(st, hx, hq, hs, hz, hy, M, N, K, gshift);

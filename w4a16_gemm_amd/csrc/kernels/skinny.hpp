@@ -69,7 +69,11 @@ constexpr size_t skinny_lds_bytes(int waves, int groups) {
 //     acc += (S * 2^24) * sum q x + (-Z * S) * sum x.
 // ks > 1: gridDim.x = ks * (workgroups per slice); partial sums go to part [ks][M][N]
 // (fp32) instead of y.
-template <int T, int SE, bool ACT, bool SUB>
+// BITS = 8: 8-bit weights (four per word, byte order 0, 2, 1, 3); a lane's 32 channels
+// of a step are 32 bytes (two loads), MFMA j takes words 2j and 2j + 1, SUB uses the
+// bytes as subnormals with both pairs of a word at weight 1 (no activation pre-scale),
+// and the zero points are bytes.
+template <int T, int SE, bool ACT, bool SUB, int BITS = 4>
 __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
     const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const half_t* __restrict__ scales,
     Zeros qzeros, half_t* __restrict__ y, float* __restrict__ part, int M, int N, int K,
@@ -79,8 +83,11 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nwaves = blockDim.x >> 6;
   const int nthreads = blockDim.x;
+  static_assert(BITS == 4 || BITS == 8, "4- or 8-bit weights");
+  constexpr int NQ = BITS / 4;            // 16-byte loads per lane and step
+  constexpr int WSH = BITS == 4 ? 3 : 2;  // log2 channels per word
   const int lr = lane & 15, lq = lane >> 4;
-  const int Wd = K >> 3;
+  const int Wd = K >> WSH;
   const int gs = gridDim.x / ks;                  // workgroups per slice
   const int slice = blockIdx.x / gs;
   const int Ks = K / ks;                          // channels per slice
@@ -119,6 +126,7 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
       }
     if constexpr (SUB) {
       const half2_t ones = half2_t{static_cast<half_t>(1.0f), static_cast<half_t>(1.0f)};
+      constexpr bool kPrescale = BITS == 4;   // the 16 q pair slots of 4-bit words
       const half_t sixteenth = static_cast<half_t>(0.0625f);
 #pragma unroll
       for (int t = 0; t < T; ++t) {
@@ -132,12 +140,14 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
         sx += __shfl_xor(sx, 16);
         sx += __shfl_xor(sx, 32);
         xs[t] = sx;
+        if constexpr (kPrescale) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          xr[t][j][2] *= sixteenth;
-          xr[t][j][3] *= sixteenth;
-          xr[t][j][6] *= sixteenth;
-          xr[t][j][7] *= sixteenth;
+          for (int j = 0; j < 4; ++j) {
+            xr[t][j][2] *= sixteenth;
+            xr[t][j][3] *= sixteenth;
+            xr[t][j][6] *= sixteenth;
+            xr[t][j][7] *= sixteenth;
+          }
         }
       }
     }
@@ -147,14 +157,17 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
   // buffer resource over the codes (N K / 2 < 2^31 bytes, checked by the host): 32-bit
   // byte offsets instead of 64-bit addresses.
   const __amdgpu_buffer_rsrc_t codes = stream_rsrc(qw, static_cast<uint32_t>(N) * static_cast<uint32_t>(Wd) * 4u);
-  auto code_offset = [&](int b) {   // bytes; step t adds 64 t (128 channels = 16 words)
+  constexpr uint32_t kStepBytes = 16u * BITS;   // 128 channels
+  auto code_offset = [&](int b) {   // bytes; step t adds kStepBytes t
     const int n = min(16 * b + lr, N - 1);
-    return (static_cast<uint32_t>(n) * static_cast<uint32_t>(Wd) + static_cast<uint32_t>((kw >> 3) + 4 * lq)) * 4u;
+    return (static_cast<uint32_t>(n) * static_cast<uint32_t>(Wd) + static_cast<uint32_t>((kw >> WSH) + 4 * NQ * lq)) * 4u;
   };
-  auto load_codes = [&](int b, uint4 (&cw)[T]) {
+  auto load_codes = [&](int b, uint4 (&cw)[T][NQ]) {
     const uint32_t off = code_offset(b);
 #pragma unroll
-    for (int t = 0; t < T; ++t) cw[t] = load_buffer16(codes, off + 64u * t);
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) cw[t][q] = load_buffer16(codes, off + kStepBytes * t + 16u * q);
   };
   // Scale and zero word of slab entries tid + u * nthreads of row block b.
   half_t sv[SE];
@@ -166,7 +179,10 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
       const int gi = g0 + (e >> 4);
       const int n = min(16 * b + (e & 15), N - 1);
       sv[u] = scales[static_cast<size_t>(gi) * N + n];
-      zv[u] = *qzeros.at(static_cast<size_t>(gi) * (N >> 3) + (n >> 3));
+      if constexpr (BITS == 4)
+        zv[u] = *qzeros.at(static_cast<size_t>(gi) * (N >> 3) + (n >> 3));
+      else
+        zv[u] = *qzeros.at(static_cast<size_t>(gi) * (N >> 2) + (n >> 2));
     }
   };
   auto write_slab = [&](int b, int buf) {
@@ -175,7 +191,8 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
       const int e = tid + u * nthreads;
       if (e < slab_n) {
         const int n = min(16 * b + (e & 15), N - 1);
-        const uint32_t z = (qzeros.word(zv[u]) >> ((n & 7) * 4)) & 0xFu;
+        const uint32_t z = BITS == 4 ? (qzeros.word(zv[u]) >> ((n & 7) * 4)) & 0xFu
+                                     : (qzeros.word8(zv[u]) >> ((n & 3) * 8)) & 0xFFu;
         if constexpr (SUB) {
           const float S = static_cast<float>(sv[u]);
           slab[buf * slab_n + e] = __builtin_bit_cast(uint2, make_float2(S * 16777216.0f, -static_cast<float>(z) * S));
@@ -190,22 +207,40 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
   // refilled with the next row block's codes as soon as it has been used, so a load
   // has a whole row block of work to land.  The slab of the next block is written and
   // its successor's scales issued; the partial tiles are summed after the barrier.
-  uint4 cw[T];
+  uint4 cw[T][NQ];
   auto row_block = [&](int b, int i) {
     const int buf = i & 1;
     const uint32_t off_next = code_offset(b + gs);
     float4_t acc = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      const uint32_t w4[4] = {cw[t].x, cw[t].y, cw[t].z, cw[t].w};
+      // this step's words: 4 (4-bit, one per MFMA) or 8 (8-bit, two per MFMA)
+      uint32_t wv[4 * NQ];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        wv[4 * q + 0] = cw[t][q].x;
+        wv[4 * q + 1] = cw[t][q].y;
+        wv[4 * q + 2] = cw[t][q].z;
+        wv[4 * q + 3] = cw[t][q].w;
+      }
+      auto refill = [&]() {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) cw[t][q] = load_buffer16(codes, off_next + kStepBytes * t + 16u * q);
+      };
       if constexpr (SUB) {
         half8_t wf[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const SubPairs sp = expand_word_subnormal(w4[j]);
-          wf[j] = __builtin_bit_cast(half8_t, uint4{sp.a0, sp.b0, sp.a1, sp.b1});
+          if constexpr (BITS == 4) {
+            const SubPairs sp = expand_word_subnormal(wv[j]);
+            wf[j] = __builtin_bit_cast(half8_t, uint4{sp.a0, sp.b0, sp.a1, sp.b1});
+          } else {
+            const uint32_t lo = wv[2 * j], hi = wv[2 * j + 1];
+            wf[j] = __builtin_bit_cast(half8_t, uint4{lo & 0x00FF00FFu, (lo >> 8) & 0x00FF00FFu,
+                                                      hi & 0x00FF00FFu, (hi >> 8) & 0x00FF00FFu});
+          }
         }
-        cw[t] = load_buffer16(codes, off_next + 64u * t);
+        refill();
         float4_t part = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) part = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j], xr[t][j], part, 0, 0, 0);
@@ -223,8 +258,15 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
         const DequantConsts dc = slab_consts(slab[buf * slab_n + gi * 16 + lr]);
         half8_t wf[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) wf[j] = dequant_word(w4[j], dc);
-        cw[t] = load_buffer16(codes, off_next + 64u * t);
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (BITS == 4) {
+            wf[j] = dequant_word(wv[j], dc);
+          } else {
+            const half4_t lo = dequant_word8(wv[2 * j], dc), hi = dequant_word8(wv[2 * j + 1], dc);
+            wf[j] = half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+        }
+        refill();
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[j], xr[t][j], acc, 0, 0, 0);
       }
