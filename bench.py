@@ -45,7 +45,7 @@ MAX_COPIES = 64
 METRIC = "W4A16 GEMV HBM GB/s (% of peak) at M=1; prefill GEMM TFLOP/s (% MFMA)"
 HEADLINE = ("c3", 1)
 SECONDARY = [("c1", 1), ("c2up", 1), ("c2down", 1), ("c3", 2), ("c3", 4), ("c3", 8), ("c3", 16),
-             ("c3s", 1), ("c3w8", 1), ("c3w8", 16), ("c4", 2048), ("c5", 1), ("c5", 512)]
+             ("c3s", 1), ("c3w8", 1), ("c3w8", 16), ("c4", 2048), ("c4w8", 2048), ("c5", 1), ("c5", 512)]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 KERNEL_SOURCES = ["w4a16_gemm_amd/csrc/kernels/nibbles.hpp", "w4a16_gemm_amd/csrc/kernels/gemv.hpp",
                   "w4a16_gemm_amd/csrc/kernels/gemm.hpp", "w4a16_gemm_amd/csrc/kernels/skinny.hpp",

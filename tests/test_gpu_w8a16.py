@@ -113,3 +113,62 @@ def test_w8a16_skinny_batches_match_oracle(case):
         y = run_gemm(prod).cpu().numpy()
         assert oracle.rel_err(y, ref["y_ref"]) <= TOL, tiled
     os.environ.pop("W4A16_TUNE_GEMM_SKINNY")
+
+
+# larger batches (M >= 33): the 8-bit large-tile kernel at every tile height, the tiled
+# kernel beside it, and the tiled kernel alone where N % 16 != 0
+LARGE = [
+    # name, M, N, K, group, act_order, sym
+    ("h1", 40, 272, 1024, 128, False, False),     # 64-row tiles
+    ("h2", 300, 528, 640, 64, True, True),        # 256-row tiles, act order, symmetric
+    ("h3", 129, 1040, 1536, 1536, False, False),  # per-channel, ragged rows and columns
+    ("h4", 100, 4112, 512, 32, False, False),     # 128-row tiles, many column tiles
+    ("h5", 64, 264, 1024, 128, False, False),     # N % 16 != 0: tiled kernel only
+]
+
+
+@pytest.mark.parametrize("case", range(len(LARGE)))
+def test_w8a16_large_batches_match_oracle(case):
+    import torch
+    name, M, N, K, g, act, sym = LARGE[case]
+    cfg = wl.custom_config(name, 670 + case, K=K, N=N, group_size=g, M_list=(M,), act_order=act, sym=sym, bits=8)
+    note(f"8-bit large {name} M={M} N={N} K={K} g={g} act={act} sym={sym}")
+    prod = product_layer(cfg, M)
+    ref = oracle_layer(cfg, M, np.arange(N))
+    ks = np.unique(np.concatenate([[0, K - 1], np.random.default_rng(case).integers(0, K, 60)]))[:40]
+    E = torch.from_numpy(wl.unit_vectors(K, ks)).to(device())
+    expect = ref["W16"][:, ks].T.copy()
+    try:
+        for big, mb in (("1", None), ("1", "2"), ("1", "4"), ("1", "8"), ("0", None)):
+            os.environ["W4A16_TUNE_GEMM_BIG"] = big
+            if mb is None:
+                os.environ.pop("W4A16_TUNE_GEMM_BIG_MB", None)
+            else:
+                os.environ["W4A16_TUNE_GEMM_BIG_MB"] = mb
+            note(f"  big={big} mb={mb}")
+            y = run_gemm(prod).cpu().numpy()
+            assert oracle.rel_err(y, ref["y_ref"]) <= TOL, (big, mb)
+            # unit-vector probes: x = e_k gives binary16(W^[:, k]) exactly
+            ye = run_gemm(prod, x=E).cpu().numpy()
+            assert np.array_equal(ye.view(np.uint16), expect.view(np.uint16)), (big, mb)
+    finally:
+        os.environ.pop("W4A16_TUNE_GEMM_BIG", None)
+        os.environ.pop("W4A16_TUNE_GEMM_BIG_MB", None)
+
+
+def test_w8a16_prefill_layer_on_sampled_rows():
+    """The 2048-token prefill layer with 8-bit weights, at its full size, on the launch
+    the timing runs use (one round of 256-column tiles and one of 192-column tiles)."""
+    import torch
+    cfg = wl.config("c4w8")
+    M = cfg.M_list[0]
+    note(f"8-bit full-size {cfg.name} M={M} (N={cfg.N} K={cfg.K})")
+    prod = product_layer(cfg, M)
+    rows = np.unique(np.concatenate([sample_rows(cfg.N, 96), np.arange(cfg.N - 8, cfg.N),
+                                     np.arange(8192 - 4, 8192 + 4)]))
+    ref = oracle_layer(cfg, M, rows)
+    assert np.array_equal(prod["codes"][rows], ref["codes"])
+    y = torch.full((M, cfg.N), float("nan"), dtype=torch.float16, device=prod["x"].device)
+    run_gemm(prod, y=y)
+    assert not bool(torch.isnan(y).any())
+    assert oracle.rel_err(y.cpu().numpy()[:, rows], ref["y_ref"]) <= TOL

@@ -373,19 +373,20 @@ int run_skinny(const SkinnyShape& sk, bool act, hipStream_t st, const half_t* hx
 // units: then one round of full-width tiles covers the first columns and one round of
 // narrower tiles (64 NB2 wide) the rest, so that neither round leaves compute units
 // idle; (b) when they would not fill one round: then narrower tiles for all columns.
-template <int NB2, int MB>
+template <int NB2, int MB, int BITS>
 int launch_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, Zeros z, half_t* y,
                int M, int N, int K, int gshift, int split, int n_split, int grid) {
-  static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_big_kernel<NB2, MB>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                       static_cast<int>(kBigLds));
+  constexpr size_t lds = BITS == 4 ? kBigLds : kBigLds8;
+  static const hipError_t lds_ok = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(gemm_big_kernel<NB2, MB, BITS>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      static_cast<int>(lds));
   if (int rc = hip_status(lds_ok, "hipFuncSetAttribute")) return rc;
-  hipLaunchKernelGGL((gemm_big_kernel<NB2, MB>), dim3(grid), dim3(512), kBigLds, st, x, qw, s, z, y, M, N, K, gshift,
-                     split, n_split);
+  hipLaunchKernelGGL((gemm_big_kernel<NB2, MB, BITS>), dim3(grid), dim3(512), lds, st, x, qw, s, z, y, M, N, K,
+                     gshift, split, n_split);
   return check_launch("gemm launch");
 }
 
-template <int MB>
+template <int MB, int BITS>
 int run_gemm_big_t(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, Zeros z,
                    half_t* y, int M, int N, int K, int gshift) {
   constexpr int BM = 32 * MB;
@@ -400,9 +401,9 @@ int run_gemm_big_t(hipStream_t st, const half_t* x, const uint32_t* qw, const ha
     if (rest > 0 && nb2 >= 1 && nb2 <= 3) {
       const int split = tiles_m * per_panel;
       const int grid = split + tiles_m * ((rest + 64 * nb2 - 1) / (64 * nb2));
-      if (nb2 == 1) return launch_big<1, MB>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
-      if (nb2 == 2) return launch_big<2, MB>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
-      return launch_big<3, MB>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
+      if (nb2 == 1) return launch_big<1, MB, BITS>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
+      if (nb2 == 2) return launch_big<2, MB, BITS>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
+      return launch_big<3, MB, BITS>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
     }
   }
   // One round or less: the narrowest tiles that still fit in one round keep the most
@@ -411,11 +412,11 @@ int run_gemm_big_t(hipStream_t st, const half_t* x, const uint32_t* qw, const ha
     for (int nb : {2, 3}) {
       const int tiles = tiles_m * ((N + 64 * nb - 1) / (64 * nb));
       if (tiles <= cus)
-        return nb == 2 ? launch_big<2, MB>(st, x, qw, s, z, y, M, N, K, gshift, 0, 0, tiles)
-                       : launch_big<3, MB>(st, x, qw, s, z, y, M, N, K, gshift, 0, 0, tiles);
+        return nb == 2 ? launch_big<2, MB, BITS>(st, x, qw, s, z, y, M, N, K, gshift, 0, 0, tiles)
+                       : launch_big<3, MB, BITS>(st, x, qw, s, z, y, M, N, K, gshift, 0, 0, tiles);
     }
   }
-  return launch_big<3, MB>(st, x, qw, s, z, y, M, N, K, gshift, full, N, full);
+  return launch_big<3, MB, BITS>(st, x, qw, s, z, y, M, N, K, gshift, full, N, full);
 }
 
 // Output elements one compute unit works through with BM = 32 MB row tiles, following
@@ -436,6 +437,7 @@ long long big_work_per_cu(int MB, int M, int N, int cus) {
   return static_cast<long long>((full + cus - 1) / cus) * BM * 256;
 }
 
+template <int BITS>
 int run_gemm_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, Zeros z, half_t* y,
                  int M, int N, int K, int gshift) {
   // Above 128 rows: 128-row tiles when their smaller tiles fill the device enough better
@@ -448,18 +450,22 @@ int run_gemm_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half
       mb_auto = 4;
   }
   const int mb = env_int("W4A16_TUNE_GEMM_BIG_MB", mb_auto);
-  if (mb == 2) return run_gemm_big_t<2>(st, x, qw, s, z, y, M, N, K, gshift);
-  if (mb == 4) return run_gemm_big_t<4>(st, x, qw, s, z, y, M, N, K, gshift);
-  return run_gemm_big_t<8>(st, x, qw, s, z, y, M, N, K, gshift);
+  if (mb == 2) return run_gemm_big_t<2, BITS>(st, x, qw, s, z, y, M, N, K, gshift);
+  if (mb == 4) return run_gemm_big_t<4, BITS>(st, x, qw, s, z, y, M, N, K, gshift);
+  return run_gemm_big_t<8, BITS>(st, x, qw, s, z, y, M, N, K, gshift);
 }
 
+// Batches past the skinny kernel: the large-tile kernel where its 32-bit element offsets
+// and load widths allow (K % 64 == 0; 8-bit weights also N % 16 == 0 for the 16-byte
+// zero-point loads), else the tiled kernel.
+template <int BITS>
 int run_gemm(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, Zeros z,
              half_t* y, int M, int N, int K, int gshift) {
   if (M >= env_int("W4A16_TUNE_GEMM_BIG_MIN_M", kBigMinM) && K % kBigBK == 0 &&
-      static_cast<long long>(M) * K < (1LL << 31) &&
-      env_int("W4A16_TUNE_GEMM_BIG", 1) != 0)
-    return run_gemm_big(st, x, qw, s, z, y, M, N, K, gshift);
-  return run_gemm_tiled<4>(st, x, qw, s, z, y, M, N, K, gshift);
+      (BITS == 4 || N % 16 == 0) && static_cast<long long>(M) * K < (1LL << 31) &&
+      static_cast<long long>(N) * (K / 32 * BITS) < (1LL << 31) && env_int("W4A16_TUNE_GEMM_BIG", 1) != 0)
+    return run_gemm_big<BITS>(st, x, qw, s, z, y, M, N, K, gshift);
+  return run_gemm_tiled<BITS>(st, x, qw, s, z, y, M, N, K, gshift);
 }
 
 enum class Path { kAuto, kGemv, kGemm };
@@ -518,7 +524,7 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
     return run_skinny<4>(sk, act, st, hx, hq, hs, hz, hy, M, N, K, gshift);
   }
 
-  if (!act) return run_gemm(st, hx, hq, hs, hz, hy, M, N, K, gshift);
+  if (!act) return run_gemm<4>(st, hx, hq, hs, hz, hy, M, N, K, gshift);
 
   // act order: gather x into stored order in stream-ordered scratch memory
   half_t* xs = nullptr;
@@ -529,7 +535,7 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
   hipLaunchKernelGGL(gather_x_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, hx,
                      perm, xs, M, K);
   int rc = check_launch("gather launch");
-  if (rc == W4A16_OK) rc = run_gemm(st, xs, hq, hs, hz, hy, M, N, K, gshift);
+  if (rc == W4A16_OK) rc = run_gemm<4>(st, xs, hq, hs, hz, hy, M, N, K, gshift);
   const int rf = hip_status(hipFreeAsync(xs, st), "hipFreeAsync");
   return rc != W4A16_OK ? rc : rf;
 }
@@ -558,8 +564,8 @@ int w4a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t*
 }
 
 // 8-bit weights ("AWQ + GPTQ Quantization, in depth", 4-bit bigger or 8-bit smaller):
-// M == 1 on the GEMV, larger M on the tiled MFMA kernel (the skinny-batch and
-// large-tile kernels are 4-bit only).
+// M == 1 on the GEMV, up to 32 rows on the skinny kernel, larger batches on the
+// large-tile kernel (the tiled MFMA kernel where its conditions do not hold).
 int w8a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
                const int32_t* g_idx, int group_size, int M, int N, int K, uint16_t* y, void* stream) {
   clear_error();
@@ -593,7 +599,7 @@ int w8a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
     return run_skinny<8>(sk, act, st, hx, hq, hs, hz, hy, M, N, K, gshift);
   if (static_cast<long long>(M) * K >= (1LL << 31) || static_cast<long long>(N) * (K / 4) >= (1LL << 31))
     return fail(W4A16_ERR_UNSUPPORTED, "8-bit layer too large for 32-bit element offsets (M=%d N=%d K=%d)", M, N, K);
-  if (!act) return run_gemm_tiled<8>(st, hx, hq, hs, hz, hy, M, N, K, gshift);
+  if (!act) return run_gemm<8>(st, hx, hq, hs, hz, hy, M, N, K, gshift);
 
   half_t* xs = nullptr;   // act order: x gathered into stored order (stream-ordered scratch)
   const size_t bytes = static_cast<size_t>(M) * K * sizeof(half_t);
@@ -603,7 +609,7 @@ int w8a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
   hipLaunchKernelGGL(gather_x_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, hx,
                      perm, xs, M, K);
   int rc = check_launch("gather launch");
-  if (rc == W4A16_OK) rc = run_gemm_tiled<8>(st, xs, hq, hs, hz, hy, M, N, K, gshift);
+  if (rc == W4A16_OK) rc = run_gemm<8>(st, xs, hq, hs, hz, hy, M, N, K, gshift);
   const int rf = hip_status(hipFreeAsync(xs, st), "hipFreeAsync");
   return rc != W4A16_OK ? rc : rf;
 }

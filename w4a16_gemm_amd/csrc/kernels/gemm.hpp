@@ -20,6 +20,8 @@
 //  * Ragged M and N are masked; a ragged K tile reads zero activations.
 #pragma once
 
+#include <type_traits>
+
 #include "nibbles.hpp"
 
 namespace w4a16 {
@@ -356,7 +358,22 @@ constexpr uint32_t kBigLdsZ = 2 * (kBigBN / 8) * 4;     // packed zero points [h
 constexpr uint32_t kBigStage = kBigLdsA + kBigLdsB + kBigLdsS + kBigLdsZ;
 constexpr size_t kBigLds = static_cast<size_t>(kBigStages) * kBigStage;
 
-template <int NB, int MB>
+// 8-bit codes: twice the code bytes ([quarter of 16 channels][column] x 16 B) and the
+// zero-point bytes of each half as one 16-byte load per lane ([half] x 512 B, byte
+// `column` of a half at offset column).
+constexpr uint32_t kBigLdsB8 = kBigBN * kBigBK;
+constexpr uint32_t kBigLdsZ8 = 2 * 512;
+constexpr uint32_t kBigStage8 = kBigLdsA + kBigLdsB8 + kBigLdsS + kBigLdsZ8;
+constexpr size_t kBigLds8 = static_cast<size_t>(kBigStages) * kBigStage8;
+
+template <int BITS>
+constexpr uint32_t big_stage_bytes() { return BITS == 4 ? kBigStage : kBigStage8; }
+
+// BITS = 8: 8-bit codes (byte order 0, 2, 1, 3): two code loads per thread and stage,
+// lane (r, q) reads the 16 bytes of channels [16 q, +16) of its column, MFMA step s
+// takes words 2s and 2s + 1; zero points are bytes; LDS read with plain loads at every
+// tile height.  Needs N % 16 == 0 (16-byte zero-point loads).
+template <int NB, int MB, int BITS = 4>
 __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uint32_t* __restrict__ qw,
                                          const half_t* __restrict__ scales, Zeros qzeros,
                                          half_t* __restrict__ y, int M, int N, int K, int gshift, int m0, int n0,
@@ -372,8 +389,13 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
   static_assert(NB >= 1 && NB <= 4, "tile width");
   static_assert(MB == 2 || MB == 4 || MB == 8, "tile height");
   constexpr int APT = BM * BK / 8 / 512;  // activation chunks (16 B) per thread per stage
-  static_assert(BL * BK / 32 == 512, "one code chunk per thread per stage (of the widest tile)");
-  static_assert(kBigStage % 16 == 0, "stage alignment");
+  static_assert(BITS == 4 || BITS == 8, "4- or 8-bit weights");
+  constexpr int CL = BITS / 4;            // code loads (16 B) per thread per stage
+  constexpr uint32_t STAGE = big_stage_bytes<BITS>();
+  constexpr uint32_t LB = BITS == 4 ? kBigLdsB : kBigLdsB8;
+  constexpr bool kAsmReads = MB == 8 && BITS == 4;
+  static_assert(BL * BK / 32 == 512, "one 4-bit code chunk per thread per stage (of the widest tile)");
+  static_assert(STAGE % 16 == 0, "stage alignment");
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int tid = threadIdx.x;
@@ -382,7 +404,7 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
   const int wm = wave >> 2, wn = wave & 3;
   const int lr = lane & 15;
   const int lq = lane >> 4;
-  const int W = K >> 3;
+  const int W = K >> (BITS == 4 ? 3 : 2);   // words per row
   const int KT = K / BK;
 
   // Activations: lane l of load i writes chunk c = (APT wave + i) * 64 + l = 8 row + slot,
@@ -396,35 +418,51 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
   }
   // Codes: chunk c = half * BL + column holds channels [32 half, +32) of the column;
   // columns past the tile (BN < BL) or past N re-read a column of the tile.
-  const int b_off = min(n0 + min(tid % BL, BN - 1), n_end - 1) * W + 4 * (tid / BL);
+  // 8-bit: chunk c = tid + 512 i holds channels [16 (c / BL), +16) of column c % BL.
+  int b_off[CL];
+#pragma unroll
+  for (int i = 0; i < CL; ++i) {
+    const int c = tid + 512 * i;
+    b_off[i] = min(n0 + min(c % BL, BN - 1), n_end - 1) * W + 4 * (c / BL);
+  }
   // Scales (wavefront 0, 16 B per lane) and zero points (wavefront 1, 4 B per lane) of
   // half h = lane / 32: 8 columns, resp. one packed word of 8 columns, per lane.
   const int sz_half = lane >> 5;
   const int s_col = min(n0 + 8 * (lane & 31), n_end - 8);
-  const int z_word = min(n0 / 8 + (lane & 31), n_end / 8 - 1);
+  const int z_word = BITS == 4 ? min(n0 / 8 + (lane & 31), n_end / 8 - 1)
+                               : min(n0 / 4 + 4 * (lane & 31), n_end / 4 - 4);   // 8-bit: 16 columns per lane
 
   // Tile t goes to stage t % NS; tiles past the end re-load the last one into a stage
   // that is never read again.  The scale / zero load comes first, so that waiting for
   // tile t alone never waits for more than that load of tile t + 1.
   auto load_tile = [&](int t) {
     const int tc = min(t, KT - 1);
-    unsigned char* stage = smem + (t % NS) * kBigStage;
+    unsigned char* stage = smem + (t % NS) * STAGE;
     const int gi = (tc * BK + 32 * sz_half) >> gshift;
     if (wave == 0)
       __builtin_amdgcn_global_load_lds(
           reinterpret_cast<const void*>(scales + static_cast<size_t>(gi) * N + s_col),
-          reinterpret_cast<void*>(stage + kBigLdsA + kBigLdsB), 16, 0, 0);
-    else if (wave == 1)
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void*>(qzeros.at(static_cast<size_t>(gi) * (N >> 3) + z_word)),
-          reinterpret_cast<void*>(stage + kBigLdsA + kBigLdsB + kBigLdsS), 4, 0, 0);
+          reinterpret_cast<void*>(stage + kBigLdsA + LB), 16, 0, 0);
+    else if (wave == 1) {
+      if constexpr (BITS == 4)
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(qzeros.at(static_cast<size_t>(gi) * (N >> 3) + z_word)),
+            reinterpret_cast<void*>(stage + kBigLdsA + LB + kBigLdsS), 4, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(
+            reinterpret_cast<const void*>(qzeros.at(static_cast<size_t>(gi) * (N >> 2) + z_word)),
+            reinterpret_cast<void*>(stage + kBigLdsA + LB + kBigLdsS), 16, 0, 0);
+    }
     const half_t* xt = x + tc * BK;
 #pragma unroll
     for (int i = 0; i < APT; ++i)
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(xt + a_off[i]),
                                        reinterpret_cast<void*>(stage + (wave * APT + i) * 64 * 16), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(qw + b_off + tc * (BK / 8)),
-                                     reinterpret_cast<void*>(stage + kBigLdsA + wave * 64 * 16), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < CL; ++i)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(qw + b_off[i] + tc * (BK * BITS / 32)),
+                                       reinterpret_cast<void*>(stage + kBigLdsA + (512 * i + wave * 64) * 16), 16, 0,
+                                       0);
   };
 
   float4_t acc[MB][NB];
@@ -438,35 +476,41 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
   // 256 nb; scale of block nb at s_lane + 32 nb; zero word of block nb at z_lane + 8 nb.
   const uint32_t base = lds_offset(smem);
   const uint32_t a_lane = base + (wm * 16 * MB + lr) * 128;
-  const uint32_t b_lane = base + kBigLdsA + ((lq >> 1) * BL + wn * 16 * NB + lr) * 16 + (lq & 1) * 8;
-  const uint32_t s_lane = base + kBigLdsA + kBigLdsB + ((lq >> 1) * BL + wn * 16 * NB + lr) * 2;
+  const uint32_t b_lane = BITS == 4 ? base + kBigLdsA + ((lq >> 1) * BL + wn * 16 * NB + lr) * 16 + (lq & 1) * 8
+                                    : base + kBigLdsA + (lq * BL + wn * 16 * NB + lr) * 16;
+  const uint32_t s_lane = base + kBigLdsA + LB + ((lq >> 1) * BL + wn * 16 * NB + lr) * 2;
   const uint32_t z_lane =
-      base + kBigLdsA + kBigLdsB + kBigLdsS + ((lq >> 1) * (BL / 8) + wn * 2 * NB + (lr >> 3)) * 4;
+      BITS == 4 ? base + kBigLdsA + LB + kBigLdsS + ((lq >> 1) * (BL / 8) + wn * 2 * NB + (lr >> 3)) * 4
+                : base + kBigLdsA + LB + kBigLdsS + (lq >> 1) * 512 + wn * 16 * NB + lr;   // a byte
   const int z_shift = 4 * (lr & 7);
 
-  // At most APT + 1 loads of this wavefront are newer than the last load of tile t once
-  // tile t + 1 has been issued after it.
+  // At most APT + CL loads of this wavefront (its activation and code loads of tile
+  // t + 1) are newer than the last load of tile t once tile t + 1 has been issued.
   load_tile(0);
   load_tile(1);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(APT + 1) : "memory");   // tile 0
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(APT + CL) : "memory");   // tile 0
   block_barrier();
 
   for (int t = 0; t < KT; ++t) {
     load_tile(t + NS - 1);
-    const uint32_t so = (t % NS) * kBigStage;
+    const uint32_t so = (t % NS) * STAGE;
     half8_t af[MB];
-    uint2 cw[NB];
+    using CodeWords = std::conditional_t<BITS == 4, uint2, uint4>;
+    CodeWords cw[NB];
     uint32_t sc[NB], zw[NB];
-    const unsigned char* st = smem + so;   // plain-load view of the same stage (MB < 8)
-    if constexpr (MB == 8) {
+    const unsigned char* st = smem + so;   // plain-load view of the same stage
+    if constexpr (kAsmReads) {
       lds_read_tile<NB>(a_lane + so + 16 * ((2 * lq) ^ (lr & 7)), b_lane + so, s_lane + so, z_lane + so, af, cw, sc,
                         zw);
     } else {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        cw[nb] = *reinterpret_cast<const uint2*>(st + (b_lane - base) + 256 * nb);
+        cw[nb] = *reinterpret_cast<const CodeWords*>(st + (b_lane - base) + 256 * nb);
         sc[nb] = *reinterpret_cast<const uint16_t*>(st + (s_lane - base) + 32 * nb);
-        zw[nb] = *reinterpret_cast<const uint32_t*>(st + (z_lane - base) + 8 * nb);
+        if constexpr (BITS == 4)
+          zw[nb] = *reinterpret_cast<const uint32_t*>(st + (z_lane - base) + 8 * nb);
+        else
+          zw[nb] = *(st + (z_lane - base) + 16 * nb);
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
@@ -475,12 +519,12 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
     DequantConsts dc[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      dc[nb] = make_consts((qzeros.word(zw[nb]) >> z_shift) & 0xFu,
+      dc[nb] = make_consts(BITS == 4 ? (qzeros.word(zw[nb]) >> z_shift) & 0xFu : (qzeros.sym ? 128u : zw[nb]),
                            __builtin_bit_cast(half_t, static_cast<uint16_t>(sc[nb])));
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (s == 1) {
-        if constexpr (MB == 8) {
+        if constexpr (kAsmReads) {
           lds_read_a8(a_lane + so + 16 * ((2 * lq + 1) ^ (lr & 7)), af);
         } else {
 #pragma unroll
@@ -491,14 +535,22 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
       }
       half8_t bf[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) bf[nb] = dequant_word(s == 0 ? cw[nb].x : cw[nb].y, dc[nb]);
+      for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (BITS == 4) {
+          bf[nb] = dequant_word(s == 0 ? cw[nb].x : cw[nb].y, dc[nb]);
+        } else {
+          const half4_t lo = dequant_word8(s == 0 ? cw[nb].x : cw[nb].z, dc[nb]);
+          const half4_t hi = dequant_word8(s == 0 ? cw[nb].y : cw[nb].w, dc[nb]);
+          bf[nb] = half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
     }
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(APT + 1) : "memory");   // tile t + 1
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(APT + CL) : "memory");   // tile t + 1
     block_barrier();
   }
   // the clamped loads past the last tile must land before the workgroup's LDS is released
@@ -524,7 +576,7 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
 // BM = 32 MB rows (256 for prefill; 128 / 64 for batches of up to 128 / 64 rows).
 // With one wave of full tiles and one of narrower tiles, both rounds fill the device
 // when the full-width tiles alone would leave most of a second round idle.
-template <int NB2, int MB>
+template <int NB2, int MB, int BITS = 4>
 __global__ __launch_bounds__(512) void gemm_big_kernel(const half_t* __restrict__ x, const uint32_t* __restrict__ qw,
                                                        const half_t* __restrict__ scales,
                                                        Zeros qzeros, half_t* __restrict__ y,
@@ -535,13 +587,13 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(const half_t* __restrict_
   if (bid < split) {
     const int tiles_n = (n_split + 255) / 256;
     const int tile = xcd_tile(bid, tiles_m, tiles_n);
-    big_tile<4, MB>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM, (tile % tiles_n) * 256,
+    big_tile<4, MB, BITS>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM, (tile % tiles_n) * 256,
                 min(N, n_split));
   } else {
     constexpr int BN2 = 64 * NB2;
     const int tiles_n = (N - n_split + BN2 - 1) / BN2;
     const int tile = xcd_tile(bid - split, tiles_m, tiles_n);
-    big_tile<NB2, MB>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM,
+    big_tile<NB2, MB, BITS>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM,
                   n_split + (tile % tiles_n) * BN2, N);
   }
 }

@@ -94,6 +94,8 @@ VARIANTS = {
     # the same layer with 8-bit weights ("in depth", 4-bit bigger or 8-bit smaller)
     "c3w8": replace(CONFIGS["c3"], name="c3w8", bits=8,
                     note="70B-class MLP up-projection, asymmetric 8-bit weights, decode"),
+    "c4w8": replace(CONFIGS["c4"], name="c4w8", bits=8,
+                    note="prefill GEMM, asymmetric 8-bit weights"),
 }
 
 
