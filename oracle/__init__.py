@@ -24,6 +24,12 @@ What it computes, in plain numpy float64 (slow and obviously correct):
                      depth", The two algorithms, compactly).
 * ``awq_search``     the AWQ grid search over alpha: loss of every alpha on the
                      calibration activations, best alpha (same page and section).
+* ``gptq_quantize`` / ``gptq_hessian`` / ``output_error``
+                     GPTQ: H = 2 X X^T with damping, the upper Cholesky factor of
+                     H^-1, column-by-column rounding with error feedback onto the
+                     columns not yet rounded, natural or act order; emits the
+                     round-to-nearest quantiser's codes / scales / zeros / g_idx
+                     (same page and section, the GPTQ half).
 * ``act_order``      GPTQ act-order group assignment g_idx from the calibration
                      activations (same page and section).
 * ``pack_codes`` / ``unpack_codes`` / ``pack_zeros`` / ``unpack_zeros``
@@ -48,6 +54,7 @@ from .quant import (round_half_even, fp16_ceil, group_index, rtn_quantize,
                     awq_scales, awq_fold_weights, awq_fold_activations,
                     act_order_h, act_order)
 from .awq_search import awq_search
+from .gptq import gptq_hessian, gptq_quantize, output_error
 from .packing import (pack_codes, unpack_codes, pack_zeros, unpack_zeros,
                       sorted_k_order, pack_codes_act_order,
                       pack_codes8, unpack_codes8, pack_zeros8, unpack_zeros8)
@@ -60,5 +67,6 @@ __all__ = [
     "pack_codes", "unpack_codes", "pack_zeros", "unpack_zeros",
     "sorted_k_order", "pack_codes_act_order",
     "dequant", "dequant_fp16", "linear", "rel_err",
+    "awq_search", "gptq_hessian", "gptq_quantize", "output_error",
     "layer_bytes", "bits_per_weight",
 ]
