@@ -386,6 +386,41 @@ def awq_search_bench(cfg: wl.LayerConfig, n_alpha: int = 11):
     }
 
 
+def gptq_bench(cfg: wl.LayerConfig):
+    """GPTQ of one layer with its calibration activations in act order: wall time of the
+    whole call (host inputs, device work, host outputs) and the layer's output error on
+    the calibration rows against round-to-nearest, both measured on the host."""
+    import torch
+    import w4a16_gemm_amd as w4
+    w = wl.weights(cfg)
+    X = wl.calibration(cfg)
+    w4.w4a16_gptq(w[:64, :256], X[:8, :256], 32, True)      # load, first-touch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    codes, S, Z, g_idx = w4.w4a16_gptq(w, X, cfg.group_size, True)
+    wall = time.perf_counter() - t0
+    rc, rs, rz = w4.w4a16_quantize(w, cfg.group_size, g_idx)
+    Wd = w.astype(np.float32)
+    Xd = X.astype(np.float32).T
+    ref = Wd @ Xd
+
+    def out_err(c, s_, z_):
+        gid = g_idx.astype(np.int64)
+        What = (c.astype(np.float32) - z_.astype(np.float32)[gid, :].T) * s_.astype(np.float32)[gid, :].T
+        return float(np.linalg.norm(ref - What @ Xd) / np.linalg.norm(ref))
+    T = X.shape[0]
+    return {
+        "workload": f"GPTQ of the {cfg.name} layer (N={cfg.N}, K={cfg.K}, group {cfg.group_size}, act order, "
+                    f"damp 0.01) with its {T} calibration tokens",
+        "wall_s": round(wall, 3),
+        "output_error_gptq": round(out_err(codes, S, Z), 5),
+        "output_error_rtn": round(out_err(rc, rs, rz), 5),
+        "note": "whole call: uploads, H = 2XX^T, factorisation and triangular inverse (one launch per pivot), "
+                "the blocked rounding with error feedback, downloads; output error ||(W - W^) X|| / ||W X|| "
+                "on the calibration rows (float32 on the host)",
+    }
+
+
 def traffic_for(hash_now: str, key: str):
     try:
         with open(TRAFFIC_FILE) as f:
@@ -409,6 +444,7 @@ def main() -> int:
     ap.add_argument("--no-dense-ref", action="store_true",
                     help="skip timing the dense binary16 library GEMM of the same shapes")
     ap.add_argument("--no-awq-search", action="store_true", help="skip timing the AWQ alpha search")
+    ap.add_argument("--no-gptq", action="store_true", help="skip timing the GPTQ quantiser")
     ap.add_argument("--no-decode-step", action="store_true",
                     help="skip the whole-decode-step workload of the 1.5B example")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -525,6 +561,9 @@ def main() -> int:
     if not args.no_awq_search and args.configs in ("all", "headline"):
         log("timing the AWQ alpha search on the c2 up-projection layer")
         line["awq_search"] = awq_search_bench(wl.CONFIGS["c2up"])
+    if not args.no_gptq and args.configs in ("all", "headline"):
+        log("timing GPTQ on the c4 prefill layer")
+        line["gptq"] = gptq_bench(wl.CONFIGS["c4"])
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (cpu_baseline)")
         line["cpu_baseline"] = cpu_baseline(hcfg, args.cpu_rows)

@@ -224,6 +224,32 @@ int w4a16_quantize_device(const uint16_t* w, int N, int K, int group_size, const
 int w4a16_awq_search(const uint16_t* w, const uint16_t* xcal, int N, int K, int T, int group_size,
                      const double* alphas, int n_alpha, double* losses, int* best, void* stream);
 
+/* GPTQ quantiser ("AWQ + GPTQ Quantization, in depth", The two algorithms, compactly,
+ * the GPTQ half and its pseudocode; "How do GPTQ and AWQ differ...", GPTQ: quantize
+ * then compensate).  With X = xcal^T (input channels x tokens):
+ *   H = 2 X X^T + damp * mean(diag(2 X X^T)) * I,   U = upper Cholesky factor of H^-1
+ * then every input channel j in visiting order is rounded on the grid of its group and
+ * its error (w_j - w^_j) / U[j][j] is fed to the channels not yet visited through
+ * row j of U.  The visiting order is the channel order, or with act_order != 0 the
+ * order of w4a16_act_order (descending sum_t X[t][k]^2, exact, ties by ascending k),
+ * whose g_idx is written.  A group's grid is the asymmetric one of w4a16_quantize
+ * (range including 0, S = smallest binary16 >= (hi - lo) / 15, Z = clamp(round(-lo / S),
+ * 0, 15), round half to even), from the group's weights as they stand when its first
+ * channel is reached.  Binary64 throughout; the results equal the column-by-column
+ * definition up to the rounding of the factorisation and of the blocked updates.
+ *   w       binary16 [N][K] (host);  xcal binary16 [T][K] (host);  damp >= 0 (0.01 is
+ *           typical)
+ *   codes   out uint8 [N][K], original channel order;  scales out binary16 [G][N];
+ *   zeros   out uint8 [G][N];  g_idx out int32 [K] (act_order != 0; may be NULL
+ *           otherwise)
+ * Pack with w4a16_pack / w4a16_pack_zeros (passing g_idx under act order).  Device
+ * memory (about 8 (N K + T K + 2 K^2) bytes) is allocated for the call and freed before
+ * it returns; the work runs on `stream`; the call returns when the outputs are on the
+ * host.  Errors: INVALID_ARG (also when the damped H is not positive definite),
+ * UNSUPPORTED, HIP. */
+int w4a16_gptq(const uint16_t* w, const uint16_t* xcal, int N, int K, int T, int group_size, int act_order,
+               double damp, uint8_t* codes, uint16_t* scales, uint8_t* zeros, int32_t* g_idx, void* stream);
+
 /* ---------------------------------------------------------------------------------
  * 8-bit weights (W8A16): the same layer with 256-level codes ("AWQ + GPTQ
  * Quantization, in depth", 4-bit bigger or 8-bit smaller).  Same conventions,

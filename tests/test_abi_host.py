@@ -26,7 +26,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = w4.lib()
     declared = _declared_functions()
-    assert len(declared) == 25
+    assert len(declared) == 26
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(w4.EXPORTS) == declared
@@ -327,3 +327,35 @@ def test_error_codes_device_argument_checks():
     assert lib.w4a16_dequant(ok, None, ok, None, 64, 8, 128, ok, None) == w4.ERR_INVALID_ARG
     assert lib.w4a16_gemm(mis, ok, ok, ok, None, 128, 1, 8, 128, ok, None) == w4.ERR_MISALIGNED
     assert "aligned" in lib.w4a16_last_error().decode()
+
+
+def test_gptq_rejects_bad_arguments_before_any_device_work():
+    """Argument checks of w4a16_gptq run on the host, before any device call."""
+    import ctypes
+    L = w4.lib()
+    N, K, T, g = 16, 64, 8, 32
+    w = np.zeros((N, K), np.float16)
+    x = np.ones((T, K), np.float16)
+    c = np.empty((N, K), np.uint8)
+    s = np.empty((K // g, N), np.float16)
+    z = np.empty((K // g, N), np.uint8)
+    gi = np.empty(K, np.int32)
+    P = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+
+    def call(N=N, K=K, T=T, g=g, act=0, damp=0.01, w=w, x=x, gidx=gi):
+        return L.w4a16_gptq(P(w), P(x), N, K, T, g, act, damp, P(c), P(s), P(z),
+                            None if gidx is None else P(gidx), None)
+
+    assert call(T=0) == w4.ERR_INVALID_ARG
+    assert call(damp=-1.0) == w4.ERR_INVALID_ARG
+    assert call(damp=float("nan")) == w4.ERR_INVALID_ARG
+    assert call(g=48) == w4.ERR_UNSUPPORTED
+    assert call(N=12) == w4.ERR_INVALID_ARG
+    assert call(act=1, gidx=None) == w4.ERR_INVALID_ARG
+    wn = w.copy()
+    wn[3, 7] = np.inf
+    assert call(w=wn) == w4.ERR_INVALID_ARG
+    xn = x.copy()
+    xn[1, 2] = np.nan
+    assert call(x=xn) == w4.ERR_INVALID_ARG
+    assert b"finite" in L.w4a16_last_error()

@@ -44,6 +44,8 @@ _SIGNATURES = {
                                        _c_void_p, _c_void_p, _c_void_p]),
     "w4a16_awq_search": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p,
                                   _c_int, _c_void_p, _c_void_p, _c_void_p]),
+    "w4a16_gptq": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_int, ctypes.c_double,
+                            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "w8a16_qweight_words": (ctypes.c_size_t, [_c_int, _c_int, _c_int]),
     "w8a16_quantize": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_void_p,
                                 _c_void_p, _c_void_p, _c_void_p]),
@@ -401,6 +403,28 @@ def w4a16_awq_search(w, xcal, group_size: int, alphas, stream=None):
     _check(lib().w4a16_awq_search(_ptr(w), _ptr(X), N, K, T, group_size, _ptr(a), a.size, _ptr(losses),
                                   ctypes.addressof(best), _stream_handle(stream, torch.device("cuda:0"))))
     return losses, best.value
+
+
+def w4a16_gptq(w, xcal, group_size: int, act_order: bool = False, damp: float = 0.01, stream=None):
+    """GPTQ on the device: (codes uint8 [N][K], scales binary16 [G][N], zeros uint8
+    [G][N], g_idx int32 [K] or None), the formats of w4a16_quantize.  w binary16 [N][K]
+    and xcal binary16 [T][K] on the host."""
+    import torch
+    w = _np(w, np.float16, 2)
+    X = _np(xcal, np.float16, 2)
+    N, K = w.shape
+    T = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError("xcal must have K columns")
+    G = K // group_size if group_size > 0 and K % group_size == 0 else 0
+    codes = np.empty((N, K), np.uint8)
+    scales = np.empty((G, N), np.float16)
+    zeros = np.empty((G, N), np.uint8)
+    g_idx = np.empty(K, np.int32) if act_order else None
+    _check(lib().w4a16_gptq(_ptr(w), _ptr(X), N, K, T, group_size, int(bool(act_order)), float(damp),
+                            _ptr(codes), _ptr(scales), _ptr(zeros), None if g_idx is None else _ptr(g_idx),
+                            _stream_handle(stream, torch.device("cuda:0"))))
+    return codes, scales, zeros, g_idx
 
 
 def w4a16_quantize_device(w, group_size: int, in_scale=None, sym: bool = False, stream=None):

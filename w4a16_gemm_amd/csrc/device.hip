@@ -13,6 +13,7 @@
 #include "kernels/aux.hpp"
 #include "kernels/gemm.hpp"
 #include "kernels/gemv.hpp"
+#include "kernels/gptq.hpp"
 #include "kernels/quantize.hpp"
 #include "kernels/skinny.hpp"
 
@@ -733,6 +734,103 @@ int w4a16_awq_search(const uint16_t* w, const uint16_t* xcal, int N, int K, int 
   for (int i = 1; i < n_alpha; ++i)
     if (losses[i] < losses[b]) b = i;
   *best = b;
+  return release(W4A16_OK);
+}
+
+// GPTQ ("AWQ + GPTQ Quantization, in depth", The two algorithms, compactly): host
+// inputs and outputs, binary64 device work on `stream`, returns when the outputs are on
+// the host.
+int w4a16_gptq(const uint16_t* w, const uint16_t* xcal, int N, int K, int T, int group_size, int act_order,
+               double damp, uint8_t* codes, uint16_t* scales, uint8_t* zeros, int32_t* g_idx, void* stream) {
+  clear_error();
+  if (!w || !xcal || !codes || !scales || !zeros || (act_order && !g_idx))
+    return fail(W4A16_ERR_INVALID_ARG, "NULL buffer");
+  if (T <= 0) return fail(W4A16_ERR_INVALID_ARG, "T must be positive (T=%d)", T);
+  if (!(damp >= 0.0) || !std::isfinite(damp)) return fail(W4A16_ERR_INVALID_ARG, "damp must be a finite number >= 0");
+  if (int rc = check_shape(N, K, group_size)) return rc;
+  const size_t nk = static_cast<size_t>(N) * K, tk = static_cast<size_t>(T) * K, kk = static_cast<size_t>(K) * K;
+  for (size_t i = 0; i < nk; ++i)
+    if (((w[i] >> 10) & 0x1F) == 0x1F) return fail(W4A16_ERR_INVALID_ARG, "weight %zu is not finite", i);
+  // visiting order: act order (descending diag(H), exact) or the channels in order
+  std::vector<int32_t> order;
+  if (int rc = act_order_rank(xcal, T, K, order)) return rc;   // also checks xcal is finite
+  if (act_order) {
+    for (int i = 0; i < K; ++i) g_idx[order[i]] = i / group_size;
+  } else {
+    for (int k = 0; k < K; ++k) order[k] = k;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int G = K / group_size;
+
+  std::vector<void*> dev;
+  auto release = [&](int rc) {
+    for (void* p : dev) (void)hipFree(p);
+    return rc;
+  };
+  auto alloc = [&](size_t bytes) -> void* {
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) return nullptr;
+    dev.push_back(p);
+    return p;
+  };
+  auto* dw = static_cast<uint16_t*>(alloc(nk * 2));
+  auto* dx = static_cast<uint16_t*>(alloc(tk * 2));
+  auto* dperm = static_cast<int32_t*>(alloc(static_cast<size_t>(K) * 4));
+  auto* dwp = static_cast<double*>(alloc(nk * 8));
+  auto* dxp = static_cast<double*>(alloc(tk * 8));
+  auto* dH = static_cast<double*>(alloc(kk * 8));
+  auto* dU = static_cast<double*>(alloc(kk * 8));
+  auto* derr = static_cast<double*>(alloc(static_cast<size_t>(N) * kGptqBlock * 8));
+  auto* dsz = static_cast<double2*>(alloc(static_cast<size_t>(N) * sizeof(double2)));
+  auto* dcp = static_cast<uint8_t*>(alloc(nk));
+  auto* dc = static_cast<uint8_t*>(alloc(nk));
+  auto* ds = static_cast<uint16_t*>(alloc(static_cast<size_t>(G) * N * 2));
+  auto* dz = static_cast<uint8_t*>(alloc(static_cast<size_t>(G) * N));
+  auto* dflag = static_cast<int*>(alloc(sizeof(int)));
+  if (dev.size() != 14) return release(fail(W4A16_ERR_HIP, "hipMalloc failed for the GPTQ buffers"));
+  const int zero = 0;
+  int flag = 0;
+  auto copy = [&](void* dst, const void* src, size_t bytes, hipMemcpyKind kind) {
+    return hip_status(hipMemcpyAsync(dst, src, bytes, kind, st), "hipMemcpyAsync");
+  };
+  if (int rc = copy(dw, w, nk * 2, hipMemcpyHostToDevice)) return release(rc);
+  if (int rc = copy(dx, xcal, tk * 2, hipMemcpyHostToDevice)) return release(rc);
+  if (int rc = copy(dperm, order.data(), static_cast<size_t>(K) * 4, hipMemcpyHostToDevice)) return release(rc);
+  if (int rc = copy(dflag, &zero, sizeof(int), hipMemcpyHostToDevice)) return release(rc);
+  auto blocks = [](size_t n) { return dim3(static_cast<unsigned>((n + 255) / 256)); };
+
+  // weights and calibration rows in visiting order, H = 2 X X^T, damping
+  hipLaunchKernelGGL(gptq_gather_kernel, blocks(nk), dim3(256), 0, st, dw, dperm, static_cast<size_t>(N), K, dwp);
+  hipLaunchKernelGGL(gptq_gather_kernel, blocks(tk), dim3(256), 0, st, dx, dperm, static_cast<size_t>(T), K, dxp);
+  const unsigned kt = static_cast<unsigned>((K + 63) / 64);
+  hipLaunchKernelGGL(gptq_gram_kernel, dim3(kt, kt), dim3(256), 0, st, dxp, T, K, dH);
+  hipLaunchKernelGGL(gptq_damp_kernel, dim3(1), dim3(256), 0, st, dH, K, damp);
+  if (int rc = check_launch("GPTQ Hessian launch")) return release(rc);
+  // H = Ut^T Ut from the bottom-right corner, then U = (Ut^T)^-1
+  for (int p = K - 1; p >= 1; --p) hipLaunchKernelGGL(gptq_chol_step_kernel, dim3(p), dim3(256), 0, st, dH, K, p);
+  hipLaunchKernelGGL(gptq_chol_finish_kernel, dim3(K), dim3(256), 0, st, dH, K, dflag);
+  hipLaunchKernelGGL(gptq_eye_kernel, blocks(kk), dim3(256), 0, st, dU, K);
+  for (int p = K - 1; p >= 1; --p) hipLaunchKernelGGL(gptq_trinv_step_kernel, dim3(p), dim3(256), 0, st, dH, dU, K, p);
+  hipLaunchKernelGGL(gptq_trinv_finish_kernel, dim3(K), dim3(256), 0, st, dH, dU, K);
+  if (int rc = check_launch("GPTQ factorisation launch")) return release(rc);
+  // rounding with error feedback, 32 visited columns at a time
+  for (int i0 = 0; i0 < K; i0 += kGptqBlock) {
+    hipLaunchKernelGGL(gptq_block_kernel, dim3(static_cast<unsigned>((N + 127) / 128)), dim3(128), 0, st, dwp, dU, N,
+                       K, i0, group_size, dsz, derr, dcp, ds, dz);
+    const int rest = K - i0 - kGptqBlock;
+    if (rest > 0)
+      hipLaunchKernelGGL(gptq_update_kernel, dim3(static_cast<unsigned>((rest + 63) / 64),
+                                                  static_cast<unsigned>((N + 63) / 64)),
+                         dim3(256), 0, st, dwp, dU, derr, N, K, i0);
+  }
+  hipLaunchKernelGGL(gptq_scatter_codes_kernel, blocks(nk), dim3(256), 0, st, dcp, dperm, N, K, dc);
+  if (int rc = check_launch("GPTQ rounding launch")) return release(rc);
+  if (int rc = copy(codes, dc, nk, hipMemcpyDeviceToHost)) return release(rc);
+  if (int rc = copy(scales, ds, static_cast<size_t>(G) * N * 2, hipMemcpyDeviceToHost)) return release(rc);
+  if (int rc = copy(zeros, dz, static_cast<size_t>(G) * N, hipMemcpyDeviceToHost)) return release(rc);
+  if (int rc = copy(&flag, dflag, sizeof(int), hipMemcpyDeviceToHost)) return release(rc);
+  if (int rc = hip_status(hipStreamSynchronize(st), "hipStreamSynchronize")) return release(rc);
+  if (flag) return release(fail(W4A16_ERR_INVALID_ARG, "the damped Hessian is not positive definite (raise damp)"));
   return release(W4A16_OK);
 }
 

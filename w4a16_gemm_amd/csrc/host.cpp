@@ -225,6 +225,22 @@ int check_shape(int N, int K, int group_size) {
   return W4A16_OK;
 }
 
+int act_order_rank(const uint16_t* xcal, int T, int K, std::vector<int32_t>& order) {
+  // sum_t X^2 exactly, in units of 2^-48 (each square is below 2^80)
+  std::vector<__int128> h(K, 0);
+  for (int t = 0; t < T; ++t)
+    for (int k = 0; k < K; ++k) {
+      const uint16_t v = xcal[static_cast<size_t>(t) * K + k];
+      if (!half_is_finite(v)) return fail(W4A16_ERR_INVALID_ARG, "calibration value not finite");
+      const __int128 u = half_abs_units(v);
+      h[k] += u * u;
+    }
+  order.resize(K);
+  for (int k = 0; k < K; ++k) order[k] = k;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return h[a] > h[b]; });
+  return W4A16_OK;
+}
+
 int check_gidx_and_sort(const int32_t* g_idx, int K, int group_size, int32_t* perm) {
   const int G = K / group_size;
   std::vector<int32_t> count(G, 0);
@@ -467,18 +483,8 @@ int w4a16_act_order(const uint16_t* xcal, int T, int K, int group_size, int32_t*
   if (!xcal || !g_idx) return fail(W4A16_ERR_INVALID_ARG, "NULL buffer");
   if (T <= 0) return fail(W4A16_ERR_INVALID_ARG, "T must be positive");
   if (int st = check_shape(8, K, group_size)) return st;
-  // sum_t X^2 exactly, in units of 2^-48 (each square is below 2^80)
-  std::vector<__int128> h(K, 0);
-  for (int t = 0; t < T; ++t)
-    for (int k = 0; k < K; ++k) {
-      const uint16_t v = xcal[static_cast<size_t>(t) * K + k];
-      if (!half_is_finite(v)) return fail(W4A16_ERR_INVALID_ARG, "calibration value not finite");
-      const __int128 u = half_abs_units(v);
-      h[k] += u * u;
-    }
-  std::vector<int32_t> order(K);
-  for (int k = 0; k < K; ++k) order[k] = k;
-  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return h[a] > h[b]; });
+  std::vector<int32_t> order;
+  if (int st = act_order_rank(xcal, T, K, order)) return st;
   for (int i = 0; i < K; ++i) g_idx[order[i]] = i / group_size;
   return W4A16_OK;
 }

@@ -4,6 +4,7 @@
 
 #include <cstddef>
 #include <cstdint>
+#include <vector>
 
 #include "w4a16.h"
 
@@ -20,6 +21,11 @@ int check_shape(int N, int K, int group_size);
 // g_idx (host memory): every value in [0, G) and every group exactly group_size
 // members.  On success fills perm (size K) with the stable sort of k by g_idx[k].
 int check_gidx_and_sort(const int32_t* g_idx, int K, int group_size, int32_t* perm);
+
+// GPTQ act order ("AWQ + GPTQ Quantization, in depth", The two algorithms, compactly):
+// input channels by descending sum_t X[t][k]^2 (exact), ties by ascending k.
+// xcal binary16 [T][K] (host); fails on a non-finite value.
+int act_order_rank(const uint16_t* xcal, int T, int K, std::vector<int32_t>& order);
 
 // Private weight-buffer layout (the ABI treats it as opaque).
 //   words [N][K/8]: word w of row n holds the codes of stored positions 8w..8w+7;
