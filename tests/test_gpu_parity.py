@@ -305,3 +305,35 @@ def test_configs_match_oracle_on_sampled_outputs(full_layers, name, M):
     # and a second run is bit-identical (each output written once, fixed order)
     y2 = run_gemm(prod, x=x).cpu().numpy()[:, rows]
     assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
+
+
+# M = 1 row shapes: with rows to spare the GEMV takes up to 4 chunks per lane (16 or 32
+# lanes per row for K = 1024 .. 4096); every lanes-per-row value forced on one layer
+GEMV_SHAPES = [
+    # name, N, K, group, act_order, bits
+    ("v1", 14344, 1024, 32, False, 4),    # 16 lanes per row, ragged last unit
+    ("v2", 8200, 2048, 64, True, 4),      # 32 lanes, 2 chunks each, act order
+    ("v3", 11008, 4096, 32, True, 4),     # 32 lanes, 4 chunks each (the act-order layer's shape)
+    ("v4", 12296, 2048, 128, False, 8),   # 8-bit: 32 lanes, 4 chunks each
+]
+
+
+@pytest.mark.parametrize("case", range(len(GEMV_SHAPES)))
+def test_gemv_row_shapes_match_oracle(case):
+    name, N, K, g, act, bits = GEMV_SHAPES[case]
+    cfg = wl.custom_config(name, 760 + case, K=K, N=N, group_size=g, M_list=(1,), act_order=act, bits=bits)
+    note(f"GEMV shapes {name} N={N} K={K} g={g} act={act} bits={bits}")
+    prod = product_layer(cfg, 1)
+    ref = oracle_layer(cfg, 1, np.arange(N))
+    C = K // (32 if bits == 4 else 16)
+    try:
+        for lpr in [None] + [l for l in (64, 32, 16, 8) if (C + l - 1) // l <= 4]:
+            if lpr is None:
+                os.environ.pop("W4A16_TUNE_GEMV_LPR", None)
+            else:
+                os.environ["W4A16_TUNE_GEMV_LPR"] = str(lpr)
+            note(f"  lanes per row {lpr or 'auto'}")
+            y = run_gemm(prod).cpu().numpy()
+            assert oracle.rel_err(y, ref["y_ref"]) <= TOL, lpr
+    finally:
+        os.environ.pop("W4A16_TUNE_GEMV_LPR", None)

@@ -202,15 +202,38 @@ struct GemvPlan {
   size_t shmem = 0;
 };
 
+GemvPlan plan_gemv_for(const GemvShape& sh, int N, int K, int gshift, bool act, int bits);
+
+// The GEMV's launch plan.  Rows of at most 256 chunks: the exact split with the most
+// chunks per lane (up to 4) that still gives about 1.5 rounds of row units over the
+// compute units, else the default shape of pick_gemv_shape.  Measured at M = 1 (lanes per
+// row forced, same process): K = 1024 / 2048 / 4096 rows with enough of them run 18% /
+// 16% / 8–11% faster with 4 / 2 / 4 chunks per lane than with the widest exact split,
+// and K = 4096 at N = 4096 (one round of 16-row units) 5% slower, hence the row-unit bound.
 GemvPlan plan_gemv(int N, int K, int gshift, bool act, int bits = 4) {
-  GemvPlan p;
   const int C = K / (bits == 4 ? 32 : 16);   // 16-byte chunks per row
-  p.sh = pick_gemv_shape(C);
-  if (p.sh.lpr == 0) return p;
+  GemvShape sh = pick_gemv_shape(C);
+  if (sh.lpr == 0) return GemvPlan{};
   // measurements only: lanes per row forced (rows of at most 256 chunks)
   const int lpr = env_int("W4A16_TUNE_GEMV_LPR", 0);
-  if (p.sh.wpr == 1 && (lpr == 8 || lpr == 16 || lpr == 32 || lpr == 64) && (C + lpr - 1) / lpr <= 4)
-    p.sh = {lpr, (C + lpr - 1) / lpr, C % lpr == 0, 1};
+  if (sh.wpr == 1 && (lpr == 8 || lpr == 16 || lpr == 32 || lpr == 64) && (C + lpr - 1) / lpr <= 4)
+    return plan_gemv_for({lpr, (C + lpr - 1) / lpr, C % lpr == 0, 1}, N, K, gshift, act, bits);
+  if (sh.wpr == 1) {
+    const int cus = device_cus();
+    for (int l : {8, 16, 32}) {
+      if (C % l != 0 || C / l > 4 || l >= sh.lpr) continue;
+      const long long units = (N + kGemvWaves * (64 / l) - 1) / (kGemvWaves * (64 / l));
+      if (2 * units < 3LL * cus) continue;
+      const GemvPlan p = plan_gemv_for({l, C / l, true, 1}, N, K, gshift, act, bits);
+      if (p.ok) return p;
+    }
+  }
+  return plan_gemv_for(sh, N, K, gshift, act, bits);
+}
+
+GemvPlan plan_gemv_for(const GemvShape& sh, int N, int K, int gshift, bool act, int bits) {
+  GemvPlan p;
+  p.sh = sh;
   if (static_cast<long long>(N) * K * bits / 8 >= (1LL << 31)) return p;   // 32-bit byte offsets into the codes
   const int G = groups_in(0, K, gshift);
   const int unit = kGemvWaves * (64 / p.sh.lpr);                    // rows per unit
