@@ -152,6 +152,41 @@ def test_unit_vector_probes_bit_exact(case):
         assert np.array_equal(yi[0].view(np.uint16), expect[i].view(np.uint16)), ks[i]
 
 
+# The large-tile kernel's two MFMA tiles (16x16x32 and 32x32x16 blocks) at every tile
+# height: forced row blocks per wavefront and tile kind on layers with several row and
+# column tiles, ragged M and N, act order and symmetric weights.
+LARGE_TILE_CASES = [
+    # name, M, N, K, group, act_order, sym
+    ("t1", 150, 520, 1024, 128, False, False),
+    ("t2", 70, 776, 640, 64, True, False),
+    ("t3", 300, 264, 512, 32, False, True),
+]
+
+
+@pytest.mark.parametrize("mb", [2, 4, 8])
+@pytest.mark.parametrize("mfma32", [0, 1])
+def test_large_tile_kinds_match_oracle(mb, mfma32):
+    import torch
+    os.environ["W4A16_FORCE_PATH"] = "gemm"
+    os.environ["W4A16_TUNE_GEMM_BIG_MB"] = str(mb)
+    os.environ["W4A16_TUNE_GEMM_MFMA32"] = str(mfma32)
+    try:
+        for i, (name, M, N, K, g, act, sym) in enumerate(LARGE_TILE_CASES):
+            cfg = wl.custom_config(name, 300 + i, K=K, N=N, group_size=g, M_list=(M,), act_order=act, sym=sym)
+            note(f"large tile {name} M={M} N={N} K={K} g={g} act={act} sym={sym} mb={mb} mfma32={mfma32}")
+            prod = product_layer(cfg, M)
+            ref = oracle_layer(cfg, M, np.arange(N))
+            y = run_gemm(prod).cpu().numpy()
+            assert oracle.rel_err(y, ref["y_ref"]) <= TOL
+            # x = e_k for 130 channels: every output exactly binary16(W^[n, k])
+            ks = np.arange(0, K, max(1, K // 130))[:130]
+            y = run_gemm(prod, x=torch.from_numpy(wl.unit_vectors(K, ks)).to(device())).cpu().numpy()
+            assert np.array_equal(y.view(np.uint16), ref["W16"][:, ks].T.copy().view(np.uint16))
+    finally:
+        for v in ("W4A16_TUNE_GEMM_BIG_MB", "W4A16_TUNE_GEMM_MFMA32"):
+            os.environ.pop(v, None)
+
+
 def test_all_ones_gives_row_sums():
     import torch
     cfg = _small_cfg("ones", 1, 520, 3072, 64, False, 50)

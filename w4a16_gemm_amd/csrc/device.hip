@@ -397,17 +397,31 @@ int run_skinny(const SkinnyShape& sk, bool act, hipStream_t st, const half_t* hx
 // units: then one round of full-width tiles covers the first columns and one round of
 // narrower tiles (64 NB2 wide) the rest, so that neither round leaves compute units
 // idle; (b) when they would not fill one round: then narrower tiles for all columns.
+template <int NB2, int MB, int BITS, bool W32>
+int launch_big_t(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, Zeros z, half_t* y,
+                 int M, int N, int K, int gshift, int split, int n_split, int grid) {
+  constexpr size_t lds = BITS == 4 ? kBigLds : kBigLds8;
+  static const hipError_t lds_ok = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(gemm_big_kernel<NB2, MB, BITS, W32>), hipFuncAttributeMaxDynamicSharedMemorySize,
+      static_cast<int>(lds));
+  if (int rc = hip_status(lds_ok, "hipFuncSetAttribute")) return rc;
+  hipLaunchKernelGGL((gemm_big_kernel<NB2, MB, BITS, W32>), dim3(grid), dim3(512), lds, st, x, qw, s, z, y, M, N,
+                     K, gshift, split, n_split);
+  return check_launch("gemm launch");
+}
+
+// 64- and 128-row tiles of 4-bit weights run the 32x32x16 MFMA tile (W4A16_TUNE_GEMM_MFMA32=0:
+// the 16x16x32 one).  Same-process A/B on random layers: M = 100 (K 4096, N 14336) 46.0 -> 40.1 us,
+// M = 200 (K 2048, N 4096) 24.8 -> 22.4 us, M = 48 36.5 -> 35.1 us; with 256-row tiles it measured
+// no faster (M = 2048 237 vs 239 us, M = 4096 459 vs 480 us), so those keep the 16x16x32 tile.
 template <int NB2, int MB, int BITS>
 int launch_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, Zeros z, half_t* y,
                int M, int N, int K, int gshift, int split, int n_split, int grid) {
-  constexpr size_t lds = BITS == 4 ? kBigLds : kBigLds8;
-  static const hipError_t lds_ok = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(gemm_big_kernel<NB2, MB, BITS>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      static_cast<int>(lds));
-  if (int rc = hip_status(lds_ok, "hipFuncSetAttribute")) return rc;
-  hipLaunchKernelGGL((gemm_big_kernel<NB2, MB, BITS>), dim3(grid), dim3(512), lds, st, x, qw, s, z, y, M, N, K,
-                     gshift, split, n_split);
-  return check_launch("gemm launch");
+  if constexpr (BITS == 4 && MB <= 4) {
+    if (env_int("W4A16_TUNE_GEMM_MFMA32", 1) != 0)
+      return launch_big_t<NB2, MB, BITS, true>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
+  }
+  return launch_big_t<NB2, MB, BITS, false>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
 }
 
 template <int MB, int BITS>

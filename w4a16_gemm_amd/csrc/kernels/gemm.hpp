@@ -369,73 +369,68 @@ constexpr size_t kBigLds8 = static_cast<size_t>(kBigStages) * kBigStage8;
 template <int BITS>
 constexpr uint32_t big_stage_bytes() { return BITS == 4 ? kBigStage : kBigStage8; }
 
-// BITS = 8: 8-bit codes (byte order 0, 2, 1, 3): two code loads per thread and stage,
-// lane (r, q) reads the 16 bytes of channels [16 q, +16) of its column, MFMA step s
-// takes words 2s and 2s + 1; zero points are bytes; LDS read with plain loads at every
-// tile height.  Needs N % 16 == 0 (16-byte zero-point loads).
-template <int NB, int MB, int BITS = 4>
-__device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uint32_t* __restrict__ qw,
-                                         const half_t* __restrict__ scales, Zeros qzeros,
-                                         half_t* __restrict__ y, int M, int N, int K, int gshift, int m0, int n0,
-                                         int n_end) {
-  // NB 16-column blocks and MB 16-row blocks per wavefront: the tile is BM x BN with
-  // BM = 32 MB and BN = 64 NB.  The LDS layout is the one of the largest tile (256 x 256)
-  // whatever the tile is.  N is the row pitch of scales, zero points and y; columns at
-  // or past n_end are not computed.  MB = 8 reads LDS through the inline-asm blocks
-  // above; the smaller tiles (few-row batches) use plain loads, which the compiler
-  // orders against the barriers and (seeing no alias with the direct-to-LDS writes)
-  // does not hold behind the prefetches.
-  constexpr int BM = 32 * MB, BN = 64 * NB, BL = kBigBN, BK = kBigBK, NS = kBigStages;
+// Direct-to-LDS loads of one K tile of a BM x BN output tile (BM = 32 MB, BN = 64 NB)
+// into a stage of the LDS ring, laid out as for the widest tile (256 x 256) whatever
+// the tile is.  N is the row pitch of scales, zero points and y; columns at or past
+// n_end are not loaded.  BITS = 8: 8-bit codes (byte order 0, 2, 1, 3), two code loads
+// per thread and stage (chunk c = tid + 512 i holds channels [16 (c / BL), +16) of
+// column c % BL) and the zero-point bytes of each half as one 16-byte load per lane;
+// needs N % 16 == 0.
+template <int NB, int MB, int BITS>
+struct BigLoader {
+  static constexpr int BM = 32 * MB, BN = 64 * NB, BL = kBigBN, BK = kBigBK, NS = kBigStages;
+  static constexpr int APT = BM * BK / 8 / 512;   // activation chunks (16 B) per thread per stage
+  static constexpr int CL = BITS / 4;             // code loads (16 B) per thread per stage
+  static constexpr uint32_t STAGE = big_stage_bytes<BITS>();
+  static constexpr uint32_t LB = BITS == 4 ? kBigLdsB : kBigLdsB8;
   static_assert(NB >= 1 && NB <= 4, "tile width");
   static_assert(MB == 2 || MB == 4 || MB == 8, "tile height");
-  constexpr int APT = BM * BK / 8 / 512;  // activation chunks (16 B) per thread per stage
   static_assert(BITS == 4 || BITS == 8, "4- or 8-bit weights");
-  constexpr int CL = BITS / 4;            // code loads (16 B) per thread per stage
-  constexpr uint32_t STAGE = big_stage_bytes<BITS>();
-  constexpr uint32_t LB = BITS == 4 ? kBigLdsB : kBigLdsB8;
-  constexpr bool kAsmReads = MB == 8 && BITS == 4;
   static_assert(BL * BK / 32 == 512, "one 4-bit code chunk per thread per stage (of the widest tile)");
   static_assert(STAGE % 16 == 0, "stage alignment");
-  extern __shared__ __align__(16) unsigned char smem[];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
-  const int lr = lane & 15;
-  const int lq = lane >> 4;
-  const int W = K >> (BITS == 4 ? 3 : 2);   // words per row
-  const int KT = K / BK;
-
-  // Activations: lane l of load i writes chunk c = (APT wave + i) * 64 + l = 8 row + slot,
-  // which receives the row's chunk slot ^ (row % 8).  Rows past M re-read row M - 1.
+  const half_t* x;
+  const uint32_t* qw;
+  const half_t* scales;
+  Zeros qzeros;
+  unsigned char* smem;
+  int N, KT, gshift, wave, sz_half, s_col, z_word;
   int a_off[APT];
-#pragma unroll
-  for (int i = 0; i < APT; ++i) {
-    const int c = (wave * APT + i) * 64 + lane;
-    const int row = c >> 3, slot = c & 7;
-    a_off[i] = min(m0 + row, M - 1) * K + 8 * (slot ^ (row & 7));
-  }
-  // Codes: chunk c = half * BL + column holds channels [32 half, +32) of the column;
-  // columns past the tile (BN < BL) or past N re-read a column of the tile.
-  // 8-bit: chunk c = tid + 512 i holds channels [16 (c / BL), +16) of column c % BL.
   int b_off[CL];
+
+  __device__ __forceinline__ BigLoader(const half_t* x_, const uint32_t* qw_, const half_t* scales_, Zeros qz,
+                                       unsigned char* smem_, int M, int N_, int K, int gshift_, int m0, int n0,
+                                       int n_end, int tid, int wave_)
+      : x(x_), qw(qw_), scales(scales_), qzeros(qz), smem(smem_), N(N_), KT(K / BK), gshift(gshift_), wave(wave_) {
+    const int lane = tid & 63;
+    const int W = K >> (BITS == 4 ? 3 : 2);   // words per row
+    // Activations: lane l of load i writes chunk c = (APT wave + i) * 64 + l = 8 row + slot,
+    // which receives the row's chunk slot ^ (row % 8).  Rows past M re-read row M - 1.
 #pragma unroll
-  for (int i = 0; i < CL; ++i) {
-    const int c = tid + 512 * i;
-    b_off[i] = min(n0 + min(c % BL, BN - 1), n_end - 1) * W + 4 * (c / BL);
+    for (int i = 0; i < APT; ++i) {
+      const int c = (wave * APT + i) * 64 + lane;
+      const int row = c >> 3, slot = c & 7;
+      a_off[i] = min(m0 + row, M - 1) * K + 8 * (slot ^ (row & 7));
+    }
+    // Codes: chunk c = half * BL + column holds channels [32 half, +32) of the column;
+    // columns past the tile (BN < BL) or past N re-read a column of the tile.
+#pragma unroll
+    for (int i = 0; i < CL; ++i) {
+      const int c = tid + 512 * i;
+      b_off[i] = min(n0 + min(c % BL, BN - 1), n_end - 1) * W + 4 * (c / BL);
+    }
+    // Scales (wavefront 0, 16 B per lane) and zero points (wavefront 1, 4 B per lane) of
+    // half h = lane / 32: 8 columns, resp. one packed word of 8 columns, per lane.
+    sz_half = lane >> 5;
+    s_col = min(n0 + 8 * (lane & 31), n_end - 8);
+    z_word = BITS == 4 ? min(n0 / 8 + (lane & 31), n_end / 8 - 1)
+                       : min(n0 / 4 + 4 * (lane & 31), n_end / 4 - 4);   // 8-bit: 16 columns per lane
   }
-  // Scales (wavefront 0, 16 B per lane) and zero points (wavefront 1, 4 B per lane) of
-  // half h = lane / 32: 8 columns, resp. one packed word of 8 columns, per lane.
-  const int sz_half = lane >> 5;
-  const int s_col = min(n0 + 8 * (lane & 31), n_end - 8);
-  const int z_word = BITS == 4 ? min(n0 / 8 + (lane & 31), n_end / 8 - 1)
-                               : min(n0 / 4 + 4 * (lane & 31), n_end / 4 - 4);   // 8-bit: 16 columns per lane
 
   // Tile t goes to stage t % NS; tiles past the end re-load the last one into a stage
   // that is never read again.  The scale / zero load comes first, so that waiting for
   // tile t alone never waits for more than that load of tile t + 1.
-  auto load_tile = [&](int t) {
+  __device__ __forceinline__ void load(int t) const {
     const int tc = min(t, KT - 1);
     unsigned char* stage = smem + (t % NS) * STAGE;
     const int gi = (tc * BK + 32 * sz_half) >> gshift;
@@ -463,7 +458,39 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(qw + b_off[i] + tc * (BK * BITS / 32)),
                                        reinterpret_cast<void*>(stage + kBigLdsA + (512 * i + wave * 64) * 16), 16, 0,
                                        0);
-  };
+  }
+};
+
+// 16x16x32 MFMA tile.  Lane (r, q) = (lane % 16, lane / 16) of a wavefront holds, per
+// 16-column block, the 16 codes of channels [16 q, 16 q + 16) of its column.  BITS = 8:
+// lane (r, q) reads the 16 bytes of channels [16 q, +16) of its column, MFMA step s
+// takes words 2s and 2s + 1; zero points are bytes; LDS read with plain loads at every
+// tile height.
+template <int NB, int MB, int BITS = 4>
+__device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uint32_t* __restrict__ qw,
+                                         const half_t* __restrict__ scales, Zeros qzeros,
+                                         half_t* __restrict__ y, int M, int N, int K, int gshift, int m0, int n0,
+                                         int n_end) {
+  // NB 16-column blocks and MB 16-row blocks per wavefront: the tile is BM x BN with
+  // BM = 32 MB and BN = 64 NB.  MB = 8 reads LDS through the inline-asm blocks above;
+  // the smaller tiles (few-row batches) use plain loads, which the compiler orders
+  // against the barriers and (seeing no alias with the direct-to-LDS writes) does not
+  // hold behind the prefetches.
+  using Loader = BigLoader<NB, MB, BITS>;
+  constexpr int BL = Loader::BL, NS = Loader::NS, APT = Loader::APT, CL = Loader::CL;
+  constexpr uint32_t STAGE = Loader::STAGE, LB = Loader::LB;
+  constexpr bool kAsmReads = MB == 8 && BITS == 4;
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int lr = lane & 15;
+  const int lq = lane >> 4;
+  const int KT = K / kBigBK;
+  const Loader ld(x, qw, scales, qzeros, smem, M, N, K, gshift, m0, n0, n_end, tid, wave);
+  auto load_tile = [&](int t) { ld.load(t); };
 
   float4_t acc[MB][NB];
 #pragma unroll
@@ -550,7 +577,7 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
         for (int nb = 0; nb < NB; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
     }
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(APT + CL) : "memory");   // tile t + 1
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(APT + CL) : "memory");   // tile t + 1; own LDS reads done
     block_barrier();
   }
   // the clamped loads past the last tile must land before the workgroup's LDS is released
@@ -571,30 +598,158 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
     }
 }
 
+// 32x32x16 MFMA tile (4-bit weights): the same LDS ring and loads as big_tile, with
+// 32 x 32 output blocks (MB / 2 row blocks by NB / 2 column blocks per wavefront).  The
+// 32x32x16 instruction does twice the work of the 16x16x32 one per issue from the same
+// operand registers, and on this part more of the dequantisation's VALU work overlaps
+// with it: a probe of independent MFMA chains with two wavefronts per SIMD ran 2.06
+// PFLOP/s with two VALU instructions per 16K flops of 32x32x16 MFMAs, 1.71 PFLOP/s
+// with 16x16x32 MFMAs.
+//  * Lane l = 32 h + c of a wavefront stands for row (A) / column (B) c of a block.
+//    Its 8 channels of MFMA step s (s = 0..3 over the 64-channel K tile) are the
+//    channels [32 h + 8 s, +8): the contraction pairs each activation with the weight
+//    of the same channel, in any assignment of channels to steps, and this one makes
+//    a lane's four B words the contiguous 16-byte code chunk (half h, column) of the
+//    stage, the scale and zero point of one group (group size >= 32).
+//  * The A fragment of step s is chunk 4 h + s of its row, at slot (4 h + s) ^ (row % 8).
+//  * D layout of the 32x32 MFMA: lane l holds column l % 32 and, in register r, row
+//    8 (r / 4) + 4 (l / 32) + r % 4.
+template <int NB, int MB>
+__device__ __forceinline__ void big_tile32(const half_t* __restrict__ x, const uint32_t* __restrict__ qw,
+                                           const half_t* __restrict__ scales, Zeros qzeros,
+                                           half_t* __restrict__ y, int M, int N, int K, int gshift, int m0, int n0,
+                                           int n_end) {
+  using Loader = BigLoader<NB, MB, 4>;
+  constexpr int BL = Loader::BL, NS = Loader::NS, APT = Loader::APT, CL = Loader::CL;
+  constexpr uint32_t STAGE = Loader::STAGE, LB = Loader::LB;
+  static_assert(NB % 2 == 0, "whole 32-column blocks per wavefront");
+  constexpr int RB = MB / 2, CB = NB / 2;   // 32-row and 32-column blocks per wavefront
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int lc = lane & 31;
+  const int lh = lane >> 5;
+  const int KT = K / kBigBK;
+  const Loader ld(x, qw, scales, qzeros, smem, M, N, K, gshift, m0, n0, n_end, tid, wave);
+
+  f32x16_t acc[RB][CB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[rb][cb][r] = 0.f;
+
+  // Byte offsets inside a stage: A fragment rb of step s at a_lane + 4096 rb + 16 ((4 h +
+  // s) ^ (c % 8)); code chunk of block cb at b_lane + 512 cb; its scale at s_lane + 64 cb
+  // and zero word at z_lane + 16 cb.
+  const int col = wn * 16 * NB + lc;   // column of block 0 inside the tile
+  const uint32_t a_lane = (wm * 16 * MB + lc) * 128;
+  const uint32_t b_lane = kBigLdsA + (lh * BL + col) * 16;
+  const uint32_t s_lane = kBigLdsA + LB + (lh * BL + col) * 2;
+  const uint32_t z_lane = kBigLdsA + LB + kBigLdsS + (lh * (BL / 8) + (col >> 3)) * 4;
+  const int z_shift = 4 * (lc & 7);
+
+  // At most APT + CL loads of this wavefront (its activation and code loads of tile
+  // t + 1) are newer than the last load of tile t once tile t + 1 has been issued.
+  ld.load(0);
+  ld.load(1);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(APT + CL) : "memory");   // tile 0
+  block_barrier();
+
+  for (int t = 0; t < KT; ++t) {
+    ld.load(t + NS - 1);
+    const unsigned char* st = smem + (t % NS) * STAGE;
+    uint4 cw[CB];
+    DequantConsts dc[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      cw[cb] = *reinterpret_cast<const uint4*>(st + b_lane + 512 * cb);
+      const uint32_t sc = *reinterpret_cast<const uint16_t*>(st + s_lane + 64 * cb);
+      const uint32_t zw = *reinterpret_cast<const uint32_t*>(st + z_lane + 16 * cb);
+      dc[cb] = make_consts((qzeros.word(zw) >> z_shift) & 0xFu, __builtin_bit_cast(half_t, static_cast<uint16_t>(sc)));
+    }
+    // A fragments one step ahead: the reads of step s + 1 are in flight during the
+    // MFMAs of step s.
+    half8_t af[2][RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+      af[0][rb] = *reinterpret_cast<const half8_t*>(st + a_lane + 4096 * rb + 16 * ((4 * lh) ^ (lc & 7)));
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s < 3) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          af[(s + 1) & 1][rb] =
+              *reinterpret_cast<const half8_t*>(st + a_lane + 4096 * rb + 16 * ((4 * lh + s + 1) ^ (lc & 7)));
+      }
+      __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of this step's MFMAs
+      half8_t bf[CB];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        bf[cb] = dequant_word(s == 0 ? cw[cb].x : s == 1 ? cw[cb].y : s == 2 ? cw[cb].z : cw[cb].w, dc[cb]);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s & 1][rb], bf[cb], acc[rb][cb], 0, 0, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(APT + CL) : "memory");   // tile t + 1; own LDS reads done
+    block_barrier();
+  }
+  // the clamped loads past the last tile must land before the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  const int nw = n0 + wn * 16 * NB;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int n = nw + 32 * cb + lc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm * 16 * MB + 32 * rb + 8 * (r >> 2) + 4 * lh + (r & 3);
+        if (m < M && n < n_end) y[static_cast<size_t>(m) * N + n] = static_cast<half_t>(acc[rb][cb][r]);
+      }
+    }
+}
+
 // One launch covers up to two column ranges: workgroups [0, split) take BM x 256
 // tiles of columns [0, n_split), the rest BM x 64 NB2 tiles of columns [n_split, N),
 // BM = 32 MB rows (256 for prefill; 128 / 64 for batches of up to 128 / 64 rows).
 // With one wave of full tiles and one of narrower tiles, both rounds fill the device
 // when the full-width tiles alone would leave most of a second round idle.
-template <int NB2, int MB, int BITS = 4>
+template <int NB2, int MB, int BITS = 4, bool W32 = false>
 __global__ __launch_bounds__(512) void gemm_big_kernel(const half_t* __restrict__ x, const uint32_t* __restrict__ qw,
                                                        const half_t* __restrict__ scales,
                                                        Zeros qzeros, half_t* __restrict__ y,
                                                        int M, int N, int K, int gshift, int split, int n_split) {
+  static_assert(!W32 || BITS == 4, "the 32x32 tile takes 4-bit weights");
   constexpr int BM = 32 * MB;
   const int tiles_m = (M + BM - 1) / BM;
   const int bid = blockIdx.x;
   if (bid < split) {
     const int tiles_n = (n_split + 255) / 256;
     const int tile = xcd_tile(bid, tiles_m, tiles_n);
-    big_tile<4, MB, BITS>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM, (tile % tiles_n) * 256,
-                min(N, n_split));
+    if constexpr (W32)
+      big_tile32<4, MB>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM, (tile % tiles_n) * 256,
+                        min(N, n_split));
+    else
+      big_tile<4, MB, BITS>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM, (tile % tiles_n) * 256,
+                            min(N, n_split));
   } else {
     constexpr int BN2 = 64 * NB2;
     const int tiles_n = (N - n_split + BN2 - 1) / BN2;
     const int tile = xcd_tile(bid - split, tiles_m, tiles_n);
-    big_tile<NB2, MB, BITS>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM,
-                  n_split + (tile % tiles_n) * BN2, N);
+    if constexpr (W32 && NB2 % 2 == 0)
+      big_tile32<NB2, MB>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM,
+                          n_split + (tile % tiles_n) * BN2, N);
+    else
+      big_tile<NB2, MB, BITS>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM,
+                              n_split + (tile % tiles_n) * BN2, N);
   }
 }
 
