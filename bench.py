@@ -421,6 +421,61 @@ def gptq_bench(cfg: wl.LayerConfig):
     }
 
 
+def measure_peaks(read_bytes: int = 1 << 30, steps: int = 20) -> dict:
+    """What the part sustains on plain work (libw4a16_peaks.so): a non-temporal streaming
+    read of a 1 GiB buffer (four times the Infinity Cache), best of a few grid sizes, and
+    an MFMA loop of independent v_mfma_f32_32x32x16_f16 chains, two wavefronts per SIMD.
+    Region events around `steps` back-to-back launches."""
+    import ctypes
+    import torch
+    from w4a16_gemm_amd import build as _build
+    lib = ctypes.CDLL(_build.PEAKS_LIB)
+    lib.w4a16_peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                           ctypes.c_void_p]
+    lib.w4a16_peak_mfma_f16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.w4a16_peaks_last_error.restype = ctypes.c_char_p
+    stream = torch.cuda.current_stream()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def region_us(launch) -> float:
+        for _ in range(3):
+            launch()
+        torch.cuda.synchronize()
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0.record(stream)
+        for _ in range(steps):
+            launch()
+        r1.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * r0.elapsed_time(r1) / steps
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"peak probe failed ({rc}): {lib.w4a16_peaks_last_error().decode()}")
+
+    buf = torch.ones(read_bytes // 2, dtype=torch.float16, device="cuda:0")
+    best = None
+    for blocks in (cus, 2 * cus, 4 * cus, 8 * cus):
+        out = torch.empty(blocks * 512, dtype=torch.int32, device="cuda:0")
+        us = region_us(lambda: check(lib.w4a16_peak_stream_read(buf.data_ptr(), read_bytes, out.data_ptr(), blocks,
+                                                                 stream.cuda_stream)))
+        if best is None or us < best[0]:
+            best = (us, blocks)
+    del buf
+    iters = 20000
+    out = torch.empty(cus * 512, dtype=torch.float32, device="cuda:0")
+    mus = region_us(lambda: check(lib.w4a16_peak_mfma_f16(out.data_ptr(), iters, cus, stream.cuda_stream)))
+    flops = cus * 8 * iters * 4 * 32768
+    return {
+        "hbm_read_GBps": round(read_bytes / best[0] / 1e3, 1),
+        "hbm_read_note": f"non-temporal 16-byte streaming read of {read_bytes >> 20} MiB, {best[1]} workgroups "
+                         f"of 512 threads: {best[0]:.1f} us per launch",
+        "mfma_f16_TFLOPs": round(flops / mus / 1e6, 1),
+        "mfma_note": f"{cus} workgroups x 8 wavefronts x {iters} rounds of four independent 32x32x16 f16 MFMA "
+                     f"chains: {mus:.1f} us per launch",
+    }
+
+
 def traffic_for(hash_now: str, key: str):
     try:
         with open(TRAFFIC_FILE) as f:
@@ -447,6 +502,8 @@ def main() -> int:
     ap.add_argument("--no-gptq", action="store_true", help="skip timing the GPTQ quantiser")
     ap.add_argument("--no-decode-step", action="store_true",
                     help="skip the whole-decode-step workload of the 1.5B example")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring the achievable streaming-read and MFMA rates")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain streaming kernel over this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -546,6 +603,15 @@ def main() -> int:
             "frac": pre["mfma_frac"], "us_per_layer": pre["us_per_layer"], "kernel": "gemm_big_kernel",
             "traffic": traffic_for(khash, "c4:M2048"),
         }
+    if not args.no_peaks:
+        log("measuring the achievable streaming-read and MFMA rates")
+        peaks = measure_peaks()
+        line["achievable"] = peaks
+        line["roofline"]["achievable"] = peaks["hbm_read_GBps"]
+        line["roofline"]["frac_of_achievable"] = round(line["roofline"]["achieved"] / peaks["hbm_read_GBps"], 4)
+        if pre:
+            line["prefill"]["achievable"] = peaks["mfma_f16_TFLOPs"]
+            line["prefill"]["frac_of_achievable"] = round(pre["TFLOPs"] / peaks["mfma_f16_TFLOPs"], 4)
     if not args.no_dense_ref:
         log("timing the dense binary16 library GEMM of the decode and prefill shapes")
         ref = {"library": "torch.matmul (hipBLASLt), binary16 weights [N][K], x @ W^T",

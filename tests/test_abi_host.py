@@ -32,6 +32,16 @@ def test_library_exports_every_declared_symbol():
     assert sorted(w4.EXPORTS) == declared
 
 
+def test_peaks_library_exports_every_declared_symbol():
+    from w4a16_gemm_amd import build
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "w4a16_peaks.h")).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(w4a16_peak\w*)\s*\(", text)))
+    assert declared == ["w4a16_peak_mfma_f16", "w4a16_peak_stream_read", "w4a16_peaks_last_error"]
+    lib = ctypes.CDLL(build.PEAKS_LIB)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
 def test_abi_version():
     assert w4.w4a16_abi_version() == 1
 

@@ -21,6 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libw4a16.so")
+PEAKS_LIB = os.path.join(HERE, "libw4a16_peaks.so")   # achievable-peak probes (bench only)
 
 ARCH = "gfx950"
 DEVICE_FLAGS = [
@@ -59,6 +60,10 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", host_o, dev_o, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    tmp = PEAKS_LIB + ".tmp"
+    _run([hipcc, "-shared", "-fPIC", "-x", "hip", os.path.join(CSRC, "peaks.hip"), *DEVICE_FLAGS, *inc, "-o", tmp],
+         verbose)
+    os.replace(tmp, PEAKS_LIB)
     return LIB
 
 
