@@ -569,9 +569,8 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
   const size_t bytes = static_cast<size_t>(M) * K * sizeof(half_t);
   if (int s = hip_status(hipMallocAsync(reinterpret_cast<void**>(&xs), bytes, st), "hipMallocAsync")) return s;
   const int32_t* perm = qweight + qweight_words(N, K, false);
-  const size_t total = static_cast<size_t>(M) * K;
-  hipLaunchKernelGGL(gather_x_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, hx,
-                     perm, xs, M, K);
+  hipLaunchKernelGGL(gather_x_kernel, dim3(static_cast<unsigned>((K / 8 + 255) / 256), std::min(M, kGatherRowsY)),
+                     dim3(256), 0, st, hx, perm, xs, M, K);
   int rc = check_launch("gather launch");
   if (rc == W4A16_OK) rc = run_gemm<4>(st, xs, hq, hs, hz, hy, M, N, K, gshift);
   const int rf = hip_status(hipFreeAsync(xs, st), "hipFreeAsync");
@@ -643,9 +642,8 @@ int w8a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
   const size_t bytes = static_cast<size_t>(M) * K * sizeof(half_t);
   if (int s = hip_status(hipMallocAsync(reinterpret_cast<void**>(&xs), bytes, st), "hipMallocAsync")) return s;
   const int32_t* perm = qweight + qweight8_words(N, K, false);
-  const size_t total = static_cast<size_t>(M) * K;
-  hipLaunchKernelGGL(gather_x_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, hx,
-                     perm, xs, M, K);
+  hipLaunchKernelGGL(gather_x_kernel, dim3(static_cast<unsigned>((K / 8 + 255) / 256), std::min(M, kGatherRowsY)),
+                     dim3(256), 0, st, hx, perm, xs, M, K);
   int rc = check_launch("gather launch");
   if (rc == W4A16_OK) rc = run_gemm<8>(st, xs, hq, hs, hz, hy, M, N, K, gshift);
   const int rf = hip_status(hipFreeAsync(xs, st), "hipFreeAsync");

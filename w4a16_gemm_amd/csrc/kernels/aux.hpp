@@ -60,15 +60,24 @@ __global__ __launch_bounds__(256) void dequant8_kernel(const uint32_t* __restric
 }
 
 // Act order, M > 1: xs[m][p] = x[m][perm[p]], so that the GEMM sees every group as
-// a contiguous run of input channels.
+// a contiguous run of input channels.  A thread takes 8 consecutive stored positions
+// (the order read once as two 16-byte loads) and writes them as one 16-byte store in
+// every row of its grid-y slice.  Needs K % 8 == 0 and 16-byte aligned perm, x rows
+// and xs rows (K % 32 == 0 and aligned buffers give all three).
+constexpr int kGatherRowsY = 64;   // grid y: row slices
+
 __global__ __launch_bounds__(256) void gather_x_kernel(const half_t* __restrict__ x,
                                                        const int32_t* __restrict__ perm,
                                                        half_t* __restrict__ xs, int M, int K) {
-  const size_t idx = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= static_cast<size_t>(M) * K) return;
-  const size_t m = idx / K;
-  const int p = static_cast<int>(idx % K);
-  xs[idx] = x[m * K + perm[p]];
+  const int p0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (p0 >= K) return;
+  const int4 a = *reinterpret_cast<const int4*>(perm + p0);
+  const int4 b = *reinterpret_cast<const int4*>(perm + p0 + 4);
+  for (int m = blockIdx.y; m < M; m += gridDim.y) {
+    const half_t* xr = x + static_cast<size_t>(m) * K;
+    const half8_t v = {xr[a.x], xr[a.y], xr[a.z], xr[a.w], xr[b.x], xr[b.y], xr[b.z], xr[b.w]};
+    *reinterpret_cast<half8_t*>(xs + static_cast<size_t>(m) * K + p0) = v;
+  }
 }
 
 // Split-K skinny batches: y[i] = binary16(sum over the ks slices of part[s][i]), the
