@@ -397,6 +397,12 @@ int run_skinny(const SkinnyShape& sk, bool act, hipStream_t st, const half_t* hx
 // units: then one round of full-width tiles covers the first columns and one round of
 // narrower tiles (64 NB2 wide) the rest, so that neither round leaves compute units
 // idle; (b) when they would not fill one round: then narrower tiles for all columns.
+// Wavefronts raise their priority (s_setprio 1) for each MFMA cluster and drop it after
+// (W4A16_TUNE_GEMM_PRIO=0: off), so that the two wavefronts of a SIMD drift into opposite
+// phases, one issuing MFMAs while the other reads LDS and dequantises.  Same-process A/B
+// (order alternated, identical outputs): M = 100 / 200 / 300 on the 32x32 tile 49.9 / 27.1 /
+// 50.2 -> 46.1 / 25.2 / 46.3 us; 256-row tiles M = 4096 485 -> 472 us, the act-order layer
+// at M = 512 78.3 -> 73.8 us, the prefill ~1.5%.
 template <int NB2, int MB, int BITS, bool W32>
 int launch_big_t(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, Zeros z, half_t* y,
                  int M, int N, int K, int gshift, int split, int n_split, int grid) {
@@ -406,7 +412,7 @@ int launch_big_t(hipStream_t st, const half_t* x, const uint32_t* qw, const half
       static_cast<int>(lds));
   if (int rc = hip_status(lds_ok, "hipFuncSetAttribute")) return rc;
   hipLaunchKernelGGL((gemm_big_kernel<NB2, MB, BITS, W32>), dim3(grid), dim3(512), lds, st, x, qw, s, z, y, M, N,
-                     K, gshift, split, n_split);
+                     K, gshift, split, n_split, env_int("W4A16_TUNE_GEMM_PRIO", 1));
   return check_launch("gemm launch");
 }
 

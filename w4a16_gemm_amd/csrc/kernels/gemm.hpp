@@ -470,7 +470,7 @@ template <int NB, int MB, int BITS = 4>
 __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uint32_t* __restrict__ qw,
                                          const half_t* __restrict__ scales, Zeros qzeros,
                                          half_t* __restrict__ y, int M, int N, int K, int gshift, int m0, int n0,
-                                         int n_end) {
+                                         int n_end, int prio) {
   // NB 16-column blocks and MB 16-row blocks per wavefront: the tile is BM x BN with
   // BM = 32 MB and BN = 64 NB.  MB = 8 reads LDS through the inline-asm blocks above;
   // the smaller tiles (few-row batches) use plain loads, which the compiler orders
@@ -571,11 +571,13 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
           bf[nb] = half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
       }
+      if (prio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
+      if (prio) __builtin_amdgcn_s_setprio(0);
     }
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(APT + CL) : "memory");   // tile t + 1; own LDS reads done
     block_barrier();
@@ -618,7 +620,7 @@ template <int NB, int MB>
 __device__ __forceinline__ void big_tile32(const half_t* __restrict__ x, const uint32_t* __restrict__ qw,
                                            const half_t* __restrict__ scales, Zeros qzeros,
                                            half_t* __restrict__ y, int M, int N, int K, int gshift, int m0, int n0,
-                                           int n_end) {
+                                           int n_end, int prio) {
   using Loader = BigLoader<NB, MB, 4>;
   constexpr int BL = Loader::BL, NS = Loader::NS, APT = Loader::APT, CL = Loader::CL;
   constexpr uint32_t STAGE = Loader::STAGE, LB = Loader::LB;
@@ -691,11 +693,13 @@ __device__ __forceinline__ void big_tile32(const half_t* __restrict__ x, const u
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
         bf[cb] = dequant_word(s == 0 ? cw[cb].x : s == 1 ? cw[cb].y : s == 2 ? cw[cb].z : cw[cb].w, dc[cb]);
+      if (prio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s & 1][rb], bf[cb], acc[rb][cb], 0, 0, 0);
+      if (prio) __builtin_amdgcn_s_setprio(0);
     }
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(APT + CL) : "memory");   // tile t + 1; own LDS reads done
     block_barrier();
@@ -717,6 +721,8 @@ __device__ __forceinline__ void big_tile32(const half_t* __restrict__ x, const u
     }
 }
 
+// prio != 0: each MFMA cluster runs at wavefront priority 1 (s_setprio), the LDS reads
+// and dequantisation between clusters at 0.
 // One launch covers up to two column ranges: workgroups [0, split) take BM x 256
 // tiles of columns [0, n_split), the rest BM x 64 NB2 tiles of columns [n_split, N),
 // BM = 32 MB rows (256 for prefill; 128 / 64 for batches of up to 128 / 64 rows).
@@ -726,7 +732,8 @@ template <int NB2, int MB, int BITS = 4, bool W32 = false>
 __global__ __launch_bounds__(512) void gemm_big_kernel(const half_t* __restrict__ x, const uint32_t* __restrict__ qw,
                                                        const half_t* __restrict__ scales,
                                                        Zeros qzeros, half_t* __restrict__ y,
-                                                       int M, int N, int K, int gshift, int split, int n_split) {
+                                                       int M, int N, int K, int gshift, int split, int n_split,
+                                                       int prio) {
   static_assert(!W32 || BITS == 4, "the 32x32 tile takes 4-bit weights");
   constexpr int BM = 32 * MB;
   const int tiles_m = (M + BM - 1) / BM;
@@ -736,20 +743,20 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(const half_t* __restrict_
     const int tile = xcd_tile(bid, tiles_m, tiles_n);
     if constexpr (W32)
       big_tile32<4, MB>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM, (tile % tiles_n) * 256,
-                        min(N, n_split));
+                        min(N, n_split), prio);
     else
       big_tile<4, MB, BITS>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM, (tile % tiles_n) * 256,
-                            min(N, n_split));
+                            min(N, n_split), prio);
   } else {
     constexpr int BN2 = 64 * NB2;
     const int tiles_n = (N - n_split + BN2 - 1) / BN2;
     const int tile = xcd_tile(bid - split, tiles_m, tiles_n);
     if constexpr (W32 && NB2 % 2 == 0)
       big_tile32<NB2, MB>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM,
-                          n_split + (tile % tiles_n) * BN2, N);
+                          n_split + (tile % tiles_n) * BN2, N, prio);
     else
       big_tile<NB2, MB, BITS>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM,
-                              n_split + (tile % tiles_n) * BN2, N);
+                              n_split + (tile % tiles_n) * BN2, N, prio);
   }
 }
 
