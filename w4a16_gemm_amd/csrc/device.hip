@@ -417,14 +417,15 @@ int launch_big_t(hipStream_t st, const half_t* x, const uint32_t* qw, const half
 }
 
 // 64- and 128-row tiles of 4-bit weights run the 32x32x16 MFMA tile (W4A16_TUNE_GEMM_MFMA32=0:
-// the 16x16x32 one).  Same-process A/B on random layers: M = 100 (K 4096, N 14336) 46.0 -> 40.1 us,
+// the 16x16x32 one; 2: the 32x32x16 one at every tile height).  Same-process A/B on random layers: M = 100 (K 4096, N 14336) 46.0 -> 40.1 us,
 // M = 200 (K 2048, N 4096) 24.8 -> 22.4 us, M = 48 36.5 -> 35.1 us; with 256-row tiles it measured
 // no faster (M = 2048 237 vs 239 us, M = 4096 459 vs 480 us), so those keep the 16x16x32 tile.
 template <int NB2, int MB, int BITS>
 int launch_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, Zeros z, half_t* y,
                int M, int N, int K, int gshift, int split, int n_split, int grid) {
-  if constexpr (BITS == 4 && MB <= 4) {
-    if (env_int("W4A16_TUNE_GEMM_MFMA32", 1) != 0)
+  if constexpr (BITS == 4) {
+    const int mode = env_int("W4A16_TUNE_GEMM_MFMA32", 1);
+    if (mode == 2 || (mode == 1 && MB <= 4))
       return launch_big_t<NB2, MB, BITS, true>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
   }
   return launch_big_t<NB2, MB, BITS, false>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
