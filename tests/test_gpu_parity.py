@@ -164,7 +164,7 @@ LARGE_TILE_CASES = [
 
 
 @pytest.mark.parametrize("mb", [2, 4, 8])
-@pytest.mark.parametrize("mfma32", [0, 1])
+@pytest.mark.parametrize("mfma32", [0, 1, 2])
 def test_large_tile_kinds_match_oracle(mb, mfma32):
     import torch
     os.environ["W4A16_FORCE_PATH"] = "gemm"
@@ -178,12 +178,17 @@ def test_large_tile_kinds_match_oracle(mb, mfma32):
             ref = oracle_layer(cfg, M, np.arange(N))
             y = run_gemm(prod).cpu().numpy()
             assert oracle.rel_err(y, ref["y_ref"]) <= TOL
+            # wavefront priority changes only the schedule: bit-identical outputs without it
+            os.environ["W4A16_TUNE_GEMM_PRIO"] = "0"
+            y0 = run_gemm(prod).cpu().numpy()
+            os.environ.pop("W4A16_TUNE_GEMM_PRIO")
+            assert np.array_equal(y0.view(np.uint16), y.view(np.uint16))
             # x = e_k for 130 channels: every output exactly binary16(W^[n, k])
             ks = np.arange(0, K, max(1, K // 130))[:130]
             y = run_gemm(prod, x=torch.from_numpy(wl.unit_vectors(K, ks)).to(device())).cpu().numpy()
             assert np.array_equal(y.view(np.uint16), ref["W16"][:, ks].T.copy().view(np.uint16))
     finally:
-        for v in ("W4A16_TUNE_GEMM_BIG_MB", "W4A16_TUNE_GEMM_MFMA32"):
+        for v in ("W4A16_TUNE_GEMM_BIG_MB", "W4A16_TUNE_GEMM_MFMA32", "W4A16_TUNE_GEMM_PRIO"):
             os.environ.pop(v, None)
 
 
