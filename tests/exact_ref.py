@@ -137,3 +137,27 @@ def quantize_exact_sym(w: np.ndarray, group_size: int, g_idx=None, in_scale=None
                 codes[n, k] = q
     return codes, S
 
+
+
+def fp16_round_exact(v: Fraction) -> Fraction:
+    """v rounded to the nearest binary16 value, ties to the even significand, found by
+    search in the list of all finite binary16 values (no overflow handling: |v| must be
+    below the largest finite value)."""
+    if v == 0:
+        return Fraction(0)
+    mag = abs(v)
+    vals = positive_fp16()
+    assert mag < vals[-1]
+    i = bisect.bisect_left(vals, mag)
+    hi = vals[i]
+    lo = vals[i - 1] if i > 0 else Fraction(0)
+    if hi == mag:
+        r = hi
+    elif mag - lo != hi - mag:
+        r = lo if mag - lo < hi - mag else hi
+    else:
+        # a tie: the neighbour whose bit pattern is even (zero counts as even); the
+        # positive binary16 values are listed by ascending bit pattern from 1, so the
+        # pattern of vals[j] is j + 1
+        r = lo if (i % 2 == 0) else hi
+    return r if v > 0 else -r

@@ -143,3 +143,98 @@ def test_act_order_is_the_natural_order_of_the_permuted_layer():
     assert np.array_equal(codes[:, perm], c2)
     assert np.array_equal(S.view(np.uint16), S2.view(np.uint16))
     assert np.array_equal(Z, Z2)
+
+
+# --- output error ----------------------------------------------------------------------
+# ||(W - W^) X^T||_F / ||W X^T||_F ("AWQ + GPTQ Quantization, in depth", The two
+# algorithms, compactly: GPTQ lowers the error of the layer's output on the calibration
+# activations).  Pinned by closed forms on layers whose dequantised weights are known
+# multiples of W, and by an exact rational recomputation.
+
+def _exact_layer(seed, N=4, K=8, g=4, T=5):
+    """A layer whose binary16 weights are exactly (q - Z) S with S a power of two, so
+    that W^ = W (and 2W, W/2 are exact binary16 values too)."""
+    rng = np.random.default_rng([901, seed])
+    G = K // g
+    codes = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    Z = rng.integers(1, 15, (G, N)).astype(np.uint8)
+    S = np.full((G, N), 2.0 ** -6, np.float16)
+    gid = np.arange(K) // g
+    w = ((codes.astype(np.float64) - Z[gid].T) * S[gid].T.astype(np.float64)).astype(np.float16)
+    x = rng.standard_normal((T, K)).astype(np.float16)
+    return w, codes, S, Z, g, x
+
+
+def _error_exact(w, codes, S, Z, g, g_idx, x):
+    """The same ratio in Fractions (squared), with the group of channel k taken from
+    g_idx or k // g."""
+    N, K = w.shape
+    gid = np.arange(K) // g if g_idx is None else np.asarray(g_idx)
+    num = Fraction(0)
+    den = Fraction(0)
+    for n in range(N):
+        for t in range(x.shape[0]):
+            e = Fraction(0)
+            v = Fraction(0)
+            for k in range(K):
+                wk = Fraction(float(w[n, k]))
+                what = (int(codes[n, k]) - int(Z[gid[k], n])) * Fraction(float(S[gid[k], n]))
+                xk = Fraction(float(x[t, k]))
+                e += (wk - what) * xk
+                v += wk * xk
+            num += e * e
+            den += v * v
+    return num / den
+
+
+def _output_error_pins_hold(err_fn) -> bool:
+    w, codes, S, Z, g, x = _exact_layer(0)
+    if abs(err_fn(w, codes, S, Z, g, None, x)) > 0.0:                    # W^ = W
+        return False
+    zc = np.repeat(Z.T, g, axis=1).astype(np.uint8)                      # q = Z: W^ = 0
+    if abs(err_fn(w, zc, S, Z, g, None, x) - 1.0) > 1e-14:
+        return False
+    half = (w.astype(np.float64) / 2).astype(np.float16)                 # W^ = 2W
+    if abs(err_fn(half, codes, S, Z, g, None, x) - 1.0) > 1e-14:
+        return False
+    double = (w.astype(np.float64) * 2).astype(np.float16)               # W^ = W/2
+    if abs(err_fn(double, codes, S, Z, g, None, x) - 0.5) > 1e-14:
+        return False
+    # rational recomputation on a layer with a real quantisation error, contiguous and
+    # with a permuted group map
+    rng = np.random.default_rng(902)
+    w2 = (rng.standard_normal((4, 8)) * 0.05).astype(np.float16)
+    x2 = rng.standard_normal((6, 8)).astype(np.float16)
+    for g_idx in (None, np.array([1, 0, 1, 0, 0, 1, 1, 0], np.int32)):
+        c2, S2, Z2 = oracle.rtn_quantize(w2, 4, g_idx)
+        ref = _error_exact(w2, c2, S2, Z2, 4, g_idx, x2)
+        got = err_fn(w2, c2, S2, Z2, 4, g_idx, x2)
+        if not (0.0 < got and abs(Fraction(got) ** 2 / ref - 1) < 1e-12):
+            return False
+    return True
+
+
+def test_output_error_pinned():
+    assert _output_error_pins_hold(output_error)
+
+
+def test_output_error_pins_catch_mistakes():
+    # planted mistakes (copies of the step, on the CPU): normalising by the quantised
+    # layer's output, dropping the activations, transposing the group map
+    def by_what(w, codes, S, Z, g, g_idx, x):
+        W = w.astype(np.float64)
+        Wh = oracle.dequant(codes, S, Z, g, g_idx)
+        X = x.astype(np.float64)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            return float(np.linalg.norm((W - Wh) @ X.T) / np.linalg.norm(Wh @ X.T))
+
+    def no_x(w, codes, S, Z, g, g_idx, x):
+        W = w.astype(np.float64)
+        Wh = oracle.dequant(codes, S, Z, g, g_idx)
+        return float(np.linalg.norm(W - Wh) / np.linalg.norm(W))
+
+    def ignores_gidx(w, codes, S, Z, g, g_idx, x):
+        return output_error(w, codes, S, Z, g, None, x)
+
+    for bad in (by_what, no_x, ignores_gidx):
+        assert not _output_error_pins_hold(bad), bad.__name__

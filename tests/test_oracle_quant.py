@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import workloads as wl
-from exact_ref import fp16_ceil_exact, quantize_exact, quantize_exact_sym
+from exact_ref import fp16_ceil_exact, fp16_round_exact, quantize_exact, quantize_exact_sym
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -306,6 +306,67 @@ def test_awq_fold_is_exactly_invariant():
             assert lhs == rhs
     # a row (output-channel) scaling would not be invariant
     assert not np.allclose((xf @ (w.astype(np.float64) * s[:, None]).T), x.astype(np.float64) @ w.astype(np.float64).T)
+
+
+def _fold_pins_hold(fold) -> bool:
+    """The activation side of the AWQ fold ("How do GPTQ and AWQ differ...", AWQ:
+    protect the salient channels: multiply a weight channel by s, divide the matching
+    activation channel by s, the product is unchanged), checked two ways:
+
+    (a) power-of-two s, activations whose quotients stay normal binary16 numbers:
+        x/s is exact, so sum_k fold(x)[m,k] * (W diag(s))[n,k] equals x W^T exactly
+        (Fractions);
+    (b) s from the calibration rule on random data (not powers of two): every element
+        is the exact quotient x/s rounded once to the nearest binary16 (exact search).
+    """
+    rng = np.random.default_rng(31)
+    # (a) binary16 activations (1 + f/1024) 2^e with e in [-4, 4]: x/s with s in 2^[-3, 3]
+    # stays in [2^-7, 2^8), where binary16 is exact for these significands
+    sig = 1.0 + rng.integers(0, 1024, (3, 8)) / 1024.0
+    x = (np.where(rng.random((3, 8)) < 0.5, -1.0, 1.0) * sig * 2.0 ** rng.integers(-4, 5, (3, 8))).astype(np.float16)
+    w = (rng.standard_normal((5, 8)) * 0.1).astype(np.float16)
+    s = 2.0 ** rng.integers(-3, 4, 8).astype(np.float64)
+    xf = fold(x, s)
+    if xf.dtype != np.float16 or xf.shape != x.shape:
+        return False
+    Wf = oracle.awq_fold_weights(w, s)
+    for m in range(3):
+        for n in range(5):
+            lhs = sum(Fraction(float(xf[m, k])) * Fraction(float(Wf[n, k])) for k in range(8))
+            rhs = sum(Fraction(float(x[m, k])) * Fraction(float(w[n, k])) for k in range(8))
+            if lhs != rhs:
+                return False
+    # (b) quotients that need rounding
+    X = (rng.standard_normal((64, 16)) * 3).astype(np.float16)
+    s = oracle.awq_scales(X)
+    x = (rng.standard_normal((4, 16)) * 2).astype(np.float16)
+    xf = fold(x, s)
+    rounded = 0
+    for m in range(4):
+        for k in range(16):
+            q = Fraction(float(x[m, k])) / Fraction(float(s[k]))
+            r = fp16_round_exact(q)
+            rounded += r != q
+            if Fraction(float(xf[m, k])) != r:
+                return False
+    return rounded > 32   # most quotients really were rounded
+
+
+def test_awq_fold_activations_pinned():
+    assert _fold_pins_hold(oracle.awq_fold_activations)
+
+
+def test_awq_fold_activation_pins_catch_mistakes():
+    # planted mistakes (on the CPU, in copies of the step): multiplying instead of
+    # dividing, and dropping the fold
+    def times_s(x, s):
+        return (np.asarray(x, np.float64) * np.asarray(s, np.float64)[None, :]).astype(np.float16)
+
+    def no_fold(x, s):
+        return np.asarray(x, np.float16).copy()
+
+    assert not _fold_pins_hold(times_s)
+    assert not _fold_pins_hold(no_fold)
 
 
 @pytest.mark.parametrize("name", ["c2up", "c2down"])
