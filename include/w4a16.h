@@ -71,15 +71,20 @@ enum w4a16_status {
   W4A16_ERR_HIP = 5           /* HIP launch or runtime error; text in w4a16_last_error */
 };
 
-/* W4A16_ABI_VERSION of the built library. */
+/* W4A16_ABI_VERSION of the built library.  Interface only (no passage of the pages
+ * defines it). */
 int w4a16_abi_version(void);
 
 /* Text of the last failure on the calling thread ("" if none).  The pointer stays
- * valid until the thread's next call into the library. */
+ * valid until the thread's next call into the library.  Interface only. */
 const char* w4a16_last_error(void);
 
 /* Number of int32 words of the packed weight buffer: N*K/8, plus K when act_order is
- * non-zero (the stored input-channel order follows the codes).  0 on bad sizes. */
+ * non-zero (the stored input-channel order follows the codes).  0 on bad sizes.
+ * Eight 4-bit codes per 32-bit word, i.e. 4 bits per weight before the per-group scale
+ * and zero point ("AWQ + GPTQ Quantization, in depth", What W4A16 buys and why
+ * decoding gets faster: packed 4-bit weights, 4.13 to 4.16 bits per weight with the
+ * group's 16-bit scale and 4-bit zero point). */
 size_t w4a16_qweight_words(int N, int K, int act_order);
 
 /* ---------------------------------------------------------------------------------
@@ -139,7 +144,13 @@ int w4a16_awq_fold_activations(const uint16_t* x, int M, int K, const double* s,
  * Errors: INVALID_ARG, UNSUPPORTED. */
 int w4a16_act_order(const uint16_t* xcal, int T, int K, int group_size, int32_t* g_idx);
 
-/* Pack 4-bit codes into the library's weight buffer.
+/* Pack 4-bit codes into the library's weight buffer: eight codes per 32-bit word
+ * ("AWQ + GPTQ Quantization, in depth", What W4A16 buys and why decoding gets faster:
+ * the weights are stored as packed 4-bit integers; the codes are the q of q =
+ * round(x/S) + Z in "LLM Quantization: A Deep Dive into GPTQ, AWQ, and Post-Training
+ * Quantization", The Math of Quantization).  Act order stores each row in the order
+ * in which GPTQ visits the input channels ("AWQ + GPTQ Quantization, in depth", The two
+ * algorithms, compactly), so that every group is a contiguous run.
  *   codes   uint8 [N][K], values 0..15, in the original input-channel order
  *   g_idx   NULL (contiguous groups) or the act-order group of every input channel;
  *           then each row is stored in group-sorted order (stable sort of k by
@@ -149,7 +160,8 @@ int w4a16_act_order(const uint16_t* xcal, int T, int K, int group_size, int32_t*
 int w4a16_pack(const uint8_t* codes, const int32_t* g_idx, int group_size, int N, int K,
                int32_t* qweight);
 
-/* Inverse of w4a16_pack: codes out uint8 [N][K] in the original input-channel order.
+/* Inverse of w4a16_pack (same passages): codes out uint8 [N][K] in the original
+ * input-channel order.
  * g_idx must be non-NULL exactly when the buffer was packed with one (only its
  * presence is used; the stored order is read from the buffer and checked).
  * Errors: INVALID_ARG, UNSUPPORTED, BAD_GIDX. */
@@ -157,7 +169,10 @@ int w4a16_unpack(const int32_t* qweight, const int32_t* g_idx, int group_size, i
                  uint8_t* codes);
 
 /* Zero points: zeros uint8 [G][N] (0..15) <-> qzeros int32 [G][N/8] (layout above).
- * Errors: INVALID_ARG. */
+ * One 4-bit zero point per (group, output row) ("AWQ + GPTQ Quantization, in depth",
+ * What W4A16 buys and why decoding gets faster: a 4-bit zero point per group; Z is the
+ * integer offset of q = round(x/S) + Z in "LLM Quantization: A Deep Dive...", The Math
+ * of Quantization).  Errors: INVALID_ARG. */
 int w4a16_pack_zeros(const uint8_t* zeros, int G, int N, int32_t* qzeros);
 int w4a16_unpack_zeros(const int32_t* qzeros, int G, int N, uint8_t* zeros);
 
@@ -165,7 +180,12 @@ int w4a16_unpack_zeros(const int32_t* qzeros, int G, int N, uint8_t* zeros);
  * The layer, device memory, asynchronous on `stream`.
  * ------------------------------------------------------------------------------ */
 
-/* y = x * W^T with W^ = (q - Z) * S, fp32 accumulation, y rounded once to binary16.
+/* y = x * W^T with W^ = (q - Z) * S, fp32 accumulation, y rounded once to binary16:
+ * the dequantisation x ~ (q - Z) * S of "LLM Quantization: A Deep Dive into GPTQ, AWQ,
+ * and Post-Training Quantization", The Math of Quantization, applied on the fly as in
+ * "AWQ + GPTQ Quantization, in depth", What W4A16 buys and why decoding gets faster
+ * (load the packed 4-bit weights, expand them to 16 bits in registers with the group's
+ * scale and zero point, multiply with the 16-bit activations).
  * All pointers are device pointers.  qzeros NULL selects symmetric weights (every
  * zero point 8, codes from w4a16_quantize_sym; no zero points stored or read).
  * g_idx non-NULL selects the act-order layout
@@ -174,27 +194,41 @@ int w4a16_unpack_zeros(const int32_t* qzeros, int G, int N, uint8_t* zeros);
  * most 512 groups per row and under 2 GB of codes, else the MFMA kernels; rows longer
  * than 8192 channels are split over several wavefronts); 2 <= M <= 32 (under 2 GB of codes)
  * the skinny-batch MFMA kernel (one launch per 16 rows; K > 8192 split over workgroups,
- * fp32 partials in stream-ordered scratch memory from the device's default pool, summed
- * by a second kernel); larger M the tiled MFMA GEMM
- * (64-, 128- or 256-row tiles), which under act order first gathers x into
- * stream-ordered scratch memory taken from and returned to the device's default memory
- * pool.  Shapes a kernel cannot take (K not a multiple of 128 for the skinny kernel, of
- * 64 for the large tiles) fall to a smaller tiled MFMA kernel, never to the host.
- * Environment: W4A16_DEBUG_CHECKS=1 also validates g_idx (synchronous copy);
- * W4A16_FORCE_PATH=gemv|gemm selects a kernel family (for tests); W4A16_TUNE_* switches
- * change kernel choices and tile shapes (measurements only).
+ * fp32 partials in workspace memory, summed by a second kernel); larger M the tiled MFMA
+ * GEMM (64-, 128- or 256-row tiles), which under act order first gathers x into
+ * workspace memory.  Shapes a kernel cannot take (K not a multiple of 128 for the skinny
+ * kernel, of 64 for the large tiles) fall to a smaller tiled MFMA kernel, never to the
+ * host.
+ * Workspace: only those two paths use one (4 * ks * min(M, 16) * N bytes for ks K slices,
+ * resp. 2 * M * K bytes).  It is owned by the library, one per (device, stream), grown
+ * with hipMalloc when a call needs more and otherwise reused; no call allocates once its
+ * stream's workspace is large enough, and no workspace is ever freed before the process
+ * ends (a captured graph may still use it).  Growth is refused (UNSUPPORTED) while the
+ * stream is being captured: before capturing such a call, run one of at least the same
+ * workspace size eagerly on the capturing stream.  The stream must belong to the current
+ * device.
+ * Environment (read when the library is loaded and by w4a16_reload_env, never per call):
+ * W4A16_DEBUG_CHECKS=1 also validates g_idx (synchronous copy); W4A16_FORCE_PATH=gemv|gemm
+ * selects a kernel family (for tests); W4A16_TUNE_* switches force other kernels or tile
+ * shapes (parity coverage and measurements only).
  * Errors: INVALID_ARG, UNSUPPORTED, MISALIGNED, BAD_GIDX (debug only), HIP. */
 int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                const int32_t* qzeros, const int32_t* g_idx, int group_size, int M, int N,
                int K, uint16_t* y, void* stream);
 
 /* Debug/parity view of the weights: w_out[n][k] = binary16((q - Z) * S) in the
- * original input-channel order, computed with the same device arithmetic that builds
+ * original input-channel order ("LLM Quantization: A Deep Dive...", The Math of
+ * Quantization: x ~ (q - Z) * S), computed with the same device arithmetic that builds
  * the GEMM's weight operand.  Device pointers; qzeros NULL = symmetric (Z = 8).
  * Errors as w4a16_gemm. */
 int w4a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
                   const int32_t* g_idx, int group_size, int N, int K, uint16_t* w_out,
                   void* stream);
+
+/* Re-reads the W4A16_* environment switches described at w4a16_gemm (they are read
+ * once, when the library is loaded).  For tests and measurements; must not run while
+ * another thread is inside a device entry point.  Interface only.  Returns W4A16_OK. */
+int w4a16_reload_env(void);
 
 /* The round-to-nearest quantiser and packing on the device, for contiguous groups:
  * writes exactly what w4a16_quantize (sym == 0) or w4a16_quantize_sym (sym != 0)
@@ -288,8 +322,9 @@ int w8a16_unpack_zeros(const int32_t* qzeros, int G, int N, uint8_t* zeros);
 
 /* y = x * W^T for 8-bit weights, device memory, asynchronous on `stream`.  M == 1
  * runs the split-K GEMV (K <= 32768, at most 512 groups per row, N*K < 2^31), larger M
- * the tiled MFMA kernel (act order: x gathered into stream-ordered scratch memory
- * first).  qzeros NULL = symmetric.  Errors as w4a16_gemm. */
+ * the skinny and tiled MFMA kernels (act order above 32 rows: x gathered into the
+ * workspace first, which works as for w4a16_gemm).  qzeros NULL = symmetric.  Errors as
+ * w4a16_gemm. */
 int w8a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                const int32_t* qzeros, const int32_t* g_idx, int group_size, int M, int N,
                int K, uint16_t* y, void* stream);

@@ -9,6 +9,7 @@ side into the oracle side.
 
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -22,6 +23,19 @@ def note(msg: str) -> None:
     """Name the case about to run on the GPU (flushed first, in case it never returns)."""
     sys.stdout.write(f"[gpu-case] {msg}\n")
     sys.stdout.flush()
+
+
+def set_knob(name: str, value) -> None:
+    """Set a W4A16_* environment switch and have the library read the switches again
+    (it reads them once, not per call)."""
+    os.environ[name] = str(value)
+    w4.w4a16_reload_env()
+
+
+def clear_knob(*names: str) -> None:
+    for name in names:
+        os.environ.pop(name, None)
+    w4.w4a16_reload_env()
 
 
 def device():

@@ -26,7 +26,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = w4.lib()
     declared = _declared_functions()
-    assert len(declared) == 26
+    assert len(declared) == 27
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(w4.EXPORTS) == declared
@@ -369,3 +369,62 @@ def test_gptq_rejects_bad_arguments_before_any_device_work():
     xn[1, 2] = np.nan
     assert call(x=xn) == w4.ERR_INVALID_ARG
     assert b"finite" in L.w4a16_last_error()
+
+
+# --- binding argument checks (refused before anything reaches the device) ----------
+
+def _layer_tensors(N=64, K=256, g=64, act=False, bits=4):
+    import torch
+    G = K // g
+    words = (w4.w4a16_qweight_words if bits == 4 else w4.w8a16_qweight_words)(N, K, act)
+    return dict(
+        x=torch.zeros((2, K), dtype=torch.float16),
+        qweight=torch.zeros(words, dtype=torch.int32),
+        scales=torch.zeros((G, N), dtype=torch.float16),
+        qzeros=torch.zeros((G, N // (8 if bits == 4 else 4)), dtype=torch.int32),
+        g_idx=torch.zeros(K, dtype=torch.int32) if act else None,
+    )
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_binding_refuses_misshaped_layer_tensors(bits):
+    import torch
+    gemm = w4.w4a16_gemm if bits == 4 else w4.w8a16_gemm
+    deq = w4.w4a16_dequant if bits == 4 else w4.w8a16_dequant
+    g = 64
+
+    def call(**over):
+        t = _layer_tensors(act=True, bits=bits)
+        t.update(over)
+        return gemm(t["x"], t["qweight"], t["scales"], t["qzeros"], t["g_idx"], g, y=over.get("y"))
+
+    K, N = 256, 64
+    bad = {
+        "scales": torch.zeros((K // g + 1, N), dtype=torch.float16),          # wrong group count
+        "qzeros": torch.zeros((K // g, N // 8 + 1 if bits == 4 else N // 4 + 1), dtype=torch.int32),
+        "g_idx": torch.zeros(K - 1, dtype=torch.int32),
+        "qweight": torch.zeros(10, dtype=torch.int32),
+        "y": torch.zeros((2, N + 1), dtype=torch.float16),
+    }
+    for name, t in bad.items():
+        with pytest.raises(ValueError, match=name):
+            call(**{name: t})
+    with pytest.raises(ValueError):
+        call(x=torch.zeros((2, K + 32), dtype=torch.float16))   # K from x: scales no longer match
+    t = _layer_tensors(bits=bits)
+    with pytest.raises(ValueError, match="out"):
+        deq(t["qweight"], t["scales"], t["qzeros"], None, g, K, out=torch.zeros((N, K - 8), dtype=torch.float16))
+    with pytest.raises(ValueError, match="qweight"):
+        deq(torch.zeros(8, dtype=torch.int32), t["scales"], t["qzeros"], None, g, K)
+    with pytest.raises(ValueError, match="scales"):
+        deq(t["qweight"], t["scales"], t["qzeros"], None, g, 2 * K)
+    # dtypes
+    with pytest.raises(TypeError):
+        call(scales=torch.zeros((K // g, N), dtype=torch.float32))
+    # well-shaped host tensors pass every shape check and stop at the device check
+    with pytest.raises(TypeError, match="ROCm device"):
+        call()
+
+
+def test_reload_env_is_exported_and_succeeds():
+    w4.w4a16_reload_env()

@@ -17,7 +17,7 @@ import pytest
 import oracle
 import w4a16_gemm_amd as w4
 import workloads as wl
-from gpu_common import codes_of_library_words, device, note, sample_rows
+from gpu_common import clear_knob, codes_of_library_words, device, note, sample_rows, set_knob
 
 pytestmark = pytest.mark.gpu
 
@@ -77,11 +77,11 @@ def test_gemv_refuses_layers_of_two_gigabytes(big_layer):
     import torch
     L = big_layer(N_ABOVE)
     x = torch.from_numpy(wl.random_activations(1, K, seed=1)).to(device())
-    os.environ["W4A16_FORCE_PATH"] = "gemv"
+    set_knob("W4A16_FORCE_PATH", "gemv")
     try:
         note("forced GEMV on a 2 GB + 64 KB layer (expects an error, no launch)")
         with pytest.raises(w4.W4A16Error) as e:
             w4.w4a16_gemm(x, L["qweight"], L["scales"], L["qzeros"], None, G128)
         assert e.value.status == w4.ERR_UNSUPPORTED
     finally:
-        os.environ.pop("W4A16_FORCE_PATH", None)
+        clear_knob("W4A16_FORCE_PATH")

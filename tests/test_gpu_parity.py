@@ -13,7 +13,7 @@ import pytest
 import oracle
 import w4a16_gemm_amd as w4
 import workloads as wl
-from gpu_common import device, note, oracle_layer, product_layer, run_gemm, sample_rows
+from gpu_common import clear_knob, device, note, oracle_layer, product_layer, run_gemm, sample_rows, set_knob
 
 pytestmark = pytest.mark.gpu
 
@@ -75,10 +75,10 @@ def _small_cfg(name, M, N, K, g, act, idx):
 @pytest.fixture(autouse=True)
 def _clear_env():
     for v in ("W4A16_FORCE_PATH", "W4A16_TUNE_GEMM_SKINNY"):
-        os.environ.pop(v, None)
+        clear_knob(v)
     yield
     for v in ("W4A16_FORCE_PATH", "W4A16_TUNE_GEMM_SKINNY"):
-        os.environ.pop(v, None)
+        clear_knob(v)
 
 
 @pytest.mark.parametrize("case", range(len(SMALL)))
@@ -96,13 +96,13 @@ def test_small_layers_match_oracle(case):
     if M <= 64:
         paths.append("gemm-tiled")      # the tiled MFMA kernel instead of the skinny one
     for path in paths:
-        os.environ["W4A16_FORCE_PATH"] = path.split("-")[0]
-        os.environ["W4A16_TUNE_GEMM_SKINNY"] = "0" if path == "gemm-tiled" else "1"
+        set_knob("W4A16_FORCE_PATH", path.split("-")[0])
+        set_knob("W4A16_TUNE_GEMM_SKINNY", "0" if path == "gemm-tiled" else "1")
         note(f"  path={path}")
         y = run_gemm(prod).cpu().numpy()
         err = oracle.rel_err(y, ref["y_ref"])
         assert err <= TOL, (path, err)
-    os.environ.pop("W4A16_TUNE_GEMM_SKINNY", None)
+    clear_knob("W4A16_TUNE_GEMM_SKINNY")
     # the device weight view is bit-exact
     W16 = w4.w4a16_dequant(prod["qweight"], prod["scales"], prod["qzeros"], prod["g_idx"], g, K).cpu().numpy()
     assert np.array_equal(W16.view(np.uint16), ref["W16"].view(np.uint16))
@@ -142,10 +142,10 @@ def test_unit_vector_probes_bit_exact(case):
     expect = ref["W16"][:, ks].T.copy()                       # [len(ks)][N]
     xe = torch.from_numpy(E).to(device())
     note(f"probe {name} gemm M={len(ks)}")
-    os.environ["W4A16_FORCE_PATH"] = "gemm"
+    set_knob("W4A16_FORCE_PATH", "gemm")
     y = run_gemm(prod, x=xe).cpu().numpy()
     assert np.array_equal(y.view(np.uint16), expect.view(np.uint16))
-    os.environ["W4A16_FORCE_PATH"] = "gemv"
+    set_knob("W4A16_FORCE_PATH", "gemv")
     for i in range(len(ks)):
         note(f"probe {name} gemv k={ks[i]}")
         yi = run_gemm(prod, x=xe[i:i + 1].contiguous()).cpu().numpy()
@@ -167,9 +167,9 @@ LARGE_TILE_CASES = [
 @pytest.mark.parametrize("mfma32", [0, 1, 2])
 def test_large_tile_kinds_match_oracle(mb, mfma32):
     import torch
-    os.environ["W4A16_FORCE_PATH"] = "gemm"
-    os.environ["W4A16_TUNE_GEMM_BIG_MB"] = str(mb)
-    os.environ["W4A16_TUNE_GEMM_MFMA32"] = str(mfma32)
+    set_knob("W4A16_FORCE_PATH", "gemm")
+    set_knob("W4A16_TUNE_GEMM_BIG_MB", str(mb))
+    set_knob("W4A16_TUNE_GEMM_MFMA32", str(mfma32))
     try:
         for i, (name, M, N, K, g, act, sym) in enumerate(LARGE_TILE_CASES):
             cfg = wl.custom_config(name, 300 + i, K=K, N=N, group_size=g, M_list=(M,), act_order=act, sym=sym)
@@ -179,9 +179,9 @@ def test_large_tile_kinds_match_oracle(mb, mfma32):
             y = run_gemm(prod).cpu().numpy()
             assert oracle.rel_err(y, ref["y_ref"]) <= TOL
             # wavefront priority changes only the schedule: bit-identical outputs without it
-            os.environ["W4A16_TUNE_GEMM_PRIO"] = "0"
+            set_knob("W4A16_TUNE_GEMM_PRIO", "0")
             y0 = run_gemm(prod).cpu().numpy()
-            os.environ.pop("W4A16_TUNE_GEMM_PRIO")
+            clear_knob("W4A16_TUNE_GEMM_PRIO")
             assert np.array_equal(y0.view(np.uint16), y.view(np.uint16))
             # x = e_k for 130 channels: every output exactly binary16(W^[n, k])
             ks = np.arange(0, K, max(1, K // 130))[:130]
@@ -189,7 +189,7 @@ def test_large_tile_kinds_match_oracle(mb, mfma32):
             assert np.array_equal(y.view(np.uint16), ref["W16"][:, ks].T.copy().view(np.uint16))
     finally:
         for v in ("W4A16_TUNE_GEMM_BIG_MB", "W4A16_TUNE_GEMM_MFMA32", "W4A16_TUNE_GEMM_PRIO"):
-            os.environ.pop(v, None)
+            clear_knob(v)
 
 
 def test_all_ones_gives_row_sums():
@@ -199,7 +199,7 @@ def test_all_ones_gives_row_sums():
     ref = oracle_layer(cfg, 1, np.arange(520), x=np.ones((1, 3072), np.float16))
     ones = torch.ones((4, 3072), dtype=torch.float16, device=device())
     for path, x in (("gemv", ones[:1]), ("gemm", ones)):
-        os.environ["W4A16_FORCE_PATH"] = path
+        set_knob("W4A16_FORCE_PATH", path)
         note(f"all-ones {path}")
         y = run_gemm(prod, x=x.contiguous()).cpu().numpy()
         for row in y:
@@ -228,11 +228,11 @@ def test_device_errors_are_reported():
     import torch
     cfg = _small_cfg("err", 2, 264, 1024, 64, False, 52)
     prod = product_layer(cfg, 2)
-    os.environ["W4A16_FORCE_PATH"] = "gemv"
+    set_knob("W4A16_FORCE_PATH", "gemv")
     with pytest.raises(w4.W4A16Error) as e:
         run_gemm(prod)
     assert e.value.status == w4.ERR_UNSUPPORTED
-    os.environ.pop("W4A16_FORCE_PATH")
+    clear_knob("W4A16_FORCE_PATH")
     raw = torch.empty(1024 * 2 + 8, dtype=torch.float16, device=device())
     x_mis = raw[1:1 + 2 * 1024].view(2, 1024)
     lib = w4.lib()
@@ -286,19 +286,19 @@ def test_symmetric_and_per_channel_layers_match_oracle(case):
     assert np.array_equal(prod["codes"], ref["codes"])
     paths = ["gemv", "gemm"] if M == 1 else ["gemm"]
     for path in paths:
-        os.environ["W4A16_FORCE_PATH"] = path
+        set_knob("W4A16_FORCE_PATH", path)
         note(f"  path={path}")
         y = run_gemm(prod).cpu().numpy()
         assert oracle.rel_err(y, ref["y_ref"]) <= TOL, path
-    os.environ.pop("W4A16_FORCE_PATH", None)
+    clear_knob("W4A16_FORCE_PATH")
     W16 = w4.w4a16_dequant(prod["qweight"], prod["scales"], prod["qzeros"], prod["g_idx"], g, K).cpu().numpy()
     assert np.array_equal(W16.view(np.uint16), ref["W16"].view(np.uint16))
     # unit-vector probes select binary16((code - 8) * S) exactly
     ks = np.unique(np.concatenate([[0, K - 1], np.random.default_rng(case).integers(0, K, 6)]))
     E = torch.from_numpy(wl.unit_vectors(K, ks)).to(device())
-    os.environ["W4A16_FORCE_PATH"] = "gemm"
+    set_knob("W4A16_FORCE_PATH", "gemm")
     ye = run_gemm(prod, x=E).cpu().numpy()
-    os.environ.pop("W4A16_FORCE_PATH")
+    clear_knob("W4A16_FORCE_PATH")
     assert np.array_equal(ye.view(np.uint16), ref["W16"][:, ks].T.copy().view(np.uint16))
 
 
@@ -369,11 +369,11 @@ def test_gemv_row_shapes_match_oracle(case):
     try:
         for lpr in [None] + [l for l in (64, 32, 16, 8) if (C + l - 1) // l <= 4]:
             if lpr is None:
-                os.environ.pop("W4A16_TUNE_GEMV_LPR", None)
+                clear_knob("W4A16_TUNE_GEMV_LPR")
             else:
-                os.environ["W4A16_TUNE_GEMV_LPR"] = str(lpr)
+                set_knob("W4A16_TUNE_GEMV_LPR", str(lpr))
             note(f"  lanes per row {lpr or 'auto'}")
             y = run_gemm(prod).cpu().numpy()
             assert oracle.rel_err(y, ref["y_ref"]) <= TOL, lpr
     finally:
-        os.environ.pop("W4A16_TUNE_GEMV_LPR", None)
+        clear_knob("W4A16_TUNE_GEMV_LPR")

@@ -15,7 +15,7 @@ import pytest
 import oracle
 import w4a16_gemm_amd as w4
 import workloads as wl
-from gpu_common import device, note, oracle_layer, product_layer, run_gemm, sample_rows
+from gpu_common import clear_knob, device, note, oracle_layer, product_layer, run_gemm, sample_rows, set_knob
 
 pytestmark = pytest.mark.gpu
 
@@ -37,9 +37,9 @@ CASES = [
 
 @pytest.fixture(autouse=True)
 def _clear_env():
-    os.environ.pop("W4A16_FORCE_PATH", None)
+    clear_knob("W4A16_FORCE_PATH")
     yield
-    os.environ.pop("W4A16_FORCE_PATH", None)
+    clear_knob("W4A16_FORCE_PATH")
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))
@@ -52,11 +52,11 @@ def test_w8a16_layers_match_oracle(case):
     ref = oracle_layer(cfg, M, np.arange(N))
     assert np.array_equal(prod["codes"], ref["codes"])
     for path in (["gemv", "gemm"] if M == 1 else ["gemm"]):
-        os.environ["W4A16_FORCE_PATH"] = path
+        set_knob("W4A16_FORCE_PATH", path)
         note(f"  path={path}")
         y = run_gemm(prod).cpu().numpy()
         assert oracle.rel_err(y, ref["y_ref"]) <= TOL, path
-    os.environ.pop("W4A16_FORCE_PATH")
+    clear_knob("W4A16_FORCE_PATH")
     W16 = w4.w8a16_dequant(prod["qweight"], prod["scales"], prod["qzeros"], prod["g_idx"], g, K).cpu().numpy()
     assert np.array_equal(W16.view(np.uint16), ref["W16"].view(np.uint16))
     back = w4.w8a16_unpack(prod["qweight"].cpu().numpy(), prod["g_idx_np"], g, N, K)
@@ -65,10 +65,10 @@ def test_w8a16_layers_match_oracle(case):
     ks = np.unique(np.concatenate([[0, K - 1], np.random.default_rng(case).integers(0, K, 6)]))
     E = torch.from_numpy(wl.unit_vectors(K, ks)).to(device())
     expect = ref["W16"][:, ks].T.copy()
-    os.environ["W4A16_FORCE_PATH"] = "gemm"
+    set_knob("W4A16_FORCE_PATH", "gemm")
     ye = run_gemm(prod, x=E).cpu().numpy()
     assert np.array_equal(ye.view(np.uint16), expect.view(np.uint16))
-    os.environ["W4A16_FORCE_PATH"] = "gemv"
+    set_knob("W4A16_FORCE_PATH", "gemv")
     for i in (0, len(ks) - 1):
         yi = run_gemm(prod, x=E[i:i + 1].contiguous()).cpu().numpy()
         assert np.array_equal(yi[0].view(np.uint16), expect[i].view(np.uint16))
@@ -109,10 +109,10 @@ def test_w8a16_skinny_batches_match_oracle(case):
     prod = product_layer(cfg, M)
     ref = oracle_layer(cfg, M, np.arange(N))
     for tiled in ("1", "0"):
-        os.environ["W4A16_TUNE_GEMM_SKINNY"] = tiled
+        set_knob("W4A16_TUNE_GEMM_SKINNY", tiled)
         y = run_gemm(prod).cpu().numpy()
         assert oracle.rel_err(y, ref["y_ref"]) <= TOL, tiled
-    os.environ.pop("W4A16_TUNE_GEMM_SKINNY")
+    clear_knob("W4A16_TUNE_GEMM_SKINNY")
 
 
 # larger batches (M >= 33): the 8-bit large-tile kernel at every tile height, the tiled
@@ -140,11 +140,11 @@ def test_w8a16_large_batches_match_oracle(case):
     expect = ref["W16"][:, ks].T.copy()
     try:
         for big, mb in (("1", None), ("1", "2"), ("1", "4"), ("1", "8"), ("0", None)):
-            os.environ["W4A16_TUNE_GEMM_BIG"] = big
+            set_knob("W4A16_TUNE_GEMM_BIG", big)
             if mb is None:
-                os.environ.pop("W4A16_TUNE_GEMM_BIG_MB", None)
+                clear_knob("W4A16_TUNE_GEMM_BIG_MB")
             else:
-                os.environ["W4A16_TUNE_GEMM_BIG_MB"] = mb
+                set_knob("W4A16_TUNE_GEMM_BIG_MB", mb)
             note(f"  big={big} mb={mb}")
             y = run_gemm(prod).cpu().numpy()
             assert oracle.rel_err(y, ref["y_ref"]) <= TOL, (big, mb)
@@ -152,8 +152,8 @@ def test_w8a16_large_batches_match_oracle(case):
             ye = run_gemm(prod, x=E).cpu().numpy()
             assert np.array_equal(ye.view(np.uint16), expect.view(np.uint16)), (big, mb)
     finally:
-        os.environ.pop("W4A16_TUNE_GEMM_BIG", None)
-        os.environ.pop("W4A16_TUNE_GEMM_BIG_MB", None)
+        clear_knob("W4A16_TUNE_GEMM_BIG")
+        clear_knob("W4A16_TUNE_GEMM_BIG_MB")
 
 
 def test_w8a16_prefill_layer_on_sampled_rows():

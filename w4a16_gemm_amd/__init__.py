@@ -40,6 +40,7 @@ _SIGNATURES = {
                             _c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
     "w4a16_dequant": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                _c_int, _c_void_p, _c_void_p]),
+    "w4a16_reload_env": (_c_int, []),
     "w4a16_quantize_device": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_int, _c_void_p,
                                        _c_void_p, _c_void_p, _c_void_p]),
     "w4a16_awq_search": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p,
@@ -206,11 +207,93 @@ def w4a16_unpack_zeros(qzeros, G: int, N: int) -> np.ndarray:
 
 # --- device entry points (torch tensors on a ROCm device) --------------------------
 
+def w4a16_reload_env() -> None:
+    """Re-read the W4A16_* environment switches (the library reads them once)."""
+    _check(lib().w4a16_reload_env())
+
+
 def _dev(t, dtype, name):
     import torch
-    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
-        raise TypeError(f"{name} must be a contiguous {dtype} tensor on a ROCm device")
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous {dtype} tensor")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must live on a ROCm device")
     return t
+
+
+def _shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _layer_shapes(qweight, scales, qzeros, g_idx, group_size: int, K: int, bits: int):
+    """Check every weight-side tensor against the layer (N from scales, K given) before
+    anything is launched, so that a mis-shaped tensor is refused instead of read past
+    its end.  Returns N."""
+    import torch
+    for t, dt, name in ((qweight, torch.int32, "qweight"), (scales, torch.float16, "scales"),
+                        (qzeros, torch.int32, "qzeros"), (g_idx, torch.int32, "g_idx")):
+        if t is not None and (not isinstance(t, torch.Tensor) or t.dtype != dt):
+            raise TypeError(f"{name} must be a {dt} tensor")
+    if scales.dim() != 2:
+        raise ValueError(f"scales must be [G][N], got shape {tuple(scales.shape)}")
+    G, N = scales.shape
+    if group_size <= 0 or K <= 0 or K % group_size != 0:
+        raise ValueError(f"K={K} is not a positive multiple of group_size={group_size}")
+    _shape(scales, (K // group_size, N), "scales")
+    if qzeros is not None:
+        _shape(qzeros, (G, N // (32 // bits)), "qzeros")
+    if g_idx is not None:
+        _shape(g_idx, (K,), "g_idx")
+    words = (w4a16_qweight_words if bits == 4 else w8a16_qweight_words)(N, K, g_idx is not None)
+    if words == 0 or qweight.numel() < words:
+        raise ValueError(f"qweight has {qweight.numel()} words, the packed {N} x {K} layer needs {words}")
+    return N
+
+
+def _layer_call(fn, x, qweight, scales, qzeros, g_idx, group_size, y, stream, bits):
+    import torch
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-d tensor [M][K]")
+    M, K = x.shape
+    N = _layer_shapes(qweight, scales, qzeros, g_idx, group_size, K, bits)
+    if y is not None:
+        _shape(y, (M, N), "y")
+    _dev(x, torch.float16, "x")
+    _dev(qweight, torch.int32, "qweight")
+    _dev(scales, torch.float16, "scales")
+    if qzeros is not None:                      # None: symmetric weights
+        _dev(qzeros, torch.int32, "qzeros")
+    if g_idx is not None:
+        _dev(g_idx, torch.int32, "g_idx")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _dev(y, torch.float16, "y")
+    _check(fn(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(),
+              None if qzeros is None else qzeros.data_ptr(),
+              None if g_idx is None else g_idx.data_ptr(), group_size, M, N, K,
+              y.data_ptr(), _stream_handle(stream, x.device)))
+    return y
+
+
+def _dequant_call(fn, qweight, scales, qzeros, g_idx, group_size, K, out, stream, bits):
+    import torch
+    N = _layer_shapes(qweight, scales, qzeros, g_idx, group_size, K, bits)
+    if out is not None:
+        _shape(out, (N, K), "out")
+    _dev(qweight, torch.int32, "qweight")
+    _dev(scales, torch.float16, "scales")
+    if qzeros is not None:
+        _dev(qzeros, torch.int32, "qzeros")
+    if g_idx is not None:
+        _dev(g_idx, torch.int32, "g_idx")
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.float16, device=qweight.device)
+    _dev(out, torch.float16, "out")
+    _check(fn(qweight.data_ptr(), scales.data_ptr(), None if qzeros is None else qzeros.data_ptr(),
+              None if g_idx is None else g_idx.data_ptr(), group_size, N, K,
+              out.data_ptr(), _stream_handle(stream, qweight.device)))
+    return out
 
 
 def _stream_handle(stream, device):
@@ -222,49 +305,14 @@ def _stream_handle(stream, device):
 
 def w4a16_gemm(x, qweight, scales, qzeros, g_idx, group_size: int, y=None, stream=None):
     """y = x W^T on the device.  x binary16 [M][K]; scales binary16 [G][N];
-    qzeros int32 [G][N/8]; qweight int32 from w4a16_pack; g_idx int32 [K] or None.
-    Returns y binary16 [M][N] (allocated unless given)."""
-    import torch
-    _dev(x, torch.float16, "x")
-    _dev(qweight, torch.int32, "qweight")
-    _dev(scales, torch.float16, "scales")
-    if qzeros is not None:                      # None: symmetric weights
-        _dev(qzeros, torch.int32, "qzeros")
-    if g_idx is not None:
-        _dev(g_idx, torch.int32, "g_idx")
-    M, K = x.shape
-    G, N = scales.shape
-    if qweight.numel() < w4a16_qweight_words(N, K, g_idx is not None):
-        raise ValueError("qweight is smaller than the packed size of an N x K layer")
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
-    _dev(y, torch.float16, "y")
-    if tuple(y.shape) != (M, N):
-        raise ValueError(f"y shape {tuple(y.shape)} != {(M, N)}")
-    _check(lib().w4a16_gemm(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(),
-                            None if qzeros is None else qzeros.data_ptr(),
-                            None if g_idx is None else g_idx.data_ptr(), group_size, M, N, K,
-                            y.data_ptr(), _stream_handle(stream, x.device)))
-    return y
+    qzeros int32 [G][N/8] or None (symmetric); qweight int32 from w4a16_pack; g_idx int32
+    [K] or None.  Returns y binary16 [M][N] (allocated unless given)."""
+    return _layer_call(lib().w4a16_gemm, x, qweight, scales, qzeros, g_idx, group_size, y, stream, 4)
 
 
 def w4a16_dequant(qweight, scales, qzeros, g_idx, group_size: int, K: int, out=None, stream=None):
     """binary16 (q - Z) * S as [N][K] in the original input-channel order."""
-    import torch
-    _dev(qweight, torch.int32, "qweight")
-    _dev(scales, torch.float16, "scales")
-    if qzeros is not None:                      # None: symmetric weights
-        _dev(qzeros, torch.int32, "qzeros")
-    if g_idx is not None:
-        _dev(g_idx, torch.int32, "g_idx")
-    G, N = scales.shape
-    if out is None:
-        out = torch.empty((N, K), dtype=torch.float16, device=qweight.device)
-    _dev(out, torch.float16, "out")
-    _check(lib().w4a16_dequant(qweight.data_ptr(), scales.data_ptr(), None if qzeros is None else qzeros.data_ptr(),
-                               None if g_idx is None else g_idx.data_ptr(), group_size, N, K,
-                               out.data_ptr(), _stream_handle(stream, qweight.device)))
-    return out
+    return _dequant_call(lib().w4a16_dequant, qweight, scales, qzeros, g_idx, group_size, K, out, stream, 4)
 
 
 __all__ = ["LIB_PATH", "EXPORTS", "W4A16Error", "lib"] + [n for n in EXPORTS if n != "w4a16_last_error"]
@@ -344,47 +392,12 @@ def w8a16_unpack_zeros(qzeros, G: int, N: int) -> np.ndarray:
 
 def w8a16_gemm(x, qweight, scales, qzeros, g_idx, group_size: int, y=None, stream=None):
     """y = x W^T for 8-bit weights on the device (qzeros int32 [G][N/4] or None)."""
-    import torch
-    _dev(x, torch.float16, "x")
-    _dev(qweight, torch.int32, "qweight")
-    _dev(scales, torch.float16, "scales")
-    if qzeros is not None:
-        _dev(qzeros, torch.int32, "qzeros")
-    if g_idx is not None:
-        _dev(g_idx, torch.int32, "g_idx")
-    M, K = x.shape
-    G, N = scales.shape
-    if qweight.numel() < w8a16_qweight_words(N, K, g_idx is not None):
-        raise ValueError("qweight is smaller than the packed size of an N x K 8-bit layer")
-    if y is None:
-        y = torch.empty((M, N), dtype=torch.float16, device=x.device)
-    _dev(y, torch.float16, "y")
-    if tuple(y.shape) != (M, N):
-        raise ValueError(f"y shape {tuple(y.shape)} != {(M, N)}")
-    _check(lib().w8a16_gemm(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(),
-                            None if qzeros is None else qzeros.data_ptr(),
-                            None if g_idx is None else g_idx.data_ptr(), group_size, M, N, K,
-                            y.data_ptr(), _stream_handle(stream, x.device)))
-    return y
+    return _layer_call(lib().w8a16_gemm, x, qweight, scales, qzeros, g_idx, group_size, y, stream, 8)
 
 
 def w8a16_dequant(qweight, scales, qzeros, g_idx, group_size: int, K: int, out=None, stream=None):
     """binary16 (q - Z) * S of an 8-bit weight buffer as [N][K] in the original order."""
-    import torch
-    _dev(qweight, torch.int32, "qweight")
-    _dev(scales, torch.float16, "scales")
-    if qzeros is not None:
-        _dev(qzeros, torch.int32, "qzeros")
-    if g_idx is not None:
-        _dev(g_idx, torch.int32, "g_idx")
-    G, N = scales.shape
-    if out is None:
-        out = torch.empty((N, K), dtype=torch.float16, device=qweight.device)
-    _dev(out, torch.float16, "out")
-    _check(lib().w8a16_dequant(qweight.data_ptr(), scales.data_ptr(), None if qzeros is None else qzeros.data_ptr(),
-                               None if g_idx is None else g_idx.data_ptr(), group_size, N, K,
-                               out.data_ptr(), _stream_handle(stream, qweight.device)))
-    return out
+    return _dequant_call(lib().w8a16_dequant, qweight, scales, qzeros, g_idx, group_size, K, out, stream, 8)
 
 
 def w4a16_awq_search(w, xcal, group_size: int, alphas, stream=None):

@@ -7,6 +7,9 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
 #include <vector>
 
 #include "internal.hpp"
@@ -36,12 +39,105 @@ int env_int(const char* name, int fallback) {
   return std::atoi(v);
 }
 
+enum class Path { kAuto, kGemv, kGemm };
+
+// Environment switches, read once per process (at the first device call, or again by
+// w4a16_reload_env), never on the per-call path.  All but debug_checks and force_path
+// only force alternative kernels or tile shapes, for parity coverage and measurements.
+struct Knobs {
+  int debug_checks = 0;         // W4A16_DEBUG_CHECKS: validate g_idx (synchronous)
+  Path force_path = Path::kAuto;   // W4A16_FORCE_PATH=gemv|gemm
+  int gemv_lpr = 0;             // W4A16_TUNE_GEMV_LPR: lanes per row of the GEMV
+  int gemv_blocks_per_cu = 1;   // W4A16_TUNE_GEMV_BLOCKS_PER_CU
+  int gemm_prio = 1;            // W4A16_TUNE_GEMM_PRIO: wavefront priority in the large tiles
+  int gemm_mfma32 = 1;          // W4A16_TUNE_GEMM_MFMA32: 32x32 blocks (0 never, 1 small tiles, 2 all)
+  int gemm_split = 1;           // W4A16_TUNE_GEMM_SPLIT: two tile widths per launch
+  int gemm_big_mb = 0;          // W4A16_TUNE_GEMM_BIG_MB: forced row blocks per wavefront (0 = auto)
+  int gemm_big_min_m = 0;       // W4A16_TUNE_GEMM_BIG_MIN_M (0 = default)
+  int gemm_big = 1;             // W4A16_TUNE_GEMM_BIG: large-tile kernel allowed
+  int skinny_chunk_max_m = 0;   // W4A16_TUNE_SKINNY_CHUNK_MAX_M (0 = default)
+  int gemm_skinny = 1;          // W4A16_TUNE_GEMM_SKINNY: skinny kernel allowed
+};
+
+Knobs read_knobs() {
+  Knobs k;
+  k.debug_checks = env_int("W4A16_DEBUG_CHECKS", 0);
+  const char* v = std::getenv("W4A16_FORCE_PATH");
+  if (v && std::strcmp(v, "gemv") == 0) k.force_path = Path::kGemv;
+  if (v && std::strcmp(v, "gemm") == 0) k.force_path = Path::kGemm;
+  k.gemv_lpr = env_int("W4A16_TUNE_GEMV_LPR", 0);
+  k.gemv_blocks_per_cu = env_int("W4A16_TUNE_GEMV_BLOCKS_PER_CU", 1);
+  k.gemm_prio = env_int("W4A16_TUNE_GEMM_PRIO", 1);
+  k.gemm_mfma32 = env_int("W4A16_TUNE_GEMM_MFMA32", 1);
+  k.gemm_split = env_int("W4A16_TUNE_GEMM_SPLIT", 1);
+  k.gemm_big_mb = env_int("W4A16_TUNE_GEMM_BIG_MB", 0);
+  k.gemm_big_min_m = env_int("W4A16_TUNE_GEMM_BIG_MIN_M", 0);
+  k.gemm_big = env_int("W4A16_TUNE_GEMM_BIG", 1);
+  k.skinny_chunk_max_m = env_int("W4A16_TUNE_SKINNY_CHUNK_MAX_M", 0);
+  k.gemm_skinny = env_int("W4A16_TUNE_GEMM_SKINNY", 1);
+  return k;
+}
+
+Knobs g_knobs = read_knobs();   // at library load; w4a16_reload_env reads again
+
+const Knobs& knobs() { return g_knobs; }
+
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return W4A16_OK;
   return fail(W4A16_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
 int check_launch(const char* what) { return hip_status(hipGetLastError(), what); }
+
+// --- scratch memory ------------------------------------------------------------
+//
+// Two layer paths need device memory beyond x, the weights and y: the fp32 partial
+// tiles of skinny launches whose K is split over workgroups, and x gathered into the
+// stored channel order for act-order batches of more than 32 rows.  The entry point
+// decides where it comes from; the kernels only see a pointer.
+using ScratchFn = int (*)(hipStream_t st, size_t bytes, void** out);
+
+// w4a16_gemm / w8a16_gemm: a library-owned workspace per (device, stream).  Calls on
+// one stream are ordered, so they share it; calls on different streams never do.  It
+// grows (by at least 2x) when a call needs more, with hipMalloc on the calling thread,
+// which is refused while the stream is being captured into a graph: a captured call
+// must follow an eager call of at least the same workspace size on the same stream.  A
+// grown-out buffer is kept, not freed, because a captured graph may still use it; the
+// memory is held until the process ends (at most twice the largest request per stream).
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  std::vector<void*> retired;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
+
+int workspace_scratch(hipStream_t st, size_t bytes, void** out) {
+  int dev = 0;
+  if (int rc = hip_status(hipGetDevice(&dev), "hipGetDevice")) return rc;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  Workspace& ws = g_ws[{dev, reinterpret_cast<uintptr_t>(st)}];
+  if (ws.bytes >= bytes) {
+    *out = ws.ptr;
+    return W4A16_OK;
+  }
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (int rc = hip_status(hipStreamIsCapturing(st, &cap), "hipStreamIsCapturing")) return rc;
+  if (cap != hipStreamCaptureStatusNone)
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "this call needs %zu bytes of workspace on a stream under graph capture, which holds %zu: "
+                "run a call of at least this size on the same stream before capturing",
+                bytes, ws.bytes);
+  constexpr size_t kGrain = size_t{2} << 20;
+  const size_t want = std::max((bytes + kGrain - 1) / kGrain * kGrain, 2 * ws.bytes);
+  void* p = nullptr;
+  if (int rc = hip_status(hipMalloc(&p, want), "hipMalloc (workspace)")) return rc;
+  if (ws.ptr) ws.retired.push_back(ws.ptr);
+  ws.ptr = p;
+  ws.bytes = want;
+  *out = p;
+  return W4A16_OK;
+}
 
 // Zero points as the kernels take them: NULL qzeros = symmetric (Z = 8 everywhere); the
 // kernels' zero-point loads then all read the first word of the scales and ignore it.
@@ -63,7 +159,7 @@ int check_device_args(const void* const* ptrs, int nptrs, int N, int K, int grou
 // Optional (W4A16_DEBUG_CHECKS=1) check of a device-resident g_idx against the order
 // stored in the weight buffer.  Synchronous.
 int debug_check_gidx(const int32_t* g_idx, const int32_t* tail_dev, int K, int group_size, hipStream_t stream) {
-  if (env_int("W4A16_DEBUG_CHECKS", 0) == 0) return W4A16_OK;
+  if (knobs().debug_checks == 0) return W4A16_OK;
   if (int st = hip_status(hipStreamSynchronize(stream), "hipStreamSynchronize")) return st;
   std::vector<int32_t> h(K), tail(K), perm(K);
   if (int st = hip_status(hipMemcpy(h.data(), g_idx, sizeof(int32_t) * K, hipMemcpyDeviceToHost), "hipMemcpy"))
@@ -123,66 +219,67 @@ int device_cus() {
 constexpr int gemv_depth(int cpl) { return cpl >= 3 ? 2 : 8 / cpl; }
 
 template <int LPR, int CPL, bool EXACT, bool ACT, int EPT, int WPR, int BITS>
-void launch_gemv_e(dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
+int launch_gemv_e(dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
                    const uint16_t* s, Zeros z, half_t* y, int N, int K, int gshift, int steps) {
   auto kern = gemv_m1_kernel<LPR, CPL, kGemvWaves, gemv_depth(CPL), EXACT, ACT, EPT, WPR, BITS>;
   // Dynamic LDS above 64 KB has to be allowed per kernel (once per process).
   static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        static_cast<int>(kGemvLdsBudget));
-  if (lds_ok != hipSuccess && shmem > 64 * 1024) return;  // reported by the caller's launch check
+  if (shmem > 64 * 1024)
+    if (int rc = hip_status(lds_ok, "hipFuncSetAttribute")) return rc;
   hipLaunchKernelGGL(kern, grid, dim3(kGemvWaves * 64), shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+  return check_launch("gemv launch");
 }
 
 // Staging rows per thread: one row (EPT = 1) is compiled only for exact splits
 // without act order, the decode shapes of large layers; everything else stages
 // whole 8-row items.
 template <int LPR, int CPL, bool EXACT, bool ACT, int BITS>
-void launch_gemv_t(int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
+int launch_gemv_t(int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
                    const uint16_t* s, Zeros z, half_t* y, int N, int K, int gshift, int steps) {
   if constexpr (EXACT && !ACT)
     if (ept == 1)
       return launch_gemv_e<LPR, CPL, EXACT, ACT, 1, 1, BITS>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
-  launch_gemv_e<LPR, CPL, EXACT, ACT, 8, 1, BITS>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+  return launch_gemv_e<LPR, CPL, EXACT, ACT, 8, 1, BITS>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
 }
 
 template <int LPR, bool EXACT, bool ACT, int BITS>
-void launch_gemv_cpl(int cpl, int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
+int launch_gemv_cpl(int cpl, int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
                      const uint16_t* s, Zeros z, half_t* y, int N, int K, int gshift, int steps) {
   switch (cpl) {
-    case 1: launch_gemv_t<LPR, 1, EXACT, ACT, BITS>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 2: launch_gemv_t<LPR, 2, EXACT, ACT, BITS>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 3: launch_gemv_t<LPR, 3, EXACT, ACT, BITS>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    default: launch_gemv_t<LPR, 4, EXACT, ACT, BITS>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 1: return launch_gemv_t<LPR, 1, EXACT, ACT, BITS>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+    case 2: return launch_gemv_t<LPR, 2, EXACT, ACT, BITS>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+    case 3: return launch_gemv_t<LPR, 3, EXACT, ACT, BITS>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+    default: return launch_gemv_t<LPR, 4, EXACT, ACT, BITS>(ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
   }
 }
 
 // Split rows (K > 8192): 64 lanes per row slice, 3 or 4 chunks per lane, whole 8-row
 // staging items (a row has more than 64 groups).
 template <int WPR, bool EXACT, bool ACT, int BITS>
-void launch_gemv_split(int cpl, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
+int launch_gemv_split(int cpl, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
                        const uint16_t* s, Zeros z, half_t* y, int N, int K, int gshift, int steps) {
-  if (cpl == 3) launch_gemv_e<64, 3, EXACT, ACT, 8, WPR, BITS>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
-  else launch_gemv_e<64, 4, EXACT, ACT, 8, WPR, BITS>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+  if (cpl == 3) return launch_gemv_e<64, 3, EXACT, ACT, 8, WPR, BITS>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+  return launch_gemv_e<64, 4, EXACT, ACT, 8, WPR, BITS>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
 }
 
 template <bool EXACT, bool ACT, int BITS>
-void launch_gemv_lpr(const GemvShape& sh, int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x,
+int launch_gemv_lpr(const GemvShape& sh, int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x,
                      const uint32_t* qw, const uint16_t* s, Zeros z, half_t* y, int N, int K,
                      int gshift, int steps) {
   if (sh.wpr > 1) {
     switch (sh.wpr) {
-      case 2: launch_gemv_split<2, EXACT, ACT, BITS>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-      case 4: launch_gemv_split<4, EXACT, ACT, BITS>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-      default: launch_gemv_split<8, EXACT, ACT, BITS>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+      case 2: return launch_gemv_split<2, EXACT, ACT, BITS>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+      case 4: return launch_gemv_split<4, EXACT, ACT, BITS>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+      default: return launch_gemv_split<8, EXACT, ACT, BITS>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
     }
-    return;
   }
   switch (sh.lpr) {
-    case 64: launch_gemv_cpl<64, EXACT, ACT, BITS>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 32: launch_gemv_cpl<32, EXACT, ACT, BITS>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    case 16: launch_gemv_cpl<16, EXACT, ACT, BITS>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
-    default: launch_gemv_cpl<8, EXACT, ACT, BITS>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps); break;
+    case 64: return launch_gemv_cpl<64, EXACT, ACT, BITS>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+    case 32: return launch_gemv_cpl<32, EXACT, ACT, BITS>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+    case 16: return launch_gemv_cpl<16, EXACT, ACT, BITS>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+    default: return launch_gemv_cpl<8, EXACT, ACT, BITS>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
   }
 }
 
@@ -215,7 +312,7 @@ GemvPlan plan_gemv(int N, int K, int gshift, bool act, int bits = 4) {
   GemvShape sh = pick_gemv_shape(C);
   if (sh.lpr == 0) return GemvPlan{};
   // measurements only: lanes per row forced (rows of at most 256 chunks)
-  const int lpr = env_int("W4A16_TUNE_GEMV_LPR", 0);
+  const int lpr = knobs().gemv_lpr;
   if (sh.wpr == 1 && (lpr == 8 || lpr == 16 || lpr == 32 || lpr == 64) && (C + lpr - 1) / lpr <= 4)
     return plan_gemv_for({lpr, (C + lpr - 1) / lpr, C % lpr == 0, 1}, N, K, gshift, act, bits);
   if (sh.wpr == 1) {
@@ -240,7 +337,7 @@ GemvPlan plan_gemv_for(const GemvShape& sh, int N, int K, int gshift, bool act, 
   if ((unit / 8) * G > kGemvWaves * 64) return p;                   // one staging item per thread and step
   p.ept = unit * G <= kGemvWaves * 64 ? 1 : 8;                      // staging rows per thread
   const int units = (N + unit - 1) / unit;
-  const int per_cu = env_int("W4A16_TUNE_GEMV_BLOCKS_PER_CU", 1);
+  const int per_cu = knobs().gemv_blocks_per_cu;
   p.blocks = std::min(units, std::max(1, device_cus() * std::max(1, per_cu)));
   if (p.blocks >= 8) p.blocks -= p.blocks % 8;                      // whole XCD rounds
   p.steps = (units + p.blocks - 1) / p.blocks;
@@ -258,13 +355,11 @@ int run_gemv(const GemvPlan& p, bool act, const half_t* x, const uint32_t* qw, c
              Zeros z, half_t* y, int N, int K, int gshift, hipStream_t st) {
   const dim3 grid(p.blocks);
   if (p.sh.exact) {
-    if (act) launch_gemv_lpr<true, true, BITS>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
-    else launch_gemv_lpr<true, false, BITS>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
-  } else {
-    if (act) launch_gemv_lpr<false, true, BITS>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
-    else launch_gemv_lpr<false, false, BITS>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
+    if (act) return launch_gemv_lpr<true, true, BITS>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
+    return launch_gemv_lpr<true, false, BITS>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
   }
-  return check_launch("gemv launch");
+  if (act) return launch_gemv_lpr<false, true, BITS>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
+  return launch_gemv_lpr<false, false, BITS>(p.sh, p.ept, grid, p.shmem, st, x, qw, s, z, y, N, K, gshift, p.steps);
 }
 
 // --- GEMM (M > 1) ---------------------------------------------------------------
@@ -370,11 +465,11 @@ int launch_skinny(const SkinnyShape& sh, hipStream_t st, const half_t* x, const 
 // tiles in stream-ordered scratch memory, reused by the launches of every 16 rows.
 template <int BITS>
 int run_skinny(const SkinnyShape& sk, bool act, hipStream_t st, const half_t* hx, const uint32_t* hq,
-               const half_t* hs, Zeros hz, half_t* hy, int M, int N, int K, int gshift) {
+               const half_t* hs, Zeros hz, half_t* hy, int M, int N, int K, int gshift, ScratchFn scratch) {
   float* part = nullptr;
   if (sk.ks > 1) {
     const size_t bytes = static_cast<size_t>(sk.ks) * std::min(M, kSkinnyMaxM) * N * sizeof(float);
-    if (int s = hip_status(hipMallocAsync(reinterpret_cast<void**>(&part), bytes, st), "hipMallocAsync")) return s;
+    if (int rc = scratch(st, bytes, reinterpret_cast<void**>(&part))) return rc;
   }
   int rc = W4A16_OK;
   for (int m0 = 0; m0 < M && rc == W4A16_OK; m0 += kSkinnyMaxM) {
@@ -384,12 +479,9 @@ int run_skinny(const SkinnyShape& sk, bool act, hipStream_t st, const half_t* hx
     rc = act ? launch_skinny<true, BITS>(sk, st, xc, hq, hs, hz, yc, part, mc, N, K, gshift)
              : launch_skinny<false, BITS>(sk, st, xc, hq, hs, hz, yc, part, mc, N, K, gshift);
   }
-  if (part) {
-    const int rf = hip_status(hipFreeAsync(part, st), "hipFreeAsync");
-    if (rc == W4A16_OK) rc = rf;
-  }
   return rc;
 }
+
 
 // Large-M GEMM.  BM x 256 tiles (BM = 256 rows; 128 or 64 when the whole batch fits in
 // fewer rows, so that small batches do not pay for padding rows), except (a) when they
@@ -412,7 +504,7 @@ int launch_big_t(hipStream_t st, const half_t* x, const uint32_t* qw, const half
       static_cast<int>(lds));
   if (int rc = hip_status(lds_ok, "hipFuncSetAttribute")) return rc;
   hipLaunchKernelGGL((gemm_big_kernel<NB2, MB, BITS, W32>), dim3(grid), dim3(512), lds, st, x, qw, s, z, y, M, N,
-                     K, gshift, split, n_split, env_int("W4A16_TUNE_GEMM_PRIO", 1));
+                     K, gshift, split, n_split, knobs().gemm_prio);
   return check_launch("gemm launch");
 }
 
@@ -424,7 +516,7 @@ template <int NB2, int MB, int BITS>
 int launch_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, Zeros z, half_t* y,
                int M, int N, int K, int gshift, int split, int n_split, int grid) {
   if constexpr (BITS == 4) {
-    const int mode = env_int("W4A16_TUNE_GEMM_MFMA32", 1);
+    const int mode = knobs().gemm_mfma32;
     if (mode == 2 || (mode == 1 && MB <= 4))
       return launch_big_t<NB2, MB, BITS, true>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
   }
@@ -438,7 +530,7 @@ int run_gemm_big_t(hipStream_t st, const half_t* x, const uint32_t* qw, const ha
   const int tiles_m = (M + BM - 1) / BM;
   const int cus = device_cus();
   const int full = tiles_m * ((N + 255) / 256);
-  if (full > cus && full < 2 * cus && cus % tiles_m == 0 && env_int("W4A16_TUNE_GEMM_SPLIT", 1) != 0) {
+  if (full > cus && full < 2 * cus && cus % tiles_m == 0 && knobs().gemm_split != 0) {
     const int per_panel = cus / tiles_m;
     const int n_split = 256 * per_panel;
     const int rest = N - n_split;
@@ -453,7 +545,7 @@ int run_gemm_big_t(hipStream_t st, const half_t* x, const uint32_t* qw, const ha
   }
   // One round or less: the narrowest tiles that still fit in one round keep the most
   // compute units busy (a BM x 128 tile takes about half as long as a BM x 256 one).
-  if (full < cus && env_int("W4A16_TUNE_GEMM_SPLIT", 1) != 0) {
+  if (full < cus && knobs().gemm_split != 0) {
     for (int nb : {2, 3}) {
       const int tiles = tiles_m * ((N + 64 * nb - 1) / (64 * nb));
       if (tiles <= cus)
@@ -489,12 +581,12 @@ int run_gemm_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half
   // to make up for doing ~1.28x the work per output (twice the dequantisation per MFMA;
   // measured: the 2048-row layer 351 vs 241 us at 0.88x the work per unit).
   int mb_auto = M <= 64 ? 2 : M <= 128 ? 4 : 8;
-  if (mb_auto == 8 && env_int("W4A16_TUNE_GEMM_SPLIT", 1) != 0) {
+  if (mb_auto == 8 && knobs().gemm_split != 0) {
     const int cus = device_cus();
     if (static_cast<double>(big_work_per_cu(4, M, N, cus)) * 1.28 < static_cast<double>(big_work_per_cu(8, M, N, cus)))
       mb_auto = 4;
   }
-  const int mb = env_int("W4A16_TUNE_GEMM_BIG_MB", mb_auto);
+  const int mb = knobs().gemm_big_mb != 0 ? knobs().gemm_big_mb : mb_auto;
   if (mb == 2) return run_gemm_big_t<2, BITS>(st, x, qw, s, z, y, M, N, K, gshift);
   if (mb == 4) return run_gemm_big_t<4, BITS>(st, x, qw, s, z, y, M, N, K, gshift);
   return run_gemm_big_t<8, BITS>(st, x, qw, s, z, y, M, N, K, gshift);
@@ -506,33 +598,30 @@ int run_gemm_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half
 template <int BITS>
 int run_gemm(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, Zeros z,
              half_t* y, int M, int N, int K, int gshift) {
-  if (M >= env_int("W4A16_TUNE_GEMM_BIG_MIN_M", kBigMinM) && K % kBigBK == 0 &&
+  if (M >= (knobs().gemm_big_min_m > 0 ? knobs().gemm_big_min_m : kBigMinM) && K % kBigBK == 0 &&
       (BITS == 4 || N % 16 == 0) && static_cast<long long>(M) * K < (1LL << 31) &&
-      static_cast<long long>(N) * (K / 32 * BITS) < (1LL << 31) && env_int("W4A16_TUNE_GEMM_BIG", 1) != 0)
+      static_cast<long long>(N) * (K / 32 * BITS) < (1LL << 31) && knobs().gemm_big != 0)
     return run_gemm_big<BITS>(st, x, qw, s, z, y, M, N, K, gshift);
   return run_gemm_tiled<BITS>(st, x, qw, s, z, y, M, N, K, gshift);
 }
 
-enum class Path { kAuto, kGemv, kGemm };
-
-Path forced_path() {
-  const char* v = std::getenv("W4A16_FORCE_PATH");
-  if (!v) return Path::kAuto;
-  if (std::strcmp(v, "gemv") == 0) return Path::kGemv;
-  if (std::strcmp(v, "gemm") == 0) return Path::kGemm;
-  return Path::kAuto;
+// Act order above the skinny batches: x gathered into the stored channel order in
+// scratch memory, then the plain GEMM on the gathered rows.
+template <int BITS>
+int run_gemm_act(hipStream_t st, const half_t* hx, const uint32_t* hq, const int32_t* perm, const half_t* hs,
+                 Zeros hz, half_t* hy, int M, int N, int K, int gshift, ScratchFn scratch) {
+  half_t* xs = nullptr;
+  if (int rc = scratch(st, static_cast<size_t>(M) * K * sizeof(half_t), reinterpret_cast<void**>(&xs))) return rc;
+  hipLaunchKernelGGL(gather_x_kernel, dim3(static_cast<unsigned>((K / 8 + 255) / 256), std::min(M, kGatherRowsY)),
+                     dim3(256), 0, st, hx, perm, xs, M, K);
+  if (int rc = check_launch("gather launch")) return rc;
+  return run_gemm<BITS>(st, xs, hq, hs, hz, hy, M, N, K, gshift);
 }
 
-}  // namespace
-}  // namespace w4a16
-
-using namespace w4a16;
-
-extern "C" {
-
-int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
-               const int32_t* g_idx, int group_size, int M, int N, int K, uint16_t* y, void* stream) {
-  clear_error();
+// The 4-bit layer call; `scratch` provides the memory of the K-split skinny launches and
+// of the act-order gather.
+int gemm4(const uint16_t* x, const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
+          const int32_t* g_idx, int group_size, int M, int N, int K, uint16_t* y, void* stream, ScratchFn scratch) {
   if (M <= 0) return fail(W4A16_ERR_INVALID_ARG, "M must be positive (M=%d)", M);
   const void* ptrs[] = {x, qweight, scales, y, qzeros};   // qzeros may be NULL: symmetric
   if (int st = check_device_args(ptrs, qzeros ? 5 : 4, N, K, group_size)) return st;
@@ -548,7 +637,7 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
   const Zeros hz = layer_zeros(qzeros, scales);
   auto* hy = reinterpret_cast<half_t*>(y);
 
-  const Path forced = forced_path();
+  const Path forced = knobs().force_path;
   const GemvPlan gp = M == 1 ? plan_gemv(N, K, gshift, act) : GemvPlan{};
   if (forced == Path::kGemv && !gp.ok)
     return fail(W4A16_ERR_UNSUPPORTED,
@@ -564,24 +653,31 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
   // (The skinny kernel, like the GEMV, addresses the codes with 32-bit byte offsets.)
   const SkinnyShape sk = pick_skinny_shape(std::min(M, kSkinnyMaxM), K, gshift);
   if (sk.waves != 0 && static_cast<long long>(N) * K / 2 < (1LL << 31) &&
-      M <= env_int("W4A16_TUNE_SKINNY_CHUNK_MAX_M", kSkinnyChunkMaxM) &&
-      env_int("W4A16_TUNE_GEMM_SKINNY", 1) != 0) {
-    return run_skinny<4>(sk, act, st, hx, hq, hs, hz, hy, M, N, K, gshift);
+      M <= (knobs().skinny_chunk_max_m > 0 ? knobs().skinny_chunk_max_m : kSkinnyChunkMaxM) &&
+      knobs().gemm_skinny != 0) {
+    return run_skinny<4>(sk, act, st, hx, hq, hs, hz, hy, M, N, K, gshift, scratch);
   }
 
   if (!act) return run_gemm<4>(st, hx, hq, hs, hz, hy, M, N, K, gshift);
+  return run_gemm_act<4>(st, hx, hq, qweight + qweight_words(N, K, false), hs, hz, hy, M, N, K, gshift, scratch);
+}
 
-  // act order: gather x into stored order in stream-ordered scratch memory
-  half_t* xs = nullptr;
-  const size_t bytes = static_cast<size_t>(M) * K * sizeof(half_t);
-  if (int s = hip_status(hipMallocAsync(reinterpret_cast<void**>(&xs), bytes, st), "hipMallocAsync")) return s;
-  const int32_t* perm = qweight + qweight_words(N, K, false);
-  hipLaunchKernelGGL(gather_x_kernel, dim3(static_cast<unsigned>((K / 8 + 255) / 256), std::min(M, kGatherRowsY)),
-                     dim3(256), 0, st, hx, perm, xs, M, K);
-  int rc = check_launch("gather launch");
-  if (rc == W4A16_OK) rc = run_gemm<4>(st, xs, hq, hs, hz, hy, M, N, K, gshift);
-  const int rf = hip_status(hipFreeAsync(xs, st), "hipFreeAsync");
-  return rc != W4A16_OK ? rc : rf;
+}  // namespace
+}  // namespace w4a16
+
+using namespace w4a16;
+
+extern "C" {
+
+int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
+               const int32_t* g_idx, int group_size, int M, int N, int K, uint16_t* y, void* stream) {
+  clear_error();
+  return gemm4(x, qweight, scales, qzeros, g_idx, group_size, M, N, K, y, stream, workspace_scratch);
+}
+
+int w4a16_reload_env(void) {
+  g_knobs = read_knobs();
+  return W4A16_OK;
 }
 
 int w4a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros, const int32_t* g_idx,
@@ -627,7 +723,7 @@ int w8a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
   const Zeros hz = layer_zeros(qzeros, scales);
   auto* hy = reinterpret_cast<half_t*>(y);
 
-  const Path forced = forced_path();
+  const Path forced = knobs().force_path;
   const GemvPlan gp = M == 1 ? plan_gemv(N, K, gshift, act, 8) : GemvPlan{};
   if (forced == Path::kGemv && !gp.ok)
     return fail(W4A16_ERR_UNSUPPORTED,
@@ -639,22 +735,13 @@ int w8a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
   // up to kSkinnyChunkMaxM rows: the skinny kernel (32-bit byte offsets into the codes)
   const SkinnyShape sk = pick_skinny_shape(std::min(M, kSkinnyMaxM), K, gshift, 8);
   if (sk.waves != 0 && static_cast<long long>(N) * K < (1LL << 31) && M <= kSkinnyChunkMaxM &&
-      env_int("W4A16_TUNE_GEMM_SKINNY", 1) != 0)
-    return run_skinny<8>(sk, act, st, hx, hq, hs, hz, hy, M, N, K, gshift);
+      knobs().gemm_skinny != 0)
+    return run_skinny<8>(sk, act, st, hx, hq, hs, hz, hy, M, N, K, gshift, workspace_scratch);
   if (static_cast<long long>(M) * K >= (1LL << 31) || static_cast<long long>(N) * (K / 4) >= (1LL << 31))
     return fail(W4A16_ERR_UNSUPPORTED, "8-bit layer too large for 32-bit element offsets (M=%d N=%d K=%d)", M, N, K);
   if (!act) return run_gemm<8>(st, hx, hq, hs, hz, hy, M, N, K, gshift);
-
-  half_t* xs = nullptr;   // act order: x gathered into stored order (stream-ordered scratch)
-  const size_t bytes = static_cast<size_t>(M) * K * sizeof(half_t);
-  if (int s = hip_status(hipMallocAsync(reinterpret_cast<void**>(&xs), bytes, st), "hipMallocAsync")) return s;
-  const int32_t* perm = qweight + qweight8_words(N, K, false);
-  hipLaunchKernelGGL(gather_x_kernel, dim3(static_cast<unsigned>((K / 8 + 255) / 256), std::min(M, kGatherRowsY)),
-                     dim3(256), 0, st, hx, perm, xs, M, K);
-  int rc = check_launch("gather launch");
-  if (rc == W4A16_OK) rc = run_gemm<8>(st, xs, hq, hs, hz, hy, M, N, K, gshift);
-  const int rf = hip_status(hipFreeAsync(xs, st), "hipFreeAsync");
-  return rc != W4A16_OK ? rc : rf;
+  return run_gemm_act<8>(st, hx, hq, qweight + qweight8_words(N, K, false), hs, hz, hy, M, N, K, gshift,
+                         workspace_scratch);
 }
 
 int w8a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros, const int32_t* g_idx,
