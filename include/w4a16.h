@@ -216,6 +216,22 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
                const int32_t* qzeros, const int32_t* g_idx, int group_size, int M, int N,
                int K, uint16_t* y, void* stream);
 
+/* w4a16_gemm for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): same arguments, same
+ * kernels and bit-identical results, but the scratch memory of the K-split skinny
+ * launches and of the act-order gather comes from one fixed 16 MiB array in device
+ * memory, a static copy per GPU (held until the process ends), instead of the growing
+ * workspace.  The call allocates nothing, ever (its first call on a device resolves the
+ * array's address there).  A call whose scratch would exceed 16 MiB (4 * ks * min(M, 16)
+ * * N bytes for ks K slices, resp. 2 * M * K bytes under act order above 32 rows) is
+ * refused with UNSUPPORTED before anything is launched.  Every call on a GPU shares that
+ * GPU's array: calls that may overlap on one GPU (different streams, or several host
+ * threads) race on it and must be serialised by the caller; calls on one stream are
+ * ordered and safe.  Errors as w4a16_gemm. */
+int w4a16_gemm_noalloc(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
+                       const int32_t* qzeros, const int32_t* g_idx, int group_size, int M, int N,
+                       int K, uint16_t* y, void* stream);
+
 /* Debug/parity view of the weights: w_out[n][k] = binary16((q - Z) * S) in the
  * original input-channel order ("LLM Quantization: A Deep Dive...", The Math of
  * Quantization: x ~ (q - Z) * S), computed with the same device arithmetic that builds

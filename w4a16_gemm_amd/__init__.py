@@ -41,6 +41,8 @@ _SIGNATURES = {
     "w4a16_dequant": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int, _c_int,
                                _c_int, _c_void_p, _c_void_p]),
     "w4a16_reload_env": (_c_int, []),
+    "w4a16_gemm_noalloc": (_c_int, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_int,
+                                    _c_int, _c_int, _c_int, _c_void_p, _c_void_p]),
     "w4a16_quantize_device": (_c_int, [_c_void_p, _c_int, _c_int, _c_int, _c_void_p, _c_int, _c_void_p,
                                        _c_void_p, _c_void_p, _c_void_p]),
     "w4a16_awq_search": (_c_int, [_c_void_p, _c_void_p, _c_int, _c_int, _c_int, _c_int, _c_void_p,
@@ -308,6 +310,14 @@ def w4a16_gemm(x, qweight, scales, qzeros, g_idx, group_size: int, y=None, strea
     qzeros int32 [G][N/8] or None (symmetric); qweight int32 from w4a16_pack; g_idx int32
     [K] or None.  Returns y binary16 [M][N] (allocated unless given)."""
     return _layer_call(lib().w4a16_gemm, x, qweight, scales, qzeros, g_idx, group_size, y, stream, 4)
+
+
+def w4a16_gemm_noalloc(x, qweight, scales, qzeros, g_idx, group_size: int, y, stream=None):
+    """w4a16_gemm with scratch from the library's fixed per-GPU array: allocates no
+    device memory (y must be given)."""
+    if y is None:
+        raise ValueError("w4a16_gemm_noalloc needs the output tensor y")
+    return _layer_call(lib().w4a16_gemm_noalloc, x, qweight, scales, qzeros, g_idx, group_size, y, stream, 4)
 
 
 def w4a16_dequant(qweight, scales, qzeros, g_idx, group_size: int, K: int, out=None, stream=None):

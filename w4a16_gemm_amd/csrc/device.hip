@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -171,6 +172,53 @@ int debug_check_gidx(const int32_t* g_idx, const int32_t* tail_dev, int K, int g
     if (tail[p] != perm[p])
       return fail(W4A16_ERR_BAD_GIDX, "g_idx does not match the order stored in qweight at %d", p);
   return W4A16_OK;
+}
+
+// w4a16_gemm_noalloc: a fixed array in device memory, one copy per GPU (each GPU that
+// runs the entry point holds it until the process ends), shared by every call on that
+// GPU.  Calls that overlap on one GPU race on it.  Every byte a call reads from it was
+// written earlier by the same call (the gather writes all M x K gathered activations,
+// every K slice writes all of its M x N partial sums), so nothing needs clearing.
+constexpr size_t kStaticScratchBytes = size_t{16} << 20;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+// The array's device address on each GPU.  In host code `scratch` names a host-side
+// stand-in, not device memory: only these addresses may be handed to kernels.
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Resolves the current device's copy of the array (once per device; the first call of
+// the entry point on a device does it before anything else).
+int static_scratch_setup(void** out) {
+  int dev = 0;
+  if (int rc = hip_status(hipGetDevice(&dev), "hipGetDevice")) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return fail(W4A16_ERR_UNSUPPORTED, "device %d beyond the supported %d", dev, kMaxDevices);
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (int rc = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress (scratch)")) return rc;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return W4A16_OK;
+}
+
+int static_scratch(hipStream_t, size_t bytes, void** out) {
+  if (bytes > kStaticScratchBytes)
+    return fail(W4A16_ERR_UNSUPPORTED,
+                "this call needs %zu bytes of scratch memory; the no-allocation entry point has %zu "
+                "(use w4a16_gemm, whose workspace grows)",
+                bytes, kStaticScratchBytes);
+  return static_scratch_setup(out);
 }
 
 // --- GEMV (M = 1) ---------------------------------------------------------------
@@ -673,6 +721,14 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
                const int32_t* g_idx, int group_size, int M, int N, int K, uint16_t* y, void* stream) {
   clear_error();
   return gemm4(x, qweight, scales, qzeros, g_idx, group_size, M, N, K, y, stream, workspace_scratch);
+}
+
+int w4a16_gemm_noalloc(const uint16_t* x, const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
+                       const int32_t* g_idx, int group_size, int M, int N, int K, uint16_t* y, void* stream) {
+  clear_error();
+  void* unused = nullptr;
+  if (int rc = static_scratch_setup(&unused)) return rc;
+  return gemm4(x, qweight, scales, qzeros, g_idx, group_size, M, N, K, y, stream, static_scratch);
 }
 
 int w4a16_reload_env(void) {
