@@ -13,8 +13,13 @@ its own roofline.  Prints one JSON line.
 Timing: all inputs are resident in device memory before the timed region; the
 weights rotate over a pool of distinct copies larger than twice the 256 MB
 Infinity Cache, so every step streams its weights from HBM.  HIP events recorded on
-the launch stream bracket every launch (their average is the per-launch kernel
-time) and the whole timed region (whole-job time per step).
+the launch stream bracket the whole timed region of back-to-back launches (the rate
+and the per-launch mean) and, in a separate pass, every launch (event pairs, which
+add the events' own overhead).  The headline layer is timed over exactly --steps
+launches after --warmup; every other layer over a fixed 200 launches (or --steps if
+larger) after 20 warm-up launches.  Before each timed region the layer runs back to
+back while amd-smi reads the gfx and memory clocks (SCLK averaged over the XCDs, MCLK);
+the line reports them with the device's name and compute-unit count.
 
 Throughput figures use algorithmic bytes (packed codes, binary16 scales, packed
 zero points, the act-order permutation, x and y) and algorithmic flops 2*M*N*K.
@@ -44,6 +49,8 @@ POOL_BYTES = 640 << 20         # > 2 x 256 MB Infinity Cache
 MAX_COPIES = 64
 METRIC = "W4A16 GEMV HBM GB/s (% of peak) at M=1; prefill GEMM TFLOP/s (% MFMA)"
 HEADLINE = ("c3", 1)
+SECONDARY_STEPS = 200          # launches per timed region of every other layer (at least)
+SECONDARY_WARMUP = 20
 SECONDARY = [("c1", 1), ("c2up", 1), ("c2down", 1), ("c3", 2), ("c3", 4), ("c3", 8), ("c3", 16),
              ("c3s", 1), ("c3w8", 1), ("c3w8", 16), ("c4", 2048), ("c4w8", 2048), ("c5", 1), ("c5", 512)]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
@@ -73,6 +80,71 @@ def kernel_hash() -> str:
 def log(msg: str) -> None:
     sys.stderr.write(f"[bench] {msg}\n")
     sys.stderr.flush()
+
+
+def _amd_smi_clocks():
+    """Current clocks from `amd-smi metric -c --json`: (mean gfx clock over the XCDs,
+    memory clock) in MHz, or None where the tool or the field is missing."""
+    import subprocess
+    try:
+        out = subprocess.run(["amd-smi", "metric", "-c", "--json", "-g", "0"], capture_output=True, text=True,
+                             timeout=20)
+        data = json.loads(out.stdout)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    gpu = data[0] if isinstance(data, list) else (data.get("gpu_data") or [data])[0]
+    clk = gpu.get("clock", {}) if isinstance(gpu, dict) else {}
+
+    def val(entry):
+        try:
+            v = entry["clk"]["value"]
+            return float(v) if v not in (None, "N/A") else None
+        except (KeyError, TypeError, ValueError):
+            return None
+    gfx = [val(v) for k, v in clk.items() if k.startswith("gfx")]
+    gfx = [g for g in gfx if g is not None]
+    mem = [val(v) for k, v in clk.items() if k.startswith("mem")]
+    mem = [m for m in mem if m is not None]
+    return (round(sum(gfx) / len(gfx), 1) if gfx else None, mem[0] if mem else None)
+
+
+def clocks_under_load(launch, sync, max_s: float = 20.0):
+    """SCLK and MCLK while the timed work runs: the layer is launched back to back in
+    batches of about 4 ms of device work (one synchronisation per batch, so the device
+    is rarely idle), and after 100 ms of that an amd-smi query runs in a thread while
+    the launches go on (not timed)."""
+    import threading
+    box = {}
+
+    def query():
+        box["clk"] = _amd_smi_clocks()
+    t0 = time.perf_counter()
+    for _ in range(8):
+        launch(0)
+    sync()
+    per = max(1e-6, (time.perf_counter() - t0) / 8)     # upper bound of one launch's time
+    batch = int(min(4096, max(64, 4e-3 / per)))
+    i = 0
+    th = threading.Thread(target=query)
+    t0 = time.perf_counter()
+    while (th.ident is None or th.is_alive()) and time.perf_counter() - t0 < max_s:
+        for _ in range(batch):
+            launch(i)
+            i += 1
+        sync()
+        if th.ident is None and time.perf_counter() - t0 > 0.1:
+            th.start()
+    if th.ident is not None:
+        th.join()
+    clk = box.get("clk")
+    return {"sclk_mhz": clk[0] if clk else None, "mclk_mhz": clk[1] if clk else None, "launches": i}
+
+
+def device_info():
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", None), "cus": p.multi_processor_count,
+            "hbm_gib": round(p.total_memory / 2**30, 1)}
 
 
 # --- GPU leg (the library only) ---------------------------------------------------
@@ -106,7 +178,7 @@ def prepare_layer(cfg: wl.LayerConfig, M_max: int):
     }
 
 
-def time_layer(cfg: wl.LayerConfig, M: int, layer, steps: int, warmup: int):
+def time_layer(cfg: wl.LayerConfig, M: int, layer, steps: int, warmup: int, sample_clocks: bool = True):
     import torch
     import w4a16_gemm_amd as w4
     lib = w4.lib()
@@ -134,6 +206,7 @@ def time_layer(cfg: wl.LayerConfig, M: int, layer, steps: int, warmup: int):
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
+    clocks = clocks_under_load(launch, torch.cuda.synchronize) if sample_clocks else None
     # per-launch events (kernel time) ...
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i in range(steps):
@@ -156,17 +229,19 @@ def time_layer(cfg: wl.LayerConfig, M: int, layer, steps: int, warmup: int):
     del pool
     return {
         "copies": copies,
-        "kernel_us_mean": 1e3 * statistics.fmean(per_launch_ms),
-        "kernel_us_median": 1e3 * statistics.median(per_launch_ms),
+        "event_pair_us_mean": 1e3 * statistics.fmean(per_launch_ms),
+        "event_pair_us_median": 1e3 * statistics.median(per_launch_ms),
         "region_us_per_step": 1e3 * region_ms / steps,
         "wall_us_per_step": 1e6 * wall_s / steps,
+        "launches_timed": steps,
+        "clocks": clocks,
     }
 
 
 def summarize(cfg, M, t):
     """Rates use the region events (back-to-back launches, no event between them);
     the per-launch event pairs add the events' own overhead and are reported aside."""
-    us = t["kernel_us_mean"]
+    us = t["event_pair_us_mean"]
     ur = t["region_us_per_step"]
     b = algo_bytes(cfg, M)
     f = algo_flops(cfg, M)
@@ -174,42 +249,85 @@ def summarize(cfg, M, t):
         "workload": f"{cfg.name}: {cfg.note}", "M": M, "N": cfg.N, "K": cfg.K, "group": cfg.group_size,
         "act_order": cfg.act_order, "awq": cfg.awq, "sym": cfg.sym, "bits": cfg.bits,
         "us_per_layer": round(ur, 3),
-        "event_pair_us_mean": round(us, 3), "event_pair_us_median": round(t["kernel_us_median"], 3),
-        "region_us_per_step": round(ur, 3),
+        "event_pair_us_mean": round(us, 3), "event_pair_us_median": round(t["event_pair_us_median"], 3),
+        "region_us_per_step": round(ur, 3), "launches_timed": t["launches_timed"],
         "algo_bytes": b, "algo_flops": f,
         "GBps": round(b / ur / 1e3, 1), "hbm_frac": round(b / ur / 1e3 / HBM_PEAK_GBS, 4),
         "TFLOPs": round(f / ur / 1e6, 2), "mfma_frac": round(f / ur / 1e6 / MFMA_F16_PEAK_TFLOPS, 4),
         "weight_copies": t["copies"],
     }
+    if t.get("clocks"):
+        out["sclk_mhz_under_load"] = t["clocks"]["sclk_mhz"]
+        out["mclk_mhz_under_load"] = t["clocks"]["mclk_mhz"]
     return out
 
 
 # --- CPU baseline (the oracle, as it stands) ----------------------------------------
 
-def cpu_baseline(cfg: wl.LayerConfig, rows: int, repeats: int = 3):
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_layer_legs(cfg: wl.LayerConfig, rows, repeats: int):
+    """Times the oracle on one layer (or the first `rows` output rows of it): the
+    offline quantiser once, the forward (binary64 dequant + numpy matmul) as the median
+    of `repeats` runs on every allowed BLAS thread and once on one thread."""
     import oracle
-    sel = np.arange(rows)
+    from threadpoolctl import threadpool_limits
+    sel = np.arange(cfg.N if rows is None else rows)
     w = wl.weights(cfg, sel)
-    codes, S, Z = oracle.rtn_quantize(w, cfg.group_size)
+    s = oracle.awq_scales(wl.calibration(cfg)) if cfg.awq else None
+    t0 = time.perf_counter()
+    codes, S, Z = oracle.rtn_quantize(w, cfg.group_size, None, s)
+    t_quant = time.perf_counter() - t0
     x = wl.activations(cfg, 1)
+    if s is not None:
+        x = oracle.awq_fold_activations(x, s)
     times = []
     for _ in range(repeats):
         t0 = time.perf_counter()
         oracle.linear(x, codes, S, Z, cfg.group_size)
         times.append(time.perf_counter() - t0)
-    t = statistics.median(times)
-    sample_bytes = rows * cfg.K // 2 + 2 * cfg.G * rows + cfg.G * rows // 2 + 2 * cfg.K + 2 * rows
+    with threadpool_limits(limits=1, user_api="blas"):
+        t0 = time.perf_counter()
+        oracle.linear(x, codes, S, Z, cfg.group_size)
+        t_one = time.perf_counter() - t0
+    n = len(sel)
+    nbytes = n * cfg.K // 2 + 2 * cfg.G * n + cfg.G * n // 2 + 2 * cfg.K + 2 * n
+    return {"rows": n, "of_rows": cfg.N, "quantize_rtn_s": round(t_quant, 3),
+            "forward_s_median": round(statistics.median(times), 3), "forward_s_1thread": round(t_one, 3),
+            "forward_GBps": round(nbytes / statistics.median(times) / 1e9, 4), "algo_bytes_sample": nbytes}
+
+
+def cpu_baseline(head: wl.LayerConfig, rows: int, repeats: int = 3):
+    """The oracle as it stands, on the host cores of this machine: the headline layer on
+    a bounded sample of its output rows, and the small decode layers whole."""
     try:
         from threadpoolctl import threadpool_info
         blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     except Exception:
         blas = 1
+    cores = len(os.sched_getaffinity(0))
+    legs = {head.name: _oracle_layer_legs(head, rows, repeats)}
+    for name in ("c1", "c2up", "c2down"):
+        legs[name] = _oracle_layer_legs(wl.CONFIGS[name], None, repeats)
+    h = legs[head.name]
     return {
-        "value": round(sample_bytes / t / 1e9, 4), "unit": "GB/s", "cores": blas, "kind": "oracle",
-        "sample": (f"float64 dequant + matmul (numpy) of the first {rows} of {cfg.N} output rows of the "
-                   f"{cfg.name} layer at M=1, median of {repeats}: {t:.2f} s; algorithmic bytes of the "
-                   f"sample / time. Elementwise dequant is single-threaded; BLAS used {blas} threads"),
-        "seconds_per_layer_extrapolated": round(t * cfg.N / rows, 2),
+        "value": h["forward_GBps"], "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "sample": (f"oracle forward (binary64 dequant + numpy matmul) of the first {h['rows']} of {head.N} output "
+                   f"rows of the {head.name} layer at M=1, median of {repeats}: {h['forward_s_median']:.2f} s; "
+                   f"algorithmic bytes of the sample / time. The elementwise dequant runs on one thread, the "
+                   f"matmul on {blas} BLAS threads"),
+        "blas_threads": blas, "cpu_model": _cpu_model(),
+        "seconds_per_layer_extrapolated": round(h["forward_s_median"] * head.N / h["rows"], 2),
+        "legs": legs,
     }
 
 
@@ -373,7 +491,7 @@ def awq_search_bench(cfg: wl.LayerConfig, n_alpha: int = 11):
     layer = prepare_layer(wl.custom_config(cfg.name + "_cal", cfg.cfg_id, K=cfg.K, N=cfg.N,
                                            group_size=cfg.group_size, M_list=(T,)), T)
     t = time_layer(wl.custom_config(cfg.name + "_cal", cfg.cfg_id, K=cfg.K, N=cfg.N, group_size=cfg.group_size,
-                                    M_list=(T,)), T, layer, 20, 5)
+                                    M_list=(T,)), T, layer, 20, 5, sample_clocks=False)
     return {
         "workload": f"AWQ alpha search on the {cfg.name} layer (N={cfg.N}, K={cfg.K}, group {cfg.group_size}) "
                     f"with its {T} calibration tokens, {n_alpha} alphas on [0, 1]",
@@ -494,7 +612,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--configs", default="all", help="'all', 'headline' or a comma list like c3:1,c4:2048")
-    ap.add_argument("--cpu-rows", type=int, default=8192, help="oracle sample size (rows)")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="oracle sample size (rows of the headline layer)")
+    ap.add_argument("--no-clocks", action="store_true", help="skip sampling SCLK/MCLK under load (amd-smi)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-ref", action="store_true",
                     help="skip timing the dense binary16 library GEMM of the same shapes")
@@ -542,9 +661,12 @@ def main() -> int:
             torch.cuda.empty_cache()
             log(f"preparing {name} (N={cfg.N} K={cfg.K} g={cfg.group_size})")
             layers[name] = prepare_layer(cfg, max(cfg.M_list))
-        steps = args.steps if (name, M) == HEADLINE else max(20, args.steps // 4)
-        log(f"timing {name} M={M}: {args.warmup} warmup + {steps} steps")
-        t = time_layer(cfg, M, layers[name], steps, args.warmup)
+        if (name, M) == HEADLINE:
+            steps, warm = args.steps, args.warmup
+        else:   # fixed counts: the other layers do not shrink with --steps
+            steps, warm = max(SECONDARY_STEPS, args.steps), max(SECONDARY_WARMUP, args.warmup)
+        log(f"timing {name} M={M}: {warm} warmup + {steps} launches")
+        t = time_layer(cfg, M, layers[name], steps, warm, sample_clocks=not args.no_clocks)
         results[f"{name}:M{M}"] = summarize(cfg, M, t)
         results[f"{name}:M{M}"]["_t"] = t
         log(f"  {results[f'{name}:M{M}']['us_per_layer']} us")
@@ -581,6 +703,7 @@ def main() -> int:
             "weight_copies_rotated": head["weight_copies"],
             "accumulate": "f32",
         },
+        "device": device_info(),
         "roofline": {
             "bound": "hbm",
             "achieved": round(head["algo_bytes"] / head["region_us_per_step"] / 1e3, 1),
@@ -589,9 +712,13 @@ def main() -> int:
             "frac": round(head["algo_bytes"] / head["region_us_per_step"] / 1e3 / HBM_PEAK_GBS, 4),
             "traffic": traffic_for(khash, hname),
             "kernel": "gemv_m1_kernel",
-            "kernel_us_mean": head["region_us_per_step"],
+            "launch_us_region_mean": head["region_us_per_step"],
+            "launch_us_note": ("HIP events on the launch stream around the timed region of back-to-back "
+                               "launches (one kernel per launch), divided by the launches"),
             "event_pair_us_per_launch": head["event_pair_us_mean"],
             "algo_bytes_per_launch": head["algo_bytes"],
+            "sclk_mhz_under_load": head.get("sclk_mhz_under_load"),
+            "mclk_mhz_under_load": head.get("mclk_mhz_under_load"),
         },
         "kernel_hash": khash,
         "configs": results,
@@ -601,7 +728,10 @@ def main() -> int:
         line["prefill"] = {
             "bound": "mfma", "achieved": pre["TFLOPs"], "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": pre["mfma_frac"], "us_per_layer": pre["us_per_layer"], "kernel": "gemm_big_kernel",
+            "launches_timed": pre["launches_timed"],
             "traffic": traffic_for(khash, "c4:M2048"),
+            "sclk_mhz_under_load": pre.get("sclk_mhz_under_load"),
+            "mclk_mhz_under_load": pre.get("mclk_mhz_under_load"),
         }
     if not args.no_peaks:
         log("measuring the achievable streaming-read and MFMA rates")
