@@ -179,6 +179,11 @@ def prepare_layer(cfg: wl.LayerConfig, M_max: int):
 
 
 def time_layer(cfg: wl.LayerConfig, M: int, layer, steps: int, warmup: int, sample_clocks: bool = True):
+    if layer["x"].shape[0] < M or layer["x"].shape[1] != cfg.K:
+        # the library takes raw pointers: a batch larger than the prepared activations
+        # would read past their end
+        raise ValueError(f"{cfg.name}: activations prepared for {tuple(layer['x'].shape)}, asked for M={M}, "
+                         f"K={cfg.K}")
     import torch
     import w4a16_gemm_amd as w4
     lib = w4.lib()
@@ -639,6 +644,8 @@ def main() -> int:
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    if not args.no_clocks:
+        _amd_smi_clocks()   # the tool's first reading can be stale: discard it
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib)
 
@@ -654,13 +661,16 @@ def main() -> int:
 
     results = {}
     layers = {}
+    rows_needed = {}
+    for name, M in todo:
+        rows_needed[name] = max(rows_needed.get(name, 1), M, max(wl.config(name).M_list))
     for name, M in todo:
         cfg = wl.config(name)
         if name not in layers:
             layers.clear()
             torch.cuda.empty_cache()
-            log(f"preparing {name} (N={cfg.N} K={cfg.K} g={cfg.group_size})")
-            layers[name] = prepare_layer(cfg, max(cfg.M_list))
+            log(f"preparing {name} (N={cfg.N} K={cfg.K} g={cfg.group_size}, {rows_needed[name]} activation rows)")
+            layers[name] = prepare_layer(cfg, rows_needed[name])
         if (name, M) == HEADLINE:
             steps, warm = args.steps, args.warmup
         else:   # fixed counts: the other layers do not shrink with --steps

@@ -341,6 +341,11 @@ __device__ __forceinline__ void lds_read_tile<4>(uint32_t a_addr, uint32_t b_add
       : "memory");
 }
 
+// An LDS pointer in the LDS address space (the destination operand of the buffer loads
+// that write straight into LDS).
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+__device__ __forceinline__ lds_ptr_t as_lds(void* p) { return (lds_ptr_t)(p); }
+
 // Workgroup barrier without the memory fence of __syncthreads(), whose release would
 // wait for every outstanding load, prefetches included.  Callers wait for exactly the
 // loads and LDS reads that must be complete (s_waitcnt) before they call it.
@@ -389,35 +394,49 @@ struct BigLoader {
   static_assert(BL * BK / 32 == 512, "one 4-bit code chunk per thread per stage (of the widest tile)");
   static_assert(STAGE % 16 == 0, "stage alignment");
 
-  const half_t* x;
-  const uint32_t* qw;
+  // The activation and code streams are raw buffer loads into LDS: a buffer resource
+  // over the tile's rows (x from row m0, the codes from column n0), a 32-bit byte offset
+  // of the lane that does not change over the K loop (at most 256 rows or columns of one
+  // row pitch) and the K tile's offset as the scalar offset, so the loop does no vector
+  // address arithmetic.
+  __amdgpu_buffer_rsrc_t xr;   // x from row m0
+  __amdgpu_buffer_rsrc_t qr;   // codes from column n0
   const half_t* scales;
   Zeros qzeros;
   unsigned char* smem;
   int N, KT, gshift, wave, sz_half, s_col, z_word;
-  int a_off[APT];
-  int b_off[CL];
+  uint32_t a_off[APT];
+  uint32_t b_off[CL];
 
   __device__ __forceinline__ BigLoader(const half_t* x_, const uint32_t* qw_, const half_t* scales_, Zeros qz,
                                        unsigned char* smem_, int M, int N_, int K, int gshift_, int m0, int n0,
                                        int n_end, int tid, int wave_)
-      : x(x_), qw(qw_), scales(scales_), qzeros(qz), smem(smem_), N(N_), KT(K / BK), gshift(gshift_), wave(wave_) {
+      : scales(scales_), qzeros(qz), smem(smem_), N(N_), KT(K / BK), gshift(gshift_), wave(wave_) {
     const int lane = tid & 63;
     const int W = K >> (BITS == 4 ? 3 : 2);   // words per row
+    // sizes: (M - m0) rows of x (M K < 2^31 elements), the codes of columns n0.. n_end
+    // (clamped to the 32-bit range; every offset used lies inside it)
+    xr = __builtin_amdgcn_make_buffer_rsrc(const_cast<half_t*>(x_ + static_cast<size_t>(m0) * K), 0,
+                                           static_cast<int>(static_cast<uint32_t>(M - m0) * K * 2u), kBufferWord3);
+    const unsigned long long qbytes = static_cast<unsigned long long>(n_end - n0) * W * 4ull;
+    qr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(qw_ + static_cast<size_t>(n0) * W), 0,
+                                           static_cast<int>(qbytes > 0xFFFFFFFFull ? 0xFFFFFFFFu
+                                                                                   : static_cast<uint32_t>(qbytes)),
+                                           kBufferWord3);
     // Activations: lane l of load i writes chunk c = (APT wave + i) * 64 + l = 8 row + slot,
     // which receives the row's chunk slot ^ (row % 8).  Rows past M re-read row M - 1.
 #pragma unroll
     for (int i = 0; i < APT; ++i) {
       const int c = (wave * APT + i) * 64 + lane;
       const int row = c >> 3, slot = c & 7;
-      a_off[i] = min(m0 + row, M - 1) * K + 8 * (slot ^ (row & 7));
+      a_off[i] = static_cast<uint32_t>(min(row, M - 1 - m0) * K + 8 * (slot ^ (row & 7))) * 2u;
     }
     // Codes: chunk c = half * BL + column holds channels [32 half, +32) of the column;
     // columns past the tile (BN < BL) or past N re-read a column of the tile.
 #pragma unroll
     for (int i = 0; i < CL; ++i) {
       const int c = tid + 512 * i;
-      b_off[i] = min(n0 + min(c % BL, BN - 1), n_end - 1) * W + 4 * (c / BL);
+      b_off[i] = static_cast<uint32_t>(min(min(c % BL, BN - 1), n_end - 1 - n0) * W + 4 * (c / BL)) * 4u;
     }
     // Scales (wavefront 0, 16 B per lane) and zero points (wavefront 1, 4 B per lane) of
     // half h = lane / 32: 8 columns, resp. one packed word of 8 columns, per lane.
@@ -448,16 +467,16 @@ struct BigLoader {
             reinterpret_cast<const void*>(qzeros.at(static_cast<size_t>(gi) * (N >> 2) + z_word)),
             reinterpret_cast<void*>(stage + kBigLdsA + LB + kBigLdsS), 16, 0, 0);
     }
-    const half_t* xt = x + tc * BK;
 #pragma unroll
     for (int i = 0; i < APT; ++i)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(xt + a_off[i]),
-                                       reinterpret_cast<void*>(stage + (wave * APT + i) * 64 * 16), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xr, as_lds(stage + (wave * APT + i) * 64 * 16), 16,
+          static_cast<int>(a_off[i]), tc * (BK * 2), 0, 0);
 #pragma unroll
     for (int i = 0; i < CL; ++i)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(qw + b_off[i] + tc * (BK * BITS / 32)),
-                                       reinterpret_cast<void*>(stage + kBigLdsA + (512 * i + wave * 64) * 16), 16, 0,
-                                       0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          qr, as_lds(stage + kBigLdsA + (512 * i + wave * 64) * 16),
+          16, static_cast<int>(b_off[i]), tc * (BK * BITS / 8), 0, 0);
   }
 };
 
@@ -518,6 +537,11 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(APT + CL) : "memory");   // tile 0
   block_barrier();
 
+  // Scale and zero-point constants of this lane's columns, rebuilt only when the K tile
+  // starts a new group (every tile at group 32 or 64, every other one at 128, once for
+  // one group per row).
+  DequantConsts dc[NB];
+  const int gmask = (1 << min(gshift, 30)) - 1;
   for (int t = 0; t < KT; ++t) {
     load_tile(t + NS - 1);
     const uint32_t so = (t % NS) * STAGE;
@@ -543,11 +567,12 @@ __device__ __forceinline__ void big_tile(const half_t* __restrict__ x, const uin
       for (int mb = 0; mb < MB; ++mb)
         af[mb] = *reinterpret_cast<const half8_t*>(st + (a_lane - base) + 16 * ((2 * lq) ^ (lr & 7)) + 2048 * mb);
     }
-    DequantConsts dc[NB];
+    if (((t * kBigBK) & gmask) == 0) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      dc[nb] = make_consts(BITS == 4 ? (qzeros.word(zw[nb]) >> z_shift) & 0xFu : (qzeros.sym ? 128u : zw[nb]),
-                           __builtin_bit_cast(half_t, static_cast<uint16_t>(sc[nb])));
+      for (int nb = 0; nb < NB; ++nb)
+        dc[nb] = make_consts(BITS == 4 ? (qzeros.word(zw[nb]) >> z_shift) & 0xFu : (qzeros.sym ? 128u : zw[nb]),
+                             __builtin_bit_cast(half_t, static_cast<uint16_t>(sc[nb])));
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (s == 1) {
@@ -662,17 +687,22 @@ __device__ __forceinline__ void big_tile32(const half_t* __restrict__ x, const u
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(APT + CL) : "memory");   // tile 0
   block_barrier();
 
+  // constants rebuilt only when the K tile starts a new group (as in big_tile)
+  DequantConsts dc[CB];
+  const int gmask = (1 << min(gshift, 30)) - 1;
   for (int t = 0; t < KT; ++t) {
     ld.load(t + NS - 1);
     const unsigned char* st = smem + (t % NS) * STAGE;
     uint4 cw[CB];
-    DequantConsts dc[CB];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      cw[cb] = *reinterpret_cast<const uint4*>(st + b_lane + 512 * cb);
-      const uint32_t sc = *reinterpret_cast<const uint16_t*>(st + s_lane + 64 * cb);
-      const uint32_t zw = *reinterpret_cast<const uint32_t*>(st + z_lane + 16 * cb);
-      dc[cb] = make_consts((qzeros.word(zw) >> z_shift) & 0xFu, __builtin_bit_cast(half_t, static_cast<uint16_t>(sc)));
+    for (int cb = 0; cb < CB; ++cb) cw[cb] = *reinterpret_cast<const uint4*>(st + b_lane + 512 * cb);
+    if (((t * kBigBK) & gmask) == 0) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const uint32_t sc = *reinterpret_cast<const uint16_t*>(st + s_lane + 64 * cb);
+        const uint32_t zw = *reinterpret_cast<const uint32_t*>(st + z_lane + 16 * cb);
+        dc[cb] = make_consts((qzeros.word(zw) >> z_shift) & 0xFu, __builtin_bit_cast(half_t, static_cast<uint16_t>(sc)));
+      }
     }
     // A fragments one step ahead: the reads of step s + 1 are in flight during the
     // MFMAs of step s.

@@ -116,13 +116,17 @@ struct DequantConsts {
   half2_t scale;       // S
 };
 
+// Built with integer operations: binary16 1024 is 0x6400 with an ulp of 1, so -(1024 +
+// z) is 0xE400 | z for z < 1024; binary16 64 is 0x5400 with an ulp of 1/16, so -(64 +
+// z) is 0xD400 | (z << 4) for z < 64 (4-bit zero points only use it).
 __device__ __forceinline__ DequantConsts make_consts(uint32_t z, half_t s) {
   DequantConsts c;
-  const half_t a = static_cast<half_t>(-1024.0f - static_cast<float>(z));
-  const half_t b = static_cast<half_t>(-64.0f - static_cast<float>(z));
-  c.neg_1024_z = half2_t{a, a};
-  c.neg_64_z = half2_t{b, b};
-  c.scale = half2_t{s, s};
+  const uint32_t a = 0xE400u | z;
+  const uint32_t b = 0xD400u | (z << 4);
+  const uint32_t sb = __builtin_bit_cast(uint16_t, s);
+  c.neg_1024_z = as_h2(a | (a << 16));
+  c.neg_64_z = as_h2(b | (b << 16));
+  c.scale = as_h2(sb | (sb << 16));
   return c;
 }
 
