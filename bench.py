@@ -611,6 +611,152 @@ def traffic_for(hash_now: str, key: str):
     return None if entry is None else entry.get("hbm_bytes_per_launch")
 
 
+# --- counter post-processing (rocprofv3 --pmc output; no GPU needed) ---------------
+
+HEADLINE_KERNELS = {"c3:M1": "gemv_m1_kernelILi64ELi4ELi8ELi2ELb1ELb0ELi1ELi1ELi4E",
+                    "c4:M2048": "gemm_big_kernelILi3ELi8ELi4ELb0E"}
+
+
+def _counter_rows(d: str):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            key = (r["Kernel_Name"], int(r["Dispatch_Id"]))
+            per.setdefault(key, {})
+            per[key][r["Counter_Name"]] = per[key].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return per
+
+
+def _means(per, match: str, skip: int = 5):
+    """Mean of every counter over the dispatches of the kernel whose name contains
+    `match` (the first `skip` warm-up dispatches left out)."""
+    keys = sorted(k for k in per if match in k[0])
+    if len(keys) > skip + 2:
+        keys = keys[skip:]
+    if not keys:
+        return None, 0
+    names = set().union(*(per[k].keys() for k in keys))
+    return {c: statistics.fmean(per[k].get(c, 0.0) for k in keys) for c in names}, len(keys)
+
+
+def summarize_pmc(dirs) -> None:
+    """Per headline kernel: counters per dispatch and derived ratios (SIMD counters are
+    summed over the device: 256 CUs x 4 SIMDs; GRBM_GUI_ACTIVE over the 8 XCDs)."""
+    merged = {}
+    for d in dirs:
+        for k, v in _counter_rows(d).items():
+            merged.setdefault(k, {}).update(v)
+    for label, match in HEADLINE_KERNELS.items():
+        m, n = _means(merged, match)
+        if m is None:
+            continue
+        print(f"## {label}: {match}  ({n} dispatches)")
+        for c in sorted(m):
+            print(f"  {c:30s} {m[c]:.6g}")
+        g = m.get("GRBM_GUI_ACTIVE")
+        simd_cycles = g / 8 * 1024 if g else None
+        if simd_cycles and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            print(f"  => MFMA busy / SIMD cycles          {m['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:.3f}")
+        if m.get("SQ_VALU_MFMA_BUSY_CYCLES") and "SQ_VALU_MFMA_COEXEC_CYCLES" in m:
+            print(f"  => VALU co-issue / MFMA busy        {m['SQ_VALU_MFMA_COEXEC_CYCLES'] / m['SQ_VALU_MFMA_BUSY_CYCLES']:.3f}")
+        if m.get("SQ_INSTS_MFMA") and "SQ_INSTS_VALU" in m:
+            print(f"  => non-MFMA VALU per MFMA           {(m['SQ_INSTS_VALU'] - m['SQ_INSTS_MFMA']) / m['SQ_INSTS_MFMA']:.3f}")
+        if simd_cycles and "SQ_ACTIVE_INST_VALU" in m:
+            print(f"  => VALU issue (x4 cycles) / SIMD cycles {4 * m['SQ_ACTIVE_INST_VALU'] / simd_cycles:.3f}")
+        if m.get("SQ_WAVE_CYCLES"):
+            for c in ("SQ_WAIT_INST_ANY", "SQ_WAIT_ANY", "SQ_ACTIVE_INST_ANY", "SQ_WAIT_INST_LDS"):
+                if c in m:
+                    print(f"  => {c} / SQ_WAVE_CYCLES   {m[c] / m['SQ_WAVE_CYCLES']:.3f}")
+        if m.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in m:
+            print(f"  => LDS bank-conflict / LDS active   {m['SQ_LDS_BANK_CONFLICT'] / m['SQ_LDS_IDX_ACTIVE']:.3f}")
+
+
+def summarize_trace(trace_dir: str, steps: int) -> None:
+    """Per headline kernel, from a `rocprofv3 --kernel-trace` of bench.py: the launches of
+    the headline layer are the first run of at least 2 `steps` consecutive dispatches of
+    that kernel with one grid; its last `steps` are the back-to-back timed region, the
+    `steps` before them the launches with an event pair around each."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    rows = []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size_X"]),
+                         int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    rows.sort()
+    for label, match in HEADLINE_KERNELS.items():
+        runs, cur = [], []
+        for d in rows:
+            if cur and (d[1] != cur[-1][1] or d[2] != cur[-1][2]):
+                runs.append(cur)
+                cur = []
+            cur.append(d)
+        runs.append(cur)
+        run = next((r for r in runs if match in r[0][1] and len(r) >= 2 * steps), None)
+        if run is None:
+            print(f"## {label}: no run of {2 * steps} launches of {match}")
+            continue
+        b2b, pairs = run[-steps:], run[-2 * steps:-steps]
+        print(f"## {label}: {run[0][1]} (grid {run[0][2]}, {len(run)} launches in the run)")
+        print("| pass | launches | mean us | median us |\n|---|---|---|---|")
+        for name, part in (("event pairs", pairs), ("back-to-back (timed region)", b2b)):
+            us = [(e - s) / 1e3 for _, _, _, s, e in part]
+            print(f"| {name} | {len(us)} | {statistics.fmean(us):.2f} | {statistics.median(us):.2f} |")
+        print(f"\nfirst start to last end of the back-to-back launches / {steps}: "
+              f"{(b2b[-1][4] - b2b[0][3]) / 1e3 / steps:.2f} us")
+    probes = {}
+    for _, name, grid, s, e in rows:
+        if "stream_read_kernel" in name or "mfma_loop_kernel" in name:
+            label = "stream_read_kernel" if "stream_read_kernel" in name else "mfma_loop_kernel"
+            probes.setdefault((label, grid), []).append((e - s) / 1e3)
+    if probes:
+        print("## achievable-peak probes\n| kernel | grid (threads) | launches | mean us | min us |\n|---|---|---|---|---|")
+        for (name, grid), us in sorted(probes.items()):
+            print(f"| {name} | {grid} | {len(us)} | {statistics.fmean(us):.2f} | {min(us):.2f} |")
+
+
+def write_traffic(fetch_dir: str, write_dir: str) -> None:
+    """profiles/traffic_counters.json from a FETCH_SIZE and a WRITE_SIZE run of
+    `bench.py --configs c3:1,c4:2048 --copy-probe-mib 512`: the counters of the plain
+    streaming copy (binary16 negation, 512 MiB in and out) give the scale to bytes."""
+    fetch, write = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    mib = 512
+    cf, _ = _means(fetch, "neg", skip=0)
+    cw, _ = _means(write, "neg", skip=0)
+    if cf is None or cw is None:
+        raise SystemExit("the calibration copy (a kernel named ...neg...) is missing from the runs")
+    fetch_scale = (mib << 20) / (cf["FETCH_SIZE"] * 1024)
+    write_scale = (mib << 20) / (cw["WRITE_SIZE"] * 1024)
+    entries = {}
+    for label, match in HEADLINE_KERNELS.items():
+        mf, n = _means(fetch, match)
+        mw, _ = _means(write, match)
+        if mf is None or mw is None:
+            continue
+        name, M = label.split(":M")
+        algo = algo_bytes(wl.config(name), int(M))
+        hbm = mf["FETCH_SIZE"] * 1024 * fetch_scale + mw["WRITE_SIZE"] * 1024 * write_scale
+        entries[label] = {"kernel_match": match, "dispatches": n, "fetch_kib": round(mf["FETCH_SIZE"], 1),
+                          "write_kib": round(mw["WRITE_SIZE"], 1), "hbm_bytes_per_launch": int(round(hbm)),
+                          "algo_bytes_per_launch": algo, "traffic_over_algo": round(hbm / algo, 4)}
+    out = {"kernel_hash": kernel_hash(),
+           "kernel_hash_note": "hash of the kernel sources listed in bench.KERNEL_SOURCES when the counters were taken",
+           "fetch_scale": round(fetch_scale, 6), "write_scale": round(write_scale, 6),
+           "calibration": f"binary16 negation kernel, {mib} MiB read + {mib} MiB written per launch",
+           "entries": entries}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -630,7 +776,23 @@ def main() -> int:
                     help="skip measuring the achievable streaming-read and MFMA rates")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain streaming kernel over this many MiB (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="print counter summaries of rocprofv3 --pmc output directories and exit (no GPU)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic_counters.json from FETCH_SIZE / WRITE_SIZE runs and exit")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print the headline layers' launch times from a rocprofv3 --kernel-trace output "
+                         "directory of a bench run with --steps as given, and exit (no GPU)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, max(args.steps, SECONDARY_STEPS))
+        return 0
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return 0
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (see the sharding notes); "
