@@ -5,6 +5,8 @@ points are only exercised on their argument checks (no kernel is launched here).
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -428,3 +430,16 @@ def test_binding_refuses_misshaped_layer_tensors(bits):
 
 def test_reload_env_is_exported_and_succeeds():
     w4.w4a16_reload_env()
+
+
+def test_library_shares_the_hip_runtime_torch_loads():
+    # loaded before anything touches torch, the library must still end up on the HIP
+    # runtime torch ships (one runtime in the process), or its launches fail
+    code = ("import w4a16_gemm_amd as w4\n"
+            "w4.lib()\n"
+            "import torch\n"
+            "libs = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(libs), sorted(libs))\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.startswith("1 "), out.stdout

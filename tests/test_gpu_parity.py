@@ -355,6 +355,7 @@ GEMV_SHAPES = [
     ("v2", 8200, 2048, 64, True, 4),      # 32 lanes, 2 chunks each, act order
     ("v3", 11008, 4096, 32, True, 4),     # 32 lanes, 4 chunks each (the act-order layer's shape)
     ("v4", 12296, 2048, 128, False, 8),   # 8-bit: 32 lanes, 4 chunks each
+    ("v5", 10248, 8192, 32, False, 4),    # 64 lanes, 6 steps: all scales staged in two rounds
 ]
 
 
@@ -372,8 +373,46 @@ def test_gemv_row_shapes_match_oracle(case):
                 clear_knob("W4A16_TUNE_GEMV_LPR")
             else:
                 set_knob("W4A16_TUNE_GEMV_LPR", str(lpr))
-            note(f"  lanes per row {lpr or 'auto'}")
-            y = run_gemm(prod).cpu().numpy()
-            assert oracle.rel_err(y, ref["y_ref"]) <= TOL, lpr
+            # scales staged once per launch (default where it fits) and per step: the
+            # same pairs and the same order of every row's sums, so identical bits
+            outs = []
+            for pre in ("1", "0"):
+                set_knob("W4A16_TUNE_GEMV_PRE", pre)
+                note(f"  lanes per row {lpr or 'auto'}, staged once {pre}")
+                y = run_gemm(prod).cpu().numpy()
+                assert oracle.rel_err(y, ref["y_ref"]) <= TOL, (lpr, pre)
+                outs.append(y)
+            assert np.array_equal(outs[0].view(np.uint16), outs[1].view(np.uint16)), lpr
     finally:
-        clear_knob("W4A16_TUNE_GEMV_LPR")
+        clear_knob("W4A16_TUNE_GEMV_LPR", "W4A16_TUNE_GEMV_PRE")
+
+
+def _runtime_libraries():
+    """The HIP runtime libraries mapped into this process (torch's and the library's)."""
+    import ctypes
+    paths = set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            p = line.split()[-1]
+            if "libamdhip64.so" in p:
+                paths.add(p)
+    return [ctypes.CDLL(p) for p in sorted(paths)]
+
+
+def test_an_earlier_failed_runtime_call_is_not_reported_as_a_launch_error():
+    # hipGetLastError keeps the last failure of any runtime call on the thread until it
+    # is read; a failed call made outside the library before a layer call (here
+    # hipSetDevice on a device that does not exist: refused on the host) must not turn
+    # into a launch error of the layer call
+    cfg = _small_cfg(*SMALL[0], 0)
+    prod = product_layer(cfg, 1)
+    ref = oracle_layer(cfg, 1, np.arange(cfg.N))
+    w4.lib()
+    libs = _runtime_libraries()
+    assert libs, "no HIP runtime mapped"
+    for path in ("gemv", "gemm"):
+        set_knob("W4A16_FORCE_PATH", path)
+        for rt in libs:
+            assert rt.hipSetDevice(9999) != 0
+        y = run_gemm(prod).cpu().numpy()
+        assert oracle.rel_err(y, ref["y_ref"]) <= TOL, path

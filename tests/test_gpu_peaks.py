@@ -14,7 +14,9 @@ pytestmark = pytest.mark.gpu
 
 
 def _lib():
+    import w4a16_gemm_amd as w4
     from w4a16_gemm_amd import build
+    w4.load_runtime_first()
     lib = ctypes.CDLL(build.PEAKS_LIB)
     lib.w4a16_peak_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
                                            ctypes.c_void_p]

@@ -76,6 +76,15 @@ class W4A16Error(RuntimeError):
         self.status = status
 
 
+def load_runtime_first() -> None:
+    """Load PyTorch (and with it the HIP runtime it ships) before a library of this
+    package: the library's dependency on the HIP runtime then resolves to that same,
+    already loaded runtime, so the device pointers and streams torch hands over belong
+    to the runtime the library launches on.  Loaded the other way round, the process
+    holds two HIP runtimes, and the library's launches fail ("no ROCm-capable device")."""
+    import torch  # noqa: F401
+
+
 def lib() -> ctypes.CDLL:
     """The loaded library; raises if it has not been built."""
     global _lib
@@ -83,6 +92,7 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
                               "`python -m w4a16_gemm_amd.build` (or __graft_entry__.build())")
+        load_runtime_first()
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGNATURES.items():
             fn = getattr(handle, name)

@@ -50,6 +50,7 @@ struct Knobs {
   Path force_path = Path::kAuto;   // W4A16_FORCE_PATH=gemv|gemm
   int gemv_lpr = 0;             // W4A16_TUNE_GEMV_LPR: lanes per row of the GEMV
   int gemv_blocks_per_cu = 1;   // W4A16_TUNE_GEMV_BLOCKS_PER_CU
+  int gemv_pre = 1;             // W4A16_TUNE_GEMV_PRE: stage all scales once (0 never, 1 when it fits)
   int gemm_prio = 1;            // W4A16_TUNE_GEMM_PRIO: wavefront priority in the large tiles
   int gemm_mfma32 = 1;          // W4A16_TUNE_GEMM_MFMA32: 32x32 blocks (0 never, 1 small tiles, 2 all)
   int gemm_split = 1;           // W4A16_TUNE_GEMM_SPLIT: two tile widths per launch
@@ -68,6 +69,7 @@ Knobs read_knobs() {
   if (v && std::strcmp(v, "gemm") == 0) k.force_path = Path::kGemm;
   k.gemv_lpr = env_int("W4A16_TUNE_GEMV_LPR", 0);
   k.gemv_blocks_per_cu = env_int("W4A16_TUNE_GEMV_BLOCKS_PER_CU", 1);
+  k.gemv_pre = env_int("W4A16_TUNE_GEMV_PRE", 1);
   k.gemm_prio = env_int("W4A16_TUNE_GEMM_PRIO", 1);
   k.gemm_mfma32 = env_int("W4A16_TUNE_GEMM_MFMA32", 1);
   k.gemm_split = env_int("W4A16_TUNE_GEMM_SPLIT", 1);
@@ -89,6 +91,15 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 int check_launch(const char* what) { return hip_status(hipGetLastError(), what); }
+
+// Start of every entry point that launches work: the library's own error cleared, and
+// the runtime's last-error state too.  hipGetLastError reports the last failure of any
+// runtime call made on the thread, by any component, until it is read; without this, a
+// launch check could report an earlier failure of someone else's call as its own.
+void begin_call() {
+  clear_error();
+  (void)hipGetLastError();
+}
 
 // --- scratch memory ------------------------------------------------------------
 //
@@ -266,10 +277,10 @@ int device_cus() {
 // Register-pipeline depth: about 8 KB of codes in flight per wavefront.
 constexpr int gemv_depth(int cpl) { return cpl >= 3 ? 2 : 8 / cpl; }
 
-template <int LPR, int CPL, bool EXACT, bool ACT, int EPT, int WPR, int BITS>
+template <int LPR, int CPL, bool EXACT, bool ACT, int EPT, int WPR, int BITS, bool PRE = false>
 int launch_gemv_e(dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
                    const uint16_t* s, Zeros z, half_t* y, int N, int K, int gshift, int steps) {
-  auto kern = gemv_m1_kernel<LPR, CPL, kGemvWaves, gemv_depth(CPL), EXACT, ACT, EPT, WPR, BITS>;
+  auto kern = gemv_m1_kernel<LPR, CPL, kGemvWaves, gemv_depth(CPL), EXACT, ACT, EPT, WPR, BITS, PRE>;
   // Dynamic LDS above 64 KB has to be allowed per kernel (once per process).
   static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -282,10 +293,12 @@ int launch_gemv_e(dim3 grid, size_t shmem, hipStream_t st, const half_t* x, cons
 
 // Staging rows per thread: one row (EPT = 1) is compiled only for exact splits
 // without act order, the decode shapes of large layers; everything else stages
-// whole 8-row items.
+// whole 8-row items.  ept == 0: every row staged once (PRE).
 template <int LPR, int CPL, bool EXACT, bool ACT, int BITS>
 int launch_gemv_t(int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
                    const uint16_t* s, Zeros z, half_t* y, int N, int K, int gshift, int steps) {
+  if (ept == 0)
+    return launch_gemv_e<LPR, CPL, EXACT, ACT, 8, 1, BITS, true>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
   if constexpr (EXACT && !ACT)
     if (ept == 1)
       return launch_gemv_e<LPR, CPL, EXACT, ACT, 1, 1, BITS>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
@@ -333,8 +346,9 @@ int launch_gemv_lpr(const GemvShape& sh, int ept, dim3 grid, size_t shmem, hipSt
 
 // LDS of one workgroup: the two-slot scale/zero ring (unit rows x (G+1) float2 each),
 // the row (slice) results, and the gathered activations under act order.
-size_t gemv_lds_bytes(int K, int G, int unit, int steps, int wpr, bool act) {
-  return 2 * static_cast<size_t>(unit) * (G + 1) * 2 * sizeof(float) +
+// pre: the table of all the workgroup's rows instead of the ring.
+size_t gemv_lds_bytes(int K, int G, int unit, int steps, int wpr, bool act, bool pre = false) {
+  return (pre ? steps : 2) * static_cast<size_t>(unit) * (G + 1) * 2 * sizeof(float) +
          static_cast<size_t>(steps) * unit * wpr * sizeof(float) + (act ? static_cast<size_t>(K) * sizeof(half_t) : 0);
 }
 
@@ -343,7 +357,7 @@ size_t gemv_lds_bytes(int K, int G, int unit, int steps, int wpr, bool act) {
 struct GemvPlan {
   bool ok = false;
   GemvShape sh;
-  int blocks = 0, steps = 0, ept = 8;
+  int blocks = 0, steps = 0, ept = 8;   // ept 0: every row staged once (PRE)
   size_t shmem = 0;
 };
 
@@ -395,6 +409,21 @@ GemvPlan plan_gemv_for(const GemvShape& sh, int N, int K, int gshift, bool act, 
   }
   p.shmem = gemv_lds_bytes(K, G, unit, p.steps, p.sh.wpr, act);
   p.ok = p.shmem <= kGemvLdsBudget;
+  // Staging every row once (PRE): whole rows, at most two rounds of two 8-row items per
+  // thread, and the table within the LDS budget.  The workgroups own consecutive units,
+  // so as many workgroups as it takes at `steps` units each (whole XCD rounds when there
+  // are enough).
+  if (p.ok && knobs().gemv_pre != 0 && p.sh.wpr == 1 && p.steps >= 2) {
+    int blocks = (units + p.steps - 1) / p.steps;
+    if (blocks >= 8) blocks += (8 - blocks % 8) % 8;
+    const long long items = static_cast<long long>(p.steps) * (unit / 8) * G;
+    const size_t shmem = gemv_lds_bytes(K, G, unit, p.steps, 1, act, true);
+    if (items <= 4LL * kGemvWaves * 64 && shmem <= kGemvLdsBudget) {
+      p.blocks = blocks;
+      p.ept = 0;
+      p.shmem = shmem;
+    }
+  }
   return p;
 }
 
@@ -719,13 +748,13 @@ extern "C" {
 
 int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
                const int32_t* g_idx, int group_size, int M, int N, int K, uint16_t* y, void* stream) {
-  clear_error();
+  begin_call();
   return gemm4(x, qweight, scales, qzeros, g_idx, group_size, M, N, K, y, stream, workspace_scratch);
 }
 
 int w4a16_gemm_noalloc(const uint16_t* x, const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
                        const int32_t* g_idx, int group_size, int M, int N, int K, uint16_t* y, void* stream) {
-  clear_error();
+  begin_call();
   void* unused = nullptr;
   if (int rc = static_scratch_setup(&unused)) return rc;
   return gemm4(x, qweight, scales, qzeros, g_idx, group_size, M, N, K, y, stream, static_scratch);
@@ -738,7 +767,7 @@ int w4a16_reload_env(void) {
 
 int w4a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros, const int32_t* g_idx,
                   int group_size, int N, int K, uint16_t* w_out, void* stream) {
-  clear_error();
+  begin_call();
   const void* ptrs[] = {qweight, scales, w_out, qzeros};   // qzeros may be NULL: symmetric
   if (int st = check_device_args(ptrs, qzeros ? 4 : 3, N, K, group_size)) return st;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -764,7 +793,7 @@ int w4a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t*
 // large-tile kernel (the tiled MFMA kernel where its conditions do not hold).
 int w8a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros,
                const int32_t* g_idx, int group_size, int M, int N, int K, uint16_t* y, void* stream) {
-  clear_error();
+  begin_call();
   if (M <= 0) return fail(W4A16_ERR_INVALID_ARG, "M must be positive (M=%d)", M);
   const void* ptrs[] = {x, qweight, scales, y, qzeros};   // qzeros may be NULL: symmetric
   if (int st = check_device_args(ptrs, qzeros ? 5 : 4, N, K, group_size)) return st;
@@ -802,7 +831,7 @@ int w8a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
 
 int w8a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t* qzeros, const int32_t* g_idx,
                   int group_size, int N, int K, uint16_t* w_out, void* stream) {
-  clear_error();
+  begin_call();
   const void* ptrs[] = {qweight, scales, w_out, qzeros};   // qzeros may be NULL: symmetric
   if (int st = check_device_args(ptrs, qzeros ? 4 : 3, N, K, group_size)) return st;
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -825,7 +854,7 @@ int w8a16_dequant(const int32_t* qweight, const uint16_t* scales, const int32_t*
 
 int w4a16_quantize_device(const uint16_t* w, int N, int K, int group_size, const double* in_scale, int sym,
                           int32_t* qweight, uint16_t* scales, int32_t* qzeros, void* stream) {
-  clear_error();
+  begin_call();
   if (!w || !qweight || !scales || (!sym && !qzeros)) return fail(W4A16_ERR_INVALID_ARG, "NULL buffer");
   if (int rc = check_shape(N, K, group_size)) return rc;
   const long long threads = static_cast<long long>(N) * (K / group_size);
@@ -846,7 +875,7 @@ int w4a16_quantize_device(const uint16_t* w, int N, int K, int group_size, const
 // `stream`, returns when the losses are on the host.
 int w4a16_awq_search(const uint16_t* w, const uint16_t* xcal, int N, int K, int T, int group_size,
                      const double* alphas, int n_alpha, double* losses, int* best, void* stream) {
-  clear_error();
+  begin_call();
   if (!w || !xcal || !alphas || !losses || !best) return fail(W4A16_ERR_INVALID_ARG, "NULL buffer");
   if (T <= 0 || n_alpha <= 0) return fail(W4A16_ERR_INVALID_ARG, "T and the grid size must be positive");
   if (int rc = check_shape(N, K, group_size)) return rc;
@@ -927,7 +956,7 @@ int w4a16_awq_search(const uint16_t* w, const uint16_t* xcal, int N, int K, int 
 // the host.
 int w4a16_gptq(const uint16_t* w, const uint16_t* xcal, int N, int K, int T, int group_size, int act_order,
                double damp, uint8_t* codes, uint16_t* scales, uint8_t* zeros, int32_t* g_idx, void* stream) {
-  clear_error();
+  begin_call();
   if (!w || !xcal || !codes || !scales || !zeros || (act_order && !g_idx))
     return fail(W4A16_ERR_INVALID_ARG, "NULL buffer");
   if (T <= 0) return fail(W4A16_ERR_INVALID_ARG, "T must be positive (T=%d)", T);

@@ -87,7 +87,16 @@ __device__ __forceinline__ float lane_group_sum(float v) {
 // chunk is 16 channels, the pairs of a word are its bytes 0 and 2 and (after a shift by
 // 8) 1 and 3 as subnormals q * 2^-24 (q < 256 fits the mantissa), both accumulated
 // with weight 1, and the zero points are bytes.
-template <int LPR, int CPL, int WAVES, int DEPTH, bool EXACT, bool ACT, int EPT, int WPR, int BITS = 4>
+//
+// PRE (one row per wavefront row-slot, WPR = 1): the workgroup owns `steps`
+// consecutive units instead of every nblk-th one, and stages the (S * 2^24, -Z * S)
+// pairs of all its rows once, before the first row: for every group the scales of its
+// rows are one contiguous run, so the whole grid reads the scale and zero-point arrays
+// front to back in a burst at the start instead of as scattered pieces between the code
+// streams of every step.  The rows then run without a barrier.  LDS: steps * STRIDE *
+// (G + 1) float2 instead of the ring.
+template <int LPR, int CPL, int WAVES, int DEPTH, bool EXACT, bool ACT, int EPT, int WPR, int BITS = 4,
+          bool PRE = false>
 __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
     const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
     Zeros qzeros, half_t* __restrict__ y, int N, int K, int gshift, int steps) {
@@ -96,6 +105,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   static_assert(WPR == 1 || (LPR == 64 && WAVES % WPR == 0 && WPR % DEPTH == 0),
                 "split rows: one row per wavefront, whole register slots per step");
   static_assert(BITS == 4 || BITS == 8, "4- or 8-bit weights");
+  static_assert(!PRE || (WPR == 1 && EPT == 8), "staging once: whole rows, 8-row items");
   constexpr int CSH = BITS == 4 ? 5 : 4;   // log2 channels per 16-byte chunk
   constexpr int XQ = 1 << (CSH - 3);       // 16-byte pieces of activations per chunk
   constexpr int XP = 4 * XQ;               // activation pairs per chunk
@@ -123,10 +133,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   // rows each), and the matrix row of the wavefront's seq-th row (seq = t WPR + s).
   auto unit_row = [&](int s) { return WPR == 1 ? wave * RPW + rr : wave / WPR + (WAVES / WPR) * s; };
   const int my_row = unit_row(0);
-  auto row_of = [&](int seq) { return (blk + (seq / WPR) * nblk) * STRIDE + unit_row(seq % WPR); };
+  // PRE: units blk * steps + t.
+  auto row_of = [&](int seq) {
+    return PRE ? (blk * steps + seq) * STRIDE + my_row : (blk + (seq / WPR) * nblk) * STRIDE + unit_row(seq % WPR);
+  };
 
+  // PRE: the ring is the table of all the workgroup's rows, [steps][STRIDE][GP].
   float2* ring = reinterpret_cast<float2*>(smem);                                   // [2][STRIDE][GP]
-  float* ybuf = reinterpret_cast<float*>(smem + 2 * static_cast<size_t>(STRIDE) * GP * sizeof(float2));
+  float* ybuf = reinterpret_cast<float*>(smem + (PRE ? steps : 2) * static_cast<size_t>(STRIDE) * GP * sizeof(float2));
   half_t* xs = reinterpret_cast<half_t*>(ybuf + static_cast<size_t>(steps) * STRIDE * WPR);
 
   // This lane's chunks (clamped into its slice and the row unless the split is exact)
@@ -212,8 +226,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
 #pragma unroll
     for (int u = 0; u < PB; ++u) pv[u] = perm4[min(tid + u * NT, (K >> 2) - 1)];
   }
-  load_item(0, 0);
-  load_item(1, 1);
+  if constexpr (!PRE) {
+    load_item(0, 0);
+    load_item(1, 1);
+  }
   uint4 wb[DEPTH][CPL];
   // the codes part of qweight, N K / 2 < 2^31 bytes (checked by the host)
   const __amdgpu_buffer_rsrc_t codes = stream_rsrc(qw, static_cast<uint32_t>(N) * static_cast<uint32_t>(W) * 4u);
@@ -225,6 +241,54 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   };
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) load_row(wb[d], row_of(d));  // clamped if there are fewer rows
+
+  // PRE: items (octet o of the workgroup's rows, group g), item g * OCTS + o, so that
+  // neighbouring threads read neighbouring 16-byte pieces of one group's run of scales;
+  // kPreBatch items per thread and round (the host allows at most two rounds), loads
+  // clamped into the items so that every thread issues the same loads.
+  constexpr int kPreBatch = 2;
+  const int pre_octs = steps * OCT;
+  const int pre_items = PRE ? pre_octs * G : 0;
+  const int pre_r0 = blk * steps * STRIDE;
+  uint4 ps[kPreBatch];
+  ZeroBits pz[kPreBatch];
+  auto pre_load = [&](int round) {
+#pragma unroll
+    for (int u = 0; u < kPreBatch; ++u) {
+      const int it = min(tid + (round * kPreBatch + u) * NT, pre_items - 1);
+      const int g = it / pre_octs, o = it - g * pre_octs;
+      const int n8 = min(pre_r0 + 8 * o, N - 8);
+      ps[u] = *reinterpret_cast<const uint4*>(scales + static_cast<size_t>(g) * N + n8);
+      if constexpr (BITS == 4)
+        pz[u] = *qzeros.at(static_cast<size_t>(g) * (N >> 3) + (n8 >> 3));
+      else
+        pz[u] = *reinterpret_cast<const uint2*>(qzeros.at(static_cast<size_t>(g) * (N >> 2) + (n8 >> 2)));
+    }
+  };
+  auto pre_put = [&](int round) {
+#pragma unroll
+    for (int u = 0; u < kPreBatch; ++u) {
+      const int it = tid + (round * kPreBatch + u) * NT;
+      if (it < pre_items) {
+        const int g = it / pre_octs, o = it - g * pre_octs;
+        const uint32_t s8[4] = {ps[u].x, ps[u].y, ps[u].z, ps[u].w};
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float S = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>((s8[r >> 1] >> (16 * (r & 1))) & 0xFFFFu)));
+          float Z;
+          if constexpr (BITS == 4) {
+            Z = static_cast<float>((qzeros.word(pz[u]) >> (4 * r)) & 0xFu);
+          } else {
+            const uint32_t zw = qzeros.word8(r < 4 ? pz[u].x : pz[u].y);
+            Z = static_cast<float>((zw >> (8 * (r & 3))) & 0xFFu);
+          }
+          ring[(8 * o + r) * GP + g] = make_float2(S * 16777216.0f, -Z * S);   // both exact in fp32
+        }
+      }
+    }
+  };
+  const int pre_rounds = PRE ? (pre_items + kPreBatch * NT - 1) / (kPreBatch * NT) : 0;
+  if constexpr (PRE) pre_load(0);
 
   // 2. Act order: gather the activations into LDS in stored order (all gathers of a
   // thread in flight together).  Step 0's items go to ring slot 0; the barrier
@@ -254,7 +318,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
                         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, g[u][3])) << 16)};
     }
   }
-  put_item(0, 0);
+  if constexpr (PRE) {
+    for (int round = 0; round < pre_rounds; ++round) {
+      if (round > 0) pre_load(round);
+      pre_put(round);
+    }
+  } else {
+    put_item(0, 0);
+  }
   __syncthreads();
   if constexpr (ACT) {
 #pragma unroll
@@ -363,11 +434,31 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
     put_item(p ^ 1, p ^ 1);
     __syncthreads();
   };
+  // PRE: row t's pairs are row t of the table; no staging and no barrier per step.
+  auto pre_step = [&](int t, int d, bool refill) {
+    const float acc = row_step(t, my_row, wb[d]);
+    if (refill) load_row(wb[d], row_of(t + DEPTH));
+    __builtin_amdgcn_sched_barrier(0);
+    keep(t, my_row, acc);
+  };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using More = std::false_type;
   using Last = std::true_type;
-  if constexpr (WPR > 1) {
+  if constexpr (PRE) {
+    int t0 = 0;
+    for (; t0 + 2 * DEPTH <= steps; t0 += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) pre_step(t0 + d, d, true);
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+      if (t0 + d < steps) pre_step(t0 + d, d, t0 + d + DEPTH < steps);
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+      if (t0 + DEPTH + d < steps) pre_step(t0 + DEPTH + d, d, false);
+    __syncthreads();   // every row result is in LDS
+  } else if constexpr (WPR > 1) {
     int t = 0;
     for (; t + 2 < steps; t += 2) {
       split_step(t, I0{}, More{});
@@ -406,7 +497,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   // barrier published every result); split rows add their slices in order
   for (int idx = tid; idx < steps * STRIDE; idx += NT) {
     const int t = idx / STRIDE;
-    const int n = (blk + t * nblk) * STRIDE + (idx - t * STRIDE);
+    const int n = PRE ? blk * steps * STRIDE + idx : (blk + t * nblk) * STRIDE + (idx - t * STRIDE);
     float v = ybuf[idx * WPR];
 #pragma unroll
     for (int s = 1; s < WPR; ++s) v += ybuf[idx * WPR + s];

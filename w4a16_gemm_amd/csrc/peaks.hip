@@ -76,6 +76,7 @@ int w4a16_peak_stream_read(const void* buf, size_t bytes, uint32_t* out, int blo
   if (!buf || !out || blocks <= 0 || bytes == 0 || bytes % 16 != 0 || bytes > (size_t{1} << 31) - 16 ||
       reinterpret_cast<uintptr_t>(buf) % 16 != 0)
     return fail(1, "stream read: NULL pointer, blocks <= 0, or bytes not a positive multiple of 16 below 2^31");
+  (void)hipGetLastError();   // the launch check below reports this launch, not an earlier call's failure
   hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<const u32x4_t*>(buf), static_cast<long long>(bytes / 16), out);
   const hipError_t e = hipGetLastError();
@@ -89,6 +90,7 @@ int w4a16_peak_mfma_f16(float* out, int iters, int blocks, void* stream) {
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                                        static_cast<int>(kMfmaLds));
   if (lds_ok != hipSuccess) return fail(5, hipGetErrorString(lds_ok));
+  (void)hipGetLastError();
   hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(kThreads), kMfmaLds, static_cast<hipStream_t>(stream),
                      out, iters);
   const hipError_t e = hipGetLastError();
