@@ -101,6 +101,31 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
   float* red = reinterpret_cast<float*>(smem);                                              // [2][W][16 m][16 n]
   uint2* slab = reinterpret_cast<uint2*>(smem + 2 * static_cast<size_t>(nwaves) * 256 * sizeof(float));  // [2][G][16]
 
+  // Codes of row block b for this lane (rows past N re-read row N - 1), read through a
+  // buffer resource over the codes (N K / 2 < 2^31 bytes, checked by the host): 32-bit
+  // byte offsets instead of 64-bit addresses.
+  const __amdgpu_buffer_rsrc_t codes = stream_rsrc(qw, static_cast<uint32_t>(N) * static_cast<uint32_t>(Wd) * 4u);
+  constexpr uint32_t kStepBytes = 16u * BITS;   // 128 channels
+  auto code_offset = [&](int b) {   // bytes; step t adds kStepBytes t
+    const int n = min(16 * b + lr, N - 1);
+    return (static_cast<uint32_t>(n) * static_cast<uint32_t>(Wd) + static_cast<uint32_t>((kw >> WSH) + 4 * NQ * lq)) * 4u;
+  };
+  auto load_codes = [&](int b, uint4 (&cw)[T][NQ]) {
+    const uint32_t off = code_offset(b);
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) cw[t][q] = load_buffer16(codes, off + kStepBytes * t + 16u * q);
+  };
+  // The first row block's codes are requested before anything else: they come from HBM,
+  // the activations (read by every workgroup) mostly from the L2, so the long wait
+  // starts first.  Same-process A/B on the 70B-class layer: M = 2 / 16 24.74 / 30.60 ->
+  // 24.51 / 30.09 us, the 1-4B down-projection at M = 16 13.62 -> 13.15 us.
+  // Row blocks b, b + gs, ... of this slice (neighbours on one XCD).
+  int b = xcd_block(blockIdx.x - slice * gs, gs);
+  uint4 cw[T][NQ];
+  load_codes(b, cw);
+
   // Activation slice: xr[t][j] = x[m][kw + 128 t + 32 q + 8 j, +8) for m = lane % 16;
   // zero for m >= M.  SUB: xs[t] = sum of x[m] over step t's 128 channels, and the
   // elements 2, 3, 6, 7 of every fragment scaled by 1/16.
@@ -153,22 +178,6 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
     }
   }
 
-  // Codes of row block b for this lane (rows past N re-read row N - 1), read through a
-  // buffer resource over the codes (N K / 2 < 2^31 bytes, checked by the host): 32-bit
-  // byte offsets instead of 64-bit addresses.
-  const __amdgpu_buffer_rsrc_t codes = stream_rsrc(qw, static_cast<uint32_t>(N) * static_cast<uint32_t>(Wd) * 4u);
-  constexpr uint32_t kStepBytes = 16u * BITS;   // 128 channels
-  auto code_offset = [&](int b) {   // bytes; step t adds kStepBytes t
-    const int n = min(16 * b + lr, N - 1);
-    return (static_cast<uint32_t>(n) * static_cast<uint32_t>(Wd) + static_cast<uint32_t>((kw >> WSH) + 4 * NQ * lq)) * 4u;
-  };
-  auto load_codes = [&](int b, uint4 (&cw)[T][NQ]) {
-    const uint32_t off = code_offset(b);
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) cw[t][q] = load_buffer16(codes, off + kStepBytes * t + 16u * q);
-  };
   // Scale and zero word of slab entries tid + u * nthreads of row block b.
   half_t sv[SE];
   uint32_t zv[SE];
@@ -207,7 +216,6 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
   // refilled with the next row block's codes as soon as it has been used, so a load
   // has a whole row block of work to land.  The slab of the next block is written and
   // its successor's scales issued; the partial tiles are summed after the barrier.
-  uint4 cw[T][NQ];
   auto row_block = [&](int b, int i) {
     const int buf = i & 1;
     const uint32_t off_next = code_offset(b + gs);
@@ -288,9 +296,6 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
     }
   };
 
-  // row blocks b, b + gs, ... of this slice (neighbours on one XCD)
-  int b = xcd_block(blockIdx.x - slice * gs, gs);
-  load_codes(b, cw);
   load_sz(b);
   write_slab(b, 0);
   load_sz(b + gs);
