@@ -613,7 +613,7 @@ def traffic_for(hash_now: str, key: str):
 
 # --- counter post-processing (rocprofv3 --pmc output; no GPU needed) ---------------
 
-HEADLINE_KERNELS = {"c3:M1": "gemv_m1_kernelILi64ELi4ELi8ELi2ELb1ELb0ELi1ELi1ELi4E",
+HEADLINE_KERNELS = {"c3:M1": "gemv_m1_kernelILi64ELi4ELi8ELi2ELb1ELb0ELi8ELi1ELi4ELb1E",
                     "c4:M2048": "gemm_big_kernelILi3ELi8ELi4ELb0E"}
 
 
