@@ -192,6 +192,35 @@ def test_large_tile_kinds_match_oracle(mb, mfma32):
             clear_knob(v)
 
 
+def test_dequantise_once_tile_matches_the_large_tile():
+    # 256-row tiles whose codes are dequantised once per workgroup into a binary16 weight
+    # tile in LDS (W4A16_TUNE_GEMM_LDSB=1): the same operands in the same MFMA order as the
+    # large tile, so the same bits; with a 192-wide second round of tiles and ragged edges
+    import torch
+    # t6: more than one round of full tiles, so the launch also runs 256-column tiles
+    cases = LARGE_TILE_CASES + [("t4", 520, 1400, 1024, 128, False, False), ("t5", 300, 776, 448, 32, True, False),
+                                ("t6", 2048, 8448, 128, 128, False, False)]
+    set_knob("W4A16_FORCE_PATH", "gemm")
+    set_knob("W4A16_TUNE_GEMM_BIG_MB", "8")
+    try:
+        for i, (name, M, N, K, g, act, sym) in enumerate(cases):
+            cfg = wl.custom_config(name, 340 + i, K=K, N=N, group_size=g, M_list=(M,), act_order=act, sym=sym)
+            note(f"dequantise-once tile {name} M={M} N={N} K={K} g={g} act={act} sym={sym}")
+            prod = product_layer(cfg, M)
+            ref = oracle_layer(cfg, M, np.arange(N))
+            set_knob("W4A16_TUNE_GEMM_LDSB", "0")
+            y0 = run_gemm(prod).cpu().numpy()
+            set_knob("W4A16_TUNE_GEMM_LDSB", "1")
+            y1 = run_gemm(prod).cpu().numpy()
+            assert oracle.rel_err(y1, ref["y_ref"]) <= TOL
+            assert np.array_equal(y1.view(np.uint16), y0.view(np.uint16))
+            ks = np.arange(0, K, max(1, K // 130))[:130]
+            yk = run_gemm(prod, x=torch.from_numpy(wl.unit_vectors(K, ks)).to(device())).cpu().numpy()
+            assert np.array_equal(yk.view(np.uint16), ref["W16"][:, ks].T.copy().view(np.uint16))
+    finally:
+        clear_knob("W4A16_TUNE_GEMM_BIG_MB", "W4A16_TUNE_GEMM_LDSB")
+
+
 def test_all_ones_gives_row_sums():
     import torch
     cfg = _small_cfg("ones", 1, 520, 3072, 64, False, 50)

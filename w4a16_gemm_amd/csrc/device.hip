@@ -54,6 +54,7 @@ struct Knobs {
   int gemm_prio = 1;            // W4A16_TUNE_GEMM_PRIO: wavefront priority in the large tiles
   int gemm_mfma32 = 1;          // W4A16_TUNE_GEMM_MFMA32: 32x32 blocks (0 never, 1 small tiles, 2 all)
   int gemm_split = 1;           // W4A16_TUNE_GEMM_SPLIT: two tile widths per launch
+  int gemm_ldsb = 0;            // W4A16_TUNE_GEMM_LDSB: 256-row tiles dequantised once into LDS
   int gemm_big_mb = 0;          // W4A16_TUNE_GEMM_BIG_MB: forced row blocks per wavefront (0 = auto)
   int gemm_big_min_m = 0;       // W4A16_TUNE_GEMM_BIG_MIN_M (0 = default)
   int gemm_big = 1;             // W4A16_TUNE_GEMM_BIG: large-tile kernel allowed
@@ -73,6 +74,7 @@ Knobs read_knobs() {
   k.gemm_prio = env_int("W4A16_TUNE_GEMM_PRIO", 1);
   k.gemm_mfma32 = env_int("W4A16_TUNE_GEMM_MFMA32", 1);
   k.gemm_split = env_int("W4A16_TUNE_GEMM_SPLIT", 1);
+  k.gemm_ldsb = env_int("W4A16_TUNE_GEMM_LDSB", 0);
   k.gemm_big_mb = env_int("W4A16_TUNE_GEMM_BIG_MB", 0);
   k.gemm_big_min_m = env_int("W4A16_TUNE_GEMM_BIG_MIN_M", 0);
   k.gemm_big = env_int("W4A16_TUNE_GEMM_BIG", 1);
@@ -572,16 +574,16 @@ int run_skinny(const SkinnyShape& sk, bool act, hipStream_t st, const half_t* hx
 // (order alternated, identical outputs): M = 100 / 200 / 300 on the 32x32 tile 49.9 / 27.1 /
 // 50.2 -> 46.1 / 25.2 / 46.3 us; 256-row tiles M = 4096 485 -> 472 us, the act-order layer
 // at M = 512 78.3 -> 73.8 us, the prefill ~1.5%.
-template <int NB2, int MB, int BITS, bool W32>
+template <int NB2, int MB, int BITS, bool W32, bool LDSB = false>
 int launch_big_t(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s, Zeros z, half_t* y,
                  int M, int N, int K, int gshift, int split, int n_split, int grid) {
-  constexpr size_t lds = BITS == 4 ? kBigLds : kBigLds8;
+  constexpr size_t lds = LDSB ? kLdsbLds : BITS == 4 ? kBigLds : kBigLds8;
   static const hipError_t lds_ok = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(gemm_big_kernel<NB2, MB, BITS, W32>), hipFuncAttributeMaxDynamicSharedMemorySize,
-      static_cast<int>(lds));
+      reinterpret_cast<const void*>(gemm_big_kernel<NB2, MB, BITS, W32, LDSB>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (int rc = hip_status(lds_ok, "hipFuncSetAttribute")) return rc;
-  hipLaunchKernelGGL((gemm_big_kernel<NB2, MB, BITS, W32>), dim3(grid), dim3(512), lds, st, x, qw, s, z, y, M, N,
-                     K, gshift, split, n_split, knobs().gemm_prio);
+  hipLaunchKernelGGL((gemm_big_kernel<NB2, MB, BITS, W32, LDSB>), dim3(grid), dim3(512), lds, st, x, qw, s, z, y, M,
+                     N, K, gshift, split, n_split, knobs().gemm_prio);
   return check_launch("gemm launch");
 }
 
@@ -596,6 +598,10 @@ int launch_big(hipStream_t st, const half_t* x, const uint32_t* qw, const half_t
     const int mode = knobs().gemm_mfma32;
     if (mode == 2 || (mode == 1 && MB <= 4))
       return launch_big_t<NB2, MB, BITS, true>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
+    // measurements: the dequantise-once tile (W4A16_TUNE_GEMM_LDSB=1)
+    if constexpr (MB == 8)
+      if (knobs().gemm_ldsb != 0)
+        return launch_big_t<NB2, MB, BITS, false, true>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
   }
   return launch_big_t<NB2, MB, BITS, false>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
 }

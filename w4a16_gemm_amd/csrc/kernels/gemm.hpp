@@ -450,32 +450,46 @@ struct BigLoader {
   // that is never read again.  The scale / zero load comes first, so that waiting for
   // tile t alone never waits for more than that load of tile t + 1.
   __device__ __forceinline__ void load(int t) const {
-    const int tc = min(t, KT - 1);
     unsigned char* stage = smem + (t % NS) * STAGE;
+    load_sz_to(t, stage + kBigLdsA);
+    load_a_to(t, stage);
+    load_codes_to(t, stage + kBigLdsA);
+  }
+  // The parts of a tile's loads, to separate buffers: the scales and zero points of its
+  // two 32-channel halves (to c + LB, c + LB + kBigLdsS), the activations (to a) and the
+  // codes (to c); tiles past the end re-load the last one.
+  __device__ __forceinline__ void load_sz_to(int t, unsigned char* c) const {
+    const int tc = min(t, KT - 1);
     const int gi = (tc * BK + 32 * sz_half) >> gshift;
     if (wave == 0)
       __builtin_amdgcn_global_load_lds(
           reinterpret_cast<const void*>(scales + static_cast<size_t>(gi) * N + s_col),
-          reinterpret_cast<void*>(stage + kBigLdsA + LB), 16, 0, 0);
+          reinterpret_cast<void*>(c + LB), 16, 0, 0);
     else if (wave == 1) {
       if constexpr (BITS == 4)
         __builtin_amdgcn_global_load_lds(
             reinterpret_cast<const void*>(qzeros.at(static_cast<size_t>(gi) * (N >> 3) + z_word)),
-            reinterpret_cast<void*>(stage + kBigLdsA + LB + kBigLdsS), 4, 0, 0);
+            reinterpret_cast<void*>(c + LB + kBigLdsS), 4, 0, 0);
       else
         __builtin_amdgcn_global_load_lds(
             reinterpret_cast<const void*>(qzeros.at(static_cast<size_t>(gi) * (N >> 2) + z_word)),
-            reinterpret_cast<void*>(stage + kBigLdsA + LB + kBigLdsS), 16, 0, 0);
+            reinterpret_cast<void*>(c + LB + kBigLdsS), 16, 0, 0);
     }
+  }
+  __device__ __forceinline__ void load_a_to(int t, unsigned char* a) const {
+    const int tc = min(t, KT - 1);
 #pragma unroll
     for (int i = 0; i < APT; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xr, as_lds(stage + (wave * APT + i) * 64 * 16), 16,
+          xr, as_lds(a + (wave * APT + i) * 64 * 16), 16,
           static_cast<int>(a_off[i]), tc * (BK * 2), 0, 0);
+  }
+  __device__ __forceinline__ void load_codes_to(int t, unsigned char* c) const {
+    const int tc = min(t, KT - 1);
 #pragma unroll
     for (int i = 0; i < CL; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          qr, as_lds(stage + kBigLdsA + (512 * i + wave * 64) * 16),
+          qr, as_lds(c + (512 * i + wave * 64) * 16),
           16, static_cast<int>(b_off[i]), tc * (BK * BITS / 8), 0, 0);
   }
 };
@@ -751,6 +765,133 @@ __device__ __forceinline__ void big_tile32(const half_t* __restrict__ x, const u
     }
 }
 
+// 256-row tile with every code dequantised once per workgroup (4-bit weights): the same
+// wavefront tiles and MFMA steps as big_tile, but in each K tile the 512 threads expand
+// the stage's codes cooperatively, thread (half h, column c) the 32 channels [32 h, +32)
+// of column c, into a binary16 weight tile in LDS, and the wavefronts read their B
+// operands from it instead of dequantising their own columns (which the two wavefronts
+// sharing a column both did).  LDS (159,488 B): activations double-buffered (2 x 32 KB),
+// codes, scales and zero points triple-buffered (3 x 9,472 B) so that a tile's codes are
+// in LDS one K tile before it is computed, and the weight tile double-buffered (2 x 32
+// KB, rows of 8 chunks of 8 channels, chunk j of column c at slot j ^ (c % 8)).  K tile t:
+// request the activations of t + 1 and the codes of t + 2, expand the codes of t + 1 into
+// weight buffer (t + 1) % 2, run the MFMAs of t on activation and weight buffers t % 2,
+// then one barrier.
+constexpr uint32_t kLdsbA = kBigBM * kBigBK * 2;
+constexpr uint32_t kLdsbC = kBigLdsB + kBigLdsS + kBigLdsZ;
+constexpr uint32_t kLdsbW = kBigBN * kBigBK * 2;
+constexpr uint32_t kLdsbOffC = 2 * kLdsbA;
+constexpr uint32_t kLdsbOffW = kLdsbOffC + 3 * kLdsbC;
+constexpr size_t kLdsbLds = static_cast<size_t>(kLdsbOffW) + 2 * kLdsbW;
+static_assert(kLdsbLds <= 160 * 1024, "fits the LDS of a compute unit");
+
+template <int NB>
+__device__ __forceinline__ void big_tile_ldsb(const half_t* __restrict__ x, const uint32_t* __restrict__ qw,
+                                              const half_t* __restrict__ scales, Zeros qzeros,
+                                              half_t* __restrict__ y, int M, int N, int K, int gshift, int m0,
+                                              int n0, int n_end, int prio) {
+  constexpr int MB = 8;
+  using Loader = BigLoader<NB, MB, 4>;
+  constexpr int BL = Loader::BL, LB = Loader::LB;
+  constexpr int BN = 64 * NB;
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int lr = lane & 15;
+  const int lq = lane >> 4;
+  const int KT = K / kBigBK;
+  const Loader ld(x, qw, scales, qzeros, smem, M, N, K, gshift, m0, n0, n_end, tid, wave);
+  auto a_buf = [&](int t) { return smem + (t & 1) * kLdsbA; };
+  auto c_buf = [&](int t) { return smem + kLdsbOffC + (t % 3) * kLdsbC; };
+  auto w_buf = [&](int t) { return smem + kLdsbOffW + (t & 1) * kLdsbW; };
+
+  // The expansion task of this thread: half eh, column ec (threads past the tile's
+  // 2 BN pairs have none).
+  const int eh = tid / BL, ec = tid % BL;
+  const bool expands = ec < BN;
+  auto expand = [&](int t) {
+    if (!expands) return;
+    const unsigned char* c = c_buf(t);
+    const uint4 w = *reinterpret_cast<const uint4*>(c + (eh * BL + ec) * 16);
+    const uint32_t sb = *reinterpret_cast<const uint16_t*>(c + LB + (eh * BL + ec) * 2);
+    const uint32_t zw = *reinterpret_cast<const uint32_t*>(c + LB + kBigLdsS + (eh * (BL / 8) + (ec >> 3)) * 4);
+    const DequantConsts dc = make_consts((qzeros.word(zw) >> (4 * (ec & 7))) & 0xFu,
+                                         __builtin_bit_cast(half_t, static_cast<uint16_t>(sb)));
+    unsigned char* wt = w_buf(t) + ec * 128;
+    const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = 4 * eh + q;
+      *reinterpret_cast<half8_t*>(wt + 16 * (j ^ (ec & 7))) = dequant_word(words[q], dc);
+    }
+  };
+
+  float4_t acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Lane offsets: A fragment mb of step s at a_lane + 16 ((2 q + s) ^ (r % 8)) + 2048 mb;
+  // B fragment nb of step s at b_lane + 2048 nb + 16 ((2 q + s) ^ (r % 8)).
+  const int a_lane = (wm * 16 * MB + lr) * 128;
+  const int b_lane = (wn * 16 * NB + lr) * 128;
+
+  ld.load_sz_to(0, c_buf(0));
+  ld.load_a_to(0, a_buf(0));
+  ld.load_codes_to(0, c_buf(0));
+  ld.load_sz_to(1, c_buf(1));
+  ld.load_codes_to(1, c_buf(1));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  block_barrier();
+  expand(0);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  block_barrier();
+
+  for (int t = 0; t < KT; ++t) {
+    ld.load_a_to(t + 1, a_buf(t + 1));
+    ld.load_sz_to(t + 2, c_buf(t + 2));
+    ld.load_codes_to(t + 2, c_buf(t + 2));
+    if (t + 1 < KT) expand(t + 1);
+    const unsigned char* at = a_buf(t);
+    const unsigned char* wt = w_buf(t);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      half8_t af[MB], bf[NB];
+      const int sl = 16 * ((2 * lq + s) ^ (lr & 7));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) bf[nb] = *reinterpret_cast<const half8_t*>(wt + b_lane + 2048 * nb + sl);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) af[mb] = *reinterpret_cast<const half8_t*>(at + a_lane + 2048 * mb + sl);
+      if (prio) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mb], bf[nb], acc[mb][nb], 0, 0, 0);
+      if (prio) __builtin_amdgcn_s_setprio(0);
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    block_barrier();
+  }
+
+  const int nw = n0 + wn * 16 * NB;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int n = nw + 16 * nb + lr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * 16 * MB + 16 * mb + 4 * lq + r;
+        if (m < M && n < n_end) y[static_cast<size_t>(m) * N + n] = static_cast<half_t>(acc[mb][nb][r]);
+      }
+    }
+}
+
 // prio != 0: each MFMA cluster runs at wavefront priority 1 (s_setprio), the LDS reads
 // and dequantisation between clusters at 0.
 // One launch covers up to two column ranges: workgroups [0, split) take BM x 256
@@ -758,20 +899,25 @@ __device__ __forceinline__ void big_tile32(const half_t* __restrict__ x, const u
 // BM = 32 MB rows (256 for prefill; 128 / 64 for batches of up to 128 / 64 rows).
 // With one wave of full tiles and one of narrower tiles, both rounds fill the device
 // when the full-width tiles alone would leave most of a second round idle.
-template <int NB2, int MB, int BITS = 4, bool W32 = false>
+// LDSB: 256-row tiles of 4-bit weights dequantised once per workgroup (big_tile_ldsb).
+template <int NB2, int MB, int BITS = 4, bool W32 = false, bool LDSB = false>
 __global__ __launch_bounds__(512) void gemm_big_kernel(const half_t* __restrict__ x, const uint32_t* __restrict__ qw,
                                                        const half_t* __restrict__ scales,
                                                        Zeros qzeros, half_t* __restrict__ y,
                                                        int M, int N, int K, int gshift, int split, int n_split,
                                                        int prio) {
   static_assert(!W32 || BITS == 4, "the 32x32 tile takes 4-bit weights");
+  static_assert(!LDSB || (BITS == 4 && MB == 8 && !W32), "the dequantise-once tile: 4-bit, 256 rows");
   constexpr int BM = 32 * MB;
   const int tiles_m = (M + BM - 1) / BM;
   const int bid = blockIdx.x;
   if (bid < split) {
     const int tiles_n = (n_split + 255) / 256;
     const int tile = xcd_tile(bid, tiles_m, tiles_n);
-    if constexpr (W32)
+    if constexpr (LDSB)
+      big_tile_ldsb<4>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM, (tile % tiles_n) * 256,
+                       min(N, n_split), prio);
+    else if constexpr (W32)
       big_tile32<4, MB>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM, (tile % tiles_n) * 256,
                         min(N, n_split), prio);
     else
@@ -781,7 +927,10 @@ __global__ __launch_bounds__(512) void gemm_big_kernel(const half_t* __restrict_
     constexpr int BN2 = 64 * NB2;
     const int tiles_n = (N - n_split + BN2 - 1) / BN2;
     const int tile = xcd_tile(bid - split, tiles_m, tiles_n);
-    if constexpr (W32 && NB2 % 2 == 0)
+    if constexpr (LDSB)
+      big_tile_ldsb<NB2>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM,
+                         n_split + (tile % tiles_n) * BN2, N, prio);
+    else if constexpr (W32 && NB2 % 2 == 0)
       big_tile32<NB2, MB>(x, qw, scales, qzeros, y, M, N, K, gshift, (tile / tiles_n) * BM,
                           n_split + (tile % tiles_n) * BN2, N, prio);
     else
