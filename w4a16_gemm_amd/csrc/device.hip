@@ -1000,7 +1000,7 @@ int w4a16_gptq(const uint16_t* w, const uint16_t* xcal, int N, int K, int T, int
   auto* dxp = static_cast<double*>(alloc(tk * 8));
   auto* dH = static_cast<double*>(alloc(kk * 8));
   auto* dU = static_cast<double*>(alloc(kk * 8));
-  auto* derr = static_cast<double*>(alloc(static_cast<size_t>(N) * kGptqBlock * 8));
+  auto* derr = static_cast<double*>(alloc(static_cast<size_t>(N) * kGptqBatch * 8));
   auto* dsz = static_cast<double2*>(alloc(static_cast<size_t>(N) * sizeof(double2)));
   auto* dcp = static_cast<uint8_t*>(alloc(nk));
   auto* dc = static_cast<uint8_t*>(alloc(nk));
@@ -1033,15 +1033,21 @@ int w4a16_gptq(const uint16_t* w, const uint16_t* xcal, int N, int K, int T, int
   for (int p = K - 1; p >= 1; --p) hipLaunchKernelGGL(gptq_trinv_step_kernel, dim3(p), dim3(256), 0, st, dH, dU, K, p);
   hipLaunchKernelGGL(gptq_trinv_finish_kernel, dim3(K), dim3(256), 0, st, dH, dU, K);
   if (int rc = check_launch("GPTQ factorisation launch")) return release(rc);
-  // rounding with error feedback, 32 visited columns at a time
-  for (int i0 = 0; i0 < K; i0 += kGptqBlock) {
-    hipLaunchKernelGGL(gptq_block_kernel, dim3(static_cast<unsigned>((N + 127) / 128)), dim3(128), 0, st, dwp, dU, N,
-                       K, i0, group_size, dsz, derr, dcp, ds, dz);
-    const int rest = K - i0 - kGptqBlock;
-    if (rest > 0)
-      hipLaunchKernelGGL(gptq_update_kernel, dim3(static_cast<unsigned>((rest + 63) / 64),
-                                                  static_cast<unsigned>((N + 63) / 64)),
-                         dim3(256), 0, st, dwp, dU, derr, N, K, i0);
+  // rounding with error feedback, 32 visited columns at a time, 128 to a batch: the
+  // block's errors go to the batch's later columns, the batch's to every column after it
+  auto update = [&](const double* e, int i0, int rank, int k_begin, int k_end) {
+    hipLaunchKernelGGL(gptq_update_kernel, dim3(static_cast<unsigned>((k_end - k_begin + 63) / 64),
+                                                static_cast<unsigned>((N + 63) / 64)),
+                       dim3(256), 0, st, dwp, dU, e, kGptqBatch, N, K, i0, rank, k_begin, k_end);
+  };
+  for (int b0 = 0; b0 < K; b0 += kGptqBatch) {
+    const int bend = std::min(b0 + kGptqBatch, K);
+    for (int i0 = b0; i0 < bend; i0 += kGptqBlock) {
+      hipLaunchKernelGGL(gptq_block_kernel, dim3(static_cast<unsigned>((N + 127) / 128)), dim3(128), 0, st, dwp, dU,
+                         N, K, i0, group_size, dsz, derr + (i0 - b0), kGptqBatch, dcp, ds, dz);
+      if (i0 + kGptqBlock < bend) update(derr + (i0 - b0), i0, kGptqBlock, i0 + kGptqBlock, bend);
+    }
+    if (bend < K) update(derr, b0, bend - b0, bend, K);
   }
   hipLaunchKernelGGL(gptq_scatter_codes_kernel, blocks(nk), dim3(256), 0, st, dcp, dperm, N, K, dc);
   if (int rc = check_launch("GPTQ rounding launch")) return release(rc);

@@ -8,12 +8,14 @@
 // U^T U = H^-1, so it is the upper Cholesky factor of H^-1.  Both steps are one
 // launch per pivot (a rank-1 update of the rows above it); the matrices stay in HBM.
 //
-// The rounding runs in blocks of 32 visited columns: a thread per output row rounds
-// the block's columns in order with their error fed forward inside the block, then a
-// rank-32 update carries the block's errors to every later column.  Group starts are
-// block starts (every group size is a multiple of 32), so a group's grid is taken
-// from columns that have received every earlier error, as in the column-by-column
-// order.  The group grid and the rounding are the round-to-nearest quantiser's
+// The rounding runs in blocks of 32 visited columns, four to a batch of 128: a thread
+// per output row rounds a block's columns in order with their error fed forward inside
+// the block; a rank-32 update carries the block's errors to the batch's later columns,
+// and after the batch one rank-128 update carries the batch's errors to every column
+// after it (so the weights beyond the batch are read and written once per batch, not
+// once per block).  Group starts are block starts (every group size is a multiple of 32,
+// and 32, 64 and 128 divide the batch), so a group's grid is taken from columns that
+// have received every earlier error, as in the column-by-column order.  The group grid and the rounding are the round-to-nearest quantiser's
 // (binary64, round half to even, binary16 scale rounded up).
 #pragma once
 
@@ -22,6 +24,7 @@
 namespace w4a16 {
 
 constexpr int kGptqBlock = 32;
+constexpr int kGptqBatch = 128;
 
 #pragma clang fp contract(off)
 
@@ -145,11 +148,12 @@ __global__ __launch_bounds__(256) void gptq_trinv_finish_kernel(const double* __
 // Visited columns [i0, i0 + 32) of every row (thread per row): the group grid at a
 // group start (from the row's current values of the group's columns), else the one
 // kept in sz; then each column rounded in order, its error e = (w - q^) / U[j][j]
-// fed to the block's later columns and kept in err[n][c] for the update kernel.
+// fed to the block's later columns and kept in err[n * err_stride + c] for the updates.
 __global__ __launch_bounds__(128) void gptq_block_kernel(const double* __restrict__ wp,
                                                          const double* __restrict__ U, int N, int K, int i0,
                                                          int group_size, double2* __restrict__ sz,
-                                                         double* __restrict__ err, uint8_t* __restrict__ codes_p,
+                                                         double* __restrict__ err, int err_stride,
+                                                         uint8_t* __restrict__ codes_p,
                                                          uint16_t* __restrict__ scales,
                                                          uint8_t* __restrict__ zeros) {
   constexpr int B = kGptqBlock;
@@ -183,7 +187,7 @@ __global__ __launch_bounds__(128) void gptq_block_kernel(const double* __restric
     Z = v.y;
   }
   uint8_t* crow = codes_p + static_cast<size_t>(n) * K + i0;
-  double* erow = err + static_cast<size_t>(n) * B;
+  double* erow = err + static_cast<size_t>(n) * err_stride;
 #pragma unroll
   for (int c = 0; c < B; ++c) {
     const double q = fmin(fmax(rint(w[c] / S) + Z, 0.0), 15.0);
@@ -197,38 +201,44 @@ __global__ __launch_bounds__(128) void gptq_block_kernel(const double* __restric
 
 #pragma clang fp contract(on)
 
-// wp[n][k] -= sum_c err[n][c] U[i0 + c][k] for the columns k >= i0 + 32 (64 x 64 tiles,
-// grid: column tiles x row tiles).
+// wp[n][k] -= sum_c err[n * err_stride + c] U[i0 + c][k], c < rank (a multiple of 32), for
+// the columns k_begin <= k < k_end (64 x 64 tiles, grid: column tiles x row tiles).  The
+// rank is taken in chunks of 32 through LDS into the same accumulators, which are
+// subtracted from the weights once.
 __global__ __launch_bounds__(256) void gptq_update_kernel(double* __restrict__ wp, const double* __restrict__ U,
-                                                          const double* __restrict__ err, int N, int K, int i0) {
+                                                          const double* __restrict__ err, int err_stride, int N,
+                                                          int K, int i0, int rank, int k_begin, int k_end) {
   constexpr int B = kGptqBlock, TILE = 64;
   __shared__ double es[TILE][B + 1];
   __shared__ double us[B][TILE];
-  const int k0 = i0 + B + blockIdx.x * TILE;
+  const int k0 = k_begin + blockIdx.x * TILE;
   const int n0 = blockIdx.y * TILE;
   const int tid = threadIdx.x;
-  for (int e = tid; e < TILE * B; e += 256) {
-    const int r = e / B, c = e % B;
-    es[r][c] = n0 + r < N ? err[static_cast<size_t>(n0 + r) * B + c] : 0.0;
-  }
-  for (int e = tid; e < B * TILE; e += 256) {
-    const int c = e / TILE, j = e % TILE;
-    us[c][j] = k0 + j < K ? U[static_cast<size_t>(i0 + c) * K + k0 + j] : 0.0;
-  }
-  __syncthreads();
   const int tr = tid / 16, tc = tid % 16;
   double acc[4][4];
   for (int a = 0; a < 4; ++a)
     for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
-  for (int c = 0; c < B; ++c)
+  for (int c0 = 0; c0 < rank; c0 += B) {
+    for (int e = tid; e < TILE * B; e += 256) {
+      const int r = e / B, c = e % B;
+      es[r][c] = n0 + r < N ? err[static_cast<size_t>(n0 + r) * err_stride + c0 + c] : 0.0;
+    }
+    for (int e = tid; e < B * TILE; e += 256) {
+      const int c = e / TILE, j = e % TILE;
+      us[c][j] = k0 + j < k_end ? U[static_cast<size_t>(i0 + c0 + c) * K + k0 + j] : 0.0;
+    }
+    __syncthreads();
+    for (int c = 0; c < B; ++c)
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc[a][b] = fma(es[tr + 16 * a][c], us[c][tc + 16 * b], acc[a][b]);
+        for (int b = 0; b < 4; ++b) acc[a][b] = fma(es[tr + 16 * a][c], us[c][tc + 16 * b], acc[a][b]);
+    __syncthreads();
+  }
   for (int a = 0; a < 4; ++a)
     for (int b = 0; b < 4; ++b) {
       const int n = n0 + tr + 16 * a, k = k0 + tc + 16 * b;
-      if (n < N && k < K) wp[static_cast<size_t>(n) * K + k] -= acc[a][b];
+      if (n < N && k < k_end) wp[static_cast<size_t>(n) * K + k] -= acc[a][b];
     }
 }
 
