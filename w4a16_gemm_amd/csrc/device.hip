@@ -1007,7 +1007,8 @@ int w4a16_gptq(const uint16_t* w, const uint16_t* xcal, int N, int K, int T, int
   auto* ds = static_cast<uint16_t*>(alloc(static_cast<size_t>(G) * N * 2));
   auto* dz = static_cast<uint8_t*>(alloc(static_cast<size_t>(G) * N));
   auto* dflag = static_cast<int*>(alloc(sizeof(int)));
-  if (dev.size() != 14) return release(fail(W4A16_ERR_HIP, "hipMalloc failed for the GPTQ buffers"));
+  auto* ddg = static_cast<double*>(alloc(static_cast<size_t>(kGptqPivots) * kGptqPivots * 8));
+  if (dev.size() != 15) return release(fail(W4A16_ERR_HIP, "hipMalloc failed for the GPTQ buffers"));
   const int zero = 0;
   int flag = 0;
   auto copy = [&](void* dst, const void* src, size_t bytes, hipMemcpyKind kind) {
@@ -1026,11 +1027,30 @@ int w4a16_gptq(const uint16_t* w, const uint16_t* xcal, int N, int K, int T, int
   hipLaunchKernelGGL(gptq_gram_kernel, dim3(kt, kt), dim3(256), 0, st, dxp, T, K, dH);
   hipLaunchKernelGGL(gptq_damp_kernel, dim3(1), dim3(256), 0, st, dH, K, damp);
   if (int rc = check_launch("GPTQ Hessian launch")) return release(rc);
-  // H = Ut^T Ut from the bottom-right corner, then U = (Ut^T)^-1
-  for (int p = K - 1; p >= 1; --p) hipLaunchKernelGGL(gptq_chol_step_kernel, dim3(p), dim3(256), 0, st, dH, K, p);
+  // H = Ut^T Ut from the bottom-right corner, then U = (Ut^T)^-1; pivots in blocks of 64
+  // from the bottom (the same operations, in the same order per element, as one pivot
+  // at a time)
+  auto tiles = [](int n) { return (n + kGptqPivots - 1) / kGptqPivots; };
+  for (int p1 = K; p1 > 0;) {
+    const int p0 = std::max(0, p1 - kGptqPivots), bs = p1 - p0;
+    hipLaunchKernelGGL(gptq_chol_panel_kernel, dim3(static_cast<unsigned>(tiles(p0) + 1)), dim3(256), 0, st, dH, K, p0,
+                       bs, ddg);
+    const int nt = tiles(p0);
+    hipLaunchKernelGGL(gptq_chol_trail_kernel, dim3(static_cast<unsigned>(std::max(1, nt * (nt + 1) / 2))), dim3(256), 0,
+                       st, dH, K, p0, bs, ddg);
+    p1 = p0;
+  }
   hipLaunchKernelGGL(gptq_chol_finish_kernel, dim3(K), dim3(256), 0, st, dH, K, dflag);
   hipLaunchKernelGGL(gptq_eye_kernel, blocks(kk), dim3(256), 0, st, dU, K);
-  for (int p = K - 1; p >= 1; --p) hipLaunchKernelGGL(gptq_trinv_step_kernel, dim3(p), dim3(256), 0, st, dH, dU, K, p);
+  for (int p1 = K; p1 > 0;) {
+    const int p0 = std::max(0, p1 - kGptqPivots), bs = p1 - p0;
+    const unsigned ct = static_cast<unsigned>(tiles(K - p0));
+    hipLaunchKernelGGL(gptq_trinv_panel_kernel, dim3(ct), dim3(256), 0, st, dH, dU, K, p0, bs);
+    if (p0 > 0)
+      hipLaunchKernelGGL(gptq_trinv_trail_kernel, dim3(ct, static_cast<unsigned>(tiles(p0))), dim3(256), 0, st, dH,
+                         dU, K, p0, bs);
+    p1 = p0;
+  }
   hipLaunchKernelGGL(gptq_trinv_finish_kernel, dim3(K), dim3(256), 0, st, dH, dU, K);
   if (int rc = check_launch("GPTQ factorisation launch")) return release(rc);
   // rounding with error feedback, 32 visited columns at a time, 128 to a batch: the

@@ -5,8 +5,10 @@
 //
 // U without forming H^-1: factor H = Ut^T Ut from the bottom-right corner (Ut^T
 // upper), then U = (Ut^T)^-1, which is upper with a positive diagonal and satisfies
-// U^T U = H^-1, so it is the upper Cholesky factor of H^-1.  Both steps are one
-// launch per pivot (a rank-1 update of the rows above it); the matrices stay in HBM.
+// U^T U = H^-1, so it is the upper Cholesky factor of H^-1.  Both are eliminations from
+// the bottom, one pivot after the other (for each pivot p: every row r < p minus a
+// multiple of row p), run with the pivots in blocks of 64: the block's own rows in one
+// launch, the rows above it in another; the matrices stay in HBM.
 //
 // The rounding runs in blocks of 32 visited columns, four to a batch of 128: a thread
 // per output row rounds a block's columns in order with their error fed forward inside
@@ -87,19 +89,6 @@ __global__ __launch_bounds__(256) void gptq_damp_kernel(double* __restrict__ H, 
   for (int i = threadIdx.x; i < K; i += 256) H[static_cast<size_t>(i) * K + i] += add;
 }
 
-// Factorisation from the bottom-right corner, pivot p (grid: p workgroups, one per
-// row r < p): H[r][c] -= (H[p][r] / H[p][p]) H[p][c] for c <= r.  Only the lower
-// triangle is kept; H[p][r] stands for H[r][p].  A pivot that is not positive is
-// caught by the finishing kernel (the updates then carry non-finite values, within
-// the same bounds).
-__global__ __launch_bounds__(256) void gptq_chol_step_kernel(double* __restrict__ H, int K, int p) {
-  const int r = blockIdx.x;
-  const double* prow = H + static_cast<size_t>(p) * K;
-  const double f = prow[r] / prow[p];
-  double* row = H + static_cast<size_t>(r) * K;
-  for (int c = threadIdx.x; c <= r; c += 256) row[c] = row[c] - f * prow[c];
-}
-
 // Row p of the factor: Ut[p][r] = H[p][r] / sqrt(H[p][p]), r <= p, in place (grid: K).
 // flag <- 1 if a pivot is not a positive finite number.
 __global__ __launch_bounds__(256) void gptq_chol_finish_kernel(double* __restrict__ H, int K,
@@ -123,19 +112,6 @@ __global__ __launch_bounds__(256) void gptq_eye_kernel(double* __restrict__ X, i
   X[i] = (i / K == i % K) ? 1.0 : 0.0;
 }
 
-// Inverse of the upper factor V = Ut^T by row elimination from the bottom, pivot p
-// (grid: p workgroups, one per row r < p): X[r][c] -= (Ut[p][r] / Ut[p][p]) X[p][c],
-// c >= p.  Row p of X is only read here and rows r < p only written.
-__global__ __launch_bounds__(256) void gptq_trinv_step_kernel(const double* __restrict__ Ut,
-                                                              double* __restrict__ X, int K, int p) {
-  const int r = blockIdx.x;
-  const double* urow = Ut + static_cast<size_t>(p) * K;
-  const double f = urow[r] / urow[p];
-  double* row = X + static_cast<size_t>(r) * K;
-  const double* prow = X + static_cast<size_t>(p) * K;
-  for (int c = p + static_cast<int>(threadIdx.x); c < K; c += 256) row[c] = row[c] - f * prow[c];
-}
-
 // U[p][c] = X[p][c] / Ut[p][p], c >= p (grid: K).
 __global__ __launch_bounds__(256) void gptq_trinv_finish_kernel(const double* __restrict__ Ut,
                                                                 double* __restrict__ X, int K) {
@@ -143,6 +119,164 @@ __global__ __launch_bounds__(256) void gptq_trinv_finish_kernel(const double* __
   const double d = Ut[static_cast<size_t>(p) * K + p];
   double* row = X + static_cast<size_t>(p) * K;
   for (int c = p + static_cast<int>(threadIdx.x); c < K; c += 256) row[c] = row[c] / d;
+}
+
+// Blocked forms of the two eliminations, pivots taken 64 at a time from the bottom
+// (block P = [p0, p0 + bs)).  Every element receives the same operations in the same
+// order as it would one pivot at a time (for each pivot p of P, descending, one multiply
+// and one subtraction with that pivot's multiplier: the factorisation's H[p][r] / H[p][p]
+// applied to row p's entries c <= r, the inverse's Ut[p][r] / Ut[p][p] applied to row p's
+// entries c >= p), so the results are the same bits; the matrices are read and written
+// once per block instead of once per pivot.
+constexpr int kGptqPivots = 64;
+
+// Factorisation, the block's own rows: rows P of columns [c0, c0 + 64) (grid: one
+// workgroup per 64 columns below p0, plus one for the block's diagonal part).  Each
+// workgroup repeats the eliminations inside the diagonal part, which give the
+// multipliers; the diagonal part's result goes to dg[i][j] (64 x 64), not into H, whose
+// diagonal part the other workgroups of the launch are still reading.
+__global__ __launch_bounds__(256) void gptq_chol_panel_kernel(double* __restrict__ H, int K, int p0, int bs,
+                                                              double* __restrict__ dg) {
+  constexpr int B = kGptqPivots;
+  __shared__ double d[B][B];   // d[i][j] = H[p0 + i][p0 + j], j <= i
+  __shared__ double t[B][B];   // t[i][c] = H[p0 + i][c0 + c]
+  const int tid = threadIdx.x;
+  const int npan = (p0 + B - 1) / B;
+  const bool diag = static_cast<int>(blockIdx.x) == npan;
+  const int c0 = static_cast<int>(blockIdx.x) * B;
+  const int nc = diag ? 0 : min(B, p0 - c0);
+  for (int e = tid; e < B * B; e += 256) {
+    const int i = e / B, j = e % B;
+    d[i][j] = (i < bs && j <= i) ? H[static_cast<size_t>(p0 + i) * K + p0 + j] : 0.0;
+    t[i][j] = (i < bs && j < nc) ? H[static_cast<size_t>(p0 + i) * K + c0 + j] : 0.0;
+  }
+  __syncthreads();
+  for (int pi = bs - 1; pi >= 1; --pi) {
+    const double dp = d[pi][pi];
+    // rows ri < pi: the diagonal part (columns cj <= ri) and the panel columns
+    for (int e = tid; e < pi * B; e += 256) {
+      const int ri = e / B, cj = e % B;
+      const double f = d[pi][ri] / dp;
+      if (cj <= ri) d[ri][cj] = d[ri][cj] - f * d[pi][cj];
+      if (cj < nc) t[ri][cj] = t[ri][cj] - f * t[pi][cj];
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < B * B; e += 256) {
+    const int i = e / B, j = e % B;
+    if (diag) {
+      if (i < bs && j <= i) dg[i * B + j] = d[i][j];
+    } else if (i < bs && j < nc) {
+      H[static_cast<size_t>(p0 + i) * K + c0 + j] = t[i][j];
+    }
+  }
+}
+
+// Factorisation, the rows above the block: H[r][c] for c <= r < p0 (64 x 64 tiles of the
+// lower triangle, grid: tile pairs (tr >= tc) listed row by row, at least one), each
+// element updated by the block's pivots in descending order with the multiplier
+// H[p][r] / H[p][p] and row p's (final) entry H[p][c]; the pivots H[p][p] come from dg.
+// Workgroup 0 also writes the block's diagonal part from dg into H (nothing in this
+// launch reads it there).
+__global__ __launch_bounds__(256) void gptq_chol_trail_kernel(double* __restrict__ H, int K, int p0, int bs,
+                                                              const double* __restrict__ dg) {
+  constexpr int B = kGptqPivots;
+  if (blockIdx.x == 0)
+    for (int e = threadIdx.x; e < B * B; e += 256) {
+      const int i = e / B, j = e % B;
+      if (i < bs && j <= i) H[static_cast<size_t>(p0 + i) * K + p0 + j] = dg[i * B + j];
+    }
+  __shared__ double fr[B][B];   // fr[pi][r] = H[p0 + pi][r0 + r] / H[p0 + pi][p0 + pi]
+  __shared__ double hc[B][B];   // hc[pi][c] = H[p0 + pi][c0 + c]
+  int tr = static_cast<int>((sqrt(8.0 * blockIdx.x + 1.0) - 1.0) / 2.0);
+  while ((tr + 1) * (tr + 2) / 2 <= static_cast<int>(blockIdx.x)) ++tr;
+  while (tr * (tr + 1) / 2 > static_cast<int>(blockIdx.x)) --tr;
+  const int tc = static_cast<int>(blockIdx.x) - tr * (tr + 1) / 2;
+  const int r0 = tr * B, c0 = tc * B;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < B * B; e += 256) {
+    const int i = e / B, j = e % B;
+    const bool pin = i < bs;
+    const double* prow = H + static_cast<size_t>(p0 + (pin ? i : 0)) * K;
+    fr[i][j] = (pin && r0 + j < p0) ? prow[r0 + j] / dg[(pin ? i : 0) * (B + 1)] : 0.0;
+    hc[i][j] = (pin && c0 + j < p0) ? prow[c0 + j] : 0.0;
+  }
+  __syncthreads();
+  const int ty = tid / 16, tx = tid % 16;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int r = r0 + ty + 16 * a, c = c0 + tx + 16 * b;
+      if (r >= p0 || c > r) continue;
+      double v = H[static_cast<size_t>(r) * K + c];
+      for (int pi = bs - 1; pi >= 0; --pi) v = v - fr[pi][ty + 16 * a] * hc[pi][tx + 16 * b];
+      H[static_cast<size_t>(r) * K + c] = v;
+    }
+}
+
+// Inverse, the block's own rows: X[p0 + i][c] for the columns c of one 64-column tile at
+// or after p0 (grid: one workgroup per tile), with the block's multipliers Ut[p][r] /
+// Ut[p][p] and only the columns c >= p of each pivot row, as in the one-pivot step.
+__global__ __launch_bounds__(256) void gptq_trinv_panel_kernel(const double* __restrict__ Ut, double* __restrict__ X,
+                                                               int K, int p0, int bs) {
+  constexpr int B = kGptqPivots;
+  __shared__ double f[B][B];   // f[pi][ri] = Ut[p0 + pi][p0 + ri] / Ut[p0 + pi][p0 + pi]
+  __shared__ double t[B][B];   // t[i][c] = X[p0 + i][c0 + c]
+  const int tid = threadIdx.x;
+  const int c0 = p0 + static_cast<int>(blockIdx.x) * B;
+  const int nc = min(B, K - c0);
+  for (int e = tid; e < B * B; e += 256) {
+    const int i = e / B, j = e % B;
+    f[i][j] = (i < bs && j < i) ? Ut[static_cast<size_t>(p0 + i) * K + p0 + j] / Ut[static_cast<size_t>(p0 + i) * K + p0 + i]
+                                : 0.0;
+    t[i][j] = (i < bs && j < nc) ? X[static_cast<size_t>(p0 + i) * K + c0 + j] : 0.0;
+  }
+  __syncthreads();
+  for (int pi = bs - 1; pi >= 1; --pi) {
+    for (int e = tid; e < pi * B; e += 256) {
+      const int ri = e / B, cj = e % B;
+      if (cj < nc && c0 + cj >= p0 + pi) t[ri][cj] = t[ri][cj] - f[pi][ri] * t[pi][cj];
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < B * B; e += 256) {
+    const int i = e / B, j = e % B;
+    if (i < bs && j < nc) X[static_cast<size_t>(p0 + i) * K + c0 + j] = t[i][j];
+  }
+}
+
+// Inverse, the rows above the block: X[r][c] for r < p0 and c >= p0 (64 x 64 tiles, grid:
+// column tiles x row tiles), each element updated by the block's pivots in descending
+// order with Ut[p][r] / Ut[p][p] and row p's (final) entry X[p][c], for the pivots p <= c.
+__global__ __launch_bounds__(256) void gptq_trinv_trail_kernel(const double* __restrict__ Ut, double* __restrict__ X,
+                                                               int K, int p0, int bs) {
+  constexpr int B = kGptqPivots;
+  __shared__ double fr[B][B];   // fr[pi][r] = Ut[p0 + pi][r0 + r] / Ut[p0 + pi][p0 + pi]
+  __shared__ double xc[B][B];   // xc[pi][c] = X[p0 + pi][c0 + c]
+  const int c0 = p0 + static_cast<int>(blockIdx.x) * B;
+  const int r0 = static_cast<int>(blockIdx.y) * B;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < B * B; e += 256) {
+    const int i = e / B, j = e % B;
+    const bool pin = i < bs;
+    const double* urow = Ut + static_cast<size_t>(p0 + (pin ? i : 0)) * K;
+    fr[i][j] = (pin && r0 + j < p0) ? urow[r0 + j] / urow[p0 + i] : 0.0;
+    xc[i][j] = (pin && c0 + j < K) ? X[static_cast<size_t>(p0 + i) * K + c0 + j] : 0.0;
+  }
+  __syncthreads();
+  const int ty = tid / 16, tx = tid % 16;
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int r = r0 + ty + 16 * a, c = c0 + tx + 16 * b;
+      if (r >= p0 || c >= K) continue;
+      double v = X[static_cast<size_t>(r) * K + c];
+      for (int pi = bs - 1; pi >= 0; --pi)
+        if (c >= p0 + pi) v = v - fr[pi][ty + 16 * a] * xc[pi][tx + 16 * b];
+      X[static_cast<size_t>(r) * K + c] = v;
+    }
 }
 
 // Visited columns [i0, i0 + 32) of every row (thread per row): the group grid at a
