@@ -538,7 +538,7 @@ def gptq_bench(cfg: wl.LayerConfig):
         "wall_s": round(wall, 3),
         "output_error_gptq": round(out_err(codes, S, Z), 5),
         "output_error_rtn": round(out_err(rc, rs, rz), 5),
-        "note": "whole call: uploads, H = 2XX^T, factorisation and triangular inverse (one launch per pivot), "
+        "note": "whole call: uploads, H = 2XX^T, factorisation and triangular inverse (pivots in blocks of 64), "
                 "the blocked rounding with error feedback, downloads; output error ||(W - W^) X|| / ||W X|| "
                 "on the calibration rows (float32 on the host)",
     }
