@@ -222,9 +222,10 @@ int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales
  * launches and of the act-order gather comes from one fixed 16 MiB array in device
  * memory, a static copy per GPU (held until the process ends), instead of the growing
  * workspace.  The call allocates nothing, ever (its first call on a device resolves the
- * array's address there).  A call whose scratch would exceed 16 MiB (4 * ks * min(M, 16)
- * * N bytes for ks K slices, resp. 2 * M * K bytes under act order above 32 rows) is
- * refused with UNSUPPORTED before anything is launched.  Every call on a GPU shares that
+ * array's address there).  A call whose scratch would exceed 16 MiB (under act order
+ * with M > 1, 2 * M * K bytes of gathered activations; for a skinny batch whose K is split
+ * over ks slices, 4 * ks * min(M, 16) * N bytes more) is refused with UNSUPPORTED before
+ * anything is launched.  Every call on a GPU shares that
  * GPU's array: calls that may overlap on one GPU (different streams, or several host
  * threads) race on it and must be serialised by the caller; calls on one stream are
  * ordered and safe.  Errors as w4a16_gemm. */
@@ -338,7 +339,7 @@ int w8a16_unpack_zeros(const int32_t* qzeros, int G, int N, uint8_t* zeros);
 
 /* y = x * W^T for 8-bit weights, device memory, asynchronous on `stream`.  M == 1
  * runs the split-K GEMV (K <= 32768, at most 512 groups per row, N*K < 2^31), larger M
- * the skinny and tiled MFMA kernels (act order above 32 rows: x gathered into the
+ * the skinny and tiled MFMA kernels (act order at M > 1: x gathered into the
  * workspace first, which works as for w4a16_gemm).  qzeros NULL = symmetric.  Errors as
  * w4a16_gemm. */
 int w8a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,

@@ -107,7 +107,7 @@ void begin_call() {
 //
 // Two layer paths need device memory beyond x, the weights and y: the fp32 partial
 // tiles of skinny launches whose K is split over workgroups, and x gathered into the
-// stored channel order for act-order batches of more than 32 rows.  The entry point
+// stored channel order for act-order batches of more than one row.  The entry point
 // decides where it comes from; the kernels only see a pointer.
 using ScratchFn = int (*)(hipStream_t st, size_t bytes, void** out);
 
@@ -503,18 +503,18 @@ SkinnyShape pick_skinny_shape(int M, int K, int gshift, int bits = 4) {
 }
 
 // ks > 1: partial sums to part [ks][M][N] fp32, then sum_slices_kernel into y.
-template <int T, int SE, bool ACT, bool SUB, int BITS = 4>
+template <int T, int SE, bool SUB, int BITS = 4>
 int launch_skinny_t(const SkinnyShape& sh, hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s,
                     Zeros z, half_t* y, float* part, int M, int N, int K, int gshift) {
   static const hipError_t lds_ok =
-      hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_skinny_kernel<T, SE, ACT, SUB, BITS>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_skinny_kernel<T, SE, SUB, BITS>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   if (int rc = hip_status(lds_ok, "hipFuncSetAttribute")) return rc;
   const size_t lds = skinny_lds_bytes(sh.waves, groups_in(0, K / sh.ks, gshift));
   const int nblk = (N + 15) / 16;
   const int per_cu = std::max(1, 16 / sh.waves);
   const int per_slice = std::min(nblk, std::max(1, device_cus() * per_cu / sh.ks));
-  hipLaunchKernelGGL((gemm_skinny_kernel<T, SE, ACT, SUB, BITS>), dim3(per_slice * sh.ks), dim3(64 * sh.waves), lds, st, x,
+  hipLaunchKernelGGL((gemm_skinny_kernel<T, SE, SUB, BITS>), dim3(per_slice * sh.ks), dim3(64 * sh.waves), lds, st, x,
                      qw, s, z, y, part, M, N, K, gshift, sh.ks);
   if (int rc = check_launch("skinny gemm launch")) return rc;
   if (sh.ks == 1) return W4A16_OK;
@@ -524,13 +524,13 @@ int launch_skinny_t(const SkinnyShape& sh, hipStream_t st, const half_t* x, cons
   return check_launch("slice sum launch");
 }
 
-template <bool ACT, int BITS = 4>
+template <int BITS = 4>
 int launch_skinny(const SkinnyShape& sh, hipStream_t st, const half_t* x, const uint32_t* qw, const half_t* s,
                   Zeros z, half_t* y, float* part, int M, int N, int K, int gshift) {
 #define W4A16_SKINNY(T_, SE_)                                                                                    \
   if (sh.t == T_ && sh.se == SE_)                                                                              \
-    return gshift == 7 ? launch_skinny_t<T_, SE_, ACT, true, BITS>(sh, st, x, qw, s, z, y, part, M, N, K, gshift) \
-                       : launch_skinny_t<T_, SE_, ACT, false, BITS>(sh, st, x, qw, s, z, y, part, M, N, K, gshift);
+    return gshift == 7 ? launch_skinny_t<T_, SE_, true, BITS>(sh, st, x, qw, s, z, y, part, M, N, K, gshift) \
+                       : launch_skinny_t<T_, SE_, false, BITS>(sh, st, x, qw, s, z, y, part, M, N, K, gshift);
   W4A16_SKINNY(1, 1) W4A16_SKINNY(1, 2) W4A16_SKINNY(1, 4)
   W4A16_SKINNY(2, 1) W4A16_SKINNY(2, 2) W4A16_SKINNY(2, 4)
   if constexpr (BITS == 4) {
@@ -540,23 +540,36 @@ int launch_skinny(const SkinnyShape& sh, hipStream_t st, const half_t* x, const 
   return fail(W4A16_ERR_UNSUPPORTED, "no skinny kernel for T=%d SE=%d", sh.t, sh.se);
 }
 
-// The skinny kernel once per 16 rows of x and y; K slices keep their fp32 partial
-// tiles in stream-ordered scratch memory, reused by the launches of every 16 rows.
+// The skinny kernel once per 16 rows of x and y.  Scratch (one request, before anything
+// is launched): under act order x gathered into the stored channel order (2 M K bytes,
+// gather_x_kernel), then the K slices' fp32 partial tiles, reused by the launches of
+// every 16 rows.  Gathering inside the kernel instead (each lane's activations read
+// through the stored order) spilled its registers: on the act-order layer (K = 4096,
+// N = 11008, group 32) M = 2 / 4 / 16 took 19.7 / 22.9 / 42.2 us that way and
+// 12.9 / 13.0 / 15.4 us with the separate gather.
 template <int BITS>
 int run_skinny(const SkinnyShape& sk, bool act, hipStream_t st, const half_t* hx, const uint32_t* hq,
                const half_t* hs, Zeros hz, half_t* hy, int M, int N, int K, int gshift, ScratchFn scratch) {
-  float* part = nullptr;
-  if (sk.ks > 1) {
-    const size_t bytes = static_cast<size_t>(sk.ks) * std::min(M, kSkinnyMaxM) * N * sizeof(float);
-    if (int rc = scratch(st, bytes, reinterpret_cast<void**>(&part))) return rc;
+  const size_t xs_bytes = act ? (static_cast<size_t>(M) * K * sizeof(half_t) + 255) / 256 * 256 : 0;
+  const size_t part_bytes = sk.ks > 1 ? static_cast<size_t>(sk.ks) * std::min(M, kSkinnyMaxM) * N * sizeof(float) : 0;
+  unsigned char* base = nullptr;
+  if (xs_bytes + part_bytes > 0)
+    if (int rc = scratch(st, xs_bytes + part_bytes, reinterpret_cast<void**>(&base))) return rc;
+  float* part = part_bytes > 0 ? reinterpret_cast<float*>(base + xs_bytes) : nullptr;
+  const half_t* x = hx;
+  if (act) {
+    const auto* perm = reinterpret_cast<const int32_t*>(hq + static_cast<size_t>(N) * (K >> (BITS == 4 ? 3 : 2)));
+    auto* xs = reinterpret_cast<half_t*>(base);
+    hipLaunchKernelGGL(gather_x_kernel, dim3(static_cast<unsigned>((K / 8 + 255) / 256), std::min(M, kGatherRowsY)),
+                       dim3(256), 0, st, hx, perm, xs, M, K);
+    if (int rc = check_launch("gather launch")) return rc;
+    x = xs;
   }
   int rc = W4A16_OK;
   for (int m0 = 0; m0 < M && rc == W4A16_OK; m0 += kSkinnyMaxM) {
     const int mc = std::min(kSkinnyMaxM, M - m0);
-    const half_t* xc = hx + static_cast<size_t>(m0) * K;
-    half_t* yc = hy + static_cast<size_t>(m0) * N;
-    rc = act ? launch_skinny<true, BITS>(sk, st, xc, hq, hs, hz, yc, part, mc, N, K, gshift)
-             : launch_skinny<false, BITS>(sk, st, xc, hq, hs, hz, yc, part, mc, N, K, gshift);
+    rc = launch_skinny<BITS>(sk, st, x + static_cast<size_t>(m0) * K, hq, hs, hz, hy + static_cast<size_t>(m0) * N,
+                             part, mc, N, K, gshift);
   }
   return rc;
 }

@@ -26,8 +26,8 @@
 //    ks slices over the workgroups: the workgroups of slice s hold the activations of
 //    channels [s K / ks, (s + 1) K / ks) and write fp32 partial tiles, which a second
 //    kernel adds in slice order and rounds once.
-// Act order: the activation slice is gathered through the stored channel order
-// when it is loaded into registers, so no scratch copy of x is needed.
+// Act order: the caller gathers x into the stored channel order first (gather_x_kernel,
+// at most 32 rows), so the kernel always reads contiguous activations.
 #pragma once
 
 #include "nibbles.hpp"
@@ -73,7 +73,7 @@ constexpr size_t skinny_lds_bytes(int waves, int groups) {
 // of a step are 32 bytes (two loads), MFMA j takes words 2j and 2j + 1, SUB uses the
 // bytes as subnormals with both pairs of a word at weight 1 (no activation pre-scale),
 // and the zero points are bytes.
-template <int T, int SE, bool ACT, bool SUB, int BITS = 4>
+template <int T, int SE, bool SUB, int BITS = 4>
 __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
     const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const half_t* __restrict__ scales,
     Zeros qzeros, half_t* __restrict__ y, float* __restrict__ part, int M, int N, int K,
@@ -134,19 +134,11 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
   {
     const int m = lr < M ? lr : 0;
     const half_t* xm = x + static_cast<size_t>(m) * K;
-    const int32_t* perm = reinterpret_cast<const int32_t*>(qw + static_cast<size_t>(N) * Wd);
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int p0 = kw + 128 * t + 32 * lq + 8 * j;
-        half8_t v;
-        if constexpr (ACT) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = xm[perm[p0 + e]];
-        } else {
-          v = *reinterpret_cast<const half8_t*>(xm + p0);
-        }
+        const half8_t v = *reinterpret_cast<const half8_t*>(xm + kw + 128 * t + 32 * lq + 8 * j);
         xr[t][j] = lr < M ? v : half8_t{};
       }
     if constexpr (SUB) {
