@@ -54,6 +54,8 @@ def test_graph_replays_match_eager(name, cfg, M):
     assert err <= TOL, err
 
 
+# the refused call records nothing, so the captured graph is empty by design
+@pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")
 def test_capture_refuses_to_grow_the_workspace():
     import torch
     dev = device()

@@ -65,6 +65,8 @@ SMALL = [
     ("s30", 9, 136, 12288, 64, True),
     ("s31", 20, 72, 28672, 128, False),
     ("s32", 2, 40, 65536, 32, False),
+    # act order at 17..32 rows: x gathered once, the skinny kernel twice over it (16 + 7)
+    ("s33", 23, 264, 4096, 128, True),
 ]
 
 

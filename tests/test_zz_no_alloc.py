@@ -1,8 +1,10 @@
 """w4a16_gemm_noalloc (scratch from the library's fixed per-GPU array, no allocation)
 against w4a16_gemm (its growing workspace) through the C ABI: bit-identical outputs on
-two calls in a row, the second with a smaller input, for both paths that use scratch
-memory (act order above 32 rows; skinny batches with K split over workgroups), a path
-without scratch, and the refusal of a call whose scratch exceeds the array."""
+two calls in a row, the second with a smaller input, for the paths that use scratch
+memory (act order above one row, on the large-tile GEMM and on the skinny kernel; skinny
+batches with K split over workgroups; both at once, the gathered activations and the
+partial tiles in one request), a path without scratch, and the refusal of a call whose
+scratch exceeds the array."""
 
 import pytest
 
@@ -15,6 +17,9 @@ pytestmark = pytest.mark.gpu
 CASES = [
     # name, config, (M of the first call, M of the second)
     ("act-order c5", wl.CONFIGS["c5"], (512, 96)),
+    ("act-order skinny c5", wl.CONFIGS["c5"], (16, 3)),
+    ("act-order skinny split-K", wl.custom_config("na-act-splitk", 73, K=16384, N=2048, group_size=128,
+                                                   M_list=(16,), act_order=True), (16, 5)),
     ("skinny split-K", wl.custom_config("na-splitk", 71, K=16384, N=4096, group_size=128, M_list=(16,)), (16, 3)),
     ("decode GEMV (no scratch)", wl.CONFIGS["c3"], (1, 1)),
 ]
