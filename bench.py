@@ -111,12 +111,13 @@ def _amd_smi_clocks():
 def clocks_under_load(launch, sync, max_s: float = 20.0):
     """SCLK and MCLK while the timed work runs: the layer is launched back to back in
     batches of about 4 ms of device work (one synchronisation per batch, so the device
-    is rarely idle), and after 100 ms of that an amd-smi query runs in a thread while
-    the launches go on (not timed)."""
+    is rarely idle), and after 100 ms of that two amd-smi queries run one after the other
+    in a thread while the launches go on (not timed); the second reading is reported."""
     import threading
     box = {}
 
-    def query():
+    def query():   # two readings, the second kept: the first can still average in idle time
+        _amd_smi_clocks()
         box["clk"] = _amd_smi_clocks()
     t0 = time.perf_counter()
     for _ in range(8):
@@ -437,15 +438,23 @@ def decode_step_bench(step: wl.DecodeStep, steps: int = 100, warmup: int = 10):
     with torch.cuda.graph(graph):
         one_step()
     graph_us = region(graph.replay, steps)
+    # each shape alone: its launches over the layers' distinct weights as one graph, so
+    # that the host's launch rate does not enter the per-launch time
     per_linear = {}
     for sh in shapes:
-        st = torch.cuda.current_stream(dev).cuda_stream
-        counter = [0]
-
-        def one():
-            call(sh, counter[0] % step.layers, st)
-            counter[0] += 1
-        us = region(one, 4 * step.layers)
+        def shape_layers(sh=sh):
+            st = torch.cuda.current_stream(dev).cuda_stream
+            for layer in range(step.layers):
+                call(sh, layer, st)
+        g1 = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            shape_layers()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g1):
+            shape_layers()
+        us = region(g1.replay, max(4, steps // 4)) / step.layers
+        del g1
         per_linear[sh["name"]] = {"K": sh["K"], "N": sh["N"], "us": round(us, 3),
                                   "GBps": round(sh["bytes"] / us / 1e3, 1)}
     step_bytes = step.layers * sum(sh["bytes"] for sh in shapes)
