@@ -111,14 +111,24 @@ def _amd_smi_clocks():
 def clocks_under_load(launch, sync, max_s: float = 20.0):
     """SCLK and MCLK while the timed work runs: the layer is launched back to back in
     batches of about 4 ms of device work (one synchronisation per batch, so the device
-    is rarely idle), and after 100 ms of that two amd-smi queries run one after the other
-    in a thread while the launches go on (not timed); the second reading is reported."""
+    is rarely idle), and after 100 ms of that amd-smi queries run one after the other in a
+    thread while the launches go on (not timed), until two consecutive readings agree."""
     import threading
     box = {}
 
-    def query():   # two readings, the second kept: the first can still average in idle time
-        _amd_smi_clocks()
-        box["clk"] = _amd_smi_clocks()
+    def query():
+        # the tool's reading can lag (a reading taken early in the process has come back at
+        # an idle-like 150-200 MHz while the launches ran): read until two consecutive
+        # readings agree within 3% (at most five), and keep the last
+        prev = None
+        for _ in range(5):
+            clk = _amd_smi_clocks()
+            box["clk"] = clk
+            if not clk or clk[0] is None:
+                return
+            if prev is not None and abs(clk[0] - prev) <= 0.03 * max(clk[0], prev):
+                return
+            prev = clk[0]
     t0 = time.perf_counter()
     for _ in range(8):
         launch(0)
@@ -487,6 +497,32 @@ def decode_step_bench(step: wl.DecodeStep, steps: int = 100, warmup: int = 10):
     }
 
 
+def shards_bench(head_us: float, prefill_us):
+    """One GPU's share of the layers under tensor parallelism, at its real shape (the
+    layer shards without any exchange when split by output rows; the down projection of
+    the same MLP splits by input channels, whole groups per GPU, and its partial outputs
+    would be summed by one all-reduce, which is not run here).  Each share is timed like
+    a secondary layer; `ideal_us` is the full layer's time divided by the degree."""
+    import torch
+    c3, c4 = wl.CONFIGS["c3"], wl.CONFIGS["c4"]
+    cases = [("c3 up, column-parallel", c3, 1, c3.K, c3.N // p, p, head_us) for p in (2, 4, 8)]
+    if prefill_us:
+        cases.append(("c4 prefill, column-parallel", c4, 2048, c4.K, c4.N // 8, 8, prefill_us))
+    cases += [("70B-class down (K=28672, N=8192), row-parallel", c3, 1, 28672 // p, 8192, p, None) for p in (8,)]
+    out = []
+    for i, (what, base, M, K, N, p, full_us) in enumerate(cases):
+        cfg = wl.custom_config(f"shard{i}", 500 + i, K=K, N=N, group_size=base.group_size, M_list=(M,))
+        layer = prepare_layer(cfg, M)
+        t = time_layer(cfg, M, layer, SECONDARY_STEPS, SECONDARY_WARMUP, sample_clocks=False)
+        r = summarize(cfg, M, t)
+        out.append({"shard": what, "degree": p, "M": M, "K": K, "N": N, "us": r["us_per_layer"],
+                    "GBps": r["GBps"], "TFLOPs": r["TFLOPs"],
+                    "ideal_us": round(full_us / p, 3) if full_us else None})
+        del layer
+        torch.cuda.empty_cache()
+    return out
+
+
 def awq_search_bench(cfg: wl.LayerConfig, n_alpha: int = 11):
     """The AWQ alpha search on one layer with its calibration activations: wall time of
     the whole search and the device time of one candidate's W4A16 GEMM at M = T (the
@@ -777,6 +813,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense-ref", action="store_true",
                     help="skip timing the dense binary16 library GEMM of the same shapes")
+    ap.add_argument("--no-shards", action="store_true",
+                    help="skip timing one GPU's share of the layers under tensor parallelism")
     ap.add_argument("--no-awq-search", action="store_true", help="skip timing the AWQ alpha search")
     ap.add_argument("--no-gptq", action="store_true", help="skip timing the GPTQ quantiser")
     ap.add_argument("--no-decode-step", action="store_true",
@@ -935,6 +973,9 @@ def main() -> int:
     if not args.no_decode_step and args.configs in ("all", "headline"):
         log("timing the decode step of the 1.5B example (eager and graph replay)")
         line["decode_step"] = decode_step_bench(wl.DECODE_1P5B)
+    if not args.no_shards and args.configs in ("all", "headline"):
+        log("timing one GPU's share of the up-projection and the prefill under tensor parallelism")
+        line["shards"] = shards_bench(head["region_us_per_step"], pre["us_per_layer"] if pre else None)
     if not args.no_awq_search and args.configs in ("all", "headline"):
         log("timing the AWQ alpha search on the c2 up-projection layer")
         line["awq_search"] = awq_search_bench(wl.CONFIGS["c2up"])
