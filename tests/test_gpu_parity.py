@@ -194,6 +194,23 @@ def test_large_tile_kinds_match_oracle(mb, mfma32):
             clear_knob(v)
 
 
+def test_large_tile_full_rounds_then_a_round_of_narrow_tiles():
+    """More than two rounds of full-width tiles: on 256 compute units, 4 row panels x 144
+    column tiles of 256 x 256 = 576 tiles run as two rounds of full tiles (columns
+    [0, 32768)) and one round of 256 x 64 tiles (the last 4096 columns), every output
+    written (NaN-filled y) and within the bar of the oracle."""
+    import torch
+    cfg = wl.custom_config("r1", 380, K=256, N=36864, group_size=128, M_list=(1024,))
+    note(f"full rounds then narrow tiles M=1024 N={cfg.N} K={cfg.K}")
+    prod = product_layer(cfg, 1024)
+    ref = oracle_layer(cfg, 1024, np.arange(cfg.N))
+    y = torch.full((1024, cfg.N), float("nan"), dtype=torch.float16, device=device())
+    run_gemm(prod, y=y)
+    out = y.cpu().numpy()
+    assert not np.isnan(out).any(), "outputs left unwritten"
+    assert oracle.rel_err(out, ref["y_ref"]) <= TOL
+
+
 def test_dequantise_once_tile_matches_the_large_tile():
     # 256-row tiles whose codes are dequantised once per workgroup into a binary16 weight
     # tile in LDS (W4A16_TUNE_GEMM_LDSB=1): the same operands in the same MFMA order as the

@@ -53,7 +53,7 @@ struct Knobs {
   int gemv_pre = 1;             // W4A16_TUNE_GEMV_PRE: stage all scales once (0 never, 1 when it fits)
   int gemm_prio = 1;            // W4A16_TUNE_GEMM_PRIO: wavefront priority in the large tiles
   int gemm_mfma32 = 1;          // W4A16_TUNE_GEMM_MFMA32: 32x32 blocks (0 never, 1 small tiles, 2 all)
-  int gemm_split = 1;           // W4A16_TUNE_GEMM_SPLIT: two tile widths per launch
+  int gemm_split = 2;           // W4A16_TUNE_GEMM_SPLIT: two tile widths per launch (1: only within two rounds)
   int gemm_ldsb = 0;            // W4A16_TUNE_GEMM_LDSB: 256-row tiles dequantised once into LDS
   int gemm_big_mb = 0;          // W4A16_TUNE_GEMM_BIG_MB: forced row blocks per wavefront (0 = auto)
   int gemm_big_min_m = 0;       // W4A16_TUNE_GEMM_BIG_MIN_M (0 = default)
@@ -73,7 +73,7 @@ Knobs read_knobs() {
   k.gemv_pre = env_int("W4A16_TUNE_GEMV_PRE", 1);
   k.gemm_prio = env_int("W4A16_TUNE_GEMM_PRIO", 1);
   k.gemm_mfma32 = env_int("W4A16_TUNE_GEMM_MFMA32", 1);
-  k.gemm_split = env_int("W4A16_TUNE_GEMM_SPLIT", 1);
+  k.gemm_split = env_int("W4A16_TUNE_GEMM_SPLIT", 2);
   k.gemm_ldsb = env_int("W4A16_TUNE_GEMM_LDSB", 0);
   k.gemm_big_mb = env_int("W4A16_TUNE_GEMM_BIG_MB", 0);
   k.gemm_big_min_m = env_int("W4A16_TUNE_GEMM_BIG_MIN_M", 0);
@@ -576,11 +576,14 @@ int run_skinny(const SkinnyShape& sk, bool act, hipStream_t st, const half_t* hx
 
 
 // Large-M GEMM.  BM x 256 tiles (BM = 256 rows; 128 or 64 when the whole batch fits in
-// fewer rows, so that small batches do not pay for padding rows), except (a) when they
-// would need more than one but less than two rounds of workgroups over the compute
-// units: then one round of full-width tiles covers the first columns and one round of
-// narrower tiles (64 NB2 wide) the rest, so that neither round leaves compute units
-// idle; (b) when they would not fill one round: then narrower tiles for all columns.
+// fewer rows, so that small batches do not pay for padding rows), except (a) when the
+// last round of workgroups over the compute units would be partly idle: then whole
+// rounds of full-width tiles cover the first columns and one round of narrower tiles
+// (64 NB2 wide) the rest, so that no round leaves compute units idle (the 2048-row
+// prefill: one round of each; 4096 rows, K = 4096, N = 14336: three rounds of full tiles
+// and one of 256 x 128, 468.8 -> 440.1 us against 3.5 rounds of full tiles, same-process
+// A/B; W4A16_TUNE_GEMM_SPLIT=1 splits only within two rounds); (b) when they would not
+// fill one round: then narrower tiles for all columns.
 // Wavefronts raise their priority (s_setprio 1) for each MFMA cluster and drop it after
 // (W4A16_TUNE_GEMM_PRIO=0: off), so that the two wavefronts of a SIMD drift into opposite
 // phases, one issuing MFMAs while the other reads LDS and dequantises.  Same-process A/B
@@ -626,13 +629,14 @@ int run_gemm_big_t(hipStream_t st, const half_t* x, const uint32_t* qw, const ha
   const int tiles_m = (M + BM - 1) / BM;
   const int cus = device_cus();
   const int full = tiles_m * ((N + 255) / 256);
-  if (full > cus && full < 2 * cus && cus % tiles_m == 0 && knobs().gemm_split != 0) {
-    const int per_panel = cus / tiles_m;
-    const int n_split = 256 * per_panel;
+  if (full > cus && cus % tiles_m == 0 && knobs().gemm_split != 0) {
+    const int per_panel = cus / tiles_m;                        // column tiles per row panel and round
+    const int rounds = full <= 2 * cus || knobs().gemm_split == 1 ? 1 : ((N + 255) / 256) / per_panel;
+    const int n_split = 256 * per_panel * rounds;
     const int rest = N - n_split;
     const int nb2 = (((rest + per_panel - 1) / per_panel) + 63) / 64;   // 64-column blocks per narrow tile
     if (rest > 0 && nb2 >= 1 && nb2 <= 3) {
-      const int split = tiles_m * per_panel;
+      const int split = tiles_m * per_panel * rounds;   // full-width tiles: columns [0, n_split)
       const int grid = split + tiles_m * ((rest + 64 * nb2 - 1) / (64 * nb2));
       if (nb2 == 1) return launch_big<1, MB, BITS>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
       if (nb2 == 2) return launch_big<2, MB, BITS>(st, x, qw, s, z, y, M, N, K, gshift, split, n_split, grid);
@@ -658,11 +662,12 @@ long long big_work_per_cu(int MB, int M, int N, int cus) {
   const long long BM = 32LL * MB;
   const int tiles_m = static_cast<int>((M + BM - 1) / BM);
   const int full = tiles_m * ((N + 255) / 256);
-  if (full > cus && full < 2 * cus && cus % tiles_m == 0) {
+  if (full > cus && cus % tiles_m == 0) {
     const int per_panel = cus / tiles_m;
-    const int rest = N - 256 * per_panel;
+    const int rounds = full <= 2 * cus || knobs().gemm_split == 1 ? 1 : ((N + 255) / 256) / per_panel;
+    const int rest = N - 256 * per_panel * rounds;
     const int nb2 = (((rest + per_panel - 1) / per_panel) + 63) / 64;
-    if (rest > 0 && nb2 >= 1 && nb2 <= 3) return BM * 256 + BM * 64 * nb2;
+    if (rest > 0 && nb2 >= 1 && nb2 <= 3) return rounds * BM * 256 + BM * 64 * nb2;
   }
   if (full < cus)
     for (int nb : {2, 3})
