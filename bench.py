@@ -111,22 +111,23 @@ def _amd_smi_clocks():
 def clocks_under_load(launch, sync, max_s: float = 20.0):
     """SCLK and MCLK while the timed work runs: the layer is launched back to back in
     batches of about 4 ms of device work (one synchronisation per batch, so the device
-    is rarely idle), and after 100 ms of that amd-smi queries run one after the other in a
+    is rarely idle), and after 1 s of that amd-smi queries run one after the other in a
     thread while the launches go on (not timed), until two consecutive readings agree."""
     import threading
     box = {}
 
     def query():
-        # the tool's reading can lag (a reading taken early in the process has come back at
-        # an idle-like 150-200 MHz while the launches ran): read until two consecutive
-        # readings agree within 3% (at most five), and keep the last
+        # the tool's reading averages over a window that can still hold the idle time
+        # before the launches (after seconds of host-side layer preparation the first
+        # layer's readings came back at an idle-like 150-200 MHz): at least three readings,
+        # then until two consecutive ones agree within 3% (at most six); the last is kept
         prev = None
-        for _ in range(5):
+        for i in range(6):
             clk = _amd_smi_clocks()
             box["clk"] = clk
             if not clk or clk[0] is None:
                 return
-            if prev is not None and abs(clk[0] - prev) <= 0.03 * max(clk[0], prev):
+            if i >= 2 and abs(clk[0] - prev) <= 0.03 * max(clk[0], prev):
                 return
             prev = clk[0]
     t0 = time.perf_counter()
@@ -143,7 +144,7 @@ def clocks_under_load(launch, sync, max_s: float = 20.0):
             launch(i)
             i += 1
         sync()
-        if th.ident is None and time.perf_counter() - t0 > 0.1:
+        if th.ident is None and time.perf_counter() - t0 > 1.0:
             th.start()
     if th.ident is not None:
         th.join()

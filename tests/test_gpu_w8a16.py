@@ -172,3 +172,19 @@ def test_w8a16_prefill_layer_on_sampled_rows():
     run_gemm(prod, y=y)
     assert not bool(torch.isnan(y).any())
     assert oracle.rel_err(y.cpu().numpy()[:, rows], ref["y_ref"]) <= TOL
+
+
+def test_w8a16_full_rounds_then_a_round_of_narrow_tiles():
+    """8-bit weights on the tile plan with more than two rounds of full-width tiles (on 256
+    compute units: two rounds of 256 x 256 tiles over columns [0, 32768), then one round of
+    256 x 64 tiles): every output written and within the bar of the oracle."""
+    import torch
+    cfg = wl.custom_config("h9", 690, K=256, N=36864, group_size=128, M_list=(1024,), bits=8)
+    note(f"8-bit full rounds then narrow tiles M=1024 N={cfg.N} K={cfg.K}")
+    prod = product_layer(cfg, 1024)
+    ref = oracle_layer(cfg, 1024, np.arange(cfg.N))
+    y = torch.full((1024, cfg.N), float("nan"), dtype=torch.float16, device=prod["x"].device)
+    run_gemm(prod, y=y)
+    out = y.cpu().numpy()
+    assert not np.isnan(out).any(), "outputs left unwritten"
+    assert oracle.rel_err(out, ref["y_ref"]) <= TOL
