@@ -210,7 +210,8 @@ int w4a16_unpack_zeros(const int32_t* qzeros, int G, int N, uint8_t* zeros);
  * Environment (read when the library is loaded and by w4a16_reload_env, never per call):
  * W4A16_DEBUG_CHECKS=1 also validates g_idx (synchronous copy); W4A16_FORCE_PATH=gemv|gemm
  * selects a kernel family (for tests); W4A16_TUNE_* switches force other kernels or tile
- * shapes (parity coverage and measurements only).
+ * shapes (parity coverage and measurements only).  W4A16_FORCE_PATH and W4A16_TUNE_* are
+ * ignored unless W4A16_TUNE=1 is set too.
  * Errors: INVALID_ARG, UNSUPPORTED, MISALIGNED, BAD_GIDX (debug only), HIP. */
 int w4a16_gemm(const uint16_t* x, const int32_t* qweight, const uint16_t* scales,
                const int32_t* qzeros, const int32_t* g_idx, int group_size, int M, int N,

@@ -29,6 +29,7 @@ def set_knob(name: str, value) -> None:
     """Set a W4A16_* environment switch and have the library read the switches again
     (it reads them once, not per call)."""
     os.environ[name] = str(value)
+    os.environ["W4A16_TUNE"] = "1"   # the library honours the switches only with this opt-in
     w4.w4a16_reload_env()
 
 

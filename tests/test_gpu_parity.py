@@ -211,6 +211,32 @@ def test_large_tile_full_rounds_then_a_round_of_narrow_tiles():
     assert oracle.rel_err(out, ref["y_ref"]) <= TOL
 
 
+def test_kernel_switches_need_the_opt_in():
+    """W4A16_FORCE_PATH (like every W4A16_TUNE_* switch) is ignored unless W4A16_TUNE=1:
+    without the opt-in a batch of one runs the decode GEMV (bit-identical to the default),
+    with it the MFMA GEMM (a different summation order: some outputs differ in their last
+    bits, all within the bar)."""
+    import os
+    cfg = wl.custom_config("k1", 390, K=4096, N=1032, group_size=128, M_list=(1,))
+    prod = product_layer(cfg, 1)
+    ref = oracle_layer(cfg, 1, np.arange(cfg.N))
+    try:
+        clear_knob("W4A16_FORCE_PATH")
+        y_default = run_gemm(prod).cpu().numpy()
+        os.environ.pop("W4A16_TUNE", None)
+        os.environ["W4A16_FORCE_PATH"] = "gemm"
+        w4.w4a16_reload_env()
+        y_ignored = run_gemm(prod).cpu().numpy()
+        set_knob("W4A16_FORCE_PATH", "gemm")   # sets the opt-in as well
+        y_forced = run_gemm(prod).cpu().numpy()
+    finally:
+        clear_knob("W4A16_FORCE_PATH")
+    assert np.array_equal(y_ignored.view(np.uint16), y_default.view(np.uint16))
+    assert not np.array_equal(y_forced.view(np.uint16), y_default.view(np.uint16))
+    for y in (y_default, y_forced):
+        assert oracle.rel_err(y, ref["y_ref"]) <= TOL
+
+
 def test_dequantise_once_tile_matches_the_large_tile():
     # 256-row tiles whose codes are dequantised once per workgroup into a binary16 weight
     # tile in LDS (W4A16_TUNE_GEMM_LDSB=1): the same operands in the same MFMA order as the

@@ -62,9 +62,13 @@ struct Knobs {
   int gemm_skinny = 1;          // W4A16_TUNE_GEMM_SKINNY: skinny kernel allowed
 };
 
+// The kernel-choice switches (W4A16_FORCE_PATH, W4A16_TUNE_*) are honoured only when
+// W4A16_TUNE=1 is set as well, so that a stray variable in a serving environment cannot
+// change which kernels run; W4A16_DEBUG_CHECKS only adds checks and needs no opt-in.
 Knobs read_knobs() {
   Knobs k;
   k.debug_checks = env_int("W4A16_DEBUG_CHECKS", 0);
+  if (env_int("W4A16_TUNE", 0) != 1) return k;
   const char* v = std::getenv("W4A16_FORCE_PATH");
   if (v && std::strcmp(v, "gemv") == 0) k.force_path = Path::kGemv;
   if (v && std::strcmp(v, "gemm") == 0) k.force_path = Path::kGemm;
