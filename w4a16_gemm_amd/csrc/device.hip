@@ -51,6 +51,7 @@ struct Knobs {
   int gemv_lpr = 0;             // W4A16_TUNE_GEMV_LPR: lanes per row of the GEMV
   int gemv_blocks_per_cu = 1;   // W4A16_TUNE_GEMV_BLOCKS_PER_CU
   int gemv_pre = 1;             // W4A16_TUNE_GEMV_PRE: stage all scales once (0 never, 1 when it fits)
+  int gemv_early = 1;           // W4A16_TUNE_GEMV_EARLY: first rows' dot products before the staging barrier
   int gemm_prio = 1;            // W4A16_TUNE_GEMM_PRIO: wavefront priority in the large tiles
   int gemm_mfma32 = 1;          // W4A16_TUNE_GEMM_MFMA32: 32x32 blocks (0 never, 1 small tiles, 2 all)
   int gemm_split = 2;           // W4A16_TUNE_GEMM_SPLIT: two tile widths per launch (1: only within two rounds)
@@ -75,6 +76,7 @@ Knobs read_knobs() {
   k.gemv_lpr = env_int("W4A16_TUNE_GEMV_LPR", 0);
   k.gemv_blocks_per_cu = env_int("W4A16_TUNE_GEMV_BLOCKS_PER_CU", 1);
   k.gemv_pre = env_int("W4A16_TUNE_GEMV_PRE", 1);
+  k.gemv_early = env_int("W4A16_TUNE_GEMV_EARLY", 1);
   k.gemm_prio = env_int("W4A16_TUNE_GEMM_PRIO", 1);
   k.gemm_mfma32 = env_int("W4A16_TUNE_GEMM_MFMA32", 1);
   k.gemm_split = env_int("W4A16_TUNE_GEMM_SPLIT", 2);
@@ -293,7 +295,8 @@ int launch_gemv_e(dim3 grid, size_t shmem, hipStream_t st, const half_t* x, cons
                                                        static_cast<int>(kGemvLdsBudget));
   if (shmem > 64 * 1024)
     if (int rc = hip_status(lds_ok, "hipFuncSetAttribute")) return rc;
-  hipLaunchKernelGGL(kern, grid, dim3(kGemvWaves * 64), shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+  hipLaunchKernelGGL(kern, grid, dim3(kGemvWaves * 64), shmem, st, x, qw, s, z, y, N, K, gshift, steps,
+                     knobs().gemv_early != 0 ? 1 : 0);
   return check_launch("gemv launch");
 }
 

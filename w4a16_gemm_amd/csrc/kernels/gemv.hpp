@@ -94,12 +94,15 @@ __device__ __forceinline__ float lane_group_sum(float v) {
 // rows are one contiguous run, so the whole grid reads the scale and zero-point arrays
 // front to back in a burst at the start instead of as scattered pieces between the code
 // streams of every step.  The rows then run without a barrier.  LDS: steps * STRIDE *
-// (G + 1) float2 instead of the ring.
+// (G + 1) float2 instead of the ring.  Without act order and with at least 2 DEPTH
+// steps (flags bit 0), the dot products of the first DEPTH rows are taken before the
+// staging barrier and their register slots refilled at once; their scaling follows the
+// barrier (the same operations in the same order, so the same bits).
 template <int LPR, int CPL, int WAVES, int DEPTH, bool EXACT, bool ACT, int EPT, int WPR, int BITS = 4,
           bool PRE = false>
 __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
     const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
-    Zeros qzeros, half_t* __restrict__ y, int N, int K, int gshift, int steps) {
+    Zeros qzeros, half_t* __restrict__ y, int N, int K, int gshift, int steps, int flags) {
   static_assert(64 % LPR == 0, "lanes per row must divide the wavefront");
   static_assert(DEPTH % 2 == 0, "the ring slot of row t is t % 2, the unrolled slot index");
   static_assert(WPR == 1 || (LPR == 64 && WAVES % WPR == 0 && WPR % DEPTH == 0),
@@ -318,57 +321,30 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
                         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, g[u][3])) << 16)};
     }
   }
-  if constexpr (PRE) {
-    for (int round = 0; round < pre_rounds; ++round) {
-      if (round > 0) pre_load(round);
-      pre_put(round);
-    }
-  } else {
-    put_item(0, 0);
-  }
-  __syncthreads();
-  if constexpr (ACT) {
+  // 3. this lane's activations as pairs (without act order straight from the loaded
+  // registers, before the barrier; under act order from LDS after it), and the
+  // per-chunk sums (dot2 with ones); chunks past the end of the row (inexact split)
+  // contribute nothing.
+  half2_t xr[CPL][XP];
+  float xsum[CPL];
+  auto build_xr = [&]() {
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
 #pragma unroll
-      for (int q = 0; q < XQ; ++q) xv[i][q] = reinterpret_cast<const uint4*>(xs)[XQ * chunk[i] + q];
-  }
-
-  // 3. this lane's activations as pairs, and the per-chunk sums (dot2 with ones);
-  // chunks past the end of the row (inexact split) contribute nothing.
-  half2_t xr[CPL][XP];
-  float xsum[CPL];
-  const half2_t ones = half2_t{static_cast<half_t>(1.0f), static_cast<half_t>(1.0f)};
-#pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    float sx = 0.f;
-#pragma unroll
-    for (int q = 0; q < XQ; ++q) {
-      const uint4 v = xv[i][q];
-      xr[i][4 * q + 0] = live[i] ? as_h2(v.x) : half2_t{0, 0};
-      xr[i][4 * q + 1] = live[i] ? as_h2(v.y) : half2_t{0, 0};
-      xr[i][4 * q + 2] = live[i] ? as_h2(v.z) : half2_t{0, 0};
-      xr[i][4 * q + 3] = live[i] ? as_h2(v.w) : half2_t{0, 0};
-    }
-#pragma unroll
-    for (int q = 0; q < XP; ++q) sx = __builtin_amdgcn_fdot2(xr[i][q], ones, sx, false);
-    xsum[i] = sx;
-  }
-
-  // 4. rows.  Row t sits in register slot t % DEPTH; its codes were requested DEPTH
-  // steps earlier, its staging items two steps earlier into set t % 2, and they were
-  // published into ring slot t % 2 by the barrier closing step t - 1.  Every step
-  // (a) requests the items of step t + 2, (b) computes row t and refills its slot,
-  // (c) stages step t + 1 and closes with the barrier.  The last DEPTH steps run
-  // without code refills, so no load is issued past the end.
-  auto row_step = [&](int slot, int row, uint4 (&w)[CPL]) {
-    const float2* szr = ring + (slot * STRIDE + row) * GP;
-    float2 sc[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i) sc[i] = szr[gcol[i]];
+      for (int q = 0; q < XQ; ++q) {
+        const uint4 v = xv[i][q];
+        xr[i][4 * q + 0] = live[i] ? as_h2(v.x) : half2_t{0, 0};
+        xr[i][4 * q + 1] = live[i] ? as_h2(v.y) : half2_t{0, 0};
+        xr[i][4 * q + 2] = live[i] ? as_h2(v.z) : half2_t{0, 0};
+        xr[i][4 * q + 3] = live[i] ? as_h2(v.w) : half2_t{0, 0};
+      }
+  };
+  // A row in two parts: the dot products of its codes with the activations (aa: pairs
+  // from the low nibbles, ab: from the high ones), which need neither the staged scales
+  // nor a barrier, and the scaling by the row's (S * 2^24, -Z * S) pairs.
+  auto row_dots = [&](uint4 (&w)[CPL], float (&aa)[CPL], float (&ab)[CPL]) {
     // The CPL chunks are interleaved word by word: 2*CPL independent dot2
     // accumulation chains (each still summed in the same order).
-    float aa[CPL], ab[CPL];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       aa[i] = 0.f;
@@ -391,6 +367,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
         }
       }
     }
+  };
+  auto row_finish = [&](int slot, int row, const float (&aa)[CPL], const float (&ab)[CPL]) {
+    const float2* szr = ring + (slot * STRIDE + row) * GP;
+    float2 sc[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) sc[i] = szr[gcol[i]];
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
@@ -400,6 +382,61 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
     }
     return acc;
   };
+  auto row_step = [&](int slot, int row, uint4 (&w)[CPL]) {
+    float aa[CPL], ab[CPL];
+    row_dots(w, aa, ab);
+    return row_finish(slot, row, aa, ab);
+  };
+
+  if constexpr (!ACT) build_xr();
+  if constexpr (PRE) {
+    for (int round = 0; round < pre_rounds; ++round) {
+      if (round > 0) pre_load(round);
+      pre_put(round);
+    }
+  } else {
+    put_item(0, 0);
+  }
+  // PRE without act order, at least 2 DEPTH rows per wavefront (flags bit 0): the first
+  // DEPTH rows' dot products are taken before the barrier and their register slots
+  // refilled with the next rows at once, so the second round of requests does not wait
+  // for the staging, the barrier and the activation sums.
+  float pa[DEPTH][CPL], pb[DEPTH][CPL];
+  bool early = false;
+  if constexpr (PRE && !ACT) {
+    early = (flags & 1) != 0 && steps >= 2 * DEPTH;
+    if (early) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        row_dots(wb[d], pa[d], pb[d]);
+        load_row(wb[d], row_of(d + DEPTH));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __syncthreads();
+  if constexpr (ACT) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+#pragma unroll
+      for (int q = 0; q < XQ; ++q) xv[i][q] = reinterpret_cast<const uint4*>(xs)[XQ * chunk[i] + q];
+    build_xr();
+  }
+  const half2_t ones = half2_t{static_cast<half_t>(1.0f), static_cast<half_t>(1.0f)};
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    float sx = 0.f;
+#pragma unroll
+    for (int q = 0; q < XP; ++q) sx = __builtin_amdgcn_fdot2(xr[i][q], ones, sx, false);
+    xsum[i] = sx;
+  }
+
+  // 4. rows.  Row t sits in register slot t % DEPTH; its codes were requested DEPTH
+  // steps earlier, its staging items two steps earlier into set t % 2, and they were
+  // published into ring slot t % 2 by the barrier closing step t - 1.  Every step
+  // (a) requests the items of step t + 2, (b) computes row t and refills its slot,
+  // (c) stages step t + 1 and closes with the barrier.  The last DEPTH steps run
+  // without code refills, so no load is issued past the end.
   // The row (slice) total ends in lane LPR - 1 of the row's lane group.
   auto keep = [&](int t, int row, float acc) {
     acc = lane_group_sum<LPR>(acc);
@@ -447,6 +484,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   using Last = std::true_type;
   if constexpr (PRE) {
     int t0 = 0;
+    if (early) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) keep(d, my_row, row_finish(d, my_row, pa[d], pb[d]));
+      t0 = DEPTH;
+    }
     for (; t0 + 2 * DEPTH <= steps; t0 += DEPTH) {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) pre_step(t0 + d, d, true);
