@@ -430,6 +430,8 @@ GEMV_SHAPES = [
     ("v3", 11008, 4096, 32, True, 4),     # 32 lanes, 4 chunks each (the act-order layer's shape)
     ("v4", 12296, 2048, 128, False, 8),   # 8-bit: 32 lanes, 4 chunks each
     ("v5", 10248, 8192, 32, False, 4),    # 64 lanes, 6 steps: all scales staged in two rounds
+    ("v6", 4200, 16384, 128, False, 4),   # rows split over two wavefronts, 3 steps: staged once
+    ("v7", 4104, 12288, 64, True, 4),     # split rows, act order, 3 steps: staged once
 ]
 
 

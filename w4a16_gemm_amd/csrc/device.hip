@@ -326,10 +326,15 @@ int launch_gemv_cpl(int cpl, int ept, dim3 grid, size_t shmem, hipStream_t st, c
 }
 
 // Split rows (K > 8192): 64 lanes per row slice, 3 or 4 chunks per lane, whole 8-row
-// staging items (a row has more than 64 groups).
+// staging items (a row has more than 64 groups); ept == 0: every row staged once (PRE).
 template <int WPR, bool EXACT, bool ACT, int BITS>
-int launch_gemv_split(int cpl, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
+int launch_gemv_split(int cpl, int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
                        const uint16_t* s, Zeros z, half_t* y, int N, int K, int gshift, int steps) {
+  if (ept == 0) {
+    if (cpl == 3)
+      return launch_gemv_e<64, 3, EXACT, ACT, 8, WPR, BITS, true>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+    return launch_gemv_e<64, 4, EXACT, ACT, 8, WPR, BITS, true>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+  }
   if (cpl == 3) return launch_gemv_e<64, 3, EXACT, ACT, 8, WPR, BITS>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
   return launch_gemv_e<64, 4, EXACT, ACT, 8, WPR, BITS>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
 }
@@ -340,9 +345,9 @@ int launch_gemv_lpr(const GemvShape& sh, int ept, dim3 grid, size_t shmem, hipSt
                      int gshift, int steps) {
   if (sh.wpr > 1) {
     switch (sh.wpr) {
-      case 2: return launch_gemv_split<2, EXACT, ACT, BITS>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
-      case 4: return launch_gemv_split<4, EXACT, ACT, BITS>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
-      default: return launch_gemv_split<8, EXACT, ACT, BITS>(sh.cpl, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+      case 2: return launch_gemv_split<2, EXACT, ACT, BITS>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+      case 4: return launch_gemv_split<4, EXACT, ACT, BITS>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+      default: return launch_gemv_split<8, EXACT, ACT, BITS>(sh.cpl, ept, grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
     }
   }
   switch (sh.lpr) {
@@ -418,15 +423,18 @@ GemvPlan plan_gemv_for(const GemvShape& sh, int N, int K, int gshift, bool act, 
   }
   p.shmem = gemv_lds_bytes(K, G, unit, p.steps, p.sh.wpr, act);
   p.ok = p.shmem <= kGemvLdsBudget;
-  // Staging every row once (PRE): whole rows, at most two rounds of two 8-row items per
-  // thread, and the table within the LDS budget.  The workgroups own consecutive units,
-  // so as many workgroups as it takes at `steps` units each (whole XCD rounds when there
-  // are enough).
-  if (p.ok && knobs().gemv_pre != 0 && p.sh.wpr == 1 && p.steps >= 2) {
+  // Staging every row once (PRE): at most two rounds of two 8-row items per thread, and
+  // the table within the LDS budget.  The workgroups own consecutive units, so as many
+  // workgroups as it takes at `steps` units each (whole XCD rounds when there are
+  // enough).  Split rows (K > 8192) too, from three steps on: the table holds whole rows,
+  // each slice reads its groups.  Same-process A/B against the per-step ring: N = 8192 at
+  // K = 12288, group 64 (4 steps) 12.60 -> 11.66 us, K = 16384 / 28672 (4 steps) -0.5%,
+  // but N = 4096, K = 14336 (2 steps) 8.94 -> 9.25 us.
+  if (p.ok && knobs().gemv_pre != 0 && p.steps >= (p.sh.wpr > 1 ? 3 : 2)) {
     int blocks = (units + p.steps - 1) / p.steps;
     if (blocks >= 8) blocks += (8 - blocks % 8) % 8;
     const long long items = static_cast<long long>(p.steps) * (unit / 8) * G;
-    const size_t shmem = gemv_lds_bytes(K, G, unit, p.steps, 1, act, true);
+    const size_t shmem = gemv_lds_bytes(K, G, unit, p.steps, p.sh.wpr, act, true);
     if (items <= 4LL * kGemvWaves * 64 && shmem <= kGemvLdsBudget) {
       p.blocks = blocks;
       p.ept = 0;

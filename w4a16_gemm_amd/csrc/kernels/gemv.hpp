@@ -88,7 +88,7 @@ __device__ __forceinline__ float lane_group_sum(float v) {
 // 8) 1 and 3 as subnormals q * 2^-24 (q < 256 fits the mantissa), both accumulated
 // with weight 1, and the zero points are bytes.
 //
-// PRE (one row per wavefront row-slot, WPR = 1): the workgroup owns `steps`
+// PRE (whole rows, or WPR slices of each): the workgroup owns `steps`
 // consecutive units instead of every nblk-th one, and stages the (S * 2^24, -Z * S)
 // pairs of all its rows once, before the first row: for every group the scales of its
 // rows are one contiguous run, so the whole grid reads the scale and zero-point arrays
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   static_assert(WPR == 1 || (LPR == 64 && WAVES % WPR == 0 && WPR % DEPTH == 0),
                 "split rows: one row per wavefront, whole register slots per step");
   static_assert(BITS == 4 || BITS == 8, "4- or 8-bit weights");
-  static_assert(!PRE || (WPR == 1 && EPT == 8), "staging once: whole rows, 8-row items");
+  static_assert(!PRE || EPT == 8, "staging once: 8-row items");
   constexpr int CSH = BITS == 4 ? 5 : 4;   // log2 channels per 16-byte chunk
   constexpr int XQ = 1 << (CSH - 3);       // 16-byte pieces of activations per chunk
   constexpr int XP = 4 * XQ;               // activation pairs per chunk
@@ -138,7 +138,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   const int my_row = unit_row(0);
   // PRE: units blk * steps + t.
   auto row_of = [&](int seq) {
-    return PRE ? (blk * steps + seq) * STRIDE + my_row : (blk + (seq / WPR) * nblk) * STRIDE + unit_row(seq % WPR);
+    return PRE ? (blk * steps + seq / WPR) * STRIDE + unit_row(seq % WPR)
+               : (blk + (seq / WPR) * nblk) * STRIDE + unit_row(seq % WPR);
   };
 
   // PRE: the ring is the table of all the workgroup's rows, [steps][STRIDE][GP].
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   float pa[DEPTH][CPL], pb[DEPTH][CPL];
   bool early = false;
   if constexpr (PRE && !ACT) {
-    early = (flags & 1) != 0 && steps >= 2 * DEPTH;
+    early = (flags & 1) != 0 && steps * WPR >= 2 * DEPTH;
     if (early) {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) {
@@ -471,34 +472,40 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
     put_item(p ^ 1, p ^ 1);
     __syncthreads();
   };
-  // PRE: row t's pairs are row t of the table; no staging and no barrier per step.
-  auto pre_step = [&](int t, int d, bool refill) {
-    const float acc = row_step(t, my_row, wb[d]);
-    if (refill) load_row(wb[d], row_of(t + DEPTH));
+  // PRE: the wavefront's seq-th row (slice) is row unit_row(seq % WPR) of step seq / WPR,
+  // whose pairs are that row of the table; no staging and no barrier per step.
+  auto pre_step = [&](int seq, int d, bool refill) {
+    const int t = seq / WPR, row = unit_row(seq % WPR);
+    const float acc = row_step(t, row, wb[d]);
+    if (refill) load_row(wb[d], row_of(seq + DEPTH));
     __builtin_amdgcn_sched_barrier(0);
-    keep(t, my_row, acc);
+    keep(t, row, acc);
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using More = std::false_type;
   using Last = std::true_type;
   if constexpr (PRE) {
+    const int total = steps * WPR;   // rows (slices) of this wavefront
     int t0 = 0;
     if (early) {
 #pragma unroll
-      for (int d = 0; d < DEPTH; ++d) keep(d, my_row, row_finish(d, my_row, pa[d], pb[d]));
+      for (int d = 0; d < DEPTH; ++d) {
+        const int t = d / WPR, row = unit_row(d % WPR);
+        keep(t, row, row_finish(t, row, pa[d], pb[d]));
+      }
       t0 = DEPTH;
     }
-    for (; t0 + 2 * DEPTH <= steps; t0 += DEPTH) {
+    for (; t0 + 2 * DEPTH <= total; t0 += DEPTH) {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) pre_step(t0 + d, d, true);
     }
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d)
-      if (t0 + d < steps) pre_step(t0 + d, d, t0 + d + DEPTH < steps);
+      if (t0 + d < total) pre_step(t0 + d, d, t0 + d + DEPTH < total);
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d)
-      if (t0 + DEPTH + d < steps) pre_step(t0 + DEPTH + d, d, false);
+      if (t0 + DEPTH + d < total) pre_step(t0 + DEPTH + d, d, false);
     __syncthreads();   // every row result is in LDS
   } else if constexpr (WPR > 1) {
     int t = 0;
