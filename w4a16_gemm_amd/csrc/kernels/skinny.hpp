@@ -170,10 +170,30 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
     }
   }
 
-  // Scale and zero word of slab entries tid + u * nthreads of row block b.
-  half_t sv[SE];
-  uint32_t zv[SE];
+  // Scale and zero word of slab entries tid + u * nthreads of row block b.  SE >= 2
+  // (many groups: group size 32 or 64 at large K) stages whole 8-row items instead: item
+  // it = (group it / 2, rows 8 (it % 2) .. +8 of the block), its 8 scales one 16-byte load
+  // and its 8 zero points one word (8-bit: two), at most one item per thread (2 G <= SE
+  // nthreads / 8); the slab entries are the same.
+  constexpr bool kItems = SE >= 2;
+  half_t sv[kItems ? 1 : SE];
+  uint32_t zv[kItems ? 1 : SE];
+  uint4 iv_s;
+  uint2 iv_z;
+  const int items = 2 * G;
+  auto item_n0 = [&](int b, int it) { return min(16 * b + 8 * (it & 1), N - 8); };   // N % 8 == 0
   auto load_sz = [&](int b) {
+    if constexpr (kItems) {
+      const int it = min(tid, items - 1);
+      const int gi = g0 + (it >> 1);
+      const int n0 = item_n0(b, it);
+      iv_s = *reinterpret_cast<const uint4*>(scales + static_cast<size_t>(gi) * N + n0);
+      if constexpr (BITS == 4)
+        iv_z.x = *qzeros.at(static_cast<size_t>(gi) * (N >> 3) + (n0 >> 3));
+      else
+        iv_z = *reinterpret_cast<const uint2*>(qzeros.at(static_cast<size_t>(gi) * (N >> 2) + (n0 >> 2)));
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < SE; ++u) {
       const int e = min(tid + u * nthreads, slab_n - 1);
@@ -187,6 +207,30 @@ __global__ __launch_bounds__(1024) void gemm_skinny_kernel(
     }
   };
   auto write_slab = [&](int b, int buf) {
+    if constexpr (kItems) {
+      if (tid < items) {
+        const int gi = tid >> 1, r0 = 8 * (tid & 1);
+        const uint32_t s8[4] = {iv_s.x, iv_s.y, iv_s.z, iv_s.w};
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const half_t S = __builtin_bit_cast(half_t, static_cast<uint16_t>((s8[r >> 1] >> (16 * (r & 1))) & 0xFFFFu));
+          uint32_t z;
+          if constexpr (BITS == 4) {
+            z = (qzeros.word(iv_z.x) >> (4 * r)) & 0xFu;
+          } else {
+            z = (qzeros.word8(r < 4 ? iv_z.x : iv_z.y) >> (8 * (r & 3))) & 0xFFu;
+          }
+          uint2* dst = slab + buf * slab_n + gi * 16 + r0 + r;
+          if constexpr (SUB) {
+            const float Sf = static_cast<float>(S);
+            *dst = __builtin_bit_cast(uint2, make_float2(Sf * 16777216.0f, -static_cast<float>(z) * Sf));
+          } else {
+            *dst = slab_entry(S, z);
+          }
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < SE; ++u) {
       const int e = tid + u * nthreads;
