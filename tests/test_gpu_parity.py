@@ -463,6 +463,27 @@ def test_gemv_row_shapes_match_oracle(case):
         clear_knob("W4A16_TUNE_GEMV_LPR", "W4A16_TUNE_GEMV_PRE")
 
 
+def test_gemv_compact_table_matches_the_ring():
+    """Group 32 on a layer whose staged-once table of float pairs would not fit in LDS
+    (K = 8192, 16392 rows: 9 steps per workgroup): the compact table of binary16 scales and
+    zero points gives the same pairs, so the same bits as the per-step ring, and sampled
+    rows (the last ones included) within the bar of the oracle."""
+    cfg = wl.custom_config("ct1", 790, K=8192, N=16392, group_size=32, M_list=(1,))
+    note(f"compact table N={cfg.N} K={cfg.K} g=32")
+    prod = product_layer(cfg, 1)
+    rows = np.unique(np.concatenate([sample_rows(cfg.N, 48), np.arange(cfg.N - 16, cfg.N)]))
+    ref = oracle_layer(cfg, 1, rows)
+    try:
+        outs = []
+        for pre in ("1", "2"):   # compact table, then the ring (2: no compact table)
+            set_knob("W4A16_TUNE_GEMV_PRE", pre)
+            outs.append(run_gemm(prod).cpu().numpy())
+    finally:
+        clear_knob("W4A16_TUNE_GEMV_PRE")
+    assert np.array_equal(outs[0].view(np.uint16), outs[1].view(np.uint16))
+    assert oracle.rel_err(outs[0][:, rows], ref["y_ref"]) <= TOL
+
+
 def _runtime_libraries():
     """The HIP runtime libraries mapped into this process (torch's and the library's)."""
     import ctypes

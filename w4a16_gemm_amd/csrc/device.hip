@@ -50,7 +50,7 @@ struct Knobs {
   Path force_path = Path::kAuto;   // W4A16_FORCE_PATH=gemv|gemm
   int gemv_lpr = 0;             // W4A16_TUNE_GEMV_LPR: lanes per row of the GEMV
   int gemv_blocks_per_cu = 1;   // W4A16_TUNE_GEMV_BLOCKS_PER_CU
-  int gemv_pre = 1;             // W4A16_TUNE_GEMV_PRE: stage all scales once (0 never, 1 when it fits)
+  int gemv_pre = 1;             // W4A16_TUNE_GEMV_PRE: stage all scales once (0 never, 1 when it fits, 2 not compact)
   int gemv_early = 1;           // W4A16_TUNE_GEMV_EARLY: first rows' dot products before the staging barrier
   int gemm_prio = 1;            // W4A16_TUNE_GEMM_PRIO: wavefront priority in the large tiles
   int gemm_mfma32 = 1;          // W4A16_TUNE_GEMM_MFMA32: 32x32 blocks (0 never, 1 small tiles, 2 all)
@@ -285,10 +285,10 @@ int device_cus() {
 // Register-pipeline depth: about 8 KB of codes in flight per wavefront.
 constexpr int gemv_depth(int cpl) { return cpl >= 3 ? 2 : 8 / cpl; }
 
-template <int LPR, int CPL, bool EXACT, bool ACT, int EPT, int WPR, int BITS, bool PRE = false>
+template <int LPR, int CPL, bool EXACT, bool ACT, int EPT, int WPR, int BITS, bool PRE = false, bool CT = false>
 int launch_gemv_e(dim3 grid, size_t shmem, hipStream_t st, const half_t* x, const uint32_t* qw,
                    const uint16_t* s, Zeros z, half_t* y, int N, int K, int gshift, int steps) {
-  auto kern = gemv_m1_kernel<LPR, CPL, kGemvWaves, gemv_depth(CPL), EXACT, ACT, EPT, WPR, BITS, PRE>;
+  auto kern = gemv_m1_kernel<LPR, CPL, kGemvWaves, gemv_depth(CPL), EXACT, ACT, EPT, WPR, BITS, PRE, CT>;
   // Dynamic LDS above 64 KB has to be allowed per kernel (once per process).
   static const hipError_t lds_ok = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -308,6 +308,10 @@ int launch_gemv_t(int ept, dim3 grid, size_t shmem, hipStream_t st, const half_t
                    const uint16_t* s, Zeros z, half_t* y, int N, int K, int gshift, int steps) {
   if (ept == 0)
     return launch_gemv_e<LPR, CPL, EXACT, ACT, 8, 1, BITS, true>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
+  if constexpr (CPL == 4 && EXACT && BITS == 4 && (LPR == 64 || LPR == 32))
+    if (ept == -1)
+      return launch_gemv_e<LPR, CPL, EXACT, ACT, 8, 1, BITS, true, true>(grid, shmem, st, x, qw, s, z, y, N, K, gshift,
+                                                                         steps);
   if constexpr (EXACT && !ACT)
     if (ept == 1)
       return launch_gemv_e<LPR, CPL, EXACT, ACT, 1, 1, BITS>(grid, shmem, st, x, qw, s, z, y, N, K, gshift, steps);
@@ -361,8 +365,8 @@ int launch_gemv_lpr(const GemvShape& sh, int ept, dim3 grid, size_t shmem, hipSt
 // LDS of one workgroup: the two-slot scale/zero ring (unit rows x (G+1) float2 each),
 // the row (slice) results, and the gathered activations under act order.
 // pre: the table of all the workgroup's rows instead of the ring.
-size_t gemv_lds_bytes(int K, int G, int unit, int steps, int wpr, bool act, bool pre = false) {
-  return (pre ? steps : 2) * static_cast<size_t>(unit) * (G + 1) * 2 * sizeof(float) +
+size_t gemv_lds_bytes(int K, int G, int unit, int steps, int wpr, bool act, bool pre = false, bool ct = false) {
+  return (pre ? steps : 2) * static_cast<size_t>(unit) * (G + 1) * (ct ? 1 : 2) * sizeof(float) +
          static_cast<size_t>(steps) * unit * wpr * sizeof(float) + (act ? static_cast<size_t>(K) * sizeof(half_t) : 0);
 }
 
@@ -371,7 +375,7 @@ size_t gemv_lds_bytes(int K, int G, int unit, int steps, int wpr, bool act, bool
 struct GemvPlan {
   bool ok = false;
   GemvShape sh;
-  int blocks = 0, steps = 0, ept = 8;   // ept 0: every row staged once (PRE)
+  int blocks = 0, steps = 0, ept = 8;   // ept 0: every row staged once (PRE); -1: PRE, compact table
   size_t shmem = 0;
 };
 
@@ -435,10 +439,18 @@ GemvPlan plan_gemv_for(const GemvShape& sh, int N, int K, int gshift, bool act, 
     if (blocks >= 8) blocks += (8 - blocks % 8) % 8;
     const long long items = static_cast<long long>(p.steps) * (unit / 8) * G;
     const size_t shmem = gemv_lds_bytes(K, G, unit, p.steps, p.sh.wpr, act, true);
+    const size_t shmem_ct = gemv_lds_bytes(K, G, unit, p.steps, p.sh.wpr, act, true, true);
+    const bool ct_ok = p.sh.wpr == 1 && p.sh.cpl == 4 && p.sh.exact && bits == 4 &&
+                       (p.sh.lpr == 64 || p.sh.lpr == 32) && knobs().gemv_pre != 2;
     if (items <= 4LL * kGemvWaves * 64 && shmem <= kGemvLdsBudget) {
       p.blocks = blocks;
       p.ept = 0;
       p.shmem = shmem;
+    } else if (ct_ok && items <= 8LL * kGemvWaves * 64 && shmem_ct <= kGemvLdsBudget) {
+      // many groups (group 32 on large layers): the compact table, two rounds of four items
+      p.blocks = blocks;
+      p.ept = -1;
+      p.shmem = shmem_ct;
     }
   }
   return p;

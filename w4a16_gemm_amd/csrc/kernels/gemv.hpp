@@ -98,8 +98,11 @@ __device__ __forceinline__ float lane_group_sum(float v) {
 // steps (flags bit 0), the dot products of the first DEPTH rows are taken before the
 // staging barrier and their register slots refilled at once; their scaling follows the
 // barrier (the same operations in the same order, so the same bits).
+// CT (with PRE): the table holds each pair as a 32-bit entry, binary16 S and the zero point
+// above it, converted to (S * 2^24, -Z * S) when a row is scaled (the same fp32 values), so
+// that tables of many groups (group size 32 on large layers) fit in LDS.
 template <int LPR, int CPL, int WAVES, int DEPTH, bool EXACT, bool ACT, int EPT, int WPR, int BITS = 4,
-          bool PRE = false>
+          bool PRE = false, bool CT = false>
 __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
     const half_t* __restrict__ x, const uint32_t* __restrict__ qw, const uint16_t* __restrict__ scales,
     Zeros qzeros, half_t* __restrict__ y, int N, int K, int gshift, int steps, int flags) {
@@ -109,6 +112,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
                 "split rows: one row per wavefront, whole register slots per step");
   static_assert(BITS == 4 || BITS == 8, "4- or 8-bit weights");
   static_assert(!PRE || EPT == 8, "staging once: 8-row items");
+  static_assert(!CT || (PRE && BITS == 4), "the compact table: staging once, 4-bit zero points");
   constexpr int CSH = BITS == 4 ? 5 : 4;   // log2 channels per 16-byte chunk
   constexpr int XQ = 1 << (CSH - 3);       // 16-byte pieces of activations per chunk
   constexpr int XP = 4 * XQ;               // activation pairs per chunk
@@ -144,7 +148,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
 
   // PRE: the ring is the table of all the workgroup's rows, [steps][STRIDE][GP].
   float2* ring = reinterpret_cast<float2*>(smem);                                   // [2][STRIDE][GP]
-  float* ybuf = reinterpret_cast<float*>(smem + (PRE ? steps : 2) * static_cast<size_t>(STRIDE) * GP * sizeof(float2));
+  uint32_t* ringc = reinterpret_cast<uint32_t*>(smem);                              // CT: [steps][STRIDE][GP]
+  float* ybuf = reinterpret_cast<float*>(smem + (PRE ? steps : 2) * static_cast<size_t>(STRIDE) * GP *
+                                                    (CT ? sizeof(uint32_t) : sizeof(float2)));
   half_t* xs = reinterpret_cast<half_t*>(ybuf + static_cast<size_t>(steps) * STRIDE * WPR);
 
   // This lane's chunks (clamped into its slice and the row unless the split is exact)
@@ -250,7 +256,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
   // neighbouring threads read neighbouring 16-byte pieces of one group's run of scales;
   // kPreBatch items per thread and round (the host allows at most two rounds), loads
   // clamped into the items so that every thread issues the same loads.
-  constexpr int kPreBatch = 2;
+  constexpr int kPreBatch = CT ? 4 : 2;
   const int pre_octs = steps * OCT;
   const int pre_items = PRE ? pre_octs * G : 0;
   const int pre_r0 = blk * steps * STRIDE;
@@ -278,6 +284,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
         const uint32_t s8[4] = {ps[u].x, ps[u].y, ps[u].z, ps[u].w};
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
+          if constexpr (CT) {
+            ringc[(8 * o + r) * GP + g] = ((s8[r >> 1] >> (16 * (r & 1))) & 0xFFFFu) |
+                                          (((qzeros.word(pz[u]) >> (4 * r)) & 0xFu) << 16);
+            continue;
+          }
           const float S = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>((s8[r >> 1] >> (16 * (r & 1))) & 0xFFFFu)));
           float Z;
           if constexpr (BITS == 4) {
@@ -370,10 +381,21 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_m1_kernel(
     }
   };
   auto row_finish = [&](int slot, int row, const float (&aa)[CPL], const float (&ab)[CPL]) {
-    const float2* szr = ring + (slot * STRIDE + row) * GP;
     float2 sc[CPL];
+    if constexpr (CT) {
+      const uint32_t* szr = ringc + (slot * STRIDE + row) * GP;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) sc[i] = szr[gcol[i]];
+      for (int i = 0; i < CPL; ++i) {
+        const uint32_t e = szr[gcol[i]];
+        const float S = static_cast<float>(__builtin_bit_cast(half_t, static_cast<uint16_t>(e & 0xFFFFu)));
+        const float Z = static_cast<float>(e >> 16);
+        sc[i] = make_float2(S * 16777216.0f, -Z * S);   // the pairs of the float table, exactly
+      }
+    } else {
+      const float2* szr = ring + (slot * STRIDE + row) * GP;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) sc[i] = szr[gcol[i]];
+    }
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
