@@ -433,8 +433,9 @@ GemvPlan plan_gemv_for(const GemvShape& sh, int N, int K, int gshift, bool act, 
   // enough).  Split rows (K > 8192) too, from three steps on: the table holds whole rows,
   // each slice reads its groups.  Same-process A/B against the per-step ring: N = 8192 at
   // K = 12288, group 64 (4 steps) 12.60 -> 11.66 us, K = 16384 / 28672 (4 steps) -0.5%,
-  // but N = 4096, K = 14336 (2 steps) 8.94 -> 9.25 us.
-  if (p.ok && knobs().gemv_pre != 0 && p.steps >= (p.sh.wpr > 1 ? 3 : 2)) {
+  // but N = 4096, K = 14336 (2 steps) 8.94 -> 9.25 us; 8-bit split rows (K = 8192, N = 28672,
+  // 14 steps) 36.08 -> 37.73 us, so those keep the ring.
+  if (p.ok && knobs().gemv_pre != 0 && p.steps >= (p.sh.wpr > 1 ? 3 : 2) && (p.sh.wpr == 1 || bits == 4)) {
     int blocks = (units + p.steps - 1) / p.steps;
     if (blocks >= 8) blocks += (8 - blocks % 8) % 8;
     const long long items = static_cast<long long>(p.steps) * (unit / 8) * G;
